@@ -1,0 +1,371 @@
+"""Pins of the fp64 reference against facts fixed outside its own code.
+
+Each test names what it pins.  None of them re-types the reference's formula
+and compares it with itself: the expected values come from closed forms worked
+by hand, exact rational arithmetic, invariants of the model (adjoint,
+linearity, partition of unity, symmetry), the physics of a voxel's projection,
+or limits where one geometry reduces to another.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+
+def geom_dict(kind=W.PARALLEL, angles=(0.0,), shift=None, zsrc=None, dch=1.0, drow=1.0,
+              sid=0.0, sdd=0.0, radius=1, ch_off=0.0, row_off=0.0, dv=1.0):
+    return dict(kind=kind, num_views=len(angles), angles=np.asarray(angles, np.float64),
+                channel_shift=None if shift is None else np.asarray(shift, np.float64),
+                source_z=None if zsrc is None else np.asarray(zsrc, np.float64),
+                delta_voxel=dv, delta_channel=dch, delta_row=drow, source_iso=sid,
+                source_detector=sdd, det_channel_offset=ch_off, det_row_offset=row_off,
+                psf_radius=radius)
+
+
+def make(orc, w: W.Workload):
+    return orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+
+
+def adjoint_gap(orc, g, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(g.recon_shape).astype(np.float32)
+    y = rng.standard_normal(g.sino_shape).astype(np.float32)
+    ax = orc.forward(g, x)
+    aty = orc.back(g, y)
+    lhs = float((ax * y.astype(np.float64)).sum())
+    rhs = float((x.astype(np.float64) * aty).sum())
+    return abs(lhs - rhs) / (np.linalg.norm(ax) * np.linalg.norm(y))
+
+
+SMALL_CONE = W.Workload("cone-24x20x12-17v", W.CONE_FLAT, 24, 20, 12, 17, 16, 30,
+                        dch=1.5, drow=1.5, sid=60.0, sdd=90.0, seed_x=7, seed_y=8)
+SMALL_HELIX = W.Workload("helical-20x20x10-23v", W.CONE_FLAT, 20, 20, 10, 23, 8, 28,
+                         dch=11 / 6, drow=11 / 6, sid=30.0, sdd=55.0,
+                         angle_step=2 * math.pi / 10, zsrc_step=0.4, seed_x=9, seed_y=10)
+SMALL_TRANS = W.Workload("translation-16x24x4-9v", W.PARALLEL, 16, 24, 4, 9, 4, 64,
+                         shift_step=3.0, seed_x=11, seed_y=12)
+
+
+# --------------------------------------------------------------------- ov ---
+def test_ov_closed_form_values(orc):
+    """The overlap of a unit cell with a centred box, at hand-worked points."""
+    assert orc.ov(0.0, 1.0) == 1.0
+    assert orc.ov(1.0, 1.0) == 0.0
+    assert orc.ov(0.5, 1.0) == 0.5
+    assert orc.ov(0.25, 0.5) == 0.25 + 0.25 - 0.25 + 0.25  # cell [-.25,.75] vs box [-.25,.25]
+    assert orc.ov(0.0, 3.0) == 1.0                    # box wider than the cell
+    assert orc.ov(1.25, 3.0) == pytest.approx(0.75, abs=0)
+    assert orc.ov(-2.0, 3.0) == 0.0
+
+
+@pytest.mark.parametrize("a", [0.3, 0.70710678, 1.0, 1.37, 1.99])
+def test_ov_partition_of_unity(orc, a):
+    """Sum over integer shifts equals the box width (partition of unity)."""
+    rng = np.random.default_rng(3)
+    for u in rng.uniform(-3, 3, 50):
+        s = sum(orc.ov(n - u, a) for n in range(-8, 9))
+        assert abs(s - a) < 1e-14
+
+
+def test_ov_matches_quadrature(orc):
+    """B2: numerical integral of the box over each cell, Q = 1e4 midpoints."""
+    q = 10_000
+    rng = np.random.default_rng(5)
+    for _ in range(40):
+        d, a = rng.uniform(-1.6, 1.6), rng.uniform(0.2, 2.5)
+        t = (np.arange(q) + 0.5) / q - 0.5 + d            # sample points of the cell
+        quad = np.mean(np.abs(t) <= a / 2)
+        assert abs(orc.ov(d, a) - quad) <= 2.0 / q
+
+
+# ----------------------------------------------------------- single voxel ---
+def one_voxel(orc, theta, u_off, radius=1, nc=11):
+    """A 1x1x1 recon with its centre projecting to channel (nc-1)/2 + u_off."""
+    g = orc.Geometry(geom_dict(angles=[theta], shift=[u_off], radius=radius), (1, 1, 1), (1, 1, nc))
+    return g, orc.forward(g, np.ones((1, 1, 1), np.float32))[0, 0]
+
+
+def test_single_voxel_axis_aligned(orc):
+    """P4: at theta = 0 a unit voxel whose centre falls on a channel centre
+    puts exactly dv into that channel and nothing elsewhere."""
+    for theta in (0.0, math.pi):
+        _, y = one_voxel(orc, theta, 0.0)
+        assert y[5] == 1.0 and np.count_nonzero(y) == 1
+    # the small disk workload: u = j + 16 at theta = 0, for every pixel
+    w = W.get(W.SMALL)
+    g = make(orc, w)
+    x = np.zeros(w.recon_shape, np.float32)
+    x[10, 37, 3] = 1.0
+    y = orc.forward(g, x)
+    assert y[0, 3, 37 + 16] == 1.0 and np.count_nonzero(y[0]) == 1
+
+
+@pytest.mark.parametrize("d,expect", [
+    (0.0, {5: 1.0}),
+    (-0.5, {5: 0.5, 4: 0.5}),        # u = 4.5 rounds (ties to even) to 4
+    (0.5, {5: 0.5, 6: 0.5}),         # u = 5.5 rounds to 6
+    (-0.25, {5: 0.5 + math.sqrt(2) / 4, 4: 0.5 - math.sqrt(2) / 4}),
+    (0.25, {5: 0.5 + math.sqrt(2) / 4, 6: 0.5 - math.sqrt(2) / 4}),
+])
+def test_single_voxel_45_degrees(orc, d, expect):
+    """P4: at 45 degrees the box has width 1/sqrt2 and height sqrt2; the cell
+    overlaps worked by hand give these tap weights."""
+    _, y = one_voxel(orc, math.pi / 4, d)
+    got = {n: y[n] for n in np.nonzero(y)[0]}
+    assert set(got) == set(expect)
+    for n, v in expect.items():
+        assert abs(got[n] - v) < 1e-15
+
+
+def test_tap_count_bounded_by_footprint(orc):
+    """With W <= 1 at most two adjacent channels receive weight; the chosen
+    channel n_c = rint(u) always carries weight."""
+    w = W.get(W.BENCH)
+    g = make(orc, w)
+    rng = np.random.default_rng(0)
+    for v, i, j in zip(rng.integers(0, w.nv, 200), rng.integers(0, w.ny, 200), rng.integers(0, w.nx, 200)):
+        taps = orc.voxel_taps(g, int(v), int(i), int(j), 0)
+        chans = sorted(t[1] for t in taps)
+        assert 1 <= len(chans) <= 2 and chans == list(range(chans[0], chans[0] + len(chans)))
+        nc = orc.vp_params(g, int(v), int(i), int(j))["nc"]
+        assert nc in chans
+
+
+# ----------------------------------------------------------------- adjoint ---
+@pytest.mark.parametrize("w", [W.get(W.SMALL), SMALL_CONE, SMALL_HELIX, SMALL_TRANS],
+                         ids=lambda w: w.name)
+def test_adjoint_identity(orc, w):
+    """P1: <Ax, y> = <x, A^T y> for the matched pair."""
+    assert adjoint_gap(orc, make(orc, w), seed=11) < 1e-12
+
+
+@pytest.mark.parametrize("w", [W.get(W.SMALL), SMALL_CONE], ids=lambda w: w.name)
+def test_linearity(orc, w):
+    """P2: A(alpha x + beta z) = alpha A x + beta A z (no hidden state)."""
+    g = make(orc, w)
+    rng = np.random.default_rng(4)
+    # values on a 1/16 grid, so the combination is exact in fp32
+    x = (rng.integers(-64, 64, w.recon_shape) / 16.0).astype(np.float32)
+    z = (rng.integers(-64, 64, w.recon_shape) / 16.0).astype(np.float32)
+    comb = (2.0 * x.astype(np.float64) - 3.0 * z.astype(np.float64))
+    assert np.array_equal(comb.astype(np.float32).astype(np.float64), comb)  # exact in fp32
+    lhs = orc.forward(g, comb.astype(np.float32))
+    rhs = 2.0 * orc.forward(g, x) - 3.0 * orc.forward(g, z)
+    assert np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs) < 1e-13
+
+
+# -------------------------------------------------------------------- mass ---
+def test_parallel_mass_per_view_and_row(orc):
+    """P3: every view of a parallel projection carries mass dv^2/dch times the
+    slice's sum, when every tap lands on the detector (small disk workload:
+    projected half-diagonal 45.3 < 47.5)."""
+    w = W.get(W.SMALL)
+    g = make(orc, w)
+    x = w.recon_input()
+    y = orc.forward(g, x)
+    slice_sum = x.astype(np.float64).sum(axis=(0, 1))
+    assert np.allclose(y.sum(axis=2), slice_sum[None, :], rtol=1e-13, atol=0)
+
+
+@pytest.mark.slow
+def test_parallel_mass_full_size_sampled_views(orc):
+    """P3 at the 512x512x64, 720-view size: projected half-diagonal
+    362 < 383.5, so each view's mass equals the slice sum."""
+    w = W.get(W.BENCH)
+    g = make(orc, w)
+    rng = np.random.default_rng(2)
+    x = rng.random(w.recon_shape).astype(np.float32)
+    views = [0, 77, 180, 359, 540, 719]
+    y = orc.forward_views(g, x, views)
+    slice_sum = x.astype(np.float64).sum(axis=(0, 1))
+    assert np.allclose(y.sum(axis=2), slice_sum[None, :], rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("w", [W.get("cone-256x256x256-360v"), SMALL_CONE],
+                         ids=lambda w: w.name)
+def test_cone_voxel_mass_is_physical(orc, w):
+    """P3 (cone): the detector integral of one voxel's cell-averaged line
+    integrals equals the physical value dv^3 (SDD/D)^2 / cos(incidence), with
+    cos(incidence) the ray's direction cosine on the detector normal.  The
+    expected value is computed from the source/voxel/detector positions, not
+    from the footprint formulas."""
+    g = make(orc, w)
+    rng = np.random.default_rng(9)
+    ang = w.angles()
+    zs = w.source_z()
+    for _ in range(60):
+        v, i, j = int(rng.integers(w.nv)), int(rng.integers(w.ny)), int(rng.integers(w.nx))
+        k = int(rng.integers(w.ns))
+        taps = orc.voxel_taps(g, v, i, j, k)
+        if not taps:
+            continue
+        rows = [t[0] for t in taps]
+        chans = [t[1] for t in taps]
+        if min(rows) == 0 or max(rows) == w.nr - 1 or min(chans) == 0 or max(chans) == w.nc - 1:
+            continue                          # tap possibly cut by the detector edge
+        total = sum(t[2] for t in taps) * w.dch * w.drow
+        # physics: source S, voxel P, detector normal e_b
+        th = ang[v]
+        e_a = np.array([math.cos(th), math.sin(th), 0.0])
+        e_b = np.array([-math.sin(th), math.cos(th), 0.0])
+        zsrc = 0.0 if zs is None else zs[v]
+        src = -w.sid * e_b + np.array([0, 0, zsrc])
+        p = np.array([j - (w.nx - 1) / 2, i - (w.ny - 1) / 2, k - (w.ns - 1) / 2])
+        ray = p - src
+        dist_plane = float(ray @ e_b)                   # D: source to voxel along the normal
+        cos_inc = dist_plane / np.linalg.norm(ray)
+        expect = (w.sdd / dist_plane) ** 2 / cos_inc
+        assert abs(total - expect) < 1e-12 * expect
+
+
+# --------------------------------------------------------- cone -> parallel ---
+def test_cone_reduces_to_parallel(orc):
+    """P7: a cone with its source 1e9 voxels away, unit pitches and R = S is
+    the parallel projector."""
+    base = W.get(W.SMALL)
+    par = make(orc, base)
+    cone = orc.Geometry(geom_dict(kind=W.CONE_FLAT, angles=base.angles(), sid=1e9, sdd=1e9),
+                        base.recon_shape, base.sino_shape)
+    x = base.recon_input()
+    yp, yc = orc.forward(par, x), orc.forward(cone, x)
+    assert np.linalg.norm(yp - yc) / np.linalg.norm(yp) < 1e-6
+    rng = np.random.default_rng(1)
+    s = rng.standard_normal(base.sino_shape).astype(np.float32)
+    bp, bc = orc.back(par, s), orc.back(cone, s)
+    assert np.linalg.norm(bp - bc) / np.linalg.norm(bp) < 1e-6
+
+
+def _box_cell_quadrature(d, a, q=20000):
+    """Overlap of the unit cell centred at d with the box [-a/2, a/2], by
+    midpoint quadrature (independent of the reference's closed form)."""
+    t = (np.arange(q) + 0.5) / q - 0.5 + d
+    return float(np.mean(np.abs(t) <= a / 2))
+
+
+@pytest.mark.parametrize("w", [W.get("cone-256x256x256-360v"), SMALL_HELIX], ids=lambda w: w.name)
+def test_cone_rows_follow_perspective(orc, w):
+    """The row profile of a voxel is its magnified height (SDD/D * dv) centred
+    on the perspective projection of its centre onto the flat detector.  Row
+    centre and width come from the source/voxel positions; the cell overlaps
+    from quadrature.  Since the centre moves by SDD/D * dv per slice, this also
+    pins the row as an affine function of the slice index."""
+    g = make(orc, w)
+    rng = np.random.default_rng(21)
+    ang, zs = w.angles(), w.source_z()
+    checked = 0
+    for _ in range(200):
+        v, i, j, k = (int(rng.integers(n)) for n in (w.nv, w.ny, w.nx, w.ns))
+        taps = orc.voxel_taps(g, v, i, j, k)
+        if not taps or min(t[0] for t in taps) == 0 or max(t[0] for t in taps) == w.nr - 1:
+            continue
+        th = ang[v]
+        e_b = np.array([-math.sin(th), math.cos(th)])
+        p = np.array([j - (w.nx - 1) / 2, i - (w.ny - 1) / 2])
+        dplane = w.sid + float(p @ e_b)
+        dz = (k - (w.ns - 1) / 2) - (0.0 if zs is None else zs[v])
+        wrow = w.sdd * w.dv / (dplane * w.drow)
+        if wrow > 2.0:
+            continue                               # three taps do not cover it
+        row_c = (w.nr - 1) / 2 + w.sdd * dz / (dplane * w.drow)
+        tot = sum(t[2] for t in taps)
+        rows = {}
+        for r_, _, wt in taps:
+            rows[r_] = rows.get(r_, 0.0) + wt / tot
+        for r_ in range(min(rows) - 1, max(rows) + 2):
+            expect = _box_cell_quadrature(r_ - row_c, wrow) / wrow
+            assert abs(rows.get(r_, 0.0) - expect) < 3e-4
+        checked += 1
+    assert checked > 50
+
+
+# ---------------------------------------------------------------- symmetry ---
+def test_symmetry_rotation_by_90_degrees(orc):
+    """P9: rotating the image by +90 degrees and the view angle by +pi/2
+    leaves the parallel projection unchanged."""
+    w = W.get(W.SMALL)
+    x = w.recon_input()
+    xr = np.ascontiguousarray(x[::-1].transpose(1, 0, 2))
+    ang = w.angles()[:10]
+    g = orc.Geometry(geom_dict(angles=ang), w.recon_shape, (10, w.nr, w.nc))
+    gr = orc.Geometry(geom_dict(angles=ang + math.pi / 2), w.recon_shape, (10, w.nr, w.nc))
+    a, b = orc.forward(g, x), orc.forward(gr, xr)
+    assert np.abs(a - b).max() < 1e-13 * np.abs(a).max()
+
+
+def test_symmetry_mirror(orc):
+    """P9: mirroring x -> -x and theta -> -theta reverses the channel axis."""
+    w = W.get(W.SMALL)
+    x = w.recon_input()
+    xm = np.ascontiguousarray(x[:, ::-1, :])
+    ang = w.angles()[1:12]
+    g = orc.Geometry(geom_dict(angles=ang), w.recon_shape, (11, w.nr, w.nc))
+    gm = orc.Geometry(geom_dict(angles=-ang), w.recon_shape, (11, w.nr, w.nc))
+    a, b = orc.forward(g, x), orc.forward(gm, xm)
+    assert np.abs(a - b[:, :, ::-1]).max() < 1e-13 * np.abs(a).max()
+
+
+# ------------------------------------------------------------ tie canaries ---
+def _exact_u(xv, yv, c, s, cch):
+    """u of the parallel geometry with every rounding of the stated order
+    carried out in exact rational arithmetic, rounding to double after each
+    operation (the IEEE definition of the fp64 ops)."""
+    xc = float(Fraction(xv) * Fraction(c))
+    ys = float(Fraction(yv) * Fraction(s))
+    t = float(Fraction(xc) + Fraction(ys))
+    return float(Fraction(t) + Fraction(cch))
+
+
+def test_tie_canaries_round_half_to_even(orc):
+    """P10: in the 512x512, 720-view workload the views at 45 and 135 degrees
+    hold 512 pixels each whose channel coordinate is exactly 383.5 (cos and sin
+    of pi/4 differ by one ulp, and the products cancel exactly); rounding half
+    to even sends every one to 384.  A fused multiply-add would move 28 and 21
+    of them off the tie, so these entries also catch FMA contraction."""
+    w = W.get(W.BENCH)
+    g = make(orc, w)
+    idx = orc.channel_index(g)
+    ang = w.angles()
+    coords = (np.arange(512) - 255.5)
+    expected_flips = {180: 28, 540: 21}
+    for v in (180, 540):
+        c, s = math.cos(ang[v]), math.sin(ang[v])
+        img = idx[v].reshape(512, 512)
+        # the anti-diagonal (v=180) / diagonal (v=540) pixels
+        pix = [(i, 511 - i) for i in range(512)] if v == 180 else [(i, i) for i in range(512)]
+        flips = 0
+        for i, j in pix:
+            u = _exact_u(coords[j], coords[i], c, s, 383.5)
+            assert u == 383.5
+            assert img[i, j] == 384
+            # the contracted form: t = fma(x, c, y*s), exact then one rounding
+            ys = float(Fraction(coords[i]) * Fraction(s))
+            t = float(Fraction(coords[j]) * Fraction(c) + Fraction(ys))
+            if round(t + 383.5) != 384:   # python round: half to even
+                flips += 1
+        assert flips == expected_flips[v]
+
+
+def test_tie_canaries_only_in_those_views(orc):
+    """P10: no other view of the small, the 512x512x64 or the translation
+    workloads has a channel coordinate within 1e-9 of a half-integer, except
+    the translation geometry, whose coordinates are exact integers."""
+    for name in (W.SMALL, W.BENCH):
+        w = W.get(name)
+        g = make(orc, w)
+        near = []
+        for v0 in range(0, w.nv, 90):
+            sub = orc.Geometry(dict(w.geometry(), num_views=min(90, w.nv - v0),
+                                    angles=w.angles()[v0:v0 + 90]),
+                               w.recon_shape, (min(90, w.nv - v0), w.nr, w.nc))
+            u = orc.channel_coord(sub)
+            frac = np.abs(u - np.floor(u) - 0.5)
+            vv = np.nonzero((frac < 1e-9).any(axis=1))[0] + v0
+            near.extend(int(v) for v in vv)
+        assert near == ([180, 540] if name == W.BENCH else [])
+    w = W.get("translation-512x512x32-64v")
+    u = orc.channel_coord(make(orc, w))
+    assert np.array_equal(u, np.round(u))
+    assert u.min() == 4.0 and u.max() == 1019.0
