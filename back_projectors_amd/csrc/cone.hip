@@ -1,0 +1,292 @@
+// Flat-detector cone-beam projector pair (circular and helical orbits) on gfx950.
+//
+// In the cone geometry one slice spreads over a band of detector rows, and
+// the row of a voxel is an affine function of its slice index, so a kernel
+// that holds a whole voxel cylinder walks up the slices and recomputes the row
+// as it goes; the taps form a 3x3 block (MBIRJAX "Projector kernels" page,
+// "The cone back kernel: a fused vertical fan"; "Sharding overview" page,
+// "Why cone beam projects whole cylinders").
+//
+// Lanes are pixels (a tile of them per workgroup), each lane walks a chunk of
+// SL slices.  Per (view, pixel) the lane computes, in fp64, the channel
+// taps and the row magnification; per slice it computes the row coordinate
+// w_k = Mr dz_k + c_row (rounded to the tap row exactly as the reference
+// model does, product then sum, no contraction), the row taps and the chord
+// scale L_k.  The sinogram window a tile and slice chunk can reach in one view
+// is staged in LDS (rows fastest); the forward adds into an LDS-private window
+// and flushes it with coalesced global atomics, exactly as the parallel pair.
+#include "launch.h"
+#include "taps.h"
+
+#pragma clang fp contract(off)
+
+namespace bpamd {
+
+// Per (view, pixel) quantities of the flat cone.
+struct ConeVP {
+    double f;      // u - n_c
+    double mr;     // SDD / (d drow): row magnification in rows per voxel unit
+    double wch;    // channel footprint width
+    double lsc;    // dv / M
+    double r2;     // d^2 + a^2 (squared in-plane source distance)
+};
+
+__device__ __forceinline__ ConeVP cone_vp(const Geo &g, const ViewK &vk, double x, double y, int ncv) {
+    ConeVP o;
+    const double xc = x * vk.c, ys = y * vk.s, yc = y * vk.c, xs = x * vk.s;
+    const double a = xc + ys;
+    const double b = yc - xs;
+    const double d = g.sid + b;
+    const double drw = d * g.drow;
+    o.mr = g.sdd / drw;
+    const double mc = g.sdd / (d * g.dch);
+    o.f = (mc * a + g.cch + vk.shift) - (double)ncv;
+    const double mm = fmax(fabs(y + vk.c * g.sid), fabs(vk.s * g.sid - x));
+    o.wch = mc * g.dv * mm / d;
+    o.lsc = g.dv / mm;
+    o.r2 = d * d + a * a;
+    return o;
+}
+
+template <int SL, int R>
+__global__ __launch_bounds__(BT *BT) void cone_back_kernel(const float *__restrict__ sino,
+                                                            float *__restrict__ recon,
+                                                            const int32_t *__restrict__ idx,
+                                                            const ViewK *__restrict__ views, Geo g, int nrp) {
+    constexpr int NT = BT * BT;
+    constexpr int NTAP = 2 * R + 1;
+    extern __shared__ float win[];        // [nwcap][nrp], rows fastest
+
+    const int tiles_x = (g.nx + BT - 1) / BT;
+    const int tj0 = (int)(blockIdx.x % tiles_x) * BT;
+    const int ti0 = (int)(blockIdx.x / tiles_x) * BT;
+    const int tj1 = min(tj0 + BT, g.nx) - 1;
+    const int ti1 = min(ti0 + BT, g.ny) - 1;
+    const int k0 = (int)blockIdx.y * SL;
+    const int nk = min(SL, g.ns - k0);
+
+    const int i = ti0 + (int)threadIdx.x / BT;
+    const int j = tj0 + (int)threadIdx.x % BT;
+    const bool valid = (i < g.ny) && (j < g.nx);
+    const int np = g.ny * g.nx;
+    const int p = valid ? i * g.nx + j : 0;
+    const double x = pix_x(g, j), y = pix_y(g, i);
+
+    float acc[SL];
+#pragma unroll
+    for (int k = 0; k < SL; ++k) acc[k] = 0.f;
+
+    const int lane = (int)threadIdx.x & 31;
+    const int grp = (int)threadIdx.x >> 5;
+
+    for (int v = 0; v < g.nv; ++v) {
+        const ViewK vk = views[v];
+        const Window wd = tile_window(g, vk, ti0, ti1, tj0, tj1, k0, k0 + nk - 1);
+        if (wd.nw <= 0 || wd.nrw <= 0) continue;   // the tile misses the detector in this view
+        __syncthreads();
+        for (int m = grp; m < wd.nrw; m += NT / 32) {
+            const int row = wd.m0 + m;
+            const bool rok = row >= 0 && row < g.nr;
+            const float *srow = sino + ((int64_t)v * g.nr + (rok ? row : 0)) * g.nc;
+            for (int c = lane; c < wd.nw; c += 32) {
+                const int n = wd.n0 + c;
+                float val = 0.f;
+                if (rok && n >= 0 && n < g.nc) val = srow[n];
+                win[c * nrp + m] = val;
+            }
+        }
+        __syncthreads();
+        const int ncv = valid ? idx[(int64_t)v * np + p] : 0;
+        if (valid && ncv >= -R && ncv <= g.nc - 1 + R) {
+            const ConeVP q = cone_vp(g, vk, x, y, ncv);
+            double hd[NTAP];
+            tap_weights_d<R>(q.f, q.wch, hd);
+            float h[NTAP];
+#pragma unroll
+            for (int t = 0; t < NTAP; ++t) h[t] = (float)hd[t];
+            const float *col = win + (ncv - R - wd.n0) * nrp - wd.m0;
+            const double wrow = q.mr * g.dv;
+#pragma unroll
+            for (int k = 0; k < SL; ++k) {
+                const double dz = slice_z(g, k0 + k) - vk.zsrc;
+                const double t0 = q.mr * dz;
+                const double wk = t0 + g.crow;
+                const double mk = rint(wk);
+                if (k < nk && mk >= -R && mk <= g.nr - 1 + R) {
+                    double gd[NTAP];
+                    tap_weights_d<R>(wk - mk, wrow, gd);
+                    const float lk = (float)q.lsc * sqrtf((float)(q.r2 + dz * dz));
+                    const float *cell = col + ((int)mk - R);
+                    float s = 0.f;
+#pragma unroll
+                    for (int sg = 0; sg < NTAP; ++sg) {
+                        float rv = 0.f;
+#pragma unroll
+                        for (int t = 0; t < NTAP; ++t) rv = fmaf(h[t], cell[t * nrp + sg], rv);
+                        s = fmaf(lk * (float)gd[sg], rv, s);
+                    }
+                    acc[k] += s;
+                }
+            }
+        }
+    }
+    if (valid) {
+        float *out = recon + (int64_t)p * g.ns + k0;
+#pragma unroll
+        for (int k = 0; k < SL; ++k)
+            if (k < nk) out[k] = acc[k];
+    }
+}
+
+template <int SL, int R>
+__global__ __launch_bounds__(FT *FT) void cone_forward_kernel(const float *__restrict__ recon,
+                                                               float *__restrict__ sino,
+                                                               const int32_t *__restrict__ idx,
+                                                               const ViewK *__restrict__ views, Geo g, int nwcap,
+                                                               int nrp, int vsplit) {
+    constexpr int NT = FT * FT;
+    constexpr int NTAP = 2 * R + 1;
+    extern __shared__ float win[];        // two buffers of [nwcap][nrp]
+
+    const int tiles_x = (g.nx + FT - 1) / FT;
+    const int tj0 = (int)(blockIdx.x % tiles_x) * FT;
+    const int ti0 = (int)(blockIdx.x / tiles_x) * FT;
+    const int tj1 = min(tj0 + FT, g.nx) - 1;
+    const int ti1 = min(ti0 + FT, g.ny) - 1;
+    const int k0 = (int)blockIdx.y * SL;
+    const int nk = min(SL, g.ns - k0);
+    const int np = g.ny * g.nx;
+
+    const int a = (int)threadIdx.x % FT, b = (int)threadIdx.x / FT;
+    const int ir = ti0 + b, jr = tj0 + a;
+    const int ic = ti0 + a, jc = tj0 + b;
+    const bool vr = ir < g.ny && jr < g.nx;
+    const bool vc = ic < g.ny && jc < g.nx;
+    float xr[SL], xq[SL];
+    {
+        const float *pr = recon + (int64_t)(vr ? ir * g.nx + jr : 0) * g.ns + k0;
+        const float *pc = recon + (int64_t)(vc ? ic * g.nx + jc : 0) * g.ns + k0;
+#pragma unroll
+        for (int k = 0; k < SL; ++k) {
+            xr[k] = (vr && k < nk) ? pr[k] : 0.f;
+            xq[k] = (vc && k < nk) ? pc[k] : 0.f;
+        }
+    }
+
+    const int cap = nwcap * nrp;
+    for (int e = (int)threadIdx.x; e < 2 * cap; e += NT) win[e] = 0.f;
+    __syncthreads();
+
+    const int vper = (g.nv + vsplit - 1) / vsplit;
+    const int vbeg = (int)blockIdx.z * vper;
+    const int vend = min(g.nv, vbeg + vper);
+    const int cnt = vend - vbeg;
+    const int start = cnt > 0 ? (int)((blockIdx.x * 7u + blockIdx.y * 3u) % (unsigned)cnt) : 0;
+    const double xm = 0.5 * (pix_x(g, tj0) + pix_x(g, tj1));
+    const double ym = 0.5 * (pix_y(g, ti0) + pix_y(g, ti1));
+
+    for (int it = 0; it < cnt; ++it) {
+        int v = vbeg + start + it;
+        if (v >= vend) v -= cnt;
+        const ViewK vk = views[v];
+        const Window wd = tile_window(g, vk, ti0, ti1, tj0, tj1, k0, k0 + nk - 1);
+        float *buf = win + (it & 1) * cap;
+        // strip along the tile axis on which the channel coordinate moves fastest
+        const bool rowmode = fabs(ym + vk.c * g.sid) >= fabs(vk.s * g.sid - xm);
+        const int i = rowmode ? ir : ic, j = rowmode ? jr : jc;
+        const bool valid = (rowmode ? vr : vc) && wd.nw > 0 && wd.nrw > 0;
+        const int ncv = valid ? idx[(int64_t)v * np + i * g.nx + j] : 0;
+        if (valid && ncv >= -R && ncv <= g.nc - 1 + R) {
+            const ConeVP q = cone_vp(g, vk, pix_x(g, j), pix_y(g, i), ncv);
+            double hd[NTAP];
+            tap_weights_d<R>(q.f, q.wch, hd);
+            float h[NTAP];
+#pragma unroll
+            for (int t = 0; t < NTAP; ++t) h[t] = (float)hd[t];
+            float *col = buf + (ncv - R - wd.n0) * nrp - wd.m0;
+            const double wrow = q.mr * g.dv;
+#pragma unroll
+            for (int k = 0; k < SL; ++k) {
+                const double dz = slice_z(g, k0 + k) - vk.zsrc;
+                const double t0 = q.mr * dz;
+                const double wk = t0 + g.crow;
+                const double mk = rint(wk);
+                if (k < nk && mk >= -R && mk <= g.nr - 1 + R) {
+                    const float xv = rowmode ? xr[k] : xq[k];
+                    double gd[NTAP];
+                    tap_weights_d<R>(wk - mk, wrow, gd);
+                    const float lk = (float)q.lsc * sqrtf((float)(q.r2 + dz * dz));
+                    float *cell = col + ((int)mk - R);
+#pragma unroll
+                    for (int sg = 0; sg < NTAP; ++sg) {
+                        const float ws = lk * (float)gd[sg] * xv;
+#pragma unroll
+                        for (int t = 0; t < NTAP; ++t) atomicAdd(&cell[t * nrp + sg], h[t] * ws);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        const int lane = (int)threadIdx.x & 31;
+        for (int m = (int)threadIdx.x >> 5; m < wd.nrw; m += NT / 32) {
+            const int row = wd.m0 + m;
+            const bool rok = row >= 0 && row < g.nr;
+            float *srow = sino + ((int64_t)v * g.nr + (rok ? row : 0)) * g.nc;
+            for (int c = lane; c < wd.nw; c += 32) {
+                const float val = buf[c * nrp + m];
+                buf[c * nrp + m] = 0.f;
+                const int n = wd.n0 + c;
+                if (val != 0.f && rok && n >= 0 && n < g.nc) unsafeAtomicAdd(&srow[n], val);
+            }
+        }
+    }
+}
+
+template <int SL, int R>
+static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, hipStream_t st) {
+    const Geo &g = p.g;
+    const int tiles = ((g.nx + BT - 1) / BT) * ((g.ny + BT - 1) / BT);
+    const int chunks = (g.ns + SL - 1) / SL;
+    hipLaunchKernelGGL((cone_back_kernel<SL, R>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino, recon,
+                       p.idx, p.views, g, p.back_nrcap);
+    return hipGetLastError();
+}
+
+template <int SL, int R>
+static hipError_t cone_fwd_t(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+    const Geo &g = p.g;
+    const int tiles = ((g.nx + FT - 1) / FT) * ((g.ny + FT - 1) / FT);
+    const int chunks = (g.ns + SL - 1) / SL;
+    hipLaunchKernelGGL((cone_forward_kernel<SL, R>), dim3(tiles, chunks, p.fwd_vsplit), dim3(FT * FT), p.fwd_lds,
+                       st, recon, sino, p.idx, p.views, g, p.fwd_nwcap, p.fwd_nrcap, p.fwd_vsplit);
+    return hipGetLastError();
+}
+
+#define BPAMD_DISPATCH_R(FN, SLV, ...)                         \
+    switch (p.g.radius) {                                      \
+    case 1: return FN<SLV, 1>(__VA_ARGS__);                    \
+    case 2: return FN<SLV, 2>(__VA_ARGS__);                    \
+    case 3: return FN<SLV, 3>(__VA_ARGS__);                    \
+    case 4: return FN<SLV, 4>(__VA_ARGS__);                    \
+    default: return hipErrorInvalidValue;                      \
+    }
+
+hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, hipStream_t st) {
+    switch (p.back_sl) {
+    case 8: BPAMD_DISPATCH_R(cone_back_t, 8, p, sino, recon, st)
+    case 16: BPAMD_DISPATCH_R(cone_back_t, 16, p, sino, recon, st)
+    case 32: BPAMD_DISPATCH_R(cone_back_t, 32, p, sino, recon, st)
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+    switch (p.fwd_sl) {
+    case 8: BPAMD_DISPATCH_R(cone_fwd_t, 8, p, recon, sino, st)
+    case 16: BPAMD_DISPATCH_R(cone_fwd_t, 16, p, recon, sino, st)
+    case 32: BPAMD_DISPATCH_R(cone_fwd_t, 32, p, recon, sino, st)
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace bpamd

@@ -1,0 +1,44 @@
+// Host-side launch plan and the launchers each kernel file exports.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "geom.h"
+
+namespace bpamd {
+
+// Everything a launch needs, fixed at creation from the shapes and the
+// geometry alone (never from data).
+struct Plan {
+    Geo g;
+    const ViewK *views = nullptr;   // device [V]
+    const int32_t *idx = nullptr;   // device [V][Ny*Nx]
+
+    // back projection: lanes = pixels of a BT x BT tile, SL slices per lane
+    int back_sl = 0;                // slices per chunk (accumulators per lane)
+    int back_nwcap = 0;             // window channels capacity
+    int back_nrcap = 0;             // window rows capacity (cone)
+    size_t back_lds = 0;            // dynamic LDS bytes
+
+    // forward projection: lanes = pixels of an FT x FT tile
+    int fwd_sl = 0;
+    int fwd_nwcap = 0;
+    int fwd_nrcap = 0;
+    size_t fwd_lds = 0;
+    int fwd_vsplit = 1;             // view ranges per tile (grid z)
+};
+
+constexpr int BT = 16;   // back tile edge (pixels), 256 threads
+constexpr int FT = 32;   // forward tile edge (pixels), 1024 threads
+
+hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
+hipError_t launch_fill_zero(float *buf, int64_t n, hipStream_t st);
+
+hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, hipStream_t st);
+hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
+hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, hipStream_t st);
+hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
+
+}  // namespace bpamd

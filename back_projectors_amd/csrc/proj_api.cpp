@@ -1,0 +1,421 @@
+// C ABI of the projector library: validation, the launch plan, the device
+// tables a handle owns, and the entry points declared in include/proj.h.
+//
+// Creation runs once per geometry (the projectors themselves are called every
+// solver iteration, MBIRJAX "Projector kernels" page, introduction), so all
+// checks, table uploads, the fp64 channel-index pass and the choice of tile
+// and window sizes happen here.  The per-call entry points then do nothing on
+// the host but argument checks and one or two kernel launches on the caller's
+// stream: no allocation, no copy, no synchronisation (page section "The rules
+// a Pallas kernel must follow": shapes from arrays, never data; no host round
+// trips; build each kernel once).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/proj.h"
+#include "launch.h"
+
+using namespace bpamd;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+proj_status fail(proj_status s, const std::string &why) {
+    g_last_error = why;
+    return s;
+}
+
+proj_status ok() {
+    g_last_error.clear();
+    return PROJ_OK;
+}
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;      // work arrays stay below 2^31 elements
+constexpr size_t kMaxLds = 64 * 1024;                 // dynamic LDS per workgroup used by the plan
+
+bool finite(double v) { return std::isfinite(v); }
+
+}  // namespace
+
+struct proj_handle_s {
+    int device = 0;
+    Plan plan;
+    int64_t recon_elems = 0, sino_elems = 0, index_elems = 0;
+    ViewK *d_views = nullptr;
+    int32_t *d_idx = nullptr;
+    size_t table_bytes = 0;
+};
+
+namespace {
+
+// Smallest slice chunk from `opts` (ascending) that covers S with the least
+// padding; chunks larger than S are not considered once one covers it.
+int pick_chunk(int64_t s, const std::vector<int> &opts) {
+    for (int o : opts)
+        if (s <= o) return o;
+    int best = opts.back();
+    int64_t best_pad = ((s + best - 1) / best) * best - s;
+    for (auto it = opts.rbegin(); it != opts.rend(); ++it) {
+        const int o = *it;
+        const int64_t pad = ((s + o - 1) / o) * o - s;
+        if (pad < best_pad) {
+            best = o;
+            best_pad = pad;
+        }
+    }
+    return best;
+}
+
+struct WinMax {
+    int nw = 0, nr = 0;
+};
+
+// Largest window over all views, tiles of edge `t` and slice chunks of `sl`.
+WinMax max_window(const Geo &g, const std::vector<ViewK> &views, int t, int sl) {
+    WinMax m;
+    const int ty = (g.ny + t - 1) / t, tx = (g.nx + t - 1) / t, nch = (g.ns + sl - 1) / sl;
+    for (int v = 0; v < g.nv; ++v)
+        for (int a = 0; a < ty; ++a)
+            for (int b = 0; b < tx; ++b) {
+                const int i0 = a * t, i1 = std::min(i0 + t, g.ny) - 1;
+                const int j0 = b * t, j1 = std::min(j0 + t, g.nx) - 1;
+                for (int c = 0; c < (g.kind == 0 ? 1 : nch); ++c) {
+                    const int k0 = c * sl, k1 = std::min(k0 + sl, g.ns) - 1;
+                    const Window w = tile_window(g, views[v], i0, i1, j0, j1, k0, k1);
+                    m.nw = std::max(m.nw, w.nw);
+                    m.nr = std::max(m.nr, w.nrw);
+                }
+            }
+    return m;
+}
+
+// Validation and planning without touching the GPU.  Fills geo/views/plan.
+proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const int64_t ss[3], Geo &g,
+                          std::vector<ViewK> &views, Plan &plan) {
+    if (!gp || !rs || !ss) return fail(PROJ_ERR_INVALID_ARGUMENT, "null geometry or shape pointer");
+    for (int d = 0; d < 3; ++d)
+        if (rs[d] < 0 || ss[d] < 0 || rs[d] >= kMaxElems || ss[d] >= kMaxElems)
+            return fail(PROJ_ERR_INVALID_ARGUMENT, "shape entries must lie in [0, 2^31)");
+    if (gp->kind != PROJ_PARALLEL && gp->kind != PROJ_CONE_FLAT)
+        return fail(PROJ_ERR_INVALID_ARGUMENT, "kind must be PROJ_PARALLEL or PROJ_CONE_FLAT");
+    if (gp->num_views != ss[0])
+        return fail(PROJ_ERR_INVALID_ARGUMENT, "num_views must equal sino_shape[0]");
+    const int64_t V = ss[0], R = ss[1], C = ss[2], Ny = rs[0], Nx = rs[1], S = rs[2];
+    if (V > 0 && !gp->angles) return fail(PROJ_ERR_INVALID_ARGUMENT, "angles is required");
+    for (int64_t v = 0; v < V; ++v) {
+        if (!finite(gp->angles[v])) return fail(PROJ_ERR_INVALID_ARGUMENT, "non-finite angle");
+        if (gp->channel_shift && !finite(gp->channel_shift[v]))
+            return fail(PROJ_ERR_INVALID_ARGUMENT, "non-finite channel_shift");
+        if (gp->source_z && !finite(gp->source_z[v]))
+            return fail(PROJ_ERR_INVALID_ARGUMENT, "non-finite source_z");
+    }
+    const double dv = gp->delta_voxel, dch = gp->delta_channel, drow = gp->delta_row;
+    if (!(finite(dv) && dv > 0) || !(finite(dch) && dch > 0) || !(finite(drow) && drow > 0))
+        return fail(PROJ_ERR_INVALID_ARGUMENT, "pitches must be finite and positive");
+    if (!finite(gp->det_channel_offset) || !finite(gp->det_row_offset))
+        return fail(PROJ_ERR_INVALID_ARGUMENT, "non-finite detector offset");
+    if (gp->psf_radius < 1 || gp->psf_radius > 4)
+        return fail(PROJ_ERR_INVALID_ARGUMENT, "psf_radius must be in [1, 4]");
+    const double half_diag = 0.5 * std::sqrt((double)Nx * Nx + (double)Ny * Ny) * dv;
+    if (gp->kind == PROJ_PARALLEL) {
+        if (R != S) return fail(PROJ_ERR_INVALID_ARGUMENT, "parallel beam needs one detector row per slice (R == S)");
+        if (drow != dv) return fail(PROJ_ERR_INVALID_ARGUMENT, "parallel beam needs delta_row == delta_voxel");
+        if (gp->source_z) return fail(PROJ_ERR_INVALID_ARGUMENT, "source_z is for cone beam only");
+    } else {
+        const double sid = gp->source_iso, sdd = gp->source_detector;
+        if (!finite(sid) || !finite(sdd)) return fail(PROJ_ERR_INVALID_ARGUMENT, "non-finite source distances");
+        if (!(sid > half_diag))
+            return fail(PROJ_ERR_INVALID_ARGUMENT, "source_iso must exceed the in-plane radius of the volume");
+        if (!(sdd > sid)) return fail(PROJ_ERR_INVALID_ARGUMENT, "source_detector must exceed source_iso");
+    }
+    if (V * Ny * Nx >= kMaxElems || Ny * Nx * S >= kMaxElems || V * R * C >= kMaxElems)
+        return fail(PROJ_ERR_UNSUPPORTED, "an array or the index table would reach 2^31 elements");
+
+    g.kind = gp->kind;
+    g.radius = gp->psf_radius;
+    g.ny = (int)Ny; g.nx = (int)Nx; g.ns = (int)S;
+    g.nv = (int)V; g.nr = (int)R; g.nc = (int)C;
+    g.dv = dv; g.dch = dch; g.drow = drow;
+    g.sid = gp->kind == PROJ_CONE_FLAT ? gp->source_iso : 0.0;
+    g.sdd = gp->kind == PROJ_CONE_FLAT ? gp->source_detector : 0.0;
+    g.cx = ((double)Nx - 1.0) / 2.0;
+    g.cy = ((double)Ny - 1.0) / 2.0;
+    g.cz = ((double)S - 1.0) / 2.0;
+    g.cch = ((double)C - 1.0) / 2.0 + gp->det_channel_offset;
+    g.crow = ((double)R - 1.0) / 2.0 + gp->det_row_offset;
+
+    views.resize((size_t)V);
+    for (int64_t v = 0; v < V; ++v) {
+        ViewK &k = views[(size_t)v];
+        k.c = std::cos(gp->angles[v]);
+        k.s = std::sin(gp->angles[v]);
+        k.shift = gp->channel_shift ? gp->channel_shift[v] : 0.0;
+        k.zsrc = gp->source_z ? gp->source_z[v] : 0.0;
+        k.cd = k.c / dch;
+        k.sd = k.s / dch;
+        k.u0 = g.cch + k.shift;
+        const double m = std::max(std::fabs(k.c), std::fabs(k.s));
+        k.W = dv * m / dch;
+        k.L = dv / m;
+    }
+
+    plan = Plan();
+    plan.g = g;
+    if (V == 0 || Ny * Nx == 0 || S == 0 || R == 0 || C == 0) return ok();   // nothing to launch
+
+    // Slice chunk per lane: the least padding first, then smaller chunks while
+    // the detector window of a tile does not fit in LDS.
+    const bool par = g.kind == 0;
+    const std::vector<int> back_opts = par ? std::vector<int>{8, 16, 32, 64} : std::vector<int>{8, 16, 32};
+    const std::vector<int> fwd_opts = par ? std::vector<int>{8, 16, 32} : std::vector<int>{8, 16};
+    auto back_bytes = [&](int sl, int &nwcap, int &nrcap) {
+        const WinMax w = max_window(g, views, BT, sl);
+        nwcap = w.nw + 2;
+        nrcap = par ? sl : ((w.nr + 2) | 1);       // odd pitch: conflict-free column strides
+        return par ? (size_t)nwcap * (sl + 1) * sizeof(float) : (size_t)nwcap * nrcap * sizeof(float);
+    };
+    auto fwd_bytes = [&](int sl, int &nwcap, int &nrcap) {
+        const WinMax w = max_window(g, views, FT, sl);
+        nwcap = w.nw + 2;
+        nrcap = par ? sl : ((w.nr + 2) | 1);
+        return 2 * (par ? (size_t)nwcap * (sl + 1) * sizeof(float) : (size_t)nwcap * nrcap * sizeof(float));
+    };
+    for (int sl = pick_chunk(S, back_opts);; sl /= 2) {
+        plan.back_sl = sl;
+        plan.back_lds = back_bytes(sl, plan.back_nwcap, plan.back_nrcap);
+        if (plan.back_lds <= kMaxLds || sl == back_opts.front()) break;
+    }
+    for (int sl = pick_chunk(S, fwd_opts);; sl /= 2) {
+        plan.fwd_sl = sl;
+        plan.fwd_lds = fwd_bytes(sl, plan.fwd_nwcap, plan.fwd_nrcap);
+        if (plan.fwd_lds <= kMaxLds || sl == fwd_opts.front()) break;
+    }
+    if (plan.back_lds > kMaxLds || plan.fwd_lds > kMaxLds) {
+        char buf[160];
+        std::snprintf(buf, sizeof buf, "detector window too large for LDS (back %zu B, forward %zu B, limit %zu B)",
+                      plan.back_lds, plan.fwd_lds, kMaxLds);
+        return fail(PROJ_ERR_UNSUPPORTED, buf);
+    }
+    const int64_t chunks_b = (S + plan.back_sl - 1) / plan.back_sl;
+    const int64_t chunks_f = (S + plan.fwd_sl - 1) / plan.fwd_sl;
+    if (chunks_b > 65535 || chunks_f > 65535) return fail(PROJ_ERR_UNSUPPORTED, "too many slices");
+    const int64_t ftiles = ((Nx + FT - 1) / FT) * ((Ny + FT - 1) / FT);
+    // enough workgroups to fill 256 CUs a few times over; each split re-reads its tile
+    int64_t vs = (2048 + ftiles * chunks_f - 1) / (ftiles * chunks_f);
+    vs = std::max<int64_t>(1, std::min<int64_t>(vs, std::min<int64_t>(V, 64)));
+    plan.fwd_vsplit = (int)vs;
+    return ok();
+}
+
+int describe(const Plan &p, int64_t table_bytes, char *buf, int len) {
+    const Geo &g = p.g;
+    return std::snprintf(buf, (size_t)std::max(len, 0),
+                         "kind=%s V=%d R=%d C=%d Ny=%d Nx=%d S=%d radius=%d | back: %dx%d px tile, %d slices/lane, "
+                         "window %d ch x %d rows, %zu B LDS | forward: %dx%d px tile, %d slices/lane, "
+                         "LDS window %d ch x %d rows x2, %zu B LDS, %d view ranges | index table %lld B",
+                         g.kind == 0 ? "parallel" : "cone_flat", g.nv, g.nr, g.nc, g.ny, g.nx, g.ns, g.radius, BT, BT,
+                         p.back_sl, p.back_nwcap, g.kind == 0 ? p.back_sl : p.back_nrcap, p.back_lds, FT, FT,
+                         p.fwd_sl, p.fwd_nwcap, g.kind == 0 ? p.fwd_sl : p.fwd_nrcap, p.fwd_lds, p.fwd_vsplit,
+                         (long long)table_bytes);
+}
+
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return na > 0 && nb > 0 && pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool switched = false;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) {
+            err = hipSetDevice(dev);
+            switched = err == hipSuccess;
+        }
+    }
+    ~DeviceGuard() {
+        if (switched) (void)hipSetDevice(prev);
+    }
+};
+
+proj_status device_fail(hipError_t e, const char *what) {
+    return fail(e == hipErrorOutOfMemory ? PROJ_ERR_OUT_OF_MEMORY : PROJ_ERR_DEVICE,
+                std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *proj_status_string(proj_status s) {
+    switch (s) {
+    case PROJ_OK: return "PROJ_OK";
+    case PROJ_ERR_INVALID_ARGUMENT: return "PROJ_ERR_INVALID_ARGUMENT";
+    case PROJ_ERR_UNSUPPORTED: return "PROJ_ERR_UNSUPPORTED";
+    case PROJ_ERR_ALIAS: return "PROJ_ERR_ALIAS";
+    case PROJ_ERR_OUT_OF_MEMORY: return "PROJ_ERR_OUT_OF_MEMORY";
+    case PROJ_ERR_DEVICE: return "PROJ_ERR_DEVICE";
+    }
+    return "PROJ_ERR_UNKNOWN";
+}
+
+const char *proj_last_error(void) { return g_last_error.c_str(); }
+
+proj_status proj_plan_query(const proj_geometry *g, const int64_t recon_shape[3], const int64_t sino_shape[3],
+                            char *buf, int len) {
+    try {
+        Geo geo;
+        std::vector<ViewK> views;
+        Plan plan;
+        const proj_status s = plan_geometry(g, recon_shape, sino_shape, geo, views, plan);
+        if (s != PROJ_OK) return s;
+        if (buf && len > 0)
+            describe(plan, (int64_t)geo.nv * geo.ny * geo.nx * (int64_t)sizeof(int32_t), buf, len);
+        return ok();
+    } catch (const std::bad_alloc &) {
+        return fail(PROJ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(PROJ_ERR_DEVICE, "unexpected internal error");
+    }
+}
+
+proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], const int64_t sino_shape[3],
+                        int hip_device, proj_handle *out) {
+    if (!out) return fail(PROJ_ERR_INVALID_ARGUMENT, "out is NULL");
+    *out = nullptr;
+    try {
+        Geo geo;
+        std::vector<ViewK> views;
+        Plan plan;
+        proj_status s = plan_geometry(gp, recon_shape, sino_shape, geo, views, plan);
+        if (s != PROJ_OK) return s;
+        int ndev = 0;
+        hipError_t e = hipGetDeviceCount(&ndev);
+        if (e != hipSuccess) return device_fail(e, "hipGetDeviceCount");
+        if (hip_device < 0 || hip_device >= ndev) return fail(PROJ_ERR_INVALID_ARGUMENT, "no such HIP device");
+        DeviceGuard dg(hip_device);
+        if (dg.err != hipSuccess) return device_fail(dg.err, "hipSetDevice");
+
+        proj_handle h = new proj_handle_s();
+        h->device = hip_device;
+        h->plan = plan;
+        h->recon_elems = recon_shape[0] * recon_shape[1] * recon_shape[2];
+        h->sino_elems = sino_shape[0] * sino_shape[1] * sino_shape[2];
+        h->index_elems = sino_shape[0] * recon_shape[0] * recon_shape[1];
+        auto cleanup = [&](proj_status st, hipError_t he, const char *what) {
+            proj_destroy(h);
+            return he != hipSuccess ? device_fail(he, what) : st;
+        };
+        if (!views.empty()) {
+            e = hipMalloc((void **)&h->d_views, views.size() * sizeof(ViewK));
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(views)");
+            e = hipMemcpy(h->d_views, views.data(), views.size() * sizeof(ViewK), hipMemcpyHostToDevice);
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(views)");
+        }
+        if (h->index_elems > 0) {
+            e = hipMalloc((void **)&h->d_idx, (size_t)h->index_elems * sizeof(int32_t));
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(index table)");
+            e = launch_channel_index(geo, h->d_views, h->d_idx, nullptr);
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "channel index pass");
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "channel index pass");
+        }
+        h->table_bytes = (size_t)h->index_elems * sizeof(int32_t) + views.size() * sizeof(ViewK);
+        h->plan.views = h->d_views;
+        h->plan.idx = h->d_idx;
+        if (std::getenv("PROJ_LOG")) {
+            char buf[512];
+            describe(h->plan, (int64_t)h->table_bytes, buf, sizeof buf);
+            std::fprintf(stderr, "[proj] %s\n", buf);
+        }
+        *out = h;
+        return ok();
+    } catch (const std::bad_alloc &) {
+        return fail(PROJ_ERR_OUT_OF_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(PROJ_ERR_DEVICE, "unexpected internal error");
+    }
+}
+
+proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev, void *hip_stream) {
+    if (!h) return fail(PROJ_ERR_INVALID_ARGUMENT, "null handle");
+    if ((h->recon_elems > 0 && !recon_dev) || (h->sino_elems > 0 && !sino_dev))
+        return fail(PROJ_ERR_INVALID_ARGUMENT, "null data pointer");
+    if (overlaps(recon_dev, h->recon_elems * 4, sino_dev, h->sino_elems * 4))
+        return fail(PROJ_ERR_ALIAS, "recon and sino buffers overlap");
+    if (h->sino_elems == 0) return ok();
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return device_fail(dg.err, "hipSetDevice");
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipError_t e = launch_fill_zero(sino_dev, h->sino_elems, st);
+    if (e != hipSuccess) return device_fail(e, "zero fill");
+    if (h->plan.back_sl == 0) return ok();     // empty volume or no views: the sinogram is zero
+    e = h->plan.g.kind == 0 ? launch_par_forward(h->plan, recon_dev, sino_dev, st)
+                            : launch_cone_forward(h->plan, recon_dev, sino_dev, st);
+    if (e != hipSuccess) return device_fail(e, "forward projection launch");
+    return ok();
+}
+
+proj_status proj_back(proj_handle h, const float *sino_dev, float *recon_dev, void *hip_stream) {
+    if (!h) return fail(PROJ_ERR_INVALID_ARGUMENT, "null handle");
+    if ((h->recon_elems > 0 && !recon_dev) || (h->sino_elems > 0 && !sino_dev))
+        return fail(PROJ_ERR_INVALID_ARGUMENT, "null data pointer");
+    if (overlaps(recon_dev, h->recon_elems * 4, sino_dev, h->sino_elems * 4))
+        return fail(PROJ_ERR_ALIAS, "recon and sino buffers overlap");
+    if (h->recon_elems == 0) return ok();
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return device_fail(dg.err, "hipSetDevice");
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipError_t e;
+    if (h->plan.back_sl == 0) {
+        e = launch_fill_zero(recon_dev, h->recon_elems, st);      // no views or empty detector
+        if (e != hipSuccess) return device_fail(e, "zero fill");
+        return ok();
+    }
+    e = h->plan.g.kind == 0 ? launch_par_back(h->plan, sino_dev, recon_dev, st)
+                            : launch_cone_back(h->plan, sino_dev, recon_dev, st);
+    if (e != hipSuccess) return device_fail(e, "back projection launch");
+    return ok();
+}
+
+proj_status proj_channel_index(proj_handle h, int32_t *index_dev, void *hip_stream) {
+    if (!h) return fail(PROJ_ERR_INVALID_ARGUMENT, "null handle");
+    if (h->index_elems == 0) return ok();
+    if (!index_dev) return fail(PROJ_ERR_INVALID_ARGUMENT, "null index pointer");
+    if (overlaps(index_dev, h->index_elems * 4, h->d_idx, h->index_elems * 4))
+        return fail(PROJ_ERR_ALIAS, "destination overlaps the handle's table");
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return device_fail(dg.err, "hipSetDevice");
+    const hipError_t e = hipMemcpyAsync(index_dev, h->d_idx, (size_t)h->index_elems * sizeof(int32_t),
+                                        hipMemcpyDeviceToDevice, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return device_fail(e, "hipMemcpyAsync(index)");
+    return ok();
+}
+
+void proj_destroy(proj_handle h) {
+    if (!h) return;
+    {
+        DeviceGuard dg(h->device);
+        if (h->d_idx) (void)hipFree(h->d_idx);
+        if (h->d_views) (void)hipFree(h->d_views);
+    }
+    delete h;
+}
+
+int proj_describe(proj_handle h, char *buf, int len) {
+    if (!h) return -1;
+    return describe(h->plan, (int64_t)h->table_bytes, buf, len);
+}
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+/*
+ * proj.h -- C ABI of the matched voxel-driven projector pair for MI355X (gfx950).
+ *
+ * The operator pair (MBIRJAX "Projector kernels" page):
+ *   - the forward projector maps a voxel-cylinder volume to a sinogram: every
+ *     voxel is mapped to a detector channel and its trapezoid footprint taps
+ *     are added into that channel and its neighbours (section "The XLA
+ *     kernels", paragraph "Forward scatters, back gathers");
+ *   - the back projector is its exact adjoint and gathers the same taps from
+ *     the sinogram into the voxels (same paragraph; "How the kernels work",
+ *     closing remark that both directions take their weights from the same
+ *     geometry code, so they stay a matched pair);
+ *   - the integer channel of every (view, pixel) is computed by a separate
+ *     step and handed to the projectors as data, so no projector rounds a
+ *     coordinate to a channel itself (paragraph "Shared machinery, and the
+ *     rounding defense");
+ *   - parallel beam: detector row r sees only slice r (paragraph "Geometry
+ *     decides whether a slice can stream"); cone beam with a flat detector:
+ *     one slice spreads over a band of rows given by an affine function of
+ *     the slice index, with a 3x3 tap block ("The cone back kernel: a fused
+ *     vertical fan").
+ * The footprint model, written out: the fp64 CPU reference under oracle/ and
+ * the design doc state it formula by formula.
+ *
+ * Layouts (all C order, float32, device memory, caller-owned):
+ *   recon  [Ny][Nx][S]  slices fastest: one contiguous voxel cylinder per
+ *                       pixel p = i*Nx + j (MBIRJAX "Sharding overview" page,
+ *                       section "The two shardings");
+ *   sino   [V][R][C]    channels fastest, one [R][C] block per view;
+ *   index  [V][Ny*Nx]   int32 channel index n_c = rint(u) of every view and
+ *                       pixel (round half to even).
+ *
+ * Threading / streams: calls are asynchronous on the HIP stream passed in
+ * (NULL = the default stream).  They allocate nothing, copy nothing between
+ * host and device and never synchronise.  A handle is immutable after
+ * proj_create; concurrent calls on different streams are allowed when their
+ * output buffers are distinct.
+ *
+ * Errors: every check runs before anything is written or launched, so an
+ * error return leaves all outputs untouched.  No C++ exception crosses this
+ * boundary.  proj_last_error() gives a human-readable reason for the last
+ * failure on the calling thread.
+ */
+#ifndef BPAMD_PROJ_H
+#define BPAMD_PROJ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct proj_handle_s *proj_handle; /* opaque; owned by the library */
+
+typedef enum {
+    PROJ_OK = 0,
+    PROJ_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad shape, non-finite or inconsistent geometry */
+    PROJ_ERR_UNSUPPORTED = -2,      /* valid request the kernels cannot serve (size limits) */
+    PROJ_ERR_ALIAS = -3,            /* input and output buffers overlap */
+    PROJ_ERR_OUT_OF_MEMORY = -4,    /* device allocation failed in proj_create */
+    PROJ_ERR_DEVICE = -5            /* a HIP call or kernel launch failed */
+} proj_status;
+
+typedef enum {
+    PROJ_PARALLEL = 0,  /* parallel beam; row r of the detector sees slice r only */
+    PROJ_CONE_FLAT = 1  /* point source, flat detector; circular or helical orbit */
+} proj_kind;
+
+/*
+ * Acquisition geometry.  Lengths are in the same unit as delta_voxel.
+ * Pixel (i, j) of slice k has its centre at
+ *     x = (j - (Nx-1)/2) dv,  y = (i - (Ny-1)/2) dv,  z = (k - (S-1)/2) dv.
+ * View v looks along angle theta_v: a parallel ray hits detector coordinate
+ * t = x cos(theta) + y sin(theta); for cone beam the source sits at distance
+ * source_iso on the far side, at height source_z[v], and the flat detector is
+ * source_detector away from the source, perpendicular to the central ray.
+ * Channel n (row m) has its centre at n = (C-1)/2 + det_channel_offset + t/dch
+ * (m = (R-1)/2 + det_row_offset + ...).  The arrays are copied by proj_create.
+ */
+typedef struct {
+    int32_t kind;                /* proj_kind */
+    int32_t num_views;           /* V; must equal sino_shape[0] */
+    const double *angles;        /* [V] radians; required when V > 0 */
+    const double *channel_shift; /* [V] lateral detector shift in channels, or NULL (all 0) */
+    const double *source_z;      /* [V] source height (cone only; helical orbits), or NULL */
+    double delta_voxel;          /* dv > 0 */
+    double delta_channel;        /* dch > 0 */
+    double delta_row;            /* drow > 0; parallel beam requires drow == dv */
+    double source_iso;           /* cone: source to rotation axis, > in-plane radius of the volume */
+    double source_detector;      /* cone: source to detector plane, > source_iso */
+    double det_channel_offset;   /* detector centre offset, channels (usually 0) */
+    double det_row_offset;       /* detector centre offset, rows (usually 0) */
+    int32_t psf_radius;          /* taps on each side of the centre channel (and row), 1..4 */
+} proj_geometry;
+
+/*
+ * proj_create: validate the geometry, copy it to the device, run the fp64
+ * channel-index pass and fix the launch plan from the shapes alone.
+ *   g            geometry (read only, copied)
+ *   recon_shape  {Ny, Nx, S}, each >= 0
+ *   sino_shape   {V, R, C}, each >= 0; parallel beam requires R == S
+ *   hip_device   HIP device ordinal the handle lives on
+ *   out          receives the handle (NULL on error)
+ * Limits: V*Ny*Nx, Ny*Nx*S and V*R*C below 2^31 elements.
+ * Synchronises the device once (creation is not on the hot path).
+ */
+proj_status proj_create(const proj_geometry *g, const int64_t recon_shape[3],
+                        const int64_t sino_shape[3], int hip_device, proj_handle *out);
+
+/*
+ * proj_forward: sino = A recon.  recon_dev [Ny][Nx][S] is read, sino_dev
+ * [V][R][C] is overwritten (entries no tap reaches become exactly 0).
+ * The two buffers must not overlap.  Asynchronous on hip_stream.
+ */
+proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev, void *hip_stream);
+
+/*
+ * proj_back: recon = A^T sino, the exact adjoint of proj_forward.  sino_dev is
+ * read, recon_dev is overwritten.  The two buffers must not overlap.
+ * Asynchronous on hip_stream.
+ */
+proj_status proj_back(proj_handle h, const float *sino_dev, float *recon_dev, void *hip_stream);
+
+/*
+ * proj_channel_index: copy the handle's channel-index table n_c[V][Ny*Nx]
+ * (int32, round half to even of the fp64 channel coordinate) into index_dev.
+ * Asynchronous on hip_stream.
+ */
+proj_status proj_channel_index(proj_handle h, int32_t *index_dev, void *hip_stream);
+
+/*
+ * proj_plan_query: run every check of proj_create and choose the launch plan
+ * without touching any GPU; write the plan's one-line description into buf
+ * (at most len bytes, may be NULL).  Returns what proj_create would return
+ * for the same arguments before it allocates.
+ */
+proj_status proj_plan_query(const proj_geometry *g, const int64_t recon_shape[3],
+                            const int64_t sino_shape[3], char *buf, int len);
+
+/* proj_destroy: free the handle's device tables.  NULL is ignored. */
+void proj_destroy(proj_handle h);
+
+/* proj_status_string: static name of a status code. */
+const char *proj_status_string(proj_status s);
+
+/* proj_last_error: reason for the last failed call on this thread ("" if none). */
+const char *proj_last_error(void);
+
+/*
+ * proj_describe: write a one-line, NUL-terminated description of the launch
+ * plan (kernels, tile sizes, table bytes) into buf (at most len bytes).
+ * Returns the length it needed.
+ */
+int proj_describe(proj_handle h, char *buf, int len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPAMD_PROJ_H */

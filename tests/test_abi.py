@@ -1,0 +1,146 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+header declares, and rejects bad requests with the documented status before
+touching a GPU.  No compute call runs here."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "proj.h")
+
+
+@pytest.fixture(scope="session")
+def bp():
+    import back_projectors_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from back_projectors_amd import build_lib
+        build_lib.build()
+    m.load_library()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(proj_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("proj_create", "proj_forward", "proj_back", "proj_channel_index", "proj_destroy"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(bp):
+    names = declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", bp.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    lib = bp.load_library()
+    for n in names:
+        getattr(lib, n)                               # resolvable through ctypes
+    assert set(bp.EXPORTS) == set(names)
+
+
+def test_status_strings(bp):
+    lib = bp.load_library()
+    for code, name in bp.STATUS.items():
+        assert lib.proj_status_string(code).decode() == name
+    assert lib.proj_status_string(17).decode() == "PROJ_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_every_workload_plans(bp, name):
+    w = W.get(name)
+    desc = bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape)
+    assert ("parallel" if w.kind == W.PARALLEL else "cone_flat") in desc
+    assert f"V={w.nv}" in desc
+
+
+def base_geo(**kw):
+    g = dict(kind=0, num_views=4, angles=np.linspace(0, 3, 4), delta_voxel=1.0, delta_channel=1.0,
+             delta_row=1.0, psf_radius=1)
+    g.update(kw)
+    return g
+
+
+CONE = dict(kind=1, source_iso=100.0, source_detector=150.0, delta_channel=1.5, delta_row=1.5)
+
+BAD = [
+    ("kind", base_geo(kind=3), (8, 8, 4), (4, 4, 16), -1),
+    ("views mismatch", base_geo(num_views=5, angles=np.zeros(5)), (8, 8, 4), (4, 4, 16), -1),
+    ("nan angle", base_geo(angles=np.array([0.0, math.nan, 1.0, 2.0])), (8, 8, 4), (4, 4, 16), -1),
+    ("inf shift", base_geo(channel_shift=np.array([0.0, math.inf, 0.0, 0.0])), (8, 8, 4), (4, 4, 16), -1),
+    ("zero pitch", base_geo(delta_channel=0.0), (8, 8, 4), (4, 4, 16), -1),
+    ("negative voxel", base_geo(delta_voxel=-1.0), (8, 8, 4), (4, 4, 16), -1),
+    ("parallel R != S", base_geo(), (8, 8, 4), (4, 5, 16), -1),
+    ("parallel drow != dv", base_geo(delta_row=2.0), (8, 8, 4), (4, 4, 16), -1),
+    ("parallel source_z", base_geo(source_z=np.zeros(4)), (8, 8, 4), (4, 4, 16), -1),
+    ("radius 0", base_geo(psf_radius=0), (8, 8, 4), (4, 4, 16), -1),
+    ("radius 5", base_geo(psf_radius=5), (8, 8, 4), (4, 4, 16), -1),
+    ("negative shape", base_geo(), (8, -8, 4), (4, 4, 16), -1),
+    ("source inside volume", base_geo(**dict(CONE, source_iso=5.0, source_detector=9.0)), (8, 8, 4), (4, 6, 16), -1),
+    ("detector before iso", base_geo(**dict(CONE, source_detector=90.0)), (8, 8, 4), (4, 6, 16), -1),
+    ("nan distance", base_geo(**dict(CONE, source_iso=math.nan)), (8, 8, 4), (4, 6, 16), -1),
+    ("index table too large", base_geo(num_views=40000, angles=np.zeros(40000)), (256, 256, 1),
+     (40000, 1, 16), -2),
+]
+
+
+@pytest.mark.parametrize("case", BAD, ids=lambda c: c[0])
+def test_invalid_requests_rejected_before_any_device_call(bp, case):
+    _, geo, rs, ss, code = case
+    with pytest.raises(bp.ProjError) as ei:
+        bp.plan_query(geo, rs, ss)
+    assert ei.value.status == code
+    # proj_create runs the same checks first, so it fails the same way on a
+    # machine without a GPU
+    lib = bp.load_library()
+    ga = bp._GeomArgs(geo, rs, ss)
+    h = ctypes.c_void_p(123)
+    st = lib.proj_create(ctypes.byref(ga.s), ga.rs, ga.ss, 0, ctypes.byref(h))
+    assert st == code and not h.value
+    assert lib.proj_last_error().decode()
+
+
+def test_null_arguments(bp):
+    lib = bp.load_library()
+    assert lib.proj_create(None, None, None, 0, None) == -1
+    assert lib.proj_forward(None, None, None, None) == -1
+    assert lib.proj_back(None, None, None, None) == -1
+    assert lib.proj_channel_index(None, None, None) == -1
+    lib.proj_destroy(None)                           # ignored
+    assert lib.proj_describe(None, None, 0) == -1
+
+
+def test_valid_geometry_without_gpu_fails_only_at_the_device(bp):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = bp.load_library()
+    w = W.get(W.SMALL)
+    ga = bp._GeomArgs(w.geometry(), w.recon_shape, w.sino_shape)
+    h = ctypes.c_void_p()
+    st = lib.proj_create(ctypes.byref(ga.s), ga.rs, ga.ss, 0, ctypes.byref(h))
+    assert st in (-1, -5)            # no device: invalid ordinal or HIP error
+    assert not h.value
+
+
+def test_product_path_fails_loudly_without_the_library(tmp_path):
+    import back_projectors_amd as m
+    saved = m._lib
+    try:
+        m._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            m.load_library(str(tmp_path / "missing.so"))
+    finally:
+        m._lib = saved

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU reference.
+
+Channel indices must match bit for bit; fp32 projections must be within
+relative L2 1e-5 and max relative error 1e-4 (denominator: the sum of
+|tap weight * input| reaching the entry), and the GPU pair must satisfy the
+adjoint identity within 1e-5.  Small geometries are compared element by
+element (several tiles, ragged edges in pixels, slices and views); the full
+benchmark sizes are compared on sampled views and pixels, which the reference
+computes one at a time.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from metrics import ADJOINT, adjoint_gap, assert_close
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def note(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def bp():
+    import back_projectors_amd as m
+    m.load_library()
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# Small geometries: ragged against the 16- and 32-pixel tiles and the slice
+# chunks, a few dozen views, every entry compared.
+PAR_RAGGED = W.Workload("parallel-45x70x20-37v", W.PARALLEL, 45, 70, 20, 37, 20, 90, seed_x=21, seed_y=22)
+PAR_FINE = W.Workload("parallel-33x29x9-31v-fine-r2", W.PARALLEL, 33, 29, 9, 31, 9, 80, dch=0.6,
+                      radius=2, seed_x=23, seed_y=24)
+PAR_WIDE = W.Workload("parallel-40x40x70-13v", W.PARALLEL, 40, 40, 70, 13, 70, 64, seed_x=25, seed_y=26)
+TRANS_SMALL = W.Workload("translation-40x48x12-9v", W.PARALLEL, 40, 48, 12, 9, 12, 96, shift_step=3.0,
+                         seed_x=27, seed_y=28)
+CONE_RAGGED = W.Workload("cone-37x40x30-23v", W.CONE_FLAT, 37, 40, 30, 23, 28, 60, dch=1.5, drow=1.5,
+                         sid=80.0, sdd=120.0, seed_x=29, seed_y=30)
+CONE_R2 = W.Workload("cone-20x24x18-11v-r2", W.CONE_FLAT, 20, 24, 18, 11, 30, 50, dch=0.9, drow=0.9,
+                     sid=40.0, sdd=70.0, radius=2, seed_x=31, seed_y=32)
+HELIX_SMALL = W.Workload("helical-36x36x40-47v", W.CONE_FLAT, 36, 36, 40, 47, 12, 60, dch=11 / 6,
+                         drow=11 / 6, sid=45.0, sdd=82.5, angle_step=2 * math.pi / 20, zsrc_step=0.6,
+                         seed_x=33, seed_y=34)
+SMALL_CASES = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, CONE_RAGGED, CONE_R2, HELIX_SMALL]
+
+
+def inputs(w):
+    rng = np.random.default_rng(w.seed_x)
+    x = w.recon_input() if w.phantom == "disk" else rng.standard_normal(w.recon_shape).astype(np.float32)
+    y = np.random.default_rng(w.seed_y).standard_normal(w.sino_shape).astype(np.float32)
+    return x, y
+
+
+@pytest.mark.parametrize("w", SMALL_CASES, ids=lambda w: w.name)
+def test_small_parity(bp, orc, w):
+    note(f"small parity {w.name} recon={w.recon_shape} sino={w.sino_shape}")
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    x, y = inputs(w)
+    # channel indices: bit-exact
+    assert np.array_equal(host(proj.channel_index()), orc.channel_index(g))
+    # forward
+    yo, ay = orc.forward(g, x, with_abs=True)
+    yg = host(proj.forward(dev(x)))
+    assert_close(yg, yo, ay, f"{w.name} forward")
+    # back (of an independent sinogram; the small disk case backs up the reference forward of x)
+    yin = yo.astype(np.float32) if w.phantom == "disk" else y
+    xo, ax = orc.back(g, yin, with_abs=True)
+    xg = host(proj.back(dev(yin)))
+    assert_close(xg, xo, ax, f"{w.name} back")
+    # adjoint identity of the GPU pair
+    ygy = host(proj.back(dev(y)))
+    gap = adjoint_gap(yg, y, x, ygy)
+    assert gap < ADJOINT, f"adjoint gap {gap:.2e}"
+    proj.close()
+
+
+def test_outputs_fully_overwritten_and_guards_untouched(bp, orc):
+    """NaN-prefilled outputs come back fully written; canaries just outside
+    the output ranges keep their values (adapted poison-the-padding test)."""
+    w = PAR_RAGGED
+    note(f"guard bands {w.name}")
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    x, y = inputs(w)
+    pad = 1024
+    ns, nr = int(np.prod(w.sino_shape)), int(np.prod(w.recon_shape))
+    sbuf = torch.full((ns + 2 * pad,), float("nan"), device="cuda:0")
+    rbuf = torch.full((nr + 2 * pad,), float("nan"), device="cuda:0")
+    sbuf[:pad] = 7.0
+    sbuf[-pad:] = 7.0
+    rbuf[:pad] = -3.0
+    rbuf[-pad:] = -3.0
+    sview = sbuf[pad:pad + ns].view(w.sino_shape)
+    rview = rbuf[pad:pad + nr].view(w.recon_shape)
+    proj.forward(dev(x), out=sview)
+    proj.back(dev(y), out=rview)
+    s, r = host(sbuf), host(rbuf)
+    assert np.all(s[:pad] == 7.0) and np.all(s[-pad:] == 7.0)
+    assert np.all(r[:pad] == -3.0) and np.all(r[-pad:] == -3.0)
+    assert np.all(np.isfinite(s[pad:-pad])) and np.all(np.isfinite(r[pad:-pad]))
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    yo, ay = orc.forward(g, x, with_abs=True)
+    assert_close(s[pad:-pad].reshape(w.sino_shape), yo, ay, "forward into a view")
+    proj.close()
+
+
+def test_repeat_calls_and_streams(bp):
+    """Calls are stateless: the same input gives the same values on a side
+    stream as on the default stream, and repeated calls agree."""
+    w = CONE_RAGGED
+    note(f"streams {w.name}")
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    x, y = inputs(w)
+    xd = dev(x)
+    a = proj.back(dev(y))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = proj.back(dev(y), stream=s)
+    s.synchronize()
+    c = proj.forward(xd)
+    d = proj.forward(xd)
+    assert np.array_equal(host(a), host(b))          # the gather is deterministic
+    assert np.allclose(host(c), host(d), rtol=1e-6, atol=1e-6)
+    proj.close()
+
+
+def test_empty_and_degenerate_shapes(bp):
+    """Zero views: back gives exact zeros.  Zero slices / pixels: nothing to
+    write.  A single pixel and a single view still projects correctly."""
+    note("empty shapes")
+    geo = dict(kind=0, num_views=0, angles=np.zeros(0), delta_channel=1.0)
+    p = bp.Projector(geo, (8, 8, 4), (0, 4, 16))
+    out = torch.full((8, 8, 4), 5.0, device="cuda:0")
+    p.back(torch.empty((0, 4, 16), device="cuda:0"), out=out)
+    assert host(out).max() == 0.0 and host(out).min() == 0.0
+    p.close()
+    geo = dict(kind=0, num_views=3, angles=np.array([0.0, 1.0, 2.0]), delta_channel=1.0)
+    p = bp.Projector(geo, (0, 5, 2), (3, 2, 10))
+    sino = torch.full((3, 2, 10), 5.0, device="cuda:0")
+    p.forward(torch.empty((0, 5, 2), device="cuda:0"), out=sino)
+    assert np.all(host(sino) == 0.0)
+    p.close()
+
+
+def test_single_voxel_matches_hand_value(bp):
+    """One unit voxel at theta = 0 lands whole in its channel (dv = 1)."""
+    note("single voxel")
+    geo = dict(kind=0, num_views=1, angles=np.array([0.0]), delta_channel=1.0)
+    p = bp.Projector(geo, (1, 1, 1), (1, 1, 11))
+    y = host(p.forward(torch.ones((1, 1, 1), device="cuda:0")))
+    expect = np.zeros((1, 1, 11), np.float32)
+    expect[0, 0, 5] = 1.0
+    assert np.array_equal(y, expect)
+    p.close()
+
+
+# ------------------------------------------------------------ full sizes ---
+FULL = ["parallel-512x512x64-720v", "cone-256x256x256-360v", "translation-512x512x32-64v",
+        "helical-512x512x96-1338v"]
+
+
+@pytest.fixture(scope="module")
+def full_cache():
+    return {}
+
+
+def full_setup(bp, orc, name, cache):
+    if name not in cache:
+        cache.clear()
+        torch.cuda.empty_cache()
+        w = W.get(name)
+        note(f"full setup {name}")
+        proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+        g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+        cache[name] = (w, proj, g)
+    return cache[name]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_index_bit_exact(bp, orc, name, full_cache):
+    w, proj, g = full_setup(bp, orc, name, full_cache)
+    note(f"full index {name}")
+    idx = host(proj.channel_index())
+    if w.nv * w.ny * w.nx <= 200_000_000:
+        ref = orc.channel_index(g)
+        assert np.array_equal(idx, ref)
+    else:
+        # the reference index of a view subset, through a geometry of those views
+        views = np.unique(np.linspace(0, w.nv - 1, 24).astype(int))
+        geo = w.geometry()
+        sub = dict(geo, num_views=len(views), angles=geo["angles"][views],
+                   source_z=None if geo["source_z"] is None else geo["source_z"][views],
+                   channel_shift=None if geo["channel_shift"] is None else geo["channel_shift"][views])
+        gs = orc.Geometry(sub, w.recon_shape, (len(views), w.nr, w.nc))
+        assert np.array_equal(idx[views], orc.channel_index(gs))
+
+
+def test_tie_canaries_on_gpu(bp, orc, full_cache):
+    """The 45 and 135 degree views of the 512x512 parallel geometry hold 512
+    exact half-integer channel coordinates each; they must round to even."""
+    w, proj, g = full_setup(bp, orc, "parallel-512x512x64-720v", full_cache)
+    idx = host(proj.channel_index())
+    u = orc.channel_coord(orc.Geometry(dict(w.geometry(), num_views=2, angles=w.angles()[[180, 540]]),
+                                       w.recon_shape, (2, w.nr, w.nc)))
+    for row, v in ((0, 180), (1, 540)):
+        ties = np.nonzero(u[row] == np.floor(u[row]) + 0.5)[0]
+        assert len(ties) == 512
+        assert np.all(idx[v, ties] % 2 == 0)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_forward_sampled_views(bp, orc, name, full_cache):
+    w, proj, g = full_setup(bp, orc, name, full_cache)
+    note(f"full forward {name}")
+    x = w.recon_input()
+    yg = host(proj.forward(dev(x)))
+    views = sorted({0, w.nv // 4, w.nv // 2 + 1, w.nv - 1})
+    if w.nv >= 720:
+        views = sorted(set(views) | {180, 540})
+    yo, ay = orc.forward_views(g, x, views, with_abs=True)
+    assert_close(yg[views], yo, ay, f"{name} forward views {views}")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_back_sampled_pixels(bp, orc, name, full_cache):
+    w, proj, g = full_setup(bp, orc, name, full_cache)
+    note(f"full back {name}")
+    y = w.sino_input()
+    xg = host(proj.back(dev(y))).reshape(w.ny * w.nx, w.ns)
+    rng = np.random.default_rng(77)
+    pix = np.unique(np.concatenate([rng.integers(0, w.ny * w.nx, 600),
+                                    [0, w.nx - 1, w.ny * w.nx - w.nx, w.ny * w.nx - 1,
+                                     (w.ny // 2) * w.nx + w.nx // 2]]))
+    xo, ax = orc.back_pixels(g, y, pix, with_abs=True)
+    assert_close(xg[pix], xo, ax, f"{name} back pixels")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_adjoint_identity(bp, orc, name, full_cache):
+    w, proj, g = full_setup(bp, orc, name, full_cache)
+    note(f"full adjoint {name}")
+    x = w.recon_input()
+    y = w.sino_input()
+    ax = host(proj.forward(dev(x)))
+    aty = host(proj.back(dev(y)))
+    gap = adjoint_gap(ax, y, x, aty)
+    assert gap < ADJOINT, f"{name}: adjoint gap {gap:.2e}"
