@@ -54,6 +54,84 @@ __global__ __launch_bounds__(256) void channel_index_kernel(Geo g, const ViewK *
     }
 }
 
+// Overlap of the unit cell centred at e with the centred box [-a/2, a/2].
+__device__ __forceinline__ double cell_overlap(double e, double a) {
+    const double hi = fmin(e + 0.5, a / 2.0);
+    const double lo = fmax(e - 0.5, -a / 2.0);
+    const double r = hi - lo;
+    return r > 0.0 ? r : 0.0;
+}
+
+// Parallel-beam tap records, one per (view, pixel): the first channel that can
+// carry weight, n_f, and the fp32 weights of channels n_f .. n_f + NTAP - 1.
+// The weights are L ov(n - u; W) evaluated in fp64 from the exact channel
+// coordinate and rounded once, taps outside [n_c - r, n_c + r] (the PSF radius)
+// or off the detector get weight 0, and a pixel none of whose taps reaches the
+// detector is marked with n_f = INT_MAX so the projectors skip it.
+__global__ __launch_bounds__(256) void par_taps_kernel(Geo g, const ViewK *__restrict__ views,
+                                                       int32_t *__restrict__ rec, int ntap) {
+    const int np = g.ny * g.nx;
+    const int64_t total = (int64_t)np * g.nv;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int v = (int)(e / np);
+        const int p = (int)(e - (int64_t)v * np);
+        const int i = p / g.nx;
+        const int j = p - i * g.nx;
+        const ViewK vk = views[v];
+        const double u = channel_coord_exact(g, vk, i, j);
+        const int nc = (int)rint(u);
+        // first cell with positive overlap, kept so that all ntap taps stay
+        // inside the PSF radius [n_c - r, n_c + r]
+        int nf = (int)floor(u - 0.5 * vk.W - 0.5) + 1;
+        if (nf < nc - g.radius) nf = nc - g.radius;
+        if (nf > nc + g.radius - ntap + 1) nf = nc + g.radius - ntap + 1;
+        int32_t *r = rec + e * (1 + ntap);
+        bool any = false;
+        for (int t = 0; t < ntap; ++t) {
+            const int n = nf + t;
+            double w = 0.0;
+            if (n <= nc + g.radius && n >= 0 && n < g.nc) w = vk.L * cell_overlap((double)n - u, vk.W);
+            const float wf = (float)w;
+            any = any || wf != 0.f;
+            r[1 + t] = __float_as_int(wf);
+        }
+        r[0] = any ? nf : INT32_MAX;
+    }
+}
+
+// The same records re-laid for the forward walk: for each view and forward
+// tile, the tile's pixels in the order of their channel coordinate (perm), each
+// record packed as ((n_f + 2^16) << 8 | pixel-in-tile, w_0, w_1, ...) in NREC
+// dwords; 0 in the first dword marks a pixel to skip (outside the image or
+// without a tap on the detector).
+__global__ __launch_bounds__(256) void par_walk_records_kernel(Geo g, const int32_t *__restrict__ rec,
+                                                               const uint8_t *__restrict__ perm,
+                                                               int32_t *__restrict__ out, int ntap, int nrec) {
+    constexpr int TP = FTX * FTY;
+    const int tiles_x = (g.nx + FTX - 1) / FTX;
+    const int ntiles = tiles_x * ((g.ny + FTY - 1) / FTY);
+    const int np = g.ny * g.nx;
+    const int64_t total = (int64_t)g.nv * ntiles * TP;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int s = (int)(e % TP);
+        const int64_t vt = e / TP;
+        const int tile = (int)(vt % ntiles);
+        const int v = (int)(vt / ntiles);
+        const int q = perm[(int64_t)v * TP + s];
+        const int i = (tile / tiles_x) * FTY + q / FTX;
+        const int j = (tile % tiles_x) * FTX + q % FTX;
+        int32_t *o = out + e * nrec;
+        for (int t = 0; t < nrec; ++t) o[t] = 0;
+        if (i >= g.ny || j >= g.nx) continue;
+        const int32_t *r = rec + ((int64_t)v * np + i * g.nx + j) * (1 + ntap);
+        if (r[0] == INT32_MAX) continue;
+        o[0] = ((r[0] + 65536) << 8) | q;
+        for (int t = 0; t < ntap; ++t) o[1 + t] = r[1 + t];
+    }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float4 *__restrict__ b4, float *__restrict__ tail,
                                                         int64_t n4, int ntail) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -68,6 +146,25 @@ hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, 
     const int64_t want = (total + 255) / 256;
     const int blocks = (int)(want < 65536 ? want : 65536);
     hipLaunchKernelGGL(channel_index_kernel, dim3(blocks), dim3(256), 0, st, g, views, idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st) {
+    const int64_t total = (int64_t)g.ny * g.nx * g.nv;
+    if (total == 0) return hipSuccess;
+    const int64_t want = (total + 255) / 256;
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(par_taps_kernel, dim3(blocks), dim3(256), 0, st, g, views, rec, ntap);
+    return hipGetLastError();
+}
+
+hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, const uint8_t *perm, int32_t *out, int ntap,
+                                   int nrec, hipStream_t st) {
+    const int64_t total = (int64_t)g.nv * ((g.nx + FTX - 1) / FTX) * ((g.ny + FTY - 1) / FTY) * FTX * FTY;
+    if (total == 0) return hipSuccess;
+    const int64_t want = (total + 255) / 256;
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(par_walk_records_kernel, dim3(blocks), dim3(256), 0, st, g, rec, perm, out, ntap, nrec);
     return hipGetLastError();
 }
 

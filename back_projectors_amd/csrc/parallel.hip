@@ -3,35 +3,40 @@
 // Detector row r sees slice r only (MBIRJAX "Projector kernels" page,
 // paragraph "Geometry decides whether a slice can stream"), so every
 // (view, pixel) pair has one set of channel taps shared by all slices of the
-// voxel cylinder.  Both kernels give each lane one pixel and loop over a chunk
-// of SL slices held in registers, so the fp64 tap weights of a (view, pixel)
-// pair are computed once per lane and reused SL times.
+// voxel cylinder.  Those taps -- the first channel n_f and NTAP fp32 weights --
+// come from the tap records the creation pass wrote in fp64; the projectors
+// do no geometry arithmetic and never round a coordinate.
 //
 // Back (gather; paragraph "Forward scatters, back gathers"): a workgroup owns
-// a BT x BT pixel tile and one slice chunk.  For each view it stages the
-// sinogram cells the tile can reach (a channel window, SL rows) in LDS with
-// coalesced reads, then every lane gathers its taps from LDS into per-slice
-// register accumulators.  Each voxel is written once; nothing collides.
+// a BT x BT pixel tile and a chunk of SL slices; lanes are pixels, each with
+// SL register accumulators.  Per view the sinogram cells the tile can reach
+// (a channel window of SL rows) are staged in LDS, channel-major with slices
+// fastest, by coalesced reads; each lane then reads its NTAP taps per slice
+// (adjacent channels, so pairs come in one ds_read2) and accumulates.  Every
+// voxel is written once and nothing collides.
 //
-// Forward (scatter without colliding global atomics): a workgroup owns an
-// FT x FT tile, keeps the tile's voxels in registers and, for each view of its
-// range, adds the taps into an LDS-private channel window.  Lanes of a 32-lane
-// half cover one tile row (or column, whichever runs across the rays), so in
-// one LDS atomic at most two lanes share an address.  The window is then added
-// to the sinogram with one coalesced global atomic per nonzero cell, i.e.
-// about 1.3/FT atomics per voxel-view instead of one per tap.
+// Forward (scatter with no colliding LDS or register updates): a workgroup
+// owns an FTX x FTY pixel tile and a chunk of 64 slices; lanes are slices and
+// each wave works on one view at a time.  The tile's voxels sit in LDS.  A
+// wave walks the tile's pixels in the order of their channel coordinate in
+// that view (a per-view permutation fixed at creation), so the channels it
+// touches only move forward: NTAP sliding registers hold the current channels
+// and a channel is spilled to the wave's own LDS window when the walk moves
+// past it.  The window is then added to the sinogram with coalesced global
+// atomics, one per cell per view and tile.  Float atomics in LDS are avoided on
+// purpose: on gfx950 they cost tens of times a plain read-modify-write.
 #include "launch.h"
-#include "taps.h"
 
 namespace bpamd {
 
-template <int SL, int R>
+template <int SL, int NTAP>
 __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restrict__ sino,
                                                            float *__restrict__ recon,
-                                                           const int32_t *__restrict__ idx,
+                                                           const int32_t *__restrict__ rec,
                                                            const ViewK *__restrict__ views, Geo g) {
     constexpr int NT = BT * BT;
     constexpr int SLP = SL + 1;           // LDS pitch of one channel column
+    constexpr int NREC = 1 + NTAP;
     extern __shared__ float win[];        // [nwcap][SLP], slices fastest
 
     const int tiles_x = (g.nx + BT - 1) / BT;
@@ -47,7 +52,6 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
     const bool valid = (i < g.ny) && (j < g.nx);
     const int np = g.ny * g.nx;
     const int p = valid ? i * g.nx + j : 0;
-    const double x = pix_x(g, j), y = pix_y(g, i);
 
     float acc[SL];
 #pragma unroll
@@ -60,29 +64,31 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
         const ViewK vk = views[v];
         const Window wd = tile_window(g, vk, ti0, ti1, tj0, tj1, k0, k0 + nk - 1);
         if (wd.nw <= 0) continue;          // the tile misses the detector in this view
+        // this lane's taps (issued before the barrier to hide their latency)
+        const int32_t *r = rec + ((int64_t)v * np + p) * NREC;
+        const int nf = valid ? r[0] : INT32_MAX;
+        float w[NTAP];
+#pragma unroll
+        for (int t = 0; t < NTAP; ++t) w[t] = valid ? __int_as_float(r[1 + t]) : 0.f;
         __syncthreads();
         // stage rows k0..k0+nk-1, channels n0..n0+nw-1 (zeros off the detector)
-        for (int r = grp; r < SL; r += NT / 32) {
-            const float *srow = sino + ((int64_t)v * g.nr + (k0 + r)) * g.nc;
+        for (int rr = grp; rr < SL; rr += NT / 32) {
+            const float *srow = sino + ((int64_t)v * g.nr + (k0 + rr)) * g.nc;
             for (int c = lane; c < wd.nw; c += 32) {
                 const int n = wd.n0 + c;
                 float val = 0.f;
-                if (r < nk && n >= 0 && n < g.nc) val = srow[n];
-                win[c * SLP + r] = val;
+                if (rr < nk && n >= 0 && n < g.nc) val = srow[n];
+                win[c * SLP + rr] = val;
             }
         }
         __syncthreads();
-        const int ncv = valid ? idx[(int64_t)v * np + p] : 0;
-        if (valid && ncv >= -R && ncv <= g.nc - 1 + R) {
-            const double u = x * vk.cd + y * vk.sd + vk.u0;
-            float w[2 * R + 1];
-            tap_weights<R>(u - (double)ncv, vk.W, vk.L, w);
-            const float *col = win + (ncv - R - wd.n0) * SLP;
+        if (nf != INT32_MAX) {
+            const float *col = win + (nf - wd.n0) * SLP;
 #pragma unroll
             for (int k = 0; k < SL; ++k) {
                 float s = acc[k];
 #pragma unroll
-                for (int t = 0; t <= 2 * R; ++t) s = fmaf(w[t], col[t * SLP + k], s);
+                for (int t = 0; t < NTAP; ++t) s = fmaf(w[t], col[t * SLP + k], s);
                 acc[k] = s;
             }
         }
@@ -95,142 +101,237 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
     }
 }
 
-template <int SL, int R>
-__global__ __launch_bounds__(FT *FT) void par_forward_kernel(const float *__restrict__ recon,
-                                                              float *__restrict__ sino,
-                                                              const int32_t *__restrict__ idx,
-                                                              const ViewK *__restrict__ views, Geo g,
-                                                              int nwcap, int vsplit) {
-    constexpr int NT = FT * FT;
-    constexpr int SLP = SL + 1;
-    extern __shared__ float win[];        // two buffers of [nwcap][SLP]
+template <int NTAP, int NREC>
+__global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__restrict__ recon,
+                                                               float *__restrict__ sino,
+                                                               const int32_t *__restrict__ wrec,
+                                                               const ViewK *__restrict__ views, Geo g, int nwcap,
+                                                               int vsplit) {
+    constexpr int TP = FTX * FTY;         // pixels per tile (two records per lane)
+    static_assert(TP == 128, "the walk keeps the tile's records in two registers per lane");
+    constexpr int XP = 64;                // LDS pitch of one voxel cylinder chunk
+    constexpr int WP = 65;                // LDS pitch of one window channel (slices fastest)
+    extern __shared__ float lds[];
+    float *xt = lds;                                   // [TP][XP]
+    const int lane = (int)threadIdx.x & 63;
+    // wave index, made visibly uniform so per-view work stays on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    float *win = lds + TP * XP + wave * nwcap * WP;    // this wave's window [nwcap][WP]
 
-    const int tiles_x = (g.nx + FT - 1) / FT;
-    const int tj0 = (int)(blockIdx.x % tiles_x) * FT;
-    const int ti0 = (int)(blockIdx.x / tiles_x) * FT;
-    const int tj1 = min(tj0 + FT, g.nx) - 1;
-    const int ti1 = min(ti0 + FT, g.ny) - 1;
-    const int k0 = (int)blockIdx.y * SL;
-    const int nk = min(SL, g.ns - k0);
-    const int np = g.ny * g.nx;
+    const int tiles_x = (g.nx + FTX - 1) / FTX;
+    const int ntiles = tiles_x * ((g.ny + FTY - 1) / FTY);
+    const int tile = (int)blockIdx.x;
+    const int tj0 = (tile % tiles_x) * FTX;
+    const int ti0 = (tile / tiles_x) * FTY;
+    const int tj1 = min(tj0 + FTX, g.nx) - 1;
+    const int ti1 = min(ti0 + FTY, g.ny) - 1;
+    const int k0 = (int)blockIdx.y * 64;
+    const int nk = min(64, g.ns - k0);
 
-    // lane -> pixel in the two orientations: along a row, or along a column
-    const int a = (int)threadIdx.x % FT, b = (int)threadIdx.x / FT;
-    const int ir = ti0 + b, jr = tj0 + a;     // row mode
-    const int ic = ti0 + a, jc = tj0 + b;     // column mode
-    const bool vr = ir < g.ny && jr < g.nx;
-    const bool vc = ic < g.ny && jc < g.nx;
-    float xr[SL], xc[SL];
-    {
-        const float *pr = recon + (int64_t)(vr ? ir * g.nx + jr : 0) * g.ns + k0;
-        const float *pc = recon + (int64_t)(vc ? ic * g.nx + jc : 0) * g.ns + k0;
-#pragma unroll
-        for (int k = 0; k < SL; ++k) {
-            xr[k] = (vr && k < nk) ? pr[k] : 0.f;
-            xc[k] = (vc && k < nk) ? pc[k] : 0.f;
-        }
+    // the tile's voxels, one 64-slice chunk per pixel
+    for (int e = (int)threadIdx.x; e < TP * 64; e += FW * 64) {
+        const int q = e >> 6, k = e & 63;
+        const int i = ti0 + q / FTX, j = tj0 + q % FTX;
+        float val = 0.f;
+        if (i < g.ny && j < g.nx && k < nk) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + k];
+        xt[q * XP + k] = val;
     }
-
-    const int cap = nwcap * SLP;
-    for (int e = (int)threadIdx.x; e < 2 * cap; e += NT) win[e] = 0.f;
+    for (int e = lane; e < nwcap * WP; e += 64) win[e] = 0.f;
     __syncthreads();
 
-    // this block's view range, visited from a staggered start so that tiles
-    // along one ray do not hit the same sinogram rows at the same time
     const int vper = (g.nv + vsplit - 1) / vsplit;
     const int vbeg = (int)blockIdx.z * vper;
     const int vend = min(g.nv, vbeg + vper);
     const int cnt = vend - vbeg;
-    const int start = cnt > 0 ? (int)((blockIdx.x * 7u + blockIdx.y * 3u) % (unsigned)cnt) : 0;
-
-    for (int it = 0; it < cnt; ++it) {
+    // staggered start, so that tiles along one ray reach a view at different times
+    const int start = cnt > 0 ? (int)((blockIdx.x * 37u + blockIdx.y * 11u) % (unsigned)cnt) : 0;
+    auto view_of = [&](int it) {
         int v = vbeg + start + it;
-        if (v >= vend) v -= cnt;
-        const ViewK vk = views[v];
+        return v >= vend ? v - cnt : v;
+    };
+    // the (view, tile) records: lane l holds walk steps l and l + 64
+    auto load_records = [&](int v, int (&ra)[NREC], int (&rb)[NREC]) {
+        const int32_t *base = wrec + ((int64_t)v * ntiles + tile) * TP * NREC;
+#pragma unroll
+        for (int t = 0; t < NREC; ++t) {
+            ra[t] = base[lane * NREC + t];
+            rb[t] = base[(lane + 64) * NREC + t];
+        }
+    };
+
+    int ra[NREC], rb[NREC];
+    int it = wave;
+    int v = it < cnt ? view_of(it) : 0;
+    if (it < cnt) load_records(v, ra, rb);
+    for (; it < cnt; it += FW) {
+        const int vc = v;
+        int na[NREC], nb[NREC];
+        if (it + FW < cnt) {              // prefetch the next view's records
+            v = view_of(it + FW);
+            load_records(v, na, nb);
+        }
+        const ViewK vk = views[vc];
         const Window wd = tile_window(g, vk, ti0, ti1, tj0, tj1, k0, k0 + nk - 1);
-        float *buf = win + (it & 1) * cap;
-        const bool rowmode = fabs(vk.cd) >= fabs(vk.sd);
-        const int i = rowmode ? ir : ic, j = rowmode ? jr : jc;
-        const bool valid = (rowmode ? vr : vc) && wd.nw > 0;
-        const int ncv = valid ? idx[(int64_t)v * np + i * g.nx + j] : 0;
-        if (valid && ncv >= -R && ncv <= g.nc - 1 + R) {
-            const double u = pix_x(g, j) * vk.cd + pix_y(g, i) * vk.sd + vk.u0;
-            float w[2 * R + 1];
-            tap_weights<R>(u - (double)ncv, vk.W, vk.L, w);
-            float *col = buf + (ncv - R - wd.n0) * SLP;
-            if (rowmode) {
+        if (wd.nw > 0) {
+            float acc[NTAP];
 #pragma unroll
-                for (int k = 0; k < SL; ++k)
+            for (int t = 0; t < NTAP; ++t) acc[t] = 0.f;
+            int cur = INT32_MIN;           // channel held by acc[0]; none yet
+            int hi = INT32_MIN;            // highest channel spilled so far in this walk
+            // The window is all zeros at the start of a walk, so the first spill
+            // of a channel is a plain store; only a channel met again (the walk
+            // order is monotone up to fp64 rounding of the sort key) is added to.
+            auto spill = [&](int n, float a) {
+                float *pw = win + (n - wd.n0) * WP + lane;
+                if (n > hi) {
+                    *pw = a;
+                    hi = n;
+                } else {
+                    *pw += a;
+                }
+            };
+            auto step = [&](int packed, float xv, int s, const int (&rr)[NREC]) {
+                if (packed == 0) return;
+                const int nf = (packed >> 8) - 65536;
+                if (nf != cur) {
+                    const int d = nf - cur;
+                    if (cur == INT32_MIN || d < 0 || d >= NTAP) {
+                        if (cur != INT32_MIN) {
 #pragma unroll
-                    for (int t = 0; t <= 2 * R; ++t) atomicAdd(&col[t * SLP + k], w[t] * xr[k]);
-            } else {
+                            for (int t = 0; t < NTAP; ++t) spill(cur + t, acc[t]);
+                        }
 #pragma unroll
-                for (int k = 0; k < SL; ++k)
+                        for (int t = 0; t < NTAP; ++t) acc[t] = 0.f;
+                    } else {
 #pragma unroll
-                    for (int t = 0; t <= 2 * R; ++t) atomicAdd(&col[t * SLP + k], w[t] * xc[k]);
+                        for (int t = 0; t < NTAP - 1; ++t)
+                            if (t < d) spill(cur + t, acc[t]);
+#pragma unroll
+                        for (int t = 0; t < NTAP; ++t) {
+                            float nv = 0.f;
+#pragma unroll
+                            for (int dd = 1; dd < NTAP; ++dd)
+                                if (d == dd && t + dd < NTAP) nv = acc[t + dd];
+                            acc[t] = nv;
+                        }
+                    }
+                    cur = nf;
+                }
+#pragma unroll
+                for (int t = 0; t < NTAP; ++t)
+                    acc[t] = fmaf(__int_as_float(__builtin_amdgcn_readlane(rr[1 + t], s)), xv, acc[t]);
+            };
+            auto walk = [&](const int (&rr)[NREC]) {
+                for (int s = 0; s < 64; s += 4) {
+                    // four steps' voxel reads issued together
+                    int pk[4];
+                    float xv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) pk[u] = __builtin_amdgcn_readlane(rr[0], s + u);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) xv[u] = xt[(pk[u] & 255) * XP + lane];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) step(pk[u], xv[u], s + u, rr);
+                }
+            };
+            walk(ra);
+            walk(rb);
+            if (cur != INT32_MIN) {
+#pragma unroll
+                for (int t = 0; t < NTAP; ++t) spill(cur + t, acc[t]);
+            }
+            // add the window to the sinogram: lanes along channels, coalesced
+            for (int k = 0; k < nk; ++k) {
+                float *srow = sino + ((int64_t)vc * g.nr + (k0 + k)) * g.nc;
+                for (int c = lane; c < wd.nw; c += 64) {
+                    const float val = win[c * WP + k];
+                    win[c * WP + k] = 0.f;
+                    const int n = wd.n0 + c;
+                    if (val != 0.f && n >= 0 && n < g.nc) unsafeAtomicAdd(&srow[n], val);
+                }
             }
         }
-        __syncthreads();
-        // flush: rows k (slices), channels n0..n0+nw-1; clear as we go
-        const int lane = (int)threadIdx.x & 31;
-        for (int r = (int)threadIdx.x >> 5; r < nk; r += NT / 32) {
-            float *srow = sino + ((int64_t)v * g.nr + (k0 + r)) * g.nc;
-            for (int c = lane; c < wd.nw; c += 32) {
-                const float val = buf[c * SLP + r];
-                buf[c * SLP + r] = 0.f;
-                const int n = wd.n0 + c;
-                if (val != 0.f && n >= 0 && n < g.nc) unsafeAtomicAdd(&srow[n], val);
-            }
+#pragma unroll
+        for (int t = 0; t < NREC; ++t) {
+            ra[t] = na[t];
+            rb[t] = nb[t];
         }
     }
 }
 
-template <int SL, int R>
+template <int SL, int NTAP>
 static hipError_t par_back_t(const Plan &p, const float *sino, float *recon, hipStream_t st) {
     const Geo &g = p.g;
     const int tiles = ((g.nx + BT - 1) / BT) * ((g.ny + BT - 1) / BT);
     const int chunks = (g.ns + SL - 1) / SL;
-    hipLaunchKernelGGL((par_back_kernel<SL, R>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino, recon,
-                       p.idx, p.views, g);
+    hipLaunchKernelGGL((par_back_kernel<SL, NTAP>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
+                       recon, p.rec, p.views, g);
     return hipGetLastError();
 }
 
-template <int SL, int R>
+template <int NTAP>
 static hipError_t par_fwd_t(const Plan &p, const float *recon, float *sino, hipStream_t st) {
     const Geo &g = p.g;
-    const int tiles = ((g.nx + FT - 1) / FT) * ((g.ny + FT - 1) / FT);
-    const int chunks = (g.ns + SL - 1) / SL;
-    hipLaunchKernelGGL((par_forward_kernel<SL, R>), dim3(tiles, chunks, p.fwd_vsplit), dim3(FT * FT), p.fwd_lds,
-                       st, recon, sino, p.idx, p.views, g, p.fwd_nwcap, p.fwd_vsplit);
+    const int tiles = ((g.nx + FTX - 1) / FTX) * ((g.ny + FTY - 1) / FTY);
+    const int chunks = (g.ns + 63) / 64;
+    constexpr int NREC = NTAP <= 3 ? 4 : 8;
+    hipLaunchKernelGGL((par_forward_kernel<NTAP, NREC>), dim3(tiles, chunks, p.fwd_vsplit), dim3(FW * 64), p.fwd_lds,
+                       st, recon, sino, p.wrec, p.views, g, p.fwd_nwcap, p.fwd_vsplit);
     return hipGetLastError();
 }
 
-#define BPAMD_DISPATCH_R(FN, SLV, ...)                         \
-    switch (p.g.radius) {                                      \
-    case 1: return FN<SLV, 1>(__VA_ARGS__);                    \
-    case 2: return FN<SLV, 2>(__VA_ARGS__);                    \
-    case 3: return FN<SLV, 3>(__VA_ARGS__);                    \
-    case 4: return FN<SLV, 4>(__VA_ARGS__);                    \
-    default: return hipErrorInvalidValue;                      \
+#define BPAMD_DISPATCH_NTAP(FN, ...)                                                                          \
+    switch (p.ntap) {                                                                                         \
+    case 2: return FN<2>(__VA_ARGS__);                                                                        \
+    case 3: return FN<3>(__VA_ARGS__);                                                                        \
+    case 4: return FN<4>(__VA_ARGS__);                                                                        \
+    case 5: return FN<5>(__VA_ARGS__);                                                                        \
+    case 6: return FN<6>(__VA_ARGS__);                                                                        \
+    case 7: return FN<7>(__VA_ARGS__);                                                                        \
+    default: return hipErrorInvalidValue;                                                                     \
     }
+
+template <int SL>
+static hipError_t par_back_sl(const Plan &p, const float *sino, float *recon, hipStream_t st) {
+    switch (p.ntap) {
+    case 2: return par_back_t<SL, 2>(p, sino, recon, st);
+    case 3: return par_back_t<SL, 3>(p, sino, recon, st);
+    case 4: return par_back_t<SL, 4>(p, sino, recon, st);
+    case 5: return par_back_t<SL, 5>(p, sino, recon, st);
+    case 6: return par_back_t<SL, 6>(p, sino, recon, st);
+    case 7: return par_back_t<SL, 7>(p, sino, recon, st);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, hipStream_t st) {
     switch (p.back_sl) {
-    case 8: BPAMD_DISPATCH_R(par_back_t, 8, p, sino, recon, st)
-    case 16: BPAMD_DISPATCH_R(par_back_t, 16, p, sino, recon, st)
-    case 32: BPAMD_DISPATCH_R(par_back_t, 32, p, sino, recon, st)
-    case 64: BPAMD_DISPATCH_R(par_back_t, 64, p, sino, recon, st)
+    case 8: return par_back_sl<8>(p, sino, recon, st);
+    case 16: return par_back_sl<16>(p, sino, recon, st);
+    case 32: return par_back_sl<32>(p, sino, recon, st);
+    case 64: return par_back_sl<64>(p, sino, recon, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st) {
-    switch (p.fwd_sl) {
-    case 8: BPAMD_DISPATCH_R(par_fwd_t, 8, p, recon, sino, st)
-    case 16: BPAMD_DISPATCH_R(par_fwd_t, 16, p, recon, sino, st)
-    case 32: BPAMD_DISPATCH_R(par_fwd_t, 32, p, recon, sino, st)
+    BPAMD_DISPATCH_NTAP(par_fwd_t, p, recon, sino, st)
+}
+
+// Dynamic LDS above the default limit needs the opt-in attribute; called once
+// per kernel by the planner when a plan asks for more.
+hipError_t par_forward_allow_lds(int ntap, size_t bytes) {
+    const void *f = nullptr;
+    switch (ntap) {
+    case 2: f = (const void *)par_forward_kernel<2, 4>; break;
+    case 3: f = (const void *)par_forward_kernel<3, 4>; break;
+    case 4: f = (const void *)par_forward_kernel<4, 8>; break;
+    case 5: f = (const void *)par_forward_kernel<5, 8>; break;
+    case 6: f = (const void *)par_forward_kernel<6, 8>; break;
+    case 7: f = (const void *)par_forward_kernel<7, 8>; break;
     default: return hipErrorInvalidValue;
     }
+    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 }  // namespace bpamd

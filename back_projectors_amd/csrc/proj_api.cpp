@@ -40,7 +40,8 @@ proj_status ok() {
 }
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;      // work arrays stay below 2^31 elements
-constexpr size_t kMaxLds = 64 * 1024;                 // dynamic LDS per workgroup used by the plan
+constexpr size_t kMaxLds = 64 * 1024;                 // dynamic LDS per workgroup without opt-in
+constexpr size_t kMaxLdsOptIn = 160 * 1024;           // gfx950 LDS per workgroup
 
 bool finite(double v) { return std::isfinite(v); }
 
@@ -52,6 +53,9 @@ struct proj_handle_s {
     int64_t recon_elems = 0, sino_elems = 0, index_elems = 0;
     ViewK *d_views = nullptr;
     int32_t *d_idx = nullptr;
+    int32_t *d_rec = nullptr;       // parallel tap records
+    int32_t *d_wrec = nullptr;      // parallel tap records in forward walk order
+    uint8_t *d_perm = nullptr;      // parallel per-view tile order
     size_t table_bytes = 0;
 };
 
@@ -79,15 +83,15 @@ struct WinMax {
     int nw = 0, nr = 0;
 };
 
-// Largest window over all views, tiles of edge `t` and slice chunks of `sl`.
-WinMax max_window(const Geo &g, const std::vector<ViewK> &views, int t, int sl) {
+// Largest window over all views, tiles of tx x ty pixels and slice chunks of `sl`.
+WinMax max_window(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_, int sl) {
     WinMax m;
-    const int ty = (g.ny + t - 1) / t, tx = (g.nx + t - 1) / t, nch = (g.ns + sl - 1) / sl;
+    const int ty = (g.ny + ty_ - 1) / ty_, tx = (g.nx + tx_ - 1) / tx_, nch = (g.ns + sl - 1) / sl;
     for (int v = 0; v < g.nv; ++v)
         for (int a = 0; a < ty; ++a)
             for (int b = 0; b < tx; ++b) {
-                const int i0 = a * t, i1 = std::min(i0 + t, g.ny) - 1;
-                const int j0 = b * t, j1 = std::min(j0 + t, g.nx) - 1;
+                const int i0 = a * ty_, i1 = std::min(i0 + ty_, g.ny) - 1;
+                const int j0 = b * tx_, j1 = std::min(j0 + tx_, g.nx) - 1;
                 for (int c = 0; c < (g.kind == 0 ? 1 : nch); ++c) {
                     const int k0 = c * sl, k1 = std::min(k0 + sl, g.ns) - 1;
                     const Window w = tile_window(g, views[v], i0, i1, j0, j1, k0, k1);
@@ -175,40 +179,61 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
     // Slice chunk per lane: the least padding first, then smaller chunks while
     // the detector window of a tile does not fit in LDS.
     const bool par = g.kind == 0;
-    const std::vector<int> back_opts = par ? std::vector<int>{8, 16, 32, 64} : std::vector<int>{8, 16, 32};
-    const std::vector<int> fwd_opts = par ? std::vector<int>{8, 16, 32} : std::vector<int>{8, 16};
-    auto back_bytes = [&](int sl, int &nwcap, int &nrcap) {
-        const WinMax w = max_window(g, views, BT, sl);
-        nwcap = w.nw + 2;
-        nrcap = par ? sl : ((w.nr + 2) | 1);       // odd pitch: conflict-free column strides
-        return par ? (size_t)nwcap * (sl + 1) * sizeof(float) : (size_t)nwcap * nrcap * sizeof(float);
-    };
-    auto fwd_bytes = [&](int sl, int &nwcap, int &nrcap) {
-        const WinMax w = max_window(g, views, FT, sl);
-        nwcap = w.nw + 2;
-        nrcap = par ? sl : ((w.nr + 2) | 1);
-        return 2 * (par ? (size_t)nwcap * (sl + 1) * sizeof(float) : (size_t)nwcap * nrcap * sizeof(float));
-    };
-    for (int sl = pick_chunk(S, back_opts);; sl /= 2) {
-        plan.back_sl = sl;
-        plan.back_lds = back_bytes(sl, plan.back_nwcap, plan.back_nrcap);
-        if (plan.back_lds <= kMaxLds || sl == back_opts.front()) break;
+    if (par) {
+        // taps that can carry weight: a box of width W covers at most ceil(W) + 1 cells
+        double wmax = 0.0;
+        for (const ViewK &k : views) wmax = std::max(wmax, k.W);
+        plan.ntap = (int)std::min<double>(2.0 * g.radius + 1.0, std::ceil(wmax) + 1.0);
+        plan.ntap = std::max(plan.ntap, 2);
+        if (plan.ntap > 7) return fail(PROJ_ERR_UNSUPPORTED, "more than 7 channel taps per voxel (detector far finer than the voxels)");
+        if (C + 4 * g.radius >= ((int64_t)1 << 23) - 65536) return fail(PROJ_ERR_UNSUPPORTED, "too many detector channels");
+        plan.nrec = plan.ntap <= 3 ? 4 : 8;
+        for (int sl = pick_chunk(S, {8, 16, 32, 64});; sl /= 2) {
+            const WinMax w = max_window(g, views, BT, BT, sl);
+            plan.back_sl = sl;
+            plan.back_nwcap = w.nw + 2;
+            plan.back_lds = (size_t)plan.back_nwcap * (sl + 1) * sizeof(float);
+            if (plan.back_lds <= kMaxLds || sl == 8) break;
+        }
+        const WinMax wf = max_window(g, views, FTX, FTY, 64);
+        plan.fwd_sl = 64;
+        plan.fwd_nwcap = wf.nw + 2;
+        plan.fwd_lds = ((size_t)FTX * FTY * 64 + (size_t)FW * plan.fwd_nwcap * 65) * sizeof(float);
+    } else {
+        auto back_bytes = [&](int sl, int &nwcap, int &nrcap) {
+            const WinMax w = max_window(g, views, BT, BT, sl);
+            nwcap = w.nw + 2;
+            nrcap = (w.nr + 2) | 1;                 // odd pitch: conflict-free column strides
+            return (size_t)nwcap * nrcap * sizeof(float);
+        };
+        auto fwd_bytes = [&](int sl, int &nwcap, int &nrcap) {
+            const WinMax w = max_window(g, views, FT, FT, sl);
+            nwcap = w.nw + 2;
+            nrcap = (w.nr + 2) | 1;
+            return 2 * (size_t)nwcap * nrcap * sizeof(float);
+        };
+        for (int sl = pick_chunk(S, {8, 16, 32});; sl /= 2) {
+            plan.back_sl = sl;
+            plan.back_lds = back_bytes(sl, plan.back_nwcap, plan.back_nrcap);
+            if (plan.back_lds <= kMaxLds || sl == 8) break;
+        }
+        for (int sl = pick_chunk(S, {8, 16});; sl /= 2) {
+            plan.fwd_sl = sl;
+            plan.fwd_lds = fwd_bytes(sl, plan.fwd_nwcap, plan.fwd_nrcap);
+            if (plan.fwd_lds <= kMaxLds || sl == 8) break;
+        }
     }
-    for (int sl = pick_chunk(S, fwd_opts);; sl /= 2) {
-        plan.fwd_sl = sl;
-        plan.fwd_lds = fwd_bytes(sl, plan.fwd_nwcap, plan.fwd_nrcap);
-        if (plan.fwd_lds <= kMaxLds || sl == fwd_opts.front()) break;
-    }
-    if (plan.back_lds > kMaxLds || plan.fwd_lds > kMaxLds) {
+    if (plan.back_lds > kMaxLds || plan.fwd_lds > kMaxLdsOptIn) {
         char buf[160];
-        std::snprintf(buf, sizeof buf, "detector window too large for LDS (back %zu B, forward %zu B, limit %zu B)",
-                      plan.back_lds, plan.fwd_lds, kMaxLds);
+        std::snprintf(buf, sizeof buf, "detector window too large for LDS (back %zu B, forward %zu B)",
+                      plan.back_lds, plan.fwd_lds);
         return fail(PROJ_ERR_UNSUPPORTED, buf);
     }
     const int64_t chunks_b = (S + plan.back_sl - 1) / plan.back_sl;
     const int64_t chunks_f = (S + plan.fwd_sl - 1) / plan.fwd_sl;
     if (chunks_b > 65535 || chunks_f > 65535) return fail(PROJ_ERR_UNSUPPORTED, "too many slices");
-    const int64_t ftiles = ((Nx + FT - 1) / FT) * ((Ny + FT - 1) / FT);
+    const int64_t ftiles = par ? ((Nx + FTX - 1) / FTX) * ((Ny + FTY - 1) / FTY)
+                               : ((Nx + FT - 1) / FT) * ((Ny + FT - 1) / FT);
     // enough workgroups to fill 256 CUs a few times over; each split re-reads its tile
     int64_t vs = (2048 + ftiles * chunks_f - 1) / (ftiles * chunks_f);
     vs = std::max<int64_t>(1, std::min<int64_t>(vs, std::min<int64_t>(V, 64)));
@@ -218,14 +243,16 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
 
 int describe(const Plan &p, int64_t table_bytes, char *buf, int len) {
     const Geo &g = p.g;
-    return std::snprintf(buf, (size_t)std::max(len, 0),
-                         "kind=%s V=%d R=%d C=%d Ny=%d Nx=%d S=%d radius=%d | back: %dx%d px tile, %d slices/lane, "
-                         "window %d ch x %d rows, %zu B LDS | forward: %dx%d px tile, %d slices/lane, "
-                         "LDS window %d ch x %d rows x2, %zu B LDS, %d view ranges | index table %lld B",
-                         g.kind == 0 ? "parallel" : "cone_flat", g.nv, g.nr, g.nc, g.ny, g.nx, g.ns, g.radius, BT, BT,
-                         p.back_sl, p.back_nwcap, g.kind == 0 ? p.back_sl : p.back_nrcap, p.back_lds, FT, FT,
-                         p.fwd_sl, p.fwd_nwcap, g.kind == 0 ? p.fwd_sl : p.fwd_nrcap, p.fwd_lds, p.fwd_vsplit,
-                         (long long)table_bytes);
+    const bool par = g.kind == 0;
+    return std::snprintf(
+        buf, (size_t)std::max(len, 0),
+        "kind=%s V=%d R=%d C=%d Ny=%d Nx=%d S=%d radius=%d taps=%d | back: %dx%d px tile, lanes=pixels, %d "
+        "slices/lane, window %d ch x %d rows, %zu B LDS | forward: %dx%d px tile, %s, %d slices, window %d ch x %d "
+        "rows, %zu B LDS, %d view ranges | tables %lld B",
+        par ? "parallel" : "cone_flat", g.nv, g.nr, g.nc, g.ny, g.nx, g.ns, g.radius, par ? p.ntap : 2 * g.radius + 1,
+        BT, BT, p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, par ? FTX : FT, par ? FTY : FT,
+        par ? "lanes=slices, wave per view, channel-ordered walk" : "lanes=pixels, LDS window", p.fwd_sl,
+        p.fwd_nwcap, par ? p.fwd_sl : p.fwd_nrcap, p.fwd_lds, p.fwd_vsplit, (long long)table_bytes);
 }
 
 bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
@@ -323,17 +350,65 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
             e = hipMemcpy(h->d_views, views.data(), views.size() * sizeof(ViewK), hipMemcpyHostToDevice);
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(views)");
         }
+        size_t rec_bytes = 0, perm_bytes = 0;
         if (h->index_elems > 0) {
             e = hipMalloc((void **)&h->d_idx, (size_t)h->index_elems * sizeof(int32_t));
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(index table)");
             e = launch_channel_index(geo, h->d_views, h->d_idx, nullptr);
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "channel index pass");
+            if (geo.kind == 0 && plan.ntap > 0) {
+                rec_bytes = (size_t)h->index_elems * (1 + plan.ntap) * sizeof(int32_t);
+                e = hipMalloc((void **)&h->d_rec, rec_bytes);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(tap records)");
+                e = launch_par_taps(geo, h->d_views, h->d_rec, plan.ntap, nullptr);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "tap record pass");
+                // per view, the forward tile's pixels ordered by channel coordinate
+                constexpr int TP = FTX * FTY;
+                std::vector<uint8_t> perm((size_t)geo.nv * TP);
+                std::vector<int> order(TP);
+                std::vector<double> key(TP);
+                for (int v = 0; v < geo.nv; ++v) {
+                    for (int q = 0; q < TP; ++q) {
+                        key[q] = (double)(q % FTX) * views[v].cd + (double)(q / FTX) * views[v].sd;
+                        order[q] = q;
+                    }
+                    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return key[a] < key[b]; });
+                    for (int q = 0; q < TP; ++q) perm[(size_t)v * TP + q] = (uint8_t)order[q];
+                }
+                perm_bytes = perm.size();
+                e = hipMalloc((void **)&h->d_perm, perm_bytes);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(tile order)");
+                e = hipMemcpy(h->d_perm, perm.data(), perm_bytes, hipMemcpyHostToDevice);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(tile order)");
+                const int64_t ntiles = (int64_t)((geo.nx + FTX - 1) / FTX) * ((geo.ny + FTY - 1) / FTY);
+                const size_t wrec_bytes = (size_t)geo.nv * ntiles * TP * plan.nrec * sizeof(int32_t);
+                e = hipMalloc((void **)&h->d_wrec, wrec_bytes);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(walk records)");
+                e = launch_par_walk_records(geo, h->d_rec, h->d_perm, h->d_wrec, plan.ntap, plan.nrec, nullptr);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "walk record pass");
+                rec_bytes += wrec_bytes;
+                if (plan.fwd_lds > kMaxLds) {
+                    int lim = 0;
+                    e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, hip_device);
+                    if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipDeviceGetAttribute");
+                    if ((size_t)lim < plan.fwd_lds) {
+                        proj_destroy(h);
+                        return fail(PROJ_ERR_UNSUPPORTED, "device LDS per workgroup below the forward plan's need");
+                    }
+                    e = par_forward_allow_lds(plan.ntap, plan.fwd_lds);
+                    if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipFuncSetAttribute(LDS)");
+                }
+            }
             e = hipDeviceSynchronize();
-            if (e != hipSuccess) return cleanup(PROJ_OK, e, "channel index pass");
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "table passes");
         }
-        h->table_bytes = (size_t)h->index_elems * sizeof(int32_t) + views.size() * sizeof(ViewK);
+        h->table_bytes = (size_t)h->index_elems * sizeof(int32_t) + views.size() * sizeof(ViewK) + rec_bytes +
+                         perm_bytes;
         h->plan.views = h->d_views;
         h->plan.idx = h->d_idx;
+        h->plan.rec = h->d_rec;
+        h->plan.perm = h->d_perm;
+        h->plan.wrec = h->d_wrec;
         if (std::getenv("PROJ_LOG")) {
             char buf[512];
             describe(h->plan, (int64_t)h->table_bytes, buf, sizeof buf);
@@ -408,6 +483,9 @@ void proj_destroy(proj_handle h) {
     {
         DeviceGuard dg(h->device);
         if (h->d_idx) (void)hipFree(h->d_idx);
+        if (h->d_rec) (void)hipFree(h->d_rec);
+        if (h->d_perm) (void)hipFree(h->d_perm);
+        if (h->d_wrec) (void)hipFree(h->d_wrec);
         if (h->d_views) (void)hipFree(h->d_views);
     }
     delete h;

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from metrics import ADJOINT, adjoint_gap, assert_close
+from metrics import ADJOINT, adjoint_gap, assert_close, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -137,7 +137,8 @@ def test_repeat_calls_and_streams(bp):
     c = proj.forward(xd)
     d = proj.forward(xd)
     assert np.array_equal(host(a), host(b))          # the gather is deterministic
-    assert np.allclose(host(c), host(d), rtol=1e-6, atol=1e-6)
+    # the forward's atomic flushes may add in another order: equal up to rounding
+    assert rel_l2(host(c), host(d)) < 1e-6
     proj.close()
 
 
