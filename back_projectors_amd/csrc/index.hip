@@ -100,36 +100,58 @@ __global__ __launch_bounds__(256) void par_taps_kernel(Geo g, const ViewK *__res
     }
 }
 
-// The same records re-laid for the forward walk: for each view and forward
-// tile, the tile's pixels in the order of their channel coordinate (perm), each
-// record packed as ((n_f + 2^16) << 8 | pixel-in-tile, w_0, w_1, ...) in NREC
-// dwords; 0 in the first dword marks a pixel to skip (outside the image or
-// without a tap on the detector).
-__global__ __launch_bounds__(256) void par_walk_records_kernel(Geo g, const int32_t *__restrict__ rec,
-                                                               const uint8_t *__restrict__ perm,
-                                                               int32_t *__restrict__ out, int ntap, int nrec) {
+// The same records re-laid for the forward walk.  One wave per (view, forward
+// tile): the tile's FTX*FTY pixels are ordered by their first tap channel n_f
+// (ties by pixel index), so a walk in this order never returns to a channel it
+// has passed.  Record r holds, in NREC dwords,
+//   dword 0: pixel-in-tile q (bits 0-7; FTX*FTY = a zero row for skipped
+//            entries), advance code (bits 8-10) and n_f + 2^16 (bits 11-31);
+//   dwords 1..: the NTAP tap weights (0 for skipped entries).
+// The advance code says how the walk's window of NTAP channels moves after
+// this record: 0 stay, 1..NTAP-1 move up by that many channels, 7 jump to the
+// next record's n_f.  Skipped pixels (outside the image, or no tap on the
+// detector) sort last with zero weights.
+__global__ __launch_bounds__(64) void par_walk_records_kernel(Geo g, const int32_t *__restrict__ rec,
+                                                              int32_t *__restrict__ out, int ntap, int nrec) {
     constexpr int TP = FTX * FTY;
+    static_assert(TP == 64, "one wave sorts one tile");
+    __shared__ int s_nf[TP];
+    __shared__ int s_sorted_nf[TP];
     const int tiles_x = (g.nx + FTX - 1) / FTX;
     const int ntiles = tiles_x * ((g.ny + FTY - 1) / FTY);
+    const int64_t vt = blockIdx.x;
+    const int tile = (int)(vt % ntiles);
+    const int v = (int)(vt / ntiles);
     const int np = g.ny * g.nx;
-    const int64_t total = (int64_t)g.nv * ntiles * TP;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int s = (int)(e % TP);
-        const int64_t vt = e / TP;
-        const int tile = (int)(vt % ntiles);
-        const int v = (int)(vt / ntiles);
-        const int q = perm[(int64_t)v * TP + s];
-        const int i = (tile / tiles_x) * FTY + q / FTX;
-        const int j = (tile % tiles_x) * FTX + q % FTX;
-        int32_t *o = out + e * nrec;
-        for (int t = 0; t < nrec; ++t) o[t] = 0;
-        if (i >= g.ny || j >= g.nx) continue;
-        const int32_t *r = rec + ((int64_t)v * np + i * g.nx + j) * (1 + ntap);
-        if (r[0] == INT32_MAX) continue;
-        o[0] = ((r[0] + 65536) << 8) | q;
-        for (int t = 0; t < ntap; ++t) o[1 + t] = r[1 + t];
+    const int q = (int)threadIdx.x;
+    const int i = (tile / tiles_x) * FTY + q / FTX;
+    const int j = (tile % tiles_x) * FTX + q % FTX;
+    const bool inside = i < g.ny && j < g.nx;
+    const int32_t *r = rec + ((int64_t)v * np + (inside ? i * g.nx + j : 0)) * (1 + ntap);
+    const int nf = inside ? r[0] : INT32_MAX;        // INT32_MAX also marks "no tap on the detector"
+    s_nf[q] = nf;
+    __syncthreads();
+    int rank = 0, nvalid = 0;
+    for (int o = 0; o < TP; ++o) {
+        const int no = s_nf[o];
+        rank += (no < nf || (no == nf && o < q)) ? 1 : 0;
+        nvalid += no != INT32_MAX ? 1 : 0;
     }
+    s_sorted_nf[rank] = nf;
+    __syncthreads();
+    int32_t *o = out + (vt * TP + rank) * nrec;
+    for (int t = 0; t < nrec; ++t) o[t] = 0;
+    if (nf == INT32_MAX) {
+        o[0] = TP;                                    // zero row, no weight, stay
+        return;
+    }
+    int adv = 0;
+    if (rank + 1 < nvalid) {
+        const int d = s_sorted_nf[rank + 1] - nf;
+        adv = d < ntap ? d : 7;
+    }
+    o[0] = q | (adv << 8) | ((nf + 65536) << 11);
+    for (int t = 0; t < ntap; ++t) o[1 + t] = r[1 + t];
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float4 *__restrict__ b4, float *__restrict__ tail,
@@ -158,13 +180,11 @@ hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int n
     return hipGetLastError();
 }
 
-hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, const uint8_t *perm, int32_t *out, int ntap,
-                                   int nrec, hipStream_t st) {
-    const int64_t total = (int64_t)g.nv * ((g.nx + FTX - 1) / FTX) * ((g.ny + FTY - 1) / FTY) * FTX * FTY;
-    if (total == 0) return hipSuccess;
-    const int64_t want = (total + 255) / 256;
-    const int blocks = (int)(want < 65536 ? want : 65536);
-    hipLaunchKernelGGL(par_walk_records_kernel, dim3(blocks), dim3(256), 0, st, g, rec, perm, out, ntap, nrec);
+hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, int32_t *out, int ntap, int nrec,
+                                   hipStream_t st) {
+    const int64_t blocks = (int64_t)g.nv * ((g.nx + FTX - 1) / FTX) * ((g.ny + FTY - 1) / FTY);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(par_walk_records_kernel, dim3((unsigned)blocks), dim3(64), 0, st, g, rec, out, ntap, nrec);
     return hipGetLastError();
 }
 

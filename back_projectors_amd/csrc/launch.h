@@ -16,7 +16,6 @@ struct Plan {
     const ViewK *views = nullptr;   // device [V]
     const int32_t *idx = nullptr;   // device [V][Ny*Nx]
     const int32_t *rec = nullptr;   // parallel: device tap records [V][Ny*Nx][1 + ntap]
-    const uint8_t *perm = nullptr;  // parallel: device [V][FTX*FTY] tile pixel order by channel
     const int32_t *wrec = nullptr;  // parallel: walk-ordered records [V][tiles][FTX*FTY][nrec]
     int nrec = 0;                   // parallel: dwords per walk record (4 or 8)
     int ntap = 0;                   // parallel: taps per record
@@ -37,14 +36,14 @@ struct Plan {
 
 constexpr int BT = 16;   // back tile edge (pixels), 256 threads
 constexpr int FT = 32;   // cone forward tile edge (pixels), 1024 threads
-constexpr int FTX = 16;  // parallel forward tile (pixels along x)
-constexpr int FTY = 8;   // parallel forward tile (pixels along y)
+constexpr int FTX = 8;   // parallel forward tile (pixels along x)
+constexpr int FTY = 8;   // parallel forward tile (pixels along y); FTX * FTY = 64, one walk record per lane
 constexpr int FW = 8;    // parallel forward waves per workgroup (one view each at a time)
 
 hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
 hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st);
-hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, const uint8_t *perm, int32_t *out, int ntap,
-                                   int nrec, hipStream_t st);
+hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, int32_t *out, int ntap, int nrec,
+                                   hipStream_t st);
 hipError_t launch_fill_zero(float *buf, int64_t n, hipStream_t st);
 
 hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, hipStream_t st);

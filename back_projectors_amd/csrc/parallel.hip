@@ -18,13 +18,14 @@
 // Forward (scatter with no colliding LDS or register updates): a workgroup
 // owns an FTX x FTY pixel tile and a chunk of 64 slices; lanes are slices and
 // each wave works on one view at a time.  The tile's voxels sit in LDS.  A
-// wave walks the tile's pixels in the order of their channel coordinate in
-// that view (a per-view permutation fixed at creation), so the channels it
-// touches only move forward: NTAP sliding registers hold the current channels
-// and a channel is spilled to the wave's own LDS window when the walk moves
-// past it.  The window is then added to the sinogram with coalesced global
-// atomics, one per cell per view and tile.  Float atomics in LDS are avoided on
-// purpose: on gfx950 they cost tens of times a plain read-modify-write.
+// wave walks the tile's pixels in the order of their first tap channel, which
+// the creation pass fixed per (view, tile) together with how far the walk's
+// channel window moves after each pixel, so the walk has no comparisons: NTAP
+// registers hold the current channels and a channel the walk leaves behind is
+// stored once into the wave's own LDS window.  The window is then added to the
+// sinogram with coalesced global atomics, one per cell per view and tile.
+// Float atomics in LDS are avoided on purpose: on gfx950 they cost tens of
+// times a plain read-modify-write.
 #include "launch.h"
 
 namespace bpamd {
@@ -107,16 +108,16 @@ __global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__res
                                                                const int32_t *__restrict__ wrec,
                                                                const ViewK *__restrict__ views, Geo g, int nwcap,
                                                                int vsplit) {
-    constexpr int TP = FTX * FTY;         // pixels per tile (two records per lane)
-    static_assert(TP == 128, "the walk keeps the tile's records in two registers per lane");
+    constexpr int TP = FTX * FTY;         // pixels per tile, one walk record per lane
+    static_assert(TP == 64, "the walk keeps the tile's records one per lane");
     constexpr int XP = 64;                // LDS pitch of one voxel cylinder chunk
     constexpr int WP = 65;                // LDS pitch of one window channel (slices fastest)
     extern __shared__ float lds[];
-    float *xt = lds;                                   // [TP][XP]
+    float *xt = lds;                                   // [TP + 1][XP]; row TP stays zero
     const int lane = (int)threadIdx.x & 63;
     // wave index, made visibly uniform so per-view work stays on the scalar unit
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    float *win = lds + TP * XP + wave * nwcap * WP;    // this wave's window [nwcap][WP]
+    float *win = lds + (TP + 1) * XP + wave * nwcap * WP;   // this wave's window [nwcap][WP]
 
     const int tiles_x = (g.nx + FTX - 1) / FTX;
     const int ntiles = tiles_x * ((g.ny + FTY - 1) / FTY);
@@ -128,12 +129,12 @@ __global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__res
     const int k0 = (int)blockIdx.y * 64;
     const int nk = min(64, g.ns - k0);
 
-    // the tile's voxels, one 64-slice chunk per pixel
-    for (int e = (int)threadIdx.x; e < TP * 64; e += FW * 64) {
+    // the tile's voxels, one 64-slice chunk per pixel, plus a zero row
+    for (int e = (int)threadIdx.x; e < (TP + 1) * 64; e += FW * 64) {
         const int q = e >> 6, k = e & 63;
         const int i = ti0 + q / FTX, j = tj0 + q % FTX;
         float val = 0.f;
-        if (i < g.ny && j < g.nx && k < nk) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + k];
+        if (q < TP && i < g.ny && j < g.nx && k < nk) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + k];
         xt[q * XP + k] = val;
     }
     for (int e = lane; e < nwcap * WP; e += 64) win[e] = 0.f;
@@ -149,113 +150,94 @@ __global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__res
         int v = vbeg + start + it;
         return v >= vend ? v - cnt : v;
     };
-    // the (view, tile) records: lane l holds walk steps l and l + 64
-    auto load_records = [&](int v, int (&ra)[NREC], int (&rb)[NREC]) {
+    // the (view, tile) records: lane l holds walk step l
+    auto load_records = [&](int v, int (&ra)[NREC]) {
         const int32_t *base = wrec + ((int64_t)v * ntiles + tile) * TP * NREC;
 #pragma unroll
-        for (int t = 0; t < NREC; ++t) {
-            ra[t] = base[lane * NREC + t];
-            rb[t] = base[(lane + 64) * NREC + t];
-        }
+        for (int t = 0; t < NREC; ++t) ra[t] = base[lane * NREC + t];
     };
 
-    int ra[NREC], rb[NREC];
+    int ra[NREC];
     int it = wave;
     int v = it < cnt ? view_of(it) : 0;
-    if (it < cnt) load_records(v, ra, rb);
+    if (it < cnt) load_records(v, ra);
     for (; it < cnt; it += FW) {
         const int vc = v;
-        int na[NREC], nb[NREC];
+        int na[NREC];
         if (it + FW < cnt) {              // prefetch the next view's records
             v = view_of(it + FW);
-            load_records(v, na, nb);
+            load_records(v, na);
         }
         const ViewK vk = views[vc];
         const Window wd = tile_window(g, vk, ti0, ti1, tj0, tj1, k0, k0 + nk - 1);
-        if (wd.nw > 0) {
+        const int p0 = __builtin_amdgcn_readlane(ra[0], 0);
+        if (wd.nw > 0 && (p0 & 255) != TP) {
+            // acc[t] holds channel cur + t; the records say when to move on, and
+            // a channel left behind is finished, so it is stored, not added
             float acc[NTAP];
 #pragma unroll
             for (int t = 0; t < NTAP; ++t) acc[t] = 0.f;
-            int cur = INT32_MIN;           // channel held by acc[0]; none yet
-            int hi = INT32_MIN;            // highest channel spilled so far in this walk
-            // The window is all zeros at the start of a walk, so the first spill
-            // of a channel is a plain store; only a channel met again (the walk
-            // order is monotone up to fp64 rounding of the sort key) is added to.
-            auto spill = [&](int n, float a) {
-                float *pw = win + (n - wd.n0) * WP + lane;
-                if (n > hi) {
-                    *pw = a;
-                    hi = n;
-                } else {
-                    *pw += a;
+            int cur = (p0 >> 11) - 65536;
+            auto store = [&](int n, float a) { win[(n - wd.n0) * WP + lane] = a; };
+#pragma unroll
+            for (int s = 0; s < TP; s += 4) {
+                int pk[4];
+                float w[4][NTAP], xv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    pk[u] = __builtin_amdgcn_readlane(ra[0], s + u);
+#pragma unroll
+                    for (int t = 0; t < NTAP; ++t) w[u][t] = __int_as_float(__builtin_amdgcn_readlane(ra[1 + t], s + u));
                 }
-            };
-            auto step = [&](int packed, float xv, int s, const int (&rr)[NREC]) {
-                if (packed == 0) return;
-                const int nf = (packed >> 8) - 65536;
-                if (nf != cur) {
-                    const int d = nf - cur;
-                    if (cur == INT32_MIN || d < 0 || d >= NTAP) {
-                        if (cur != INT32_MIN) {
 #pragma unroll
-                            for (int t = 0; t < NTAP; ++t) spill(cur + t, acc[t]);
-                        }
+                for (int u = 0; u < 4; ++u) xv[u] = xt[(pk[u] & 255) * XP + lane];
 #pragma unroll
-                        for (int t = 0; t < NTAP; ++t) acc[t] = 0.f;
-                    } else {
+                for (int u = 0; u < 4; ++u) {
 #pragma unroll
-                        for (int t = 0; t < NTAP - 1; ++t)
-                            if (t < d) spill(cur + t, acc[t]);
+                    for (int t = 0; t < NTAP; ++t) acc[t] = fmaf(w[u][t], xv[u], acc[t]);
+                    const int adv = (pk[u] >> 8) & 7;
+                    if (adv != 0) {
+                        if (adv == 7) {
 #pragma unroll
-                        for (int t = 0; t < NTAP; ++t) {
-                            float nv = 0.f;
+                            for (int t = 0; t < NTAP; ++t) {
+                                store(cur + t, acc[t]);
+                                acc[t] = 0.f;
+                            }
+                            if (s + u + 1 < TP) cur = (__builtin_amdgcn_readlane(ra[0], s + u + 1) >> 11) - 65536;
+                        } else {
 #pragma unroll
-                            for (int dd = 1; dd < NTAP; ++dd)
-                                if (d == dd && t + dd < NTAP) nv = acc[t + dd];
-                            acc[t] = nv;
+                            for (int t = 0; t < NTAP - 1; ++t)
+                                if (t < adv) store(cur + t, acc[t]);
+#pragma unroll
+                            for (int t = 0; t < NTAP; ++t) {
+                                float nv = 0.f;
+#pragma unroll
+                                for (int dd = 1; dd < NTAP; ++dd)
+                                    if (adv == dd && t + dd < NTAP) nv = acc[t + dd];
+                                acc[t] = nv;
+                            }
+                            cur += adv;
                         }
                     }
-                    cur = nf;
                 }
-#pragma unroll
-                for (int t = 0; t < NTAP; ++t)
-                    acc[t] = fmaf(__int_as_float(__builtin_amdgcn_readlane(rr[1 + t], s)), xv, acc[t]);
-            };
-            auto walk = [&](const int (&rr)[NREC]) {
-                for (int s = 0; s < 64; s += 4) {
-                    // four steps' voxel reads issued together
-                    int pk[4];
-                    float xv[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) pk[u] = __builtin_amdgcn_readlane(rr[0], s + u);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) xv[u] = xt[(pk[u] & 255) * XP + lane];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) step(pk[u], xv[u], s + u, rr);
-                }
-            };
-            walk(ra);
-            walk(rb);
-            if (cur != INT32_MIN) {
-#pragma unroll
-                for (int t = 0; t < NTAP; ++t) spill(cur + t, acc[t]);
             }
-            // add the window to the sinogram: lanes along channels, coalesced
-            for (int k = 0; k < nk; ++k) {
-                float *srow = sino + ((int64_t)vc * g.nr + (k0 + k)) * g.nc;
-                for (int c = lane; c < wd.nw; c += 64) {
-                    const float val = win[c * WP + k];
-                    win[c * WP + k] = 0.f;
-                    const int n = wd.n0 + c;
-                    if (val != 0.f && n >= 0 && n < g.nc) unsafeAtomicAdd(&srow[n], val);
-                }
+#pragma unroll
+            for (int t = 0; t < NTAP; ++t) store(cur + t, acc[t]);
+            // add the window to the sinogram: lanes run along channels, coalesced
+            const int total = wd.nw * nk;
+            const float rnw = 1.0f / (float)wd.nw;
+            for (int e = lane; e < total; e += 64) {
+                const int k = (int)(((float)e + 0.5f) * rnw);   // exact: e < 2^22 and nw is small
+                const int c = e - k * wd.nw;
+                const float val = win[c * WP + k];
+                win[c * WP + k] = 0.f;
+                const int n = wd.n0 + c;
+                if (val != 0.f && n >= 0 && n < g.nc)
+                    unsafeAtomicAdd(&sino[((int64_t)vc * g.nr + (k0 + k)) * g.nc + n], val);
             }
         }
 #pragma unroll
-        for (int t = 0; t < NREC; ++t) {
-            ra[t] = na[t];
-            rb[t] = nb[t];
-        }
+        for (int t = 0; t < NREC; ++t) ra[t] = na[t];
     }
 }
 

@@ -55,7 +55,6 @@ struct proj_handle_s {
     int32_t *d_idx = nullptr;
     int32_t *d_rec = nullptr;       // parallel tap records
     int32_t *d_wrec = nullptr;      // parallel tap records in forward walk order
-    uint8_t *d_perm = nullptr;      // parallel per-view tile order
     size_t table_bytes = 0;
 };
 
@@ -186,7 +185,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         plan.ntap = (int)std::min<double>(2.0 * g.radius + 1.0, std::ceil(wmax) + 1.0);
         plan.ntap = std::max(plan.ntap, 2);
         if (plan.ntap > 7) return fail(PROJ_ERR_UNSUPPORTED, "more than 7 channel taps per voxel (detector far finer than the voxels)");
-        if (C + 4 * g.radius >= ((int64_t)1 << 23) - 65536) return fail(PROJ_ERR_UNSUPPORTED, "too many detector channels");
+        if (C + 4 * g.radius >= ((int64_t)1 << 20) - 65536) return fail(PROJ_ERR_UNSUPPORTED, "too many detector channels");
         plan.nrec = plan.ntap <= 3 ? 4 : 8;
         for (int sl = pick_chunk(S, {8, 16, 32, 64});; sl /= 2) {
             const WinMax w = max_window(g, views, BT, BT, sl);
@@ -198,7 +197,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         const WinMax wf = max_window(g, views, FTX, FTY, 64);
         plan.fwd_sl = 64;
         plan.fwd_nwcap = wf.nw + 2;
-        plan.fwd_lds = ((size_t)FTX * FTY * 64 + (size_t)FW * plan.fwd_nwcap * 65) * sizeof(float);
+        plan.fwd_lds = ((size_t)(FTX * FTY + 1) * 64 + (size_t)FW * plan.fwd_nwcap * 65) * sizeof(float);
     } else {
         auto back_bytes = [&](int sl, int &nwcap, int &nrcap) {
             const WinMax w = max_window(g, views, BT, BT, sl);
@@ -350,7 +349,7 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
             e = hipMemcpy(h->d_views, views.data(), views.size() * sizeof(ViewK), hipMemcpyHostToDevice);
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(views)");
         }
-        size_t rec_bytes = 0, perm_bytes = 0;
+        size_t rec_bytes = 0;
         if (h->index_elems > 0) {
             e = hipMalloc((void **)&h->d_idx, (size_t)h->index_elems * sizeof(int32_t));
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(index table)");
@@ -362,29 +361,12 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(tap records)");
                 e = launch_par_taps(geo, h->d_views, h->d_rec, plan.ntap, nullptr);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "tap record pass");
-                // per view, the forward tile's pixels ordered by channel coordinate
                 constexpr int TP = FTX * FTY;
-                std::vector<uint8_t> perm((size_t)geo.nv * TP);
-                std::vector<int> order(TP);
-                std::vector<double> key(TP);
-                for (int v = 0; v < geo.nv; ++v) {
-                    for (int q = 0; q < TP; ++q) {
-                        key[q] = (double)(q % FTX) * views[v].cd + (double)(q / FTX) * views[v].sd;
-                        order[q] = q;
-                    }
-                    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return key[a] < key[b]; });
-                    for (int q = 0; q < TP; ++q) perm[(size_t)v * TP + q] = (uint8_t)order[q];
-                }
-                perm_bytes = perm.size();
-                e = hipMalloc((void **)&h->d_perm, perm_bytes);
-                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(tile order)");
-                e = hipMemcpy(h->d_perm, perm.data(), perm_bytes, hipMemcpyHostToDevice);
-                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(tile order)");
                 const int64_t ntiles = (int64_t)((geo.nx + FTX - 1) / FTX) * ((geo.ny + FTY - 1) / FTY);
                 const size_t wrec_bytes = (size_t)geo.nv * ntiles * TP * plan.nrec * sizeof(int32_t);
                 e = hipMalloc((void **)&h->d_wrec, wrec_bytes);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(walk records)");
-                e = launch_par_walk_records(geo, h->d_rec, h->d_perm, h->d_wrec, plan.ntap, plan.nrec, nullptr);
+                e = launch_par_walk_records(geo, h->d_rec, h->d_wrec, plan.ntap, plan.nrec, nullptr);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "walk record pass");
                 rec_bytes += wrec_bytes;
                 if (plan.fwd_lds > kMaxLds) {
@@ -402,12 +384,10 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
             e = hipDeviceSynchronize();
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "table passes");
         }
-        h->table_bytes = (size_t)h->index_elems * sizeof(int32_t) + views.size() * sizeof(ViewK) + rec_bytes +
-                         perm_bytes;
+        h->table_bytes = (size_t)h->index_elems * sizeof(int32_t) + views.size() * sizeof(ViewK) + rec_bytes;
         h->plan.views = h->d_views;
         h->plan.idx = h->d_idx;
         h->plan.rec = h->d_rec;
-        h->plan.perm = h->d_perm;
         h->plan.wrec = h->d_wrec;
         if (std::getenv("PROJ_LOG")) {
             char buf[512];
@@ -484,7 +464,6 @@ void proj_destroy(proj_handle h) {
         DeviceGuard dg(h->device);
         if (h->d_idx) (void)hipFree(h->d_idx);
         if (h->d_rec) (void)hipFree(h->d_rec);
-        if (h->d_perm) (void)hipFree(h->d_perm);
         if (h->d_wrec) (void)hipFree(h->d_wrec);
         if (h->d_views) (void)hipFree(h->d_views);
     }
