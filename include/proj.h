@@ -19,8 +19,12 @@
  *     one slice spreads over a band of rows given by an affine function of
  *     the slice index, with a 3x3 tap block ("The cone back kernel: a fused
  *     vertical fan").
- * The footprint model, written out: the fp64 CPU reference under oracle/ and
- * the design doc state it formula by formula.
+ * The footprint model, per (view, pixel): channel coordinate u (parallel:
+ * (x cos t + y sin t)/dch + centre + shift; flat cone: SDD a/(d dch) + centre +
+ * shift), n_c = rint(u), and tap n in [n_c - r, n_c + r] weighted by
+ * L * |[n - 1/2, n + 1/2] ∩ [u - W/2, u + W/2]| with W = dv max(|cos|,|sin|)/dch
+ * and L = dv / max(|cos|,|sin|) (the cone adds the fan obliquity and a row
+ * factor of the same form); the fp64 CPU reference under oracle/ writes it out.
  *
  * Layouts (all C order, float32, device memory, caller-owned):
  *   recon  [Ny][Nx][S]  slices fastest: one contiguous voxel cylinder per
