@@ -138,106 +138,125 @@ __global__ __launch_bounds__(BT *BT) void cone_back_kernel(const float *__restri
     }
 }
 
-template <int SL, int R>
-__global__ __launch_bounds__(FT *FT) void cone_forward_kernel(const float *__restrict__ recon,
-                                                               float *__restrict__ sino,
-                                                               const int32_t *__restrict__ idx,
-                                                               const ViewK *__restrict__ views, Geo g, int nwcap,
-                                                               int nrp, int vsplit) {
-    constexpr int NT = FT * FT;
+// Forward: a workgroup owns a CTX x CTY pixel tile and a chunk of 64*P slices;
+// each wave works on one view at a time into its own LDS window (channels x
+// rows, rows fastest).  Lane l takes slices l*P + ph, ph = 0..P-1, and P is
+// chosen at creation so that P times the smallest row magnification is at
+// least one: the slices of one instruction then fall on distinct detector
+// rows, so every tap is a plain read-modify-write with no two lanes on the
+// same cell (float atomics in LDS are avoided: on gfx950 they cost tens of
+// times a plain update).  The finished window is added to the sinogram with
+// coalesced global atomics, one per cell per view and tile.
+template <int R, int P>
+__global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__restrict__ recon,
+                                                                 float *__restrict__ sino,
+                                                                 const int32_t *__restrict__ idx,
+                                                                 const ViewK *__restrict__ views, Geo g, int nwcap,
+                                                                 int nrp, int vsplit) {
     constexpr int NTAP = 2 * R + 1;
-    extern __shared__ float win[];        // two buffers of [nwcap][nrp]
+    constexpr int TP = CTX * CTY;
+    constexpr int CH = 64 * P;            // slices per chunk
+    extern __shared__ float lds[];
+    float *xt = lds;                                   // [TP][P][64]
+    const int lane = (int)threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    float *win = lds + TP * CH + wave * nwcap * nrp;   // this wave's window [nwcap][nrp]
 
-    const int tiles_x = (g.nx + FT - 1) / FT;
-    const int tj0 = (int)(blockIdx.x % tiles_x) * FT;
-    const int ti0 = (int)(blockIdx.x / tiles_x) * FT;
-    const int tj1 = min(tj0 + FT, g.nx) - 1;
-    const int ti1 = min(ti0 + FT, g.ny) - 1;
-    const int k0 = (int)blockIdx.y * SL;
-    const int nk = min(SL, g.ns - k0);
+    const int tiles_x = (g.nx + CTX - 1) / CTX;
+    const int tj0 = (int)(blockIdx.x % tiles_x) * CTX;
+    const int ti0 = (int)(blockIdx.x / tiles_x) * CTY;
+    const int tj1 = min(tj0 + CTX, g.nx) - 1;
+    const int ti1 = min(ti0 + CTY, g.ny) - 1;
+    const int k0 = (int)blockIdx.y * CH;
+    const int nk = min(CH, g.ns - k0);
     const int np = g.ny * g.nx;
 
-    const int a = (int)threadIdx.x % FT, b = (int)threadIdx.x / FT;
-    const int ir = ti0 + b, jr = tj0 + a;
-    const int ic = ti0 + a, jc = tj0 + b;
-    const bool vr = ir < g.ny && jr < g.nx;
-    const bool vc = ic < g.ny && jc < g.nx;
-    float xr[SL], xq[SL];
-    {
-        const float *pr = recon + (int64_t)(vr ? ir * g.nx + jr : 0) * g.ns + k0;
-        const float *pc = recon + (int64_t)(vc ? ic * g.nx + jc : 0) * g.ns + k0;
-#pragma unroll
-        for (int k = 0; k < SL; ++k) {
-            xr[k] = (vr && k < nk) ? pr[k] : 0.f;
-            xq[k] = (vc && k < nk) ? pc[k] : 0.f;
-        }
+    for (int e = (int)threadIdx.x; e < TP * CH; e += CFW * 64) {
+        const int q = e / CH, kk = e - q * CH;
+        const int i = ti0 + q / CTX, j = tj0 + q % CTX;
+        float val = 0.f;
+        if (i < g.ny && j < g.nx && kk < nk) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + kk];
+        xt[(q * P + kk % P) * 64 + kk / P] = val;
     }
-
-    const int cap = nwcap * nrp;
-    for (int e = (int)threadIdx.x; e < 2 * cap; e += NT) win[e] = 0.f;
+    for (int e = lane; e < nwcap * nrp; e += 64) win[e] = 0.f;
     __syncthreads();
 
     const int vper = (g.nv + vsplit - 1) / vsplit;
     const int vbeg = (int)blockIdx.z * vper;
     const int vend = min(g.nv, vbeg + vper);
     const int cnt = vend - vbeg;
-    const int start = cnt > 0 ? (int)((blockIdx.x * 7u + blockIdx.y * 3u) % (unsigned)cnt) : 0;
-    const double xm = 0.5 * (pix_x(g, tj0) + pix_x(g, tj1));
-    const double ym = 0.5 * (pix_y(g, ti0) + pix_y(g, ti1));
+    const int start = cnt > 0 ? (int)((blockIdx.x * 37u + blockIdx.y * 11u) % (unsigned)cnt) : 0;
 
-    for (int it = 0; it < cnt; ++it) {
+    for (int it = wave; it < cnt; it += CFW) {
         int v = vbeg + start + it;
         if (v >= vend) v -= cnt;
         const ViewK vk = views[v];
         const Window wd = tile_window(g, vk, ti0, ti1, tj0, tj1, k0, k0 + nk - 1);
-        float *buf = win + (it & 1) * cap;
-        // strip along the tile axis on which the channel coordinate moves fastest
-        const bool rowmode = fabs(ym + vk.c * g.sid) >= fabs(vk.s * g.sid - xm);
-        const int i = rowmode ? ir : ic, j = rowmode ? jr : jc;
-        const bool valid = (rowmode ? vr : vc) && wd.nw > 0 && wd.nrw > 0;
-        const int ncv = valid ? idx[(int64_t)v * np + i * g.nx + j] : 0;
-        if (valid && ncv >= -R && ncv <= g.nc - 1 + R) {
-            const ConeVP q = cone_vp(g, vk, pix_x(g, j), pix_y(g, i), ncv);
+        if (wd.nw <= 0 || wd.nrw <= 0) continue;
+        // per-lane slice offsets of this view
+        double dzs[P];
+#pragma unroll
+        for (int ph = 0; ph < P; ++ph) dzs[ph] = slice_z(g, k0 + lane * P + ph) - vk.zsrc;
+        for (int q = 0; q < TP; ++q) {
+            const int i = ti0 + q / CTX, j = tj0 + q % CTX;
+            if (i >= g.ny || j >= g.nx) continue;
+            const int ncv = idx[(int64_t)v * np + i * g.nx + j];
+            if (ncv < -R || ncv > g.nc - 1 + R) continue;
+            const ConeVP cv = cone_vp(g, vk, pix_x(g, j), pix_y(g, i), ncv);
             double hd[NTAP];
-            tap_weights_d<R>(q.f, q.wch, hd);
+            tap_weights_d<R>(cv.f, cv.wch, hd);
             float h[NTAP];
 #pragma unroll
             for (int t = 0; t < NTAP; ++t) h[t] = (float)hd[t];
-            float *col = buf + (ncv - R - wd.n0) * nrp - wd.m0;
-            const double wrow = q.mr * g.dv;
+            const double wrow = cv.mr * g.dv;
+            float *col = win + (ncv - R - wd.n0) * nrp - wd.m0;
 #pragma unroll
-            for (int k = 0; k < SL; ++k) {
-                const double dz = slice_z(g, k0 + k) - vk.zsrc;
-                const double t0 = q.mr * dz;
+            for (int ph = 0; ph < P; ++ph) {
+                const int kk = lane * P + ph;
+                const double t0 = cv.mr * dzs[ph];
                 const double wk = t0 + g.crow;
                 const double mk = rint(wk);
-                if (k < nk && mk >= -R && mk <= g.nr - 1 + R) {
-                    const float xv = rowmode ? xr[k] : xq[k];
-                    double gd[NTAP];
-                    tap_weights_d<R>(wk - mk, wrow, gd);
-                    const float lk = (float)q.lsc * sqrtf((float)(q.r2 + dz * dz));
-                    float *cell = col + ((int)mk - R);
+                const bool ok = kk < nk && mk >= -R && mk <= g.nr - 1 + R;
+                double gd[NTAP];
+                tap_weights_d<R>(wk - mk, wrow, gd);
+                const float xv = xt[(q * P + ph) * 64 + lane];
+                const float lk = (float)cv.lsc * sqrtf((float)(cv.r2 + dzs[ph] * dzs[ph]));
+                float c[NTAP];
 #pragma unroll
-                    for (int sg = 0; sg < NTAP; ++sg) {
-                        const float ws = lk * (float)gd[sg] * xv;
+                for (int sg = 0; sg < NTAP; ++sg) c[sg] = lk * (float)gd[sg] * xv;
+                float *cell = col + (ok ? (int)mk - R : 0);
+                // One row offset at a time: within a round the active lanes hold
+                // distinct rows and the channel taps distinct columns, so plain
+                // read-modify-writes are race free.  A lane's next row overlaps its
+                // neighbour's previous one, hence the ordering fence between rounds
+                // (the wave issues LDS operations in order; the fence stops the
+                // compiler from hoisting the next round's reads).
 #pragma unroll
-                        for (int t = 0; t < NTAP; ++t) atomicAdd(&cell[t * nrp + sg], h[t] * ws);
+                for (int sg = 0; sg < NTAP; ++sg) {
+                    if (ok) {
+                        float old[NTAP];
+#pragma unroll
+                        for (int t = 0; t < NTAP; ++t)
+                            if (h[t] != 0.f) old[t] = cell[t * nrp + sg];
+#pragma unroll
+                        for (int t = 0; t < NTAP; ++t)
+                            if (h[t] != 0.f) cell[t * nrp + sg] = fmaf(h[t], c[sg], old[t]);
                     }
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 }
             }
         }
-        __syncthreads();
-        const int lane = (int)threadIdx.x & 31;
-        for (int m = (int)threadIdx.x >> 5; m < wd.nrw; m += NT / 32) {
-            const int row = wd.m0 + m;
-            const bool rok = row >= 0 && row < g.nr;
-            float *srow = sino + ((int64_t)v * g.nr + (rok ? row : 0)) * g.nc;
-            for (int c = lane; c < wd.nw; c += 32) {
-                const float val = buf[c * nrp + m];
-                buf[c * nrp + m] = 0.f;
-                const int n = wd.n0 + c;
-                if (val != 0.f && rok && n >= 0 && n < g.nc) unsafeAtomicAdd(&srow[n], val);
-            }
+        // add the window to the sinogram: lanes along channels, coalesced
+        const int total = wd.nw * wd.nrw;
+        const float rnw = 1.0f / (float)wd.nw;
+        for (int e = lane; e < total; e += 64) {
+            const int m = (int)(((float)e + 0.5f) * rnw);
+            const int c = e - m * wd.nw;
+            const float val = win[c * nrp + m];
+            win[c * nrp + m] = 0.f;
+            const int row = wd.m0 + m, n = wd.n0 + c;
+            if (val != 0.f && row >= 0 && row < g.nr && n >= 0 && n < g.nc)
+                unsafeAtomicAdd(&sino[((int64_t)v * g.nr + row) * g.nc + n], val);
         }
     }
 }
@@ -252,14 +271,24 @@ static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, hi
     return hipGetLastError();
 }
 
-template <int SL, int R>
+template <int R, int P>
 static hipError_t cone_fwd_t(const Plan &p, const float *recon, float *sino, hipStream_t st) {
     const Geo &g = p.g;
-    const int tiles = ((g.nx + FT - 1) / FT) * ((g.ny + FT - 1) / FT);
-    const int chunks = (g.ns + SL - 1) / SL;
-    hipLaunchKernelGGL((cone_forward_kernel<SL, R>), dim3(tiles, chunks, p.fwd_vsplit), dim3(FT * FT), p.fwd_lds,
+    const int tiles = ((g.nx + CTX - 1) / CTX) * ((g.ny + CTY - 1) / CTY);
+    const int chunks = (g.ns + 64 * P - 1) / (64 * P);
+    hipLaunchKernelGGL((cone_forward_kernel<R, P>), dim3(tiles, chunks, p.fwd_vsplit), dim3(CFW * 64), p.fwd_lds,
                        st, recon, sino, p.idx, p.views, g, p.fwd_nwcap, p.fwd_nrcap, p.fwd_vsplit);
     return hipGetLastError();
+}
+
+template <int R>
+static hipError_t cone_fwd_r(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+    switch (p.cone_stride) {
+    case 1: return cone_fwd_t<R, 1>(p, recon, sino, st);
+    case 2: return cone_fwd_t<R, 2>(p, recon, sino, st);
+    case 3: return cone_fwd_t<R, 3>(p, recon, sino, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 #define BPAMD_DISPATCH_R(FN, SLV, ...)                         \
@@ -281,12 +310,25 @@ hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, hipS
 }
 
 hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st) {
-    switch (p.fwd_sl) {
-    case 8: BPAMD_DISPATCH_R(cone_fwd_t, 8, p, recon, sino, st)
-    case 16: BPAMD_DISPATCH_R(cone_fwd_t, 16, p, recon, sino, st)
-    case 32: BPAMD_DISPATCH_R(cone_fwd_t, 32, p, recon, sino, st)
+    switch (p.g.radius) {
+    case 1: return cone_fwd_r<1>(p, recon, sino, st);
+    case 2: return cone_fwd_r<2>(p, recon, sino, st);
+    case 3: return cone_fwd_r<3>(p, recon, sino, st);
+    case 4: return cone_fwd_r<4>(p, recon, sino, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+// Dynamic LDS above the default limit needs the opt-in attribute.
+hipError_t cone_forward_allow_lds(int radius, int stride, size_t bytes) {
+    const void *f = nullptr;
+#define BPAMD_CF(RR, PP) \
+    if (radius == RR && stride == PP) f = (const void *)cone_forward_kernel<RR, PP>;
+    BPAMD_CF(1, 1) BPAMD_CF(1, 2) BPAMD_CF(1, 3) BPAMD_CF(2, 1) BPAMD_CF(2, 2) BPAMD_CF(2, 3)
+    BPAMD_CF(3, 1) BPAMD_CF(3, 2) BPAMD_CF(3, 3) BPAMD_CF(4, 1) BPAMD_CF(4, 2) BPAMD_CF(4, 3)
+#undef BPAMD_CF
+    if (!f) return hipErrorInvalidValue;
+    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 }  // namespace bpamd

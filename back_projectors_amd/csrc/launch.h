@@ -26,19 +26,22 @@ struct Plan {
     int back_nrcap = 0;             // window rows capacity (cone)
     size_t back_lds = 0;            // dynamic LDS bytes
 
-    // forward projection: lanes = pixels of an FT x FT tile
+    // forward projection (parallel: FTX x FTY tiles; cone: CTX x CTY tiles)
     int fwd_sl = 0;
     int fwd_nwcap = 0;
     int fwd_nrcap = 0;
     size_t fwd_lds = 0;
     int fwd_vsplit = 1;             // view ranges per tile (grid z)
+    int cone_stride = 1;            // cone forward: slices between the lanes of one instruction
 };
 
 constexpr int BT = 16;   // back tile edge (pixels), 256 threads
-constexpr int FT = 32;   // cone forward tile edge (pixels), 1024 threads
 constexpr int FTX = 8;   // parallel forward tile (pixels along x)
 constexpr int FTY = 8;   // parallel forward tile (pixels along y); FTX * FTY = 64, one walk record per lane
 constexpr int FW = 8;    // parallel forward waves per workgroup (one view each at a time)
+constexpr int CTX = 8;   // cone forward tile (pixels along x)
+constexpr int CTY = 8;   // cone forward tile (pixels along y)
+constexpr int CFW = 4;   // cone forward waves per workgroup (one view each at a time)
 
 hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
 hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st);
@@ -51,5 +54,6 @@ hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hi
 hipError_t par_forward_allow_lds(int ntap, size_t bytes);
 hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, hipStream_t st);
 hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
+hipError_t cone_forward_allow_lds(int radius, int stride, size_t bytes);
 
 }  // namespace bpamd

@@ -205,22 +205,32 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
             nrcap = (w.nr + 2) | 1;                 // odd pitch: conflict-free column strides
             return (size_t)nwcap * nrcap * sizeof(float);
         };
-        auto fwd_bytes = [&](int sl, int &nwcap, int &nrcap) {
-            const WinMax w = max_window(g, views, FT, FT, sl);
-            nwcap = w.nw + 2;
-            nrcap = (w.nr + 2) | 1;
-            return 2 * (size_t)nwcap * nrcap * sizeof(float);
-        };
         for (int sl = pick_chunk(S, {8, 16, 32});; sl /= 2) {
             plan.back_sl = sl;
             plan.back_lds = back_bytes(sl, plan.back_nwcap, plan.back_nrcap);
             if (plan.back_lds <= kMaxLds || sl == 8) break;
         }
-        for (int sl = pick_chunk(S, {8, 16});; sl /= 2) {
-            plan.fwd_sl = sl;
-            plan.fwd_lds = fwd_bytes(sl, plan.fwd_nwcap, plan.fwd_nrcap);
-            if (plan.fwd_lds <= kMaxLds || sl == 8) break;
-        }
+        // smallest row magnification (rows per slice) over the whole scan: lanes
+        // of one forward instruction take slices `stride` apart, so that their
+        // rows differ
+        double amin = 1e300;
+        const double xs[2] = {pix_x(g, 0), pix_x(g, g.nx - 1)}, ys[2] = {pix_y(g, 0), pix_y(g, g.ny - 1)};
+        for (const ViewK &k : views)
+            for (double xx : xs)
+                for (double yy : ys) {
+                    const double d = g.sid + (yy * k.c - xx * k.s);
+                    amin = std::min(amin, g.sdd * g.dv / (d * g.drow));
+                }
+        int stride = 1;
+        while (stride * amin < 1.0 + 1e-9 && stride <= 3) ++stride;
+        if (stride > 3)
+            return fail(PROJ_ERR_UNSUPPORTED, "row magnification below 1/3 (detector rows far finer than the voxels)");
+        plan.cone_stride = stride;
+        plan.fwd_sl = 64 * stride;
+        const WinMax wf = max_window(g, views, CTX, CTY, plan.fwd_sl);
+        plan.fwd_nwcap = wf.nw + 2;
+        plan.fwd_nrcap = (wf.nr + 2) | 1;
+        plan.fwd_lds = ((size_t)CTX * CTY * plan.fwd_sl + (size_t)CFW * plan.fwd_nwcap * plan.fwd_nrcap) * sizeof(float);
     }
     if (plan.back_lds > kMaxLds || plan.fwd_lds > kMaxLdsOptIn) {
         char buf[160];
@@ -232,7 +242,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
     const int64_t chunks_f = (S + plan.fwd_sl - 1) / plan.fwd_sl;
     if (chunks_b > 65535 || chunks_f > 65535) return fail(PROJ_ERR_UNSUPPORTED, "too many slices");
     const int64_t ftiles = par ? ((Nx + FTX - 1) / FTX) * ((Ny + FTY - 1) / FTY)
-                               : ((Nx + FT - 1) / FT) * ((Ny + FT - 1) / FT);
+                               : ((Nx + CTX - 1) / CTX) * ((Ny + CTY - 1) / CTY);
     // enough workgroups to fill 256 CUs a few times over; each split re-reads its tile
     int64_t vs = (2048 + ftiles * chunks_f - 1) / (ftiles * chunks_f);
     vs = std::max<int64_t>(1, std::min<int64_t>(vs, std::min<int64_t>(V, 64)));
@@ -249,8 +259,9 @@ int describe(const Plan &p, int64_t table_bytes, char *buf, int len) {
         "slices/lane, window %d ch x %d rows, %zu B LDS | forward: %dx%d px tile, %s, %d slices, window %d ch x %d "
         "rows, %zu B LDS, %d view ranges | tables %lld B",
         par ? "parallel" : "cone_flat", g.nv, g.nr, g.nc, g.ny, g.nx, g.ns, g.radius, par ? p.ntap : 2 * g.radius + 1,
-        BT, BT, p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, par ? FTX : FT, par ? FTY : FT,
-        par ? "lanes=slices, wave per view, channel-ordered walk" : "lanes=pixels, LDS window", p.fwd_sl,
+        BT, BT, p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, par ? FTX : CTX, par ? FTY : CTY,
+        par ? "lanes=slices, wave per view, channel-ordered walk" : "lanes=strided slices, wave per view, LDS window",
+        p.fwd_sl,
         p.fwd_nwcap, par ? p.fwd_sl : p.fwd_nrcap, p.fwd_lds, p.fwd_vsplit, (long long)table_bytes);
 }
 
@@ -383,6 +394,17 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
             }
             e = hipDeviceSynchronize();
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "table passes");
+        }
+        if (geo.kind != 0 && plan.fwd_sl > 0 && plan.fwd_lds > kMaxLds) {
+            int lim = 0;
+            e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, hip_device);
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipDeviceGetAttribute");
+            if ((size_t)lim < plan.fwd_lds) {
+                proj_destroy(h);
+                return fail(PROJ_ERR_UNSUPPORTED, "device LDS per workgroup below the forward plan's need");
+            }
+            e = cone_forward_allow_lds(geo.radius, plan.cone_stride, plan.fwd_lds);
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipFuncSetAttribute(LDS)");
         }
         h->table_bytes = (size_t)h->index_elems * sizeof(int32_t) + views.size() * sizeof(ViewK) + rec_bytes;
         h->plan.views = h->d_views;
