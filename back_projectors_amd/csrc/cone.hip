@@ -52,16 +52,17 @@ template <int SL, int R>
 __global__ __launch_bounds__(BT *BT) void cone_back_kernel(const float *__restrict__ sino,
                                                             float *__restrict__ recon,
                                                             const int32_t *__restrict__ idx,
-                                                            const ViewK *__restrict__ views, Geo g, int nrp) {
+                                                            const ViewK *__restrict__ views,
+                                                            const int4 *__restrict__ wtab, Geo g, int nrp) {
     constexpr int NT = BT * BT;
     constexpr int NTAP = 2 * R + 1;
     extern __shared__ float win[];        // [nwcap][nrp], rows fastest
 
     const int tiles_x = (g.nx + BT - 1) / BT;
+    const int ntiles = tiles_x * ((g.ny + BT - 1) / BT);
+    const int nch = (g.ns + SL - 1) / SL;
     const int tj0 = (int)(blockIdx.x % tiles_x) * BT;
     const int ti0 = (int)(blockIdx.x / tiles_x) * BT;
-    const int tj1 = min(tj0 + BT, g.nx) - 1;
-    const int ti1 = min(ti0 + BT, g.ny) - 1;
     const int k0 = (int)blockIdx.y * SL;
     const int nk = min(SL, g.ns - k0);
 
@@ -80,9 +81,14 @@ __global__ __launch_bounds__(BT *BT) void cone_back_kernel(const float *__restri
     const int grp = (int)threadIdx.x >> 5;
 
     for (int v = 0; v < g.nv; ++v) {
+        const int4 w4 = wtab[((int64_t)v * ntiles + blockIdx.x) * nch + blockIdx.y];
+        if (w4.y <= 0 || w4.w <= 0) continue;      // the tile misses the detector in this view
+        Window wd;
+        wd.n0 = w4.x;
+        wd.nw = w4.y;
+        wd.m0 = w4.z;
+        wd.nrw = w4.w;
         const ViewK vk = views[v];
-        const Window wd = tile_window(g, vk, ti0, ti1, tj0, tj1, k0, k0 + nk - 1);
-        if (wd.nw <= 0 || wd.nrw <= 0) continue;   // the tile misses the detector in this view
         __syncthreads();
         for (int m = grp; m < wd.nrw; m += NT / 32) {
             const int row = wd.m0 + m;
@@ -151,7 +157,8 @@ template <int R, int P>
 __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__restrict__ recon,
                                                                  float *__restrict__ sino,
                                                                  const int32_t *__restrict__ idx,
-                                                                 const ViewK *__restrict__ views, Geo g, int nwcap,
+                                                                 const ViewK *__restrict__ views,
+                                                                 const int4 *__restrict__ wtab, Geo g, int nwcap,
                                                                  int nrp, int vsplit) {
     constexpr int NTAP = 2 * R + 1;
     constexpr int TP = CTX * CTY;
@@ -163,10 +170,10 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
     float *win = lds + TP * CH + wave * nwcap * nrp;   // this wave's window [nwcap][nrp]
 
     const int tiles_x = (g.nx + CTX - 1) / CTX;
+    const int ntiles = tiles_x * ((g.ny + CTY - 1) / CTY);
+    const int nch = (g.ns + CH - 1) / CH;
     const int tj0 = (int)(blockIdx.x % tiles_x) * CTX;
     const int ti0 = (int)(blockIdx.x / tiles_x) * CTY;
-    const int tj1 = min(tj0 + CTX, g.nx) - 1;
-    const int ti1 = min(ti0 + CTY, g.ny) - 1;
     const int k0 = (int)blockIdx.y * CH;
     const int nk = min(CH, g.ns - k0);
     const int np = g.ny * g.nx;
@@ -190,9 +197,14 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
     for (int it = wave; it < cnt; it += CFW) {
         int v = vbeg + start + it;
         if (v >= vend) v -= cnt;
+        const int4 w4 = wtab[((int64_t)v * ntiles + blockIdx.x) * nch + blockIdx.y];
+        if (w4.y <= 0 || w4.w <= 0) continue;
+        Window wd;
+        wd.n0 = w4.x;
+        wd.nw = w4.y;
+        wd.m0 = w4.z;
+        wd.nrw = w4.w;
         const ViewK vk = views[v];
-        const Window wd = tile_window(g, vk, ti0, ti1, tj0, tj1, k0, k0 + nk - 1);
-        if (wd.nw <= 0 || wd.nrw <= 0) continue;
         // per-lane slice offsets of this view
         double dzs[P];
 #pragma unroll
@@ -267,7 +279,7 @@ static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, hi
     const int tiles = ((g.nx + BT - 1) / BT) * ((g.ny + BT - 1) / BT);
     const int chunks = (g.ns + SL - 1) / SL;
     hipLaunchKernelGGL((cone_back_kernel<SL, R>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino, recon,
-                       p.idx, p.views, g, p.back_nrcap);
+                       p.idx, p.views, p.bwin, g, p.back_nrcap);
     return hipGetLastError();
 }
 
@@ -277,7 +289,7 @@ static hipError_t cone_fwd_t(const Plan &p, const float *recon, float *sino, hip
     const int tiles = ((g.nx + CTX - 1) / CTX) * ((g.ny + CTY - 1) / CTY);
     const int chunks = (g.ns + 64 * P - 1) / (64 * P);
     hipLaunchKernelGGL((cone_forward_kernel<R, P>), dim3(tiles, chunks, p.fwd_vsplit), dim3(CFW * 64), p.fwd_lds,
-                       st, recon, sino, p.idx, p.views, g, p.fwd_nwcap, p.fwd_nrcap, p.fwd_vsplit);
+                       st, recon, sino, p.idx, p.views, p.fwin, g, p.fwd_nwcap, p.fwd_nrcap, p.fwd_vsplit);
     return hipGetLastError();
 }
 

@@ -64,6 +64,7 @@ struct Window {
     int n0, nw;   // channels [n0, n0 + nw)
     int m0, nrw;  // rows [m0, m0 + nrw) (cone) ; unused for parallel
 };
+static_assert(sizeof(Window) == 16, "windows are read by the kernels as int4 tables");
 
 __host__ __device__ inline double cone_u_approx(const Geo &g, const ViewK &vk, double x, double y) {
     double a = x * vk.c + y * vk.s;

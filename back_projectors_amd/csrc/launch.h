@@ -18,6 +18,8 @@ struct Plan {
     const int32_t *rec = nullptr;   // parallel: device tap records [V][Ny*Nx][1 + ntap]
     const int32_t *wrec = nullptr;  // parallel: walk-ordered records [V][tiles][FTX*FTY][nrec]
     int nrec = 0;                   // parallel: dwords per walk record (4 or 8)
+    const int4 *bwin = nullptr;     // back windows [V][tiles][chunks] (n0, nw, m0, nrw)
+    const int4 *fwin = nullptr;     // forward windows [V][tiles][chunks]
     int ntap = 0;                   // parallel: taps per record
 
     // back projection: lanes = pixels of a BT x BT tile, SL slices per lane
@@ -25,6 +27,7 @@ struct Plan {
     int back_nwcap = 0;             // window channels capacity
     int back_nrcap = 0;             // window rows capacity (cone)
     size_t back_lds = 0;            // dynamic LDS bytes
+    int back_ncg = 1;               // parallel back: 32-channel staging groups (1 or 2)
 
     // forward projection (parallel: FTX x FTY tiles; cone: CTX x CTY tiles)
     int fwd_sl = 0;

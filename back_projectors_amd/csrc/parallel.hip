@@ -30,21 +30,21 @@
 
 namespace bpamd {
 
-template <int SL, int NTAP>
+template <int SL, int NTAP, int NCG>
 __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restrict__ sino,
                                                            float *__restrict__ recon,
                                                            const int32_t *__restrict__ rec,
-                                                           const ViewK *__restrict__ views, Geo g) {
-    constexpr int NT = BT * BT;
+                                                           const int4 *__restrict__ wtab, Geo g, int nwcap) {
     constexpr int SLP = SL + 1;           // LDS pitch of one channel column
     constexpr int NREC = 1 + NTAP;
-    extern __shared__ float win[];        // [nwcap][SLP], slices fastest
+    constexpr int RPT = (SL + 7) / 8;     // staged rows per thread: 8 row groups of 32 lanes
+    extern __shared__ float lds[];        // two windows of [nwcap][SLP], slices fastest
 
     const int tiles_x = (g.nx + BT - 1) / BT;
-    const int tj0 = (int)(blockIdx.x % tiles_x) * BT;
-    const int ti0 = (int)(blockIdx.x / tiles_x) * BT;
-    const int tj1 = min(tj0 + BT, g.nx) - 1;
-    const int ti1 = min(ti0 + BT, g.ny) - 1;
+    const int ntiles = tiles_x * ((g.ny + BT - 1) / BT);
+    const int tile = (int)blockIdx.x;
+    const int tj0 = (tile % tiles_x) * BT;
+    const int ti0 = (tile / tiles_x) * BT;
     const int k0 = (int)blockIdx.y * SL;
     const int nk = min(SL, g.ns - k0);
 
@@ -53,46 +53,88 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
     const bool valid = (i < g.ny) && (j < g.nx);
     const int np = g.ny * g.nx;
     const int p = valid ? i * g.nx + j : 0;
+    const int clane = (int)threadIdx.x & 31;       // staging: channel within a 32-wide group
+    const int rgrp = (int)threadIdx.x >> 5;        // staging: rows rgrp, rgrp + 8, ...
+
+    // the sinogram cells of one view the tile can reach, into registers
+    auto load_view = [&](int v, const int4 &w, float (&st)[NCG][RPT]) {
+        const float *base = sino + ((int64_t)v * g.nr + k0) * g.nc;
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+            const int c = clane + 32 * cg;
+            const int n = w.x + c;
+            const bool cok = c < w.y && n >= 0 && n < g.nc;
+#pragma unroll
+            for (int u = 0; u < RPT; ++u) {
+                const int r = rgrp + 8 * u;
+                st[cg][u] = (cok && r < nk) ? base[(int64_t)r * g.nc + n] : 0.f;
+            }
+        }
+    };
+    auto store_view = [&](float *buf, const float (&st)[NCG][RPT]) {
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+            const int c = clane + 32 * cg;
+            if (c < nwcap) {
+#pragma unroll
+                for (int u = 0; u < RPT; ++u) {
+                    const int r = rgrp + 8 * u;
+                    if (r < SL) buf[c * SLP + r] = st[cg][u];
+                }
+            }
+        }
+    };
+    auto load_taps = [&](int v, int &nf, float (&w)[NTAP]) {
+        const int32_t *r = rec + ((int64_t)v * np + p) * NREC;
+        nf = valid ? r[0] : INT32_MAX;
+#pragma unroll
+        for (int t = 0; t < NTAP; ++t) w[t] = valid ? __int_as_float(r[1 + t]) : 0.f;
+    };
 
     float acc[SL];
 #pragma unroll
     for (int k = 0; k < SL; ++k) acc[k] = 0.f;
+    if (g.nv == 0) return;
 
-    const int lane = (int)threadIdx.x & 31;
-    const int grp = (int)threadIdx.x >> 5;
-
+    // double-buffered pipeline: view v + 1 is fetched while view v is gathered
+    float st[NCG][RPT];
+    int4 wcur = wtab[tile];
+    load_view(0, wcur, st);
+    store_view(lds, st);
+    int nf;
+    float w[NTAP];
+    load_taps(0, nf, w);
+    __syncthreads();
     for (int v = 0; v < g.nv; ++v) {
-        const ViewK vk = views[v];
-        const Window wd = tile_window(g, vk, ti0, ti1, tj0, tj1, k0, k0 + nk - 1);
-        if (wd.nw <= 0) continue;          // the tile misses the detector in this view
-        // this lane's taps (issued before the barrier to hide their latency)
-        const int32_t *r = rec + ((int64_t)v * np + p) * NREC;
-        const int nf = valid ? r[0] : INT32_MAX;
-        float w[NTAP];
-#pragma unroll
-        for (int t = 0; t < NTAP; ++t) w[t] = valid ? __int_as_float(r[1 + t]) : 0.f;
-        __syncthreads();
-        // stage rows k0..k0+nk-1, channels n0..n0+nw-1 (zeros off the detector)
-        for (int rr = grp; rr < SL; rr += NT / 32) {
-            const float *srow = sino + ((int64_t)v * g.nr + (k0 + rr)) * g.nc;
-            for (int c = lane; c < wd.nw; c += 32) {
-                const int n = wd.n0 + c;
-                float val = 0.f;
-                if (rr < nk && n >= 0 && n < g.nc) val = srow[n];
-                win[c * SLP + rr] = val;
-            }
+        const float *buf = lds + (v & 1) * nwcap * SLP;
+        const bool more = v + 1 < g.nv;
+        int4 wnext = wcur;
+        float nst[NCG][RPT];
+        int nnf = INT32_MAX;
+        float nw[NTAP];
+        if (more) {
+            wnext = wtab[(int64_t)(v + 1) * ntiles + tile];
+            load_view(v + 1, wnext, nst);
+            load_taps(v + 1, nnf, nw);
         }
-        __syncthreads();
-        if (nf != INT32_MAX) {
-            const float *col = win + (nf - wd.n0) * SLP;
+        if (nf != INT32_MAX && wcur.y > 0) {
+            const float *col = buf + (nf - wcur.x) * SLP;
 #pragma unroll
             for (int k = 0; k < SL; ++k) {
-                float s = acc[k];
+                float sacc = acc[k];
 #pragma unroll
-                for (int t = 0; t < NTAP; ++t) s = fmaf(w[t], col[t * SLP + k], s);
-                acc[k] = s;
+                for (int t = 0; t < NTAP; ++t) sacc = fmaf(w[t], col[t * SLP + k], sacc);
+                acc[k] = sacc;
             }
         }
+        if (more) {
+            store_view(lds + ((v + 1) & 1) * nwcap * SLP, nst);
+            wcur = wnext;
+            nf = nnf;
+#pragma unroll
+            for (int t = 0; t < NTAP; ++t) w[t] = nw[t];
+        }
+        __syncthreads();
     }
     if (valid) {
         float *out = recon + (int64_t)p * g.ns + k0;
@@ -106,7 +148,7 @@ template <int NTAP, int NREC>
 __global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__restrict__ recon,
                                                                float *__restrict__ sino,
                                                                const int32_t *__restrict__ wrec,
-                                                               const ViewK *__restrict__ views, Geo g, int nwcap,
+                                                               const int4 *__restrict__ wtab, Geo g, int nwcap,
                                                                int vsplit) {
     constexpr int TP = FTX * FTY;         // pixels per tile, one walk record per lane
     static_assert(TP == 64, "the walk keeps the tile's records one per lane");
@@ -124,8 +166,6 @@ __global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__res
     const int tile = (int)blockIdx.x;
     const int tj0 = (tile % tiles_x) * FTX;
     const int ti0 = (tile / tiles_x) * FTY;
-    const int tj1 = min(tj0 + FTX, g.nx) - 1;
-    const int ti1 = min(ti0 + FTY, g.ny) - 1;
     const int k0 = (int)blockIdx.y * 64;
     const int nk = min(64, g.ns - k0);
 
@@ -168,8 +208,10 @@ __global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__res
             v = view_of(it + FW);
             load_records(v, na);
         }
-        const ViewK vk = views[vc];
-        const Window wd = tile_window(g, vk, ti0, ti1, tj0, tj1, k0, k0 + nk - 1);
+        const int4 w4 = wtab[(int64_t)vc * ntiles + tile];
+        Window wd;
+        wd.n0 = w4.x;
+        wd.nw = w4.y;
         const int p0 = __builtin_amdgcn_readlane(ra[0], 0);
         if (wd.nw > 0 && (p0 & 255) != TP) {
             // acc[t] holds channel cur + t; the records say when to move on, and
@@ -246,8 +288,12 @@ static hipError_t par_back_t(const Plan &p, const float *sino, float *recon, hip
     const Geo &g = p.g;
     const int tiles = ((g.nx + BT - 1) / BT) * ((g.ny + BT - 1) / BT);
     const int chunks = (g.ns + SL - 1) / SL;
-    hipLaunchKernelGGL((par_back_kernel<SL, NTAP>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
-                       recon, p.rec, p.views, g);
+    if (p.back_ncg == 1)
+        hipLaunchKernelGGL((par_back_kernel<SL, NTAP, 1>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
+                           recon, p.rec, p.bwin, g, p.back_nwcap);
+    else
+        hipLaunchKernelGGL((par_back_kernel<SL, NTAP, 2>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
+                           recon, p.rec, p.bwin, g, p.back_nwcap);
     return hipGetLastError();
 }
 
@@ -258,7 +304,7 @@ static hipError_t par_fwd_t(const Plan &p, const float *recon, float *sino, hipS
     const int chunks = (g.ns + 63) / 64;
     constexpr int NREC = NTAP <= 3 ? 4 : 8;
     hipLaunchKernelGGL((par_forward_kernel<NTAP, NREC>), dim3(tiles, chunks, p.fwd_vsplit), dim3(FW * 64), p.fwd_lds,
-                       st, recon, sino, p.wrec, p.views, g, p.fwd_nwcap, p.fwd_vsplit);
+                       st, recon, sino, p.wrec, p.fwin, g, p.fwd_nwcap, p.fwd_vsplit);
     return hipGetLastError();
 }
 

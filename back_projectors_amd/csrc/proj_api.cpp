@@ -55,6 +55,8 @@ struct proj_handle_s {
     int32_t *d_idx = nullptr;
     int32_t *d_rec = nullptr;       // parallel tap records
     int32_t *d_wrec = nullptr;      // parallel tap records in forward walk order
+    Window *d_bwin = nullptr;       // back projection windows per (view, tile, chunk)
+    Window *d_fwin = nullptr;       // forward projection windows per (view, tile, chunk)
     size_t table_bytes = 0;
 };
 
@@ -82,23 +84,33 @@ struct WinMax {
     int nw = 0, nr = 0;
 };
 
-// Largest window over all views, tiles of tx x ty pixels and slice chunks of `sl`.
-WinMax max_window(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_, int sl) {
+// Windows of every (view, tile, slice chunk), in that order (tiles row-major,
+// as the kernels number them), and their maxima.
+WinMax window_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_, int sl,
+                    std::vector<Window> *out) {
     WinMax m;
-    const int ty = (g.ny + ty_ - 1) / ty_, tx = (g.nx + tx_ - 1) / tx_, nch = (g.ns + sl - 1) / sl;
+    const int ty = (g.ny + ty_ - 1) / ty_, tx = (g.nx + tx_ - 1) / tx_;
+    const int nch = g.kind == 0 ? 1 : (g.ns + sl - 1) / sl;
+    if (out) out->resize((size_t)g.nv * ty * tx * nch);
+    size_t e = 0;
     for (int v = 0; v < g.nv; ++v)
         for (int a = 0; a < ty; ++a)
             for (int b = 0; b < tx; ++b) {
                 const int i0 = a * ty_, i1 = std::min(i0 + ty_, g.ny) - 1;
                 const int j0 = b * tx_, j1 = std::min(j0 + tx_, g.nx) - 1;
-                for (int c = 0; c < (g.kind == 0 ? 1 : nch); ++c) {
+                for (int c = 0; c < nch; ++c, ++e) {
                     const int k0 = c * sl, k1 = std::min(k0 + sl, g.ns) - 1;
                     const Window w = tile_window(g, views[v], i0, i1, j0, j1, k0, k1);
                     m.nw = std::max(m.nw, w.nw);
                     m.nr = std::max(m.nr, w.nrw);
+                    if (out) (*out)[e] = w;
                 }
             }
     return m;
+}
+
+WinMax max_window(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_, int sl) {
+    return window_table(g, views, tx_, ty_, sl, nullptr);
 }
 
 // Validation and planning without touching the GPU.  Fills geo/views/plan.
@@ -191,9 +203,12 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
             const WinMax w = max_window(g, views, BT, BT, sl);
             plan.back_sl = sl;
             plan.back_nwcap = w.nw + 2;
-            plan.back_lds = (size_t)plan.back_nwcap * (sl + 1) * sizeof(float);
+            plan.back_lds = 2 * (size_t)plan.back_nwcap * (sl + 1) * sizeof(float);
             if (plan.back_lds <= kMaxLds || sl == 8) break;
         }
+        if (plan.back_nwcap > 64)
+            return fail(PROJ_ERR_UNSUPPORTED, "back projection window wider than 64 channels (detector far finer than the voxels)");
+        plan.back_ncg = plan.back_nwcap <= 32 ? 1 : 2;
         const WinMax wf = max_window(g, views, FTX, FTY, 64);
         plan.fwd_sl = 64;
         plan.fwd_nwcap = wf.nw + 2;
@@ -395,6 +410,24 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
             e = hipDeviceSynchronize();
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "table passes");
         }
+        if (plan.back_sl > 0) {
+            // every (view, tile, chunk) window, from the same code that sized the plan
+            std::vector<Window> bw, fw;
+            window_table(geo, views, BT, BT, plan.back_sl, &bw);
+            if (geo.kind == 0)
+                window_table(geo, views, FTX, FTY, 64, &fw);
+            else
+                window_table(geo, views, CTX, CTY, plan.fwd_sl, &fw);
+            e = hipMalloc((void **)&h->d_bwin, bw.size() * sizeof(Window));
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(windows)");
+            e = hipMemcpy(h->d_bwin, bw.data(), bw.size() * sizeof(Window), hipMemcpyHostToDevice);
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(windows)");
+            e = hipMalloc((void **)&h->d_fwin, fw.size() * sizeof(Window));
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(windows)");
+            e = hipMemcpy(h->d_fwin, fw.data(), fw.size() * sizeof(Window), hipMemcpyHostToDevice);
+            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(windows)");
+            rec_bytes += (bw.size() + fw.size()) * sizeof(Window);
+        }
         if (geo.kind != 0 && plan.fwd_sl > 0 && plan.fwd_lds > kMaxLds) {
             int lim = 0;
             e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, hip_device);
@@ -411,6 +444,8 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
         h->plan.idx = h->d_idx;
         h->plan.rec = h->d_rec;
         h->plan.wrec = h->d_wrec;
+        h->plan.bwin = reinterpret_cast<const int4 *>(h->d_bwin);
+        h->plan.fwin = reinterpret_cast<const int4 *>(h->d_fwin);
         if (std::getenv("PROJ_LOG")) {
             char buf[512];
             describe(h->plan, (int64_t)h->table_bytes, buf, sizeof buf);
@@ -487,6 +522,8 @@ void proj_destroy(proj_handle h) {
         if (h->d_idx) (void)hipFree(h->d_idx);
         if (h->d_rec) (void)hipFree(h->d_rec);
         if (h->d_wrec) (void)hipFree(h->d_wrec);
+        if (h->d_bwin) (void)hipFree(h->d_bwin);
+        if (h->d_fwin) (void)hipFree(h->d_fwin);
         if (h->d_views) (void)hipFree(h->d_views);
     }
     delete h;
