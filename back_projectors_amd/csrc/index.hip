@@ -103,16 +103,26 @@ __global__ __launch_bounds__(256) void par_taps_kernel(Geo g, const ViewK *__res
 // The same records re-laid for the forward walk.  One wave per (view, forward
 // tile): the tile's FTX*FTY pixels are ordered by their first tap channel n_f
 // (ties by pixel index), so a walk in this order never returns to a channel it
-// has passed.  Record r holds, in NREC dwords,
-//   dword 0: pixel-in-tile q (bits 0-7; FTX*FTY = a zero row for skipped
-//            entries), advance code (bits 8-10) and n_f + 2^16 (bits 11-31);
-//   dwords 1..: the NTAP tap weights (0 for skipped entries).
-// The advance code says how the walk's window of NTAP channels moves after
-// this record: 0 stay, 1..NTAP-1 move up by that many channels, 7 jump to the
-// next record's n_f.  Skipped pixels (outside the image, or no tap on the
-// detector) sort last with zero weights.
+// has passed.  The walk keeps NTAP accumulators as a ring: channel n lives in
+// accumulator n mod NTAP, so a step touches every accumulator exactly once and
+// nothing is ever moved between registers.  Per (view, tile) the records are
+// 2 + NTAP fields of 64 dwords, one dword per step:
+//   field 0: LDS byte offset of the step's voxel row, q * 256 (bit 31 set in
+//            every step when no pixel of the tile reaches the detector);
+//   field 1: 0 when nothing is flushed after this step; else bits 0-6 = the
+//            accumulators to flush, bits 7-13 = those among them below
+//            n_f mod NTAP (their channel lies one ring turn up), bits 14-31 =
+//            (n_f - (n_f mod NTAP)) / NTAP + 1, the ring turn of the step;
+//   field 2 + r: the weight for accumulator r, i.e. the tap weight of channel
+//            n_f + ((r - n_f) mod NTAP).
+// Accumulator r thus holds channel NTAP * (turn - 1) + r, plus NTAP when its
+// bit 7 + r is set.  It is flushed once its channel is below the next step's
+// n_f (every channel finishes there, since the walk never comes back), and all
+// of them after the last step that reaches the detector.  Steps of pixels that
+// miss the detector (or lie outside the image) sort last, with zero weights
+// and nothing to flush.
 __global__ __launch_bounds__(64) void par_walk_records_kernel(Geo g, const int32_t *__restrict__ rec,
-                                                              int32_t *__restrict__ out, int ntap, int nrec) {
+                                                              uint32_t *__restrict__ out, int ntap) {
     constexpr int TP = FTX * FTY;
     static_assert(TP == 64, "one wave sorts one tile");
     __shared__ int s_nf[TP];
@@ -139,19 +149,23 @@ __global__ __launch_bounds__(64) void par_walk_records_kernel(Geo g, const int32
     }
     s_sorted_nf[rank] = nf;
     __syncthreads();
-    int32_t *o = out + (vt * TP + rank) * nrec;
-    for (int t = 0; t < nrec; ++t) o[t] = 0;
-    if (nf == INT32_MAX) {
-        o[0] = TP;                                    // zero row, no weight, stay
-        return;
+    uint32_t *o = out + vt * TP * (2 + ntap) + rank;   // field f of this step: o[f * TP]
+    o[0] = (uint32_t)q * 256u | (nvalid == 0 ? 0x80000000u : 0u);
+    o[TP] = 0u;
+    for (int t = 0; t < ntap; ++t) o[(2 + t) * TP] = 0u;
+    if (nf == INT32_MAX) return;
+    const int cm = ((nf % ntap) + ntap) % ntap;
+    const int turn = (nf - cm) / ntap + 1;           // >= 0: n_f >= 1 - ntap
+    // channels nf .. nf + fin - 1 are finished after this step
+    const int fin = rank + 1 < nvalid ? min(s_sorted_nf[rank + 1] - nf, ntap) : ntap;
+    uint32_t mask = 0, up = 0;
+    for (int d = 0; d < fin; ++d) {
+        const int rr = (cm + d) % ntap;
+        mask |= 1u << rr;
+        if (rr < cm) up |= 1u << rr;
     }
-    int adv = 0;
-    if (rank + 1 < nvalid) {
-        const int d = s_sorted_nf[rank + 1] - nf;
-        adv = d < ntap ? d : 7;
-    }
-    o[0] = q | (adv << 8) | ((nf + 65536) << 11);
-    for (int t = 0; t < ntap; ++t) o[1 + t] = r[1 + t];
+    if (mask) o[TP] = mask | (up << 7) | ((uint32_t)turn << 14);
+    for (int rr = 0; rr < ntap; ++rr) o[(2 + rr) * TP] = (uint32_t)r[1 + (rr - cm + ntap) % ntap];
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float4 *__restrict__ b4, float *__restrict__ tail,
@@ -180,11 +194,10 @@ hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int n
     return hipGetLastError();
 }
 
-hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, int32_t *out, int ntap, int nrec,
-                                   hipStream_t st) {
+hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, uint32_t *out, int ntap, hipStream_t st) {
     const int64_t blocks = (int64_t)g.nv * ((g.nx + FTX - 1) / FTX) * ((g.ny + FTY - 1) / FTY);
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(par_walk_records_kernel, dim3((unsigned)blocks), dim3(64), 0, st, g, rec, out, ntap, nrec);
+    hipLaunchKernelGGL(par_walk_records_kernel, dim3((unsigned)blocks), dim3(64), 0, st, g, rec, out, ntap);
     return hipGetLastError();
 }
 

@@ -16,10 +16,12 @@ struct Plan {
     const ViewK *views = nullptr;   // device [V]
     const int32_t *idx = nullptr;   // device [V][Ny*Nx]
     const int32_t *rec = nullptr;   // parallel: device tap records [V][Ny*Nx][1 + ntap]
-    const int32_t *wrec = nullptr;  // parallel: walk-ordered records [V][tiles][FTX*FTY][nrec]
-    int nrec = 0;                   // parallel: dwords per walk record (4 or 8)
+    const uint32_t *wrec = nullptr; // parallel: forward walk steps [V][tiles][FTX*FTY][1 + ntap]
+    float *facc = nullptr;          // parallel: forward accumulation buffer [V][fwd_cb][fwd_s64]
+    int fwd_cb = 0;                 // parallel: channels of facc (C plus ntap - 1 guards each side)
+    int fwd_s64 = 0;                // parallel: slices of facc (S rounded up to 64)
     const int4 *bwin = nullptr;     // back windows [V][tiles][chunks] (n0, nw, m0, nrw)
-    const int4 *fwin = nullptr;     // forward windows [V][tiles][chunks]
+    const int4 *fwin = nullptr;     // cone forward windows [V][tiles][chunks]
     int ntap = 0;                   // parallel: taps per record
 
     // back projection: lanes = pixels of a BT x BT tile, SL slices per lane
@@ -48,13 +50,11 @@ constexpr int CFW = 4;   // cone forward waves per workgroup (one view each at a
 
 hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
 hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st);
-hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, int32_t *out, int ntap, int nrec,
-                                   hipStream_t st);
+hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, uint32_t *out, int ntap, hipStream_t st);
 hipError_t launch_fill_zero(float *buf, int64_t n, hipStream_t st);
 
 hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, hipStream_t st);
 hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
-hipError_t par_forward_allow_lds(int ntap, size_t bytes);
 hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, hipStream_t st);
 hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
 hipError_t cone_forward_allow_lds(int radius, int stride, size_t bytes);

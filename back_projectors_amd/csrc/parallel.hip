@@ -26,6 +26,8 @@
 // sinogram with coalesced global atomics, one per cell per view and tile.
 // Float atomics in LDS are avoided on purpose: on gfx950 they cost tens of
 // times a plain read-modify-write.
+#include <utility>
+
 #include "launch.h"
 
 namespace bpamd {
@@ -144,22 +146,41 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
     }
 }
 
-template <int NTAP, int NREC>
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N - 1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// Lane N of each 16-lane row, broadcast to its row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + N, 0xf, 0xf, false);
+}
+
+// acc += w' * x, where w' is lane N of the row of w: one v_fmac with the
+// broadcast folded into its DPP operand.  The s_nop gives the two wait states
+// a DPP read needs after a VALU write of its source.
+template <int N>
+__device__ __forceinline__ void fmac_row_bcast(float &acc, uint32_t w, float x) {
+    asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(w), "v"(x), "n"(N));
+}
+
+template <int K>
 __global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__restrict__ recon,
-                                                               float *__restrict__ sino,
-                                                               const int32_t *__restrict__ wrec,
-                                                               const int4 *__restrict__ wtab, Geo g, int nwcap,
-                                                               int vsplit) {
-    constexpr int TP = FTX * FTY;         // pixels per tile, one walk record per lane
-    static_assert(TP == 64, "the walk keeps the tile's records one per lane");
-    constexpr int XP = 64;                // LDS pitch of one voxel cylinder chunk
-    constexpr int WP = 65;                // LDS pitch of one window channel (slices fastest)
-    extern __shared__ float lds[];
-    float *xt = lds;                                   // [TP + 1][XP]; row TP stays zero
+                                                               float *__restrict__ facc,
+                                                               const uint32_t *__restrict__ wrec, Geo g, int cb,
+                                                               int s64, int vsplit) {
+    constexpr int TP = FTX * FTY;         // pixels per tile = walk steps per view
+    static_assert(TP == 64, "a view's 64 steps sit in 4 registers of 16-lane rows");
+    constexpr int NF = 2 + K;             // record fields per step
+    constexpr int D = 4;                  // voxel reads in flight ahead of the step using them
+    __shared__ float xt[TP * 64];         // the tile's voxels, [pixel][slice]
     const int lane = (int)threadIdx.x & 63;
-    // wave index, made visibly uniform so per-view work stays on the scalar unit
+    // wave index, made visibly uniform so that per-view control stays scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    float *win = lds + (TP + 1) * XP + wave * nwcap * WP;   // this wave's window [nwcap][WP]
 
     const int tiles_x = (g.nx + FTX - 1) / FTX;
     const int ntiles = tiles_x * ((g.ny + FTY - 1) / FTY);
@@ -169,15 +190,13 @@ __global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__res
     const int k0 = (int)blockIdx.y * 64;
     const int nk = min(64, g.ns - k0);
 
-    // the tile's voxels, one 64-slice chunk per pixel, plus a zero row
-    for (int e = (int)threadIdx.x; e < (TP + 1) * 64; e += FW * 64) {
+    for (int e = (int)threadIdx.x; e < TP * 64; e += FW * 64) {
         const int q = e >> 6, k = e & 63;
         const int i = ti0 + q / FTX, j = tj0 + q % FTX;
         float val = 0.f;
-        if (q < TP && i < g.ny && j < g.nx && k < nk) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + k];
-        xt[q * XP + k] = val;
+        if (i < g.ny && j < g.nx && k < nk) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + k];
+        xt[e] = val;
     }
-    for (int e = lane; e < nwcap * WP; e += 64) win[e] = 0.f;
     __syncthreads();
 
     const int vper = (g.nv + vsplit - 1) / vsplit;
@@ -186,100 +205,103 @@ __global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__res
     const int cnt = vend - vbeg;
     // staggered start, so that tiles along one ray reach a view at different times
     const int start = cnt > 0 ? (int)((blockIdx.x * 37u + blockIdx.y * 11u) % (unsigned)cnt) : 0;
-    auto view_of = [&](int it) {
-        int v = vbeg + start + it;
+    auto view_of = [&](int i) {
+        const int v = vbeg + start + i;
         return v >= vend ? v - cnt : v;
     };
-    // the (view, tile) records: lane l holds walk step l
-    auto load_records = [&](int v, int (&ra)[NREC]) {
-        const int32_t *base = wrec + ((int64_t)v * ntiles + tile) * TP * NREC;
+    const char *xb = reinterpret_cast<const char *>(xt);
+    const uint32_t l4 = (uint32_t)lane * 4u;
+    const uint32_t s4 = (uint32_t)s64 * 4u;         // bytes between channels of the accumulation buffer
+    const uint32_t ks = (uint32_t)K * s4;           // bytes per ring turn
+    // a view's records: field f, steps 16 j .. 16 j + 15 in every row of R[f][j]
+    auto load_records = [&](int v, uint32_t (&R)[NF][4]) {
+        const uint32_t *b = wrec + ((int64_t)v * ntiles + tile) * (NF * TP) + (lane & 15);
 #pragma unroll
-        for (int t = 0; t < NREC; ++t) ra[t] = base[lane * NREC + t];
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) R[f][j] = b[f * TP + 16 * j];
     };
 
-    int ra[NREC];
-    int it = wave;
-    int v = it < cnt ? view_of(it) : 0;
-    if (it < cnt) load_records(v, ra);
-    for (; it < cnt; it += FW) {
-        const int vc = v;
-        int na[NREC];
-        if (it + FW < cnt) {              // prefetch the next view's records
-            v = view_of(it + FW);
-            load_records(v, na);
-        }
-        const int4 w4 = wtab[(int64_t)vc * ntiles + tile];
-        Window wd;
-        wd.n0 = w4.x;
-        wd.nw = w4.y;
-        const int p0 = __builtin_amdgcn_readlane(ra[0], 0);
-        if (wd.nw > 0 && (p0 & 255) != TP) {
-            // acc[t] holds channel cur + t; the records say when to move on, and
-            // a channel left behind is finished, so it is stored, not added
-            float acc[NTAP];
+    // one view: its records in R; the records of the view two turns later
+    // are fetched into P meanwhile (always issued, for a static wait count)
+    auto walk_view = [&](int i, uint32_t (&R)[NF][4], uint32_t (&P)[NF][4]) {
+        const int v = view_of(i);
+        load_records(view_of(min(i + 2 * FW, cnt - 1)), P);
+        if (__builtin_amdgcn_readfirstlane(R[0][0]) >> 31) return;   // the tile misses the detector
+        // steps followed by a flush, one bit per step
+        uint64_t fl = 0;
 #pragma unroll
-            for (int t = 0; t < NTAP; ++t) acc[t] = 0.f;
-            int cur = (p0 >> 11) - 65536;
-            auto store = [&](int n, float a) { win[(n - wd.n0) * WP + lane] = a; };
+        for (int j = 0; j < 4; ++j) fl |= (__builtin_amdgcn_ballot_w64(R[1][j] != 0u) & 0xffffull) << (16 * j);
+        // byte base such that ring turn T, accumulator r is at T * ks + r * s4
+        char *fb = reinterpret_cast<char *>(facc + ((int64_t)v * cb + (K - 1)) * s64 + k0) - ks;
+        float acc[K];
 #pragma unroll
-            for (int s = 0; s < TP; s += 4) {
-                int pk[4];
-                float w[4][NTAP], xv[4];
+        for (int r = 0; r < K; ++r) acc[r] = 0.f;
+        float xq[TP];
+        auto read_x = [&](auto SC) {
+            constexpr int S = decltype(SC)::value;
+            xq[S] = *reinterpret_cast<const float *>(xb + (row_bcast<S & 15>(R[0][S >> 4]) + l4));
+        };
+        static_for(read_x, std::make_integer_sequence<int, D>{});
+        static_for(
+            [&](auto SC) {
+                constexpr int S = decltype(SC)::value;
+                if constexpr (S + D < TP) read_x(std::integral_constant<int, S + D>{});
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    pk[u] = __builtin_amdgcn_readlane(ra[0], s + u);
+                for (int r = 0; r < K; ++r) fmac_row_bcast<S & 15>(acc[r], R[2 + r][S >> 4], xq[S]);
+                if ((fl >> S) & 1u) {
+                    const uint32_t f = (uint32_t)__builtin_amdgcn_readlane((int)R[1][S >> 4], S & 15);
+                    const uint32_t tb = (f >> 14) * ks;
 #pragma unroll
-                    for (int t = 0; t < NTAP; ++t) w[u][t] = __int_as_float(__builtin_amdgcn_readlane(ra[1 + t], s + u));
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) xv[u] = xt[(pk[u] & 255) * XP + lane];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-#pragma unroll
-                    for (int t = 0; t < NTAP; ++t) acc[t] = fmaf(w[u][t], xv[u], acc[t]);
-                    const int adv = (pk[u] >> 8) & 7;
-                    if (adv != 0) {
-                        if (adv == 7) {
-#pragma unroll
-                            for (int t = 0; t < NTAP; ++t) {
-                                store(cur + t, acc[t]);
-                                acc[t] = 0.f;
-                            }
-                            if (s + u + 1 < TP) cur = (__builtin_amdgcn_readlane(ra[0], s + u + 1) >> 11) - 65536;
-                        } else {
-#pragma unroll
-                            for (int t = 0; t < NTAP - 1; ++t)
-                                if (t < adv) store(cur + t, acc[t]);
-#pragma unroll
-                            for (int t = 0; t < NTAP; ++t) {
-                                float nv = 0.f;
-#pragma unroll
-                                for (int dd = 1; dd < NTAP; ++dd)
-                                    if (adv == dd && t + dd < NTAP) nv = acc[t + dd];
-                                acc[t] = nv;
-                            }
-                            cur += adv;
+                    for (int r = 0; r < K; ++r) {
+                        if (f & (1u << r)) {
+                            const uint32_t off = tb + (uint32_t)r * s4 + ((f >> (7 + r)) & 1u ? ks : 0u);
+                            unsafeAtomicAdd(reinterpret_cast<float *>(fb + (off + l4)), acc[r]);
+                            acc[r] = 0.f;
                         }
                     }
                 }
-            }
+            },
+            std::make_integer_sequence<int, TP>{});
+    };
+
+    // three record buffers in rotation (no copies, so no early waits)
+    if (wave >= cnt) return;
+    uint32_t RA[NF][4], RB[NF][4], RC[NF][4];
+    load_records(view_of(wave), RA);
+    load_records(view_of(min(wave + FW, cnt - 1)), RB);
+    for (int it = wave; it < cnt; it += 3 * FW) {
+        walk_view(it, RA, RC);
+        if (it + FW >= cnt) break;
+        walk_view(it + FW, RB, RA);
+        if (it + 2 * FW >= cnt) break;
+        walk_view(it + 2 * FW, RC, RB);
+    }
+}
+
+// facc [V][cb][s64] (slices fastest, K - 1 guard channels each side) ->
+// sino [V][R][C] (channels fastest), through a 64 x 64 LDS tile.
+__global__ __launch_bounds__(256) void par_unpack_kernel(const float *__restrict__ facc, float *__restrict__ sino,
+                                                         int nr, int nc, int cb, int s64, int guard, int tn) {
+    __shared__ float t[64][65];
+    const int v = (int)(blockIdx.x / (unsigned)tn);
+    const int n0 = (int)(blockIdx.x % (unsigned)tn) * 64;
+    const int r0 = (int)blockIdx.y * 64;
+    const int a = (int)threadIdx.x & 63, b = (int)threadIdx.x >> 6;
+    const float *src = facc + ((int64_t)v * cb + guard + n0) * s64 + r0;
 #pragma unroll
-            for (int t = 0; t < NTAP; ++t) store(cur + t, acc[t]);
-            // add the window to the sinogram: lanes run along channels, coalesced
-            const int total = wd.nw * nk;
-            const float rnw = 1.0f / (float)wd.nw;
-            for (int e = lane; e < total; e += 64) {
-                const int k = (int)(((float)e + 0.5f) * rnw);   // exact: e < 2^22 and nw is small
-                const int c = e - k * wd.nw;
-                const float val = win[c * WP + k];
-                win[c * WP + k] = 0.f;
-                const int n = wd.n0 + c;
-                if (val != 0.f && n >= 0 && n < g.nc)
-                    unsafeAtomicAdd(&sino[((int64_t)vc * g.nr + (k0 + k)) * g.nc + n], val);
-            }
+    for (int u = 0; u < 16; ++u) {
+        const int n = b + 4 * u;
+        t[n][a] = n0 + n < nc ? src[(int64_t)n * s64 + a] : 0.f;
+    }
+    __syncthreads();
+    float *dst = sino + ((int64_t)v * nr + r0) * nc + n0;
+    if (n0 + a < nc) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int r = b + 4 * u;
+            if (r0 + r < nr) dst[(int64_t)r * nc + a] = t[a][r];
         }
-#pragma unroll
-        for (int t = 0; t < NREC; ++t) ra[t] = na[t];
     }
 }
 
@@ -297,27 +319,15 @@ static hipError_t par_back_t(const Plan &p, const float *sino, float *recon, hip
     return hipGetLastError();
 }
 
-template <int NTAP>
-static hipError_t par_fwd_t(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+template <int K>
+static hipError_t par_fwd_t(const Plan &p, const float *recon, hipStream_t st) {
     const Geo &g = p.g;
     const int tiles = ((g.nx + FTX - 1) / FTX) * ((g.ny + FTY - 1) / FTY);
     const int chunks = (g.ns + 63) / 64;
-    constexpr int NREC = NTAP <= 3 ? 4 : 8;
-    hipLaunchKernelGGL((par_forward_kernel<NTAP, NREC>), dim3(tiles, chunks, p.fwd_vsplit), dim3(FW * 64), p.fwd_lds,
-                       st, recon, sino, p.wrec, p.fwin, g, p.fwd_nwcap, p.fwd_vsplit);
+    hipLaunchKernelGGL((par_forward_kernel<K>), dim3(tiles, chunks, p.fwd_vsplit), dim3(FW * 64), 0, st, recon,
+                       p.facc, p.wrec, g, p.fwd_cb, p.fwd_s64, p.fwd_vsplit);
     return hipGetLastError();
 }
-
-#define BPAMD_DISPATCH_NTAP(FN, ...)                                                                          \
-    switch (p.ntap) {                                                                                         \
-    case 2: return FN<2>(__VA_ARGS__);                                                                        \
-    case 3: return FN<3>(__VA_ARGS__);                                                                        \
-    case 4: return FN<4>(__VA_ARGS__);                                                                        \
-    case 5: return FN<5>(__VA_ARGS__);                                                                        \
-    case 6: return FN<6>(__VA_ARGS__);                                                                        \
-    case 7: return FN<7>(__VA_ARGS__);                                                                        \
-    default: return hipErrorInvalidValue;                                                                     \
-    }
 
 template <int SL>
 static hipError_t par_back_sl(const Plan &p, const float *sino, float *recon, hipStream_t st) {
@@ -342,24 +352,26 @@ hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, hipSt
     }
 }
 
+// Zero the accumulation buffer, walk, then unpack into the sinogram (which the
+// unpack writes in full, so the sinogram needs no fill of its own).
 hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st) {
-    BPAMD_DISPATCH_NTAP(par_fwd_t, p, recon, sino, st)
-}
-
-// Dynamic LDS above the default limit needs the opt-in attribute; called once
-// per kernel by the planner when a plan asks for more.
-hipError_t par_forward_allow_lds(int ntap, size_t bytes) {
-    const void *f = nullptr;
-    switch (ntap) {
-    case 2: f = (const void *)par_forward_kernel<2, 4>; break;
-    case 3: f = (const void *)par_forward_kernel<3, 4>; break;
-    case 4: f = (const void *)par_forward_kernel<4, 8>; break;
-    case 5: f = (const void *)par_forward_kernel<5, 8>; break;
-    case 6: f = (const void *)par_forward_kernel<6, 8>; break;
-    case 7: f = (const void *)par_forward_kernel<7, 8>; break;
+    const Geo &g = p.g;
+    hipError_t e = launch_fill_zero(p.facc, (int64_t)g.nv * p.fwd_cb * p.fwd_s64, st);
+    if (e != hipSuccess) return e;
+    switch (p.ntap) {
+    case 2: e = par_fwd_t<2>(p, recon, st); break;
+    case 3: e = par_fwd_t<3>(p, recon, st); break;
+    case 4: e = par_fwd_t<4>(p, recon, st); break;
+    case 5: e = par_fwd_t<5>(p, recon, st); break;
+    case 6: e = par_fwd_t<6>(p, recon, st); break;
+    case 7: e = par_fwd_t<7>(p, recon, st); break;
     default: return hipErrorInvalidValue;
     }
-    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    const int tn = (g.nc + 63) / 64;
+    hipLaunchKernelGGL(par_unpack_kernel, dim3((unsigned)(g.nv * tn), (g.nr + 63) / 64), dim3(256), 0, st, p.facc,
+                       sino, g.nr, g.nc, p.fwd_cb, p.fwd_s64, p.ntap - 1, tn);
+    return hipGetLastError();
 }
 
 }  // namespace bpamd

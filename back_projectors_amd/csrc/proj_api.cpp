@@ -54,9 +54,11 @@ struct proj_handle_s {
     ViewK *d_views = nullptr;
     int32_t *d_idx = nullptr;
     int32_t *d_rec = nullptr;       // parallel tap records
-    int32_t *d_wrec = nullptr;      // parallel tap records in forward walk order
+    uint32_t *d_wrec = nullptr;     // parallel forward walk steps
+    float *d_facc = nullptr;        // parallel forward accumulation buffer (slices fastest)
+    hipEvent_t fwd_done = nullptr;  // parallel: last forward on this handle, orders calls that share d_facc
     Window *d_bwin = nullptr;       // back projection windows per (view, tile, chunk)
-    Window *d_fwin = nullptr;       // forward projection windows per (view, tile, chunk)
+    Window *d_fwin = nullptr;       // cone forward windows per (view, tile, chunk)
     size_t table_bytes = 0;
 };
 
@@ -197,8 +199,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         plan.ntap = (int)std::min<double>(2.0 * g.radius + 1.0, std::ceil(wmax) + 1.0);
         plan.ntap = std::max(plan.ntap, 2);
         if (plan.ntap > 7) return fail(PROJ_ERR_UNSUPPORTED, "more than 7 channel taps per voxel (detector far finer than the voxels)");
-        if (C + 4 * g.radius >= ((int64_t)1 << 20) - 65536) return fail(PROJ_ERR_UNSUPPORTED, "too many detector channels");
-        plan.nrec = plan.ntap <= 3 ? 4 : 8;
+        if (C + plan.ntap > 16384) return fail(PROJ_ERR_UNSUPPORTED, "more than 16384 - taps detector channels");
         for (int sl = pick_chunk(S, {8, 16, 32, 64});; sl /= 2) {
             const WinMax w = max_window(g, views, BT, BT, sl);
             plan.back_sl = sl;
@@ -209,10 +210,13 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         if (plan.back_nwcap > 64)
             return fail(PROJ_ERR_UNSUPPORTED, "back projection window wider than 64 channels (detector far finer than the voxels)");
         plan.back_ncg = plan.back_nwcap <= 32 ? 1 : 2;
-        const WinMax wf = max_window(g, views, FTX, FTY, 64);
         plan.fwd_sl = 64;
-        plan.fwd_nwcap = wf.nw + 2;
-        plan.fwd_lds = ((size_t)(FTX * FTY + 1) * 64 + (size_t)FW * plan.fwd_nwcap * 65) * sizeof(float);
+        plan.fwd_lds = (size_t)FTX * FTY * 64 * sizeof(float);
+        plan.fwd_cb = (int)C + 2 * (plan.ntap - 1);
+        plan.fwd_s64 = (int)(((S + 63) / 64) * 64);
+        // the walk addresses one view of the buffer with 32-bit byte offsets
+        if ((int64_t)(plan.fwd_cb + 2 * plan.ntap) * plan.fwd_s64 * 4 >= ((int64_t)1 << 31))
+            return fail(PROJ_ERR_UNSUPPORTED, "forward accumulation buffer too large per view");
     } else {
         auto back_bytes = [&](int sl, int &nwcap, int &nrcap) {
             const WinMax w = max_window(g, views, BT, BT, sl);
@@ -272,10 +276,11 @@ int describe(const Plan &p, int64_t table_bytes, char *buf, int len) {
         buf, (size_t)std::max(len, 0),
         "kind=%s V=%d R=%d C=%d Ny=%d Nx=%d S=%d radius=%d taps=%d | back: %dx%d px tile, lanes=pixels, %d "
         "slices/lane, window %d ch x %d rows, %zu B LDS | forward: %dx%d px tile, %s, %d slices, window %d ch x %d "
-        "rows, %zu B LDS, %d view ranges | tables %lld B",
+        "rows, %zu B LDS, %d view ranges | tables and buffers %lld B",
         par ? "parallel" : "cone_flat", g.nv, g.nr, g.nc, g.ny, g.nx, g.ns, g.radius, par ? p.ntap : 2 * g.radius + 1,
         BT, BT, p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, par ? FTX : CTX, par ? FTY : CTY,
-        par ? "lanes=slices, wave per view, channel-ordered walk" : "lanes=strided slices, wave per view, LDS window",
+        par ? "lanes=slices, wave per view, channel-ordered walk, ring accumulators"
+            : "lanes=strided slices, wave per view, LDS window",
         p.fwd_sl,
         p.fwd_nwcap, par ? p.fwd_sl : p.fwd_nrcap, p.fwd_lds, p.fwd_vsplit, (long long)table_bytes);
 }
@@ -389,23 +394,18 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "tap record pass");
                 constexpr int TP = FTX * FTY;
                 const int64_t ntiles = (int64_t)((geo.nx + FTX - 1) / FTX) * ((geo.ny + FTY - 1) / FTY);
-                const size_t wrec_bytes = (size_t)geo.nv * ntiles * TP * plan.nrec * sizeof(int32_t);
+                const size_t wrec_bytes = (size_t)geo.nv * ntiles * TP * (2 + plan.ntap) * sizeof(uint32_t);
                 e = hipMalloc((void **)&h->d_wrec, wrec_bytes);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(walk records)");
-                e = launch_par_walk_records(geo, h->d_rec, h->d_wrec, plan.ntap, plan.nrec, nullptr);
+                e = launch_par_walk_records(geo, h->d_rec, h->d_wrec, plan.ntap, nullptr);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "walk record pass");
                 rec_bytes += wrec_bytes;
-                if (plan.fwd_lds > kMaxLds) {
-                    int lim = 0;
-                    e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, hip_device);
-                    if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipDeviceGetAttribute");
-                    if ((size_t)lim < plan.fwd_lds) {
-                        proj_destroy(h);
-                        return fail(PROJ_ERR_UNSUPPORTED, "device LDS per workgroup below the forward plan's need");
-                    }
-                    e = par_forward_allow_lds(plan.ntap, plan.fwd_lds);
-                    if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipFuncSetAttribute(LDS)");
-                }
+                const size_t facc_bytes = (size_t)geo.nv * plan.fwd_cb * plan.fwd_s64 * sizeof(float);
+                e = hipMalloc((void **)&h->d_facc, facc_bytes);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(forward accumulation buffer)");
+                rec_bytes += facc_bytes;
+                e = hipEventCreateWithFlags(&h->fwd_done, hipEventDisableTiming);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipEventCreateWithFlags");
             }
             e = hipDeviceSynchronize();
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "table passes");
@@ -414,18 +414,17 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
             // every (view, tile, chunk) window, from the same code that sized the plan
             std::vector<Window> bw, fw;
             window_table(geo, views, BT, BT, plan.back_sl, &bw);
-            if (geo.kind == 0)
-                window_table(geo, views, FTX, FTY, 64, &fw);
-            else
-                window_table(geo, views, CTX, CTY, plan.fwd_sl, &fw);
+            if (geo.kind != 0) window_table(geo, views, CTX, CTY, plan.fwd_sl, &fw);
             e = hipMalloc((void **)&h->d_bwin, bw.size() * sizeof(Window));
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(windows)");
             e = hipMemcpy(h->d_bwin, bw.data(), bw.size() * sizeof(Window), hipMemcpyHostToDevice);
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(windows)");
-            e = hipMalloc((void **)&h->d_fwin, fw.size() * sizeof(Window));
-            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(windows)");
-            e = hipMemcpy(h->d_fwin, fw.data(), fw.size() * sizeof(Window), hipMemcpyHostToDevice);
-            if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(windows)");
+            if (!fw.empty()) {
+                e = hipMalloc((void **)&h->d_fwin, fw.size() * sizeof(Window));
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(windows)");
+                e = hipMemcpy(h->d_fwin, fw.data(), fw.size() * sizeof(Window), hipMemcpyHostToDevice);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(windows)");
+            }
             rec_bytes += (bw.size() + fw.size()) * sizeof(Window);
         }
         if (geo.kind != 0 && plan.fwd_sl > 0 && plan.fwd_lds > kMaxLds) {
@@ -444,6 +443,7 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
         h->plan.idx = h->d_idx;
         h->plan.rec = h->d_rec;
         h->plan.wrec = h->d_wrec;
+        h->plan.facc = h->d_facc;
         h->plan.bwin = reinterpret_cast<const int4 *>(h->d_bwin);
         h->plan.fwin = reinterpret_cast<const int4 *>(h->d_fwin);
         if (std::getenv("PROJ_LOG")) {
@@ -470,11 +470,24 @@ proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev,
     DeviceGuard dg(h->device);
     if (dg.err != hipSuccess) return device_fail(dg.err, "hipSetDevice");
     hipStream_t st = (hipStream_t)hip_stream;
-    hipError_t e = launch_fill_zero(sino_dev, h->sino_elems, st);
-    if (e != hipSuccess) return device_fail(e, "zero fill");
+    hipError_t e;
+    if (h->plan.back_sl == 0 || h->plan.g.kind != 0) {
+        e = launch_fill_zero(sino_dev, h->sino_elems, st);
+        if (e != hipSuccess) return device_fail(e, "zero fill");
+    }
     if (h->plan.back_sl == 0) return ok();     // empty volume or no views: the sinogram is zero
-    e = h->plan.g.kind == 0 ? launch_par_forward(h->plan, recon_dev, sino_dev, st)
-                            : launch_cone_forward(h->plan, recon_dev, sino_dev, st);
+    if (h->plan.g.kind == 0) {
+        // the accumulation buffer belongs to the handle: a call on another
+        // stream waits on the GPU for the previous one
+        e = hipStreamWaitEvent(st, h->fwd_done, 0);
+        if (e != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
+        e = launch_par_forward(h->plan, recon_dev, sino_dev, st);
+        if (e != hipSuccess) return device_fail(e, "forward projection launch");
+        e = hipEventRecord(h->fwd_done, st);
+        if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+        return ok();
+    }
+    e = launch_cone_forward(h->plan, recon_dev, sino_dev, st);
     if (e != hipSuccess) return device_fail(e, "forward projection launch");
     return ok();
 }
@@ -522,6 +535,8 @@ void proj_destroy(proj_handle h) {
         if (h->d_idx) (void)hipFree(h->d_idx);
         if (h->d_rec) (void)hipFree(h->d_rec);
         if (h->d_wrec) (void)hipFree(h->d_wrec);
+        if (h->d_facc) (void)hipFree(h->d_facc);
+        if (h->fwd_done) (void)hipEventDestroy(h->fwd_done);
         if (h->d_bwin) (void)hipFree(h->d_bwin);
         if (h->d_fwin) (void)hipFree(h->d_fwin);
         if (h->d_views) (void)hipFree(h->d_views);
