@@ -100,15 +100,15 @@ __global__ __launch_bounds__(256) void par_taps_kernel(Geo g, const ViewK *__res
     }
 }
 
-// The same records re-laid for the forward walk.  One wave per (view, forward
-// tile): the tile's FTX*FTY pixels are ordered by their first tap channel n_f
-// (ties by pixel index), so a walk in this order never returns to a channel it
-// has passed.  The walk keeps NTAP accumulators as a ring: channel n lives in
-// accumulator n mod NTAP, so a step touches every accumulator exactly once and
-// nothing is ever moved between registers.  Per (view, tile) the records are
-// 2 + NTAP fields of 64 dwords, one dword per step:
-//   field 0: LDS byte offset of the step's voxel row, q * 256 (bit 31 set in
-//            every step when no pixel of the tile reaches the detector);
+// The same records re-laid for the forward walk.  One workgroup per (view,
+// region of RSX x RSY pixels): the region's pixels are ordered by their first
+// tap channel n_f (ties by pixel index: a stable counting sort), so a walk in
+// this order never returns to a channel it has passed.  The walk keeps NTAP
+// accumulators as a ring: channel n lives in accumulator n mod NTAP, so a step
+// touches every accumulator exactly once and nothing is ever moved between
+// registers.  Steps are grouped by 16; per (view, region, group) the records
+// are 2 + NTAP fields of 16 dwords, one dword per step:
+//   field 0: LDS byte offset of the step's voxel row (pixel-in-region * 64);
 //   field 1: 0 when nothing is flushed after this step; else bits 0-6 = the
 //            accumulators to flush, bits 7-13 = those among them below
 //            n_f mod NTAP (their channel lies one ring turn up), bits 14-31 =
@@ -120,52 +120,101 @@ __global__ __launch_bounds__(256) void par_taps_kernel(Geo g, const ViewK *__res
 // n_f (every channel finishes there, since the walk never comes back), and all
 // of them after the last step that reaches the detector.  Steps of pixels that
 // miss the detector (or lie outside the image) sort last, with zero weights
-// and nothing to flush.
-__global__ __launch_bounds__(64) void par_walk_records_kernel(Geo g, const int32_t *__restrict__ rec,
-                                                              uint32_t *__restrict__ out, int ntap) {
-    constexpr int TP = FTX * FTY;
-    static_assert(TP == 64, "one wave sorts one tile");
-    __shared__ int s_nf[TP];
-    __shared__ int s_sorted_nf[TP];
-    const int tiles_x = (g.nx + FTX - 1) / FTX;
-    const int ntiles = tiles_x * ((g.ny + FTY - 1) / FTY);
-    const int64_t vt = blockIdx.x;
-    const int tile = (int)(vt % ntiles);
-    const int v = (int)(vt / ntiles);
+// and nothing to flush, and so do the steps that pad the walk to whole groups.
+// Dynamic LDS: 2 * RSX * RSY + nbin + 1 ints.
+__global__ __launch_bounds__(256) void par_region_records_kernel(Geo g, const int32_t *__restrict__ rec,
+                                                                 uint32_t *__restrict__ out, int ntap, int rsx,
+                                                                 int rsy, int nrx, int nreg, int ng, int nbin) {
+    extern __shared__ int sh[];
+    const int rp = rsx * rsy;
+    int *key = sh;                      // [rp] n_f - min n_f, or nbin - 1 for "no tap on the detector"
+    int *perm = sh + rp;                // [rp] pixel at each walk position; later n_f at each position
+    int *bin = sh + 2 * rp;             // [nbin + 1] counts, then running starts
+    __shared__ int s_min, s_nvalid;
+    const int64_t vr = blockIdx.x;
+    const int region = (int)(vr % nreg);
+    const int v = (int)(vr / nreg);
+    const int i0 = (region / nrx) * rsy, j0 = (region % nrx) * rsx;
     const int np = g.ny * g.nx;
-    const int q = (int)threadIdx.x;
-    const int i = (tile / tiles_x) * FTY + q / FTX;
-    const int j = (tile % tiles_x) * FTX + q % FTX;
-    const bool inside = i < g.ny && j < g.nx;
-    const int32_t *r = rec + ((int64_t)v * np + (inside ? i * g.nx + j : 0)) * (1 + ntap);
-    const int nf = inside ? r[0] : INT32_MAX;        // INT32_MAX also marks "no tap on the detector"
-    s_nf[q] = nf;
-    __syncthreads();
-    int rank = 0, nvalid = 0;
-    for (int o = 0; o < TP; ++o) {
-        const int no = s_nf[o];
-        rank += (no < nf || (no == nf && o < q)) ? 1 : 0;
-        nvalid += no != INT32_MAX ? 1 : 0;
+    const int nf_ = 2 + ntap;
+    const int t = (int)threadIdx.x;
+    auto nf_of = [&](int p) {
+        const int i = i0 + p / rsx, j = j0 + p % rsx;
+        if (i >= g.ny || j >= g.nx) return (int)INT32_MAX;
+        return rec[((int64_t)v * np + i * g.nx + j) * (1 + ntap)];
+    };
+    if (t == 0) {
+        s_min = INT32_MAX;
+        s_nvalid = 0;
     }
-    s_sorted_nf[rank] = nf;
+    for (int e = t; e <= nbin; e += 256) bin[e] = 0;
     __syncthreads();
-    uint32_t *o = out + vt * TP * (2 + ntap) + rank;   // field f of this step: o[f * TP]
-    o[0] = (uint32_t)q * 256u | (nvalid == 0 ? 0x80000000u : 0u);
-    o[TP] = 0u;
-    for (int t = 0; t < ntap; ++t) o[(2 + t) * TP] = 0u;
-    if (nf == INT32_MAX) return;
-    const int cm = ((nf % ntap) + ntap) % ntap;
-    const int turn = (nf - cm) / ntap + 1;           // >= 0: n_f >= 1 - ntap
-    // channels nf .. nf + fin - 1 are finished after this step
-    const int fin = rank + 1 < nvalid ? min(s_sorted_nf[rank + 1] - nf, ntap) : ntap;
-    uint32_t mask = 0, up = 0;
-    for (int d = 0; d < fin; ++d) {
-        const int rr = (cm + d) % ntap;
-        mask |= 1u << rr;
-        if (rr < cm) up |= 1u << rr;
+    for (int p = t; p < rp; p += 256) {
+        const int nf = nf_of(p);
+        if (nf != INT32_MAX) {
+            atomicMin(&s_min, nf);
+            atomicAdd(&s_nvalid, 1);
+        }
     }
-    if (mask) o[TP] = mask | (up << 7) | ((uint32_t)turn << 14);
-    for (int rr = 0; rr < ntap; ++rr) o[(2 + rr) * TP] = (uint32_t)r[1 + (rr - cm + ntap) % ntap];
+    __syncthreads();
+    const int nfmin = s_min, nvalid = s_nvalid;
+    for (int p = t; p < rp; p += 256) {
+        const int nf = nf_of(p);
+        const int k = nf == INT32_MAX ? nbin - 1 : min(nf - nfmin, nbin - 2);   // the plan bounds n_f - min < nbin - 1
+        key[p] = k;
+        atomicAdd(&bin[k], 1);
+    }
+    __syncthreads();
+    if (t == 0) {                       // exclusive scan: bins are few
+        int run = 0;
+        for (int e = 0; e < nbin; ++e) {
+            const int c = bin[e];
+            bin[e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    if (t < 64) {                       // stable scatter, 64 pixels at a time in pixel order
+        for (int c0 = 0; c0 < rp; c0 += 64) {
+            const int p = c0 + t;
+            const int k = p < rp ? key[p] : -1;
+            int below = 0;
+            for (int l = 0; l < t; ++l) below += (c0 + l < rp && key[c0 + l] == k) ? 1 : 0;
+            if (p < rp) perm[bin[k] + below] = p;
+            // one wave, in lockstep: every lane reads its start before any lane adds
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            if (p < rp) atomicAdd(&bin[k], 1);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        }
+    }
+    __syncthreads();
+    // key[] now holds the n_f of each walk position
+    for (int q = t; q < rp; q += 256) key[q] = q < nvalid ? nf_of(perm[q]) : INT32_MAX;
+    __syncthreads();
+    uint32_t *o = out + vr * (int64_t)ng * nf_ * 16;
+    for (int q = t; q < ng * 16; q += 256) {
+        uint32_t *oq = o + (q >> 4) * nf_ * 16 + (q & 15);     // field f of this step: oq[f * 16]
+        const int p = q < rp ? perm[q] : 0;
+        oq[0] = (uint32_t)p * 64u;
+        oq[16] = 0u;
+        for (int r = 0; r < ntap; ++r) oq[(2 + r) * 16] = 0u;
+        if (q >= nvalid) continue;
+        const int nf = key[q];
+        const int cm = ((nf % ntap) + ntap) % ntap;
+        const int turn = (nf - cm) / ntap + 1;           // >= 0: n_f >= 1 - ntap
+        // channels nf .. nf + fin - 1 are finished after this step
+        const int fin = q + 1 < nvalid ? min(key[q + 1] - nf, ntap) : ntap;
+        uint32_t mask = 0, up = 0;
+        for (int d = 0; d < fin; ++d) {
+            const int rr = (cm + d) % ntap;
+            mask |= 1u << rr;
+            if (rr < cm) up |= 1u << rr;
+        }
+        if (mask) oq[16] = mask | (up << 7) | ((uint32_t)turn << 14);
+        const int i = i0 + p / rsx, j = j0 + p % rsx;
+        const int32_t *rp_ = rec + ((int64_t)v * np + i * g.nx + j) * (1 + ntap);
+        for (int rr = 0; rr < ntap; ++rr) oq[(2 + rr) * 16] = (uint32_t)rp_[1 + (rr - cm + ntap) % ntap];
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float4 *__restrict__ b4, float *__restrict__ tail,
@@ -194,10 +243,16 @@ hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int n
     return hipGetLastError();
 }
 
-hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, uint32_t *out, int ntap, hipStream_t st) {
-    const int64_t blocks = (int64_t)g.nv * ((g.nx + FTX - 1) / FTX) * ((g.ny + FTY - 1) / FTY);
+hipError_t launch_par_region_records(const Geo &g, const int32_t *rec, uint32_t *out, int ntap, int rsx, int rsy,
+                                    int nbin, hipStream_t st) {
+    const int nrx = (g.nx + rsx - 1) / rsx, nry = (g.ny + rsy - 1) / rsy;
+    const int nreg = nrx * nry;
+    const int ng = fwd_groups(rsx, rsy);
+    const int64_t blocks = (int64_t)g.nv * nreg;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(par_walk_records_kernel, dim3((unsigned)blocks), dim3(64), 0, st, g, rec, out, ntap);
+    const size_t lds = (size_t)(2 * rsx * rsy + nbin + 1) * sizeof(int);
+    hipLaunchKernelGGL(par_region_records_kernel, dim3((unsigned)blocks), dim3(256), lds, st, g, rec, out, ntap, rsx,
+                       rsy, nrx, nreg, ng, nbin);
     return hipGetLastError();
 }
 

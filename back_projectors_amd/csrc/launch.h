@@ -16,10 +16,12 @@ struct Plan {
     const ViewK *views = nullptr;   // device [V]
     const int32_t *idx = nullptr;   // device [V][Ny*Nx]
     const int32_t *rec = nullptr;   // parallel: device tap records [V][Ny*Nx][1 + ntap]
-    const uint32_t *wrec = nullptr; // parallel: forward walk steps [V][tiles][FTX*FTY][1 + ntap]
-    float *facc = nullptr;          // parallel: forward accumulation buffer [V][fwd_cb][fwd_s64]
+    const uint32_t *wrec = nullptr; // parallel: forward walk records [V + 1][regions][groups][2 + ntap][16]
+    float *facc = nullptr;          // parallel: forward accumulation buffer [V][fwd_cb][fwd_s16]
     int fwd_cb = 0;                 // parallel: channels of facc (C plus ntap - 1 guards each side)
-    int fwd_s64 = 0;                // parallel: slices of facc (S rounded up to 64)
+    int fwd_s16 = 0;                // parallel: slices of facc (S rounded up to 16)
+    int rsx = 0, rsy = 0;           // parallel: forward region (pixels along x, y)
+    int fwd_nbin = 0;               // parallel: bins of the walk-order sort (n_f span of a region + 2)
     const int4 *bwin = nullptr;     // back windows [V][tiles][chunks] (n0, nw, m0, nrw)
     const int4 *fwin = nullptr;     // cone forward windows [V][tiles][chunks]
     int ntap = 0;                   // parallel: taps per record
@@ -41,20 +43,25 @@ struct Plan {
 };
 
 constexpr int BT = 16;   // back tile edge (pixels), 256 threads
-constexpr int FTX = 8;   // parallel forward tile (pixels along x)
-constexpr int FTY = 8;   // parallel forward tile (pixels along y); FTX * FTY = 64, one walk record per lane
-constexpr int FW = 8;    // parallel forward waves per workgroup (one view each at a time)
+constexpr int FRW = 16;  // parallel forward waves per workgroup (four views each at a time)
+constexpr int FRS = 48;  // parallel forward region edge (pixels): 48 * 48 voxels of 16 slices = 144 KiB of LDS
+
+// Groups of 16 walk steps per (view, region): every pixel of the region, then
+// zero steps up to a multiple of 5 groups (the walk rotates five record buffers).
+inline int fwd_groups(int rsx, int rsy) { return ((rsx * rsy + 79) / 80) * 5; }
 constexpr int CTX = 8;   // cone forward tile (pixels along x)
 constexpr int CTY = 8;   // cone forward tile (pixels along y)
 constexpr int CFW = 4;   // cone forward waves per workgroup (one view each at a time)
 
 hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
 hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st);
-hipError_t launch_par_walk_records(const Geo &g, const int32_t *rec, uint32_t *out, int ntap, hipStream_t st);
+hipError_t launch_par_region_records(const Geo &g, const int32_t *rec, uint32_t *out, int ntap, int rsx, int rsy,
+                                    int nbin, hipStream_t st);
 hipError_t launch_fill_zero(float *buf, int64_t n, hipStream_t st);
 
 hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, hipStream_t st);
 hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
+hipError_t par_forward_allow_lds(int ntap, size_t bytes);
 hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, hipStream_t st);
 hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
 hipError_t cone_forward_allow_lds(int radius, int stride, size_t bytes);

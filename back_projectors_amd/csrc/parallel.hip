@@ -160,126 +160,152 @@ __device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
 
 // acc += w' * x, where w' is lane N of the row of w: one v_fmac with the
 // broadcast folded into its DPP operand.  The s_nop gives the two wait states
-// a DPP read needs after a VALU write of its source.
+// a DPP read needs after a VALU write of its source; the second product of a
+// pair is covered by the first.
 template <int N>
 __device__ __forceinline__ void fmac_row_bcast(float &acc, uint32_t w, float x) {
     asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
         : "+v"(acc)
         : "v"(w), "v"(x), "n"(N));
 }
+template <int N>
+__device__ __forceinline__ void fmac2_row_bcast(float &a0, float &a1, uint32_t w0, uint32_t w1, float x) {
+    asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+        : "+v"(a0), "+v"(a1)
+        : "v"(w0), "v"(w1), "v"(x), "n"(N));
+}
+
+// Lane N of each 16-lane row, broadcast to its row, without a prior value.
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast_nb(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + N, 0xf, 0xf, true);
+}
 
 template <int K>
-__global__ __launch_bounds__(FW * 64) void par_forward_kernel(const float *__restrict__ recon,
-                                                               float *__restrict__ facc,
-                                                               const uint32_t *__restrict__ wrec, Geo g, int cb,
-                                                               int s64, int vsplit) {
-    constexpr int TP = FTX * FTY;         // pixels per tile = walk steps per view
-    static_assert(TP == 64, "a view's 64 steps sit in 4 registers of 16-lane rows");
+__global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__restrict__ recon,
+                                                                float *__restrict__ facc,
+                                                                const uint32_t *__restrict__ wrec, Geo g, int cb,
+                                                                int s16, int rsx, int rsy, int nrx, int nreg, int ng,
+                                                                int vsplit) {
     constexpr int NF = 2 + K;             // record fields per step
     constexpr int D = 4;                  // voxel reads in flight ahead of the step using them
-    __shared__ float xt[TP * 64];         // the tile's voxels, [pixel][slice]
+    extern __shared__ float xr[];         // the region's voxels, [pixel][16 slices]
     const int lane = (int)threadIdx.x & 63;
+    const int row = lane >> 4, sl = lane & 15;
     // wave index, made visibly uniform so that per-view control stays scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int region = (int)blockIdx.x;
+    const int i0 = (region / nrx) * rsy, j0 = (region % nrx) * rsx;
+    const int k0 = (int)blockIdx.y * 16;
+    const int rp = rsx * rsy;
 
-    const int tiles_x = (g.nx + FTX - 1) / FTX;
-    const int ntiles = tiles_x * ((g.ny + FTY - 1) / FTY);
-    const int tile = (int)blockIdx.x;
-    const int tj0 = (tile % tiles_x) * FTX;
-    const int ti0 = (tile / tiles_x) * FTY;
-    const int k0 = (int)blockIdx.y * 64;
-    const int nk = min(64, g.ns - k0);
-
-    for (int e = (int)threadIdx.x; e < TP * 64; e += FW * 64) {
-        const int q = e >> 6, k = e & 63;
-        const int i = ti0 + q / FTX, j = tj0 + q % FTX;
+    for (int e = (int)threadIdx.x; e < rp * 16; e += FRW * 64) {
+        const int p = e >> 4, k = e & 15;
+        const int i = i0 + p / rsx, j = j0 + p % rsx;
         float val = 0.f;
-        if (i < g.ny && j < g.nx && k < nk) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + k];
-        xt[e] = val;
+        if (i < g.ny && j < g.nx && k0 + k < g.ns) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + k];
+        xr[e] = val;
     }
     __syncthreads();
 
     const int vper = (g.nv + vsplit - 1) / vsplit;
     const int vbeg = (int)blockIdx.z * vper;
     const int vend = min(g.nv, vbeg + vper);
-    const int cnt = vend - vbeg;
-    // staggered start, so that tiles along one ray reach a view at different times
-    const int start = cnt > 0 ? (int)((blockIdx.x * 37u + blockIdx.y * 11u) % (unsigned)cnt) : 0;
-    auto view_of = [&](int i) {
-        const int v = vbeg + start + i;
-        return v >= vend ? v - cnt : v;
-    };
-    const char *xb = reinterpret_cast<const char *>(xt);
-    const uint32_t l4 = (uint32_t)lane * 4u;
-    const uint32_t s4 = (uint32_t)s64 * 4u;         // bytes between channels of the accumulation buffer
+    const char *xb = reinterpret_cast<const char *>(xr);
+    char *fv = reinterpret_cast<char *>(facc + (int64_t)vbeg * cb * s16);
+    const uint32_t l4 = (uint32_t)sl * 4u;
+    const uint32_t s4 = (uint32_t)s16 * 4u;         // bytes between channels of the accumulation buffer
     const uint32_t ks = (uint32_t)K * s4;           // bytes per ring turn
-    // a view's records: field f, steps 16 j .. 16 j + 15 in every row of R[f][j]
-    auto load_records = [&](int v, uint32_t (&R)[NF][4]) {
-        const uint32_t *b = wrec + ((int64_t)v * ntiles + tile) * (NF * TP) + (lane & 15);
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) R[f][j] = b[f * TP + 16 * j];
-    };
+    const int64_t gstride = (int64_t)NF * 16;       // dwords per group of 16 steps
+    constexpr int PD = 4;                           // groups of records in flight ahead of their use
 
-    // one view: its records in R; the records of the view two turns later
-    // are fetched into P meanwhile (always issued, for a static wait count)
-    auto walk_view = [&](int i, uint32_t (&R)[NF][4], uint32_t (&P)[NF][4]) {
-        const int v = view_of(i);
-        load_records(view_of(min(i + 2 * FW, cnt - 1)), P);
-        if (__builtin_amdgcn_readfirstlane(R[0][0]) >> 31) return;   // the tile misses the detector
-        // steps followed by a flush, one bit per step
-        uint64_t fl = 0;
+    // each row of a wave walks its own view; views past the range walk the
+    // all-zero records of view nv (no weights, no flushes)
+    for (int q0 = vbeg + wave * 4; q0 < vend; q0 += FRW * 4) {
+        const int vrow = q0 + row < vend ? q0 + row : g.nv;
+        const uint32_t *rb = wrec + ((int64_t)vrow * nreg + region) * ng * gstride + sl;
+        // byte offset from fv (this workgroup's first view) of ring turn 0,
+        // accumulator r, for this lane: turn T, accumulator r is at
+        // vb[r] + T * ks (modulo 2^32; the sum itself stays below 2^31)
+        uint32_t vb[K];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fl |= (__builtin_amdgcn_ballot_w64(R[1][j] != 0u) & 0xffffull) << (16 * j);
-        // byte base such that ring turn T, accumulator r is at T * ks + r * s4
-        char *fb = reinterpret_cast<char *>(facc + ((int64_t)v * cb + (K - 1)) * s64 + k0) - ks;
+        for (int r = 0; r < K; ++r)
+            vb[r] = (uint32_t)(((min(vrow, g.nv - 1) - vbeg) * cb + (K - 1)) * s16 + k0) * 4u + l4 + r * s4 - ks;
         float acc[K];
 #pragma unroll
         for (int r = 0; r < K; ++r) acc[r] = 0.f;
-        float xq[TP];
-        auto read_x = [&](auto SC) {
-            constexpr int S = decltype(SC)::value;
-            xq[S] = *reinterpret_cast<const float *>(xb + (row_bcast<S & 15>(R[0][S >> 4]) + l4));
+
+        auto load_group = [&](int gi, uint32_t (&R)[NF]) {
+            const uint32_t *b = rb + (int64_t)gi * gstride;
+#pragma unroll
+            for (int f = 0; f < NF; ++f) R[f] = b[f * 16];
         };
-        static_for(read_x, std::make_integer_sequence<int, D>{});
-        static_for(
-            [&](auto SC) {
+        // one group of 16 steps from R; the group PD turns later is fetched
+        // into P meanwhile (always issued, for a static wait count)
+        auto walk_group = [&](int gi, uint32_t (&R)[NF], uint32_t (&P)[NF]) {
+            load_group(min(gi + PD, ng - 1), P);
+            uint64_t m = __builtin_amdgcn_ballot_w64(R[1] != 0u);
+            m |= m >> 32;
+            m |= m >> 16;
+            const uint32_t fl = (uint32_t)m & 0xffffu;      // steps after which some row flushes
+            float xq[16];
+            auto read_x = [&](auto SC) {
                 constexpr int S = decltype(SC)::value;
-                if constexpr (S + D < TP) read_x(std::integral_constant<int, S + D>{});
+                xq[S] = *reinterpret_cast<const float *>(xb + (row_bcast<S>(R[0]) + l4));
+            };
+            static_for(read_x, std::make_integer_sequence<int, D>{});
+            static_for(
+                [&](auto SC) {
+                    constexpr int S = decltype(SC)::value;
+                    if constexpr (S + D < 16) read_x(std::integral_constant<int, S + D>{});
 #pragma unroll
-                for (int r = 0; r < K; ++r) fmac_row_bcast<S & 15>(acc[r], R[2 + r][S >> 4], xq[S]);
-                if ((fl >> S) & 1u) {
-                    const uint32_t f = (uint32_t)__builtin_amdgcn_readlane((int)R[1][S >> 4], S & 15);
-                    const uint32_t tb = (f >> 14) * ks;
+                    for (int r = 0; r < K; r += 2) {
+                        if (r + 1 < K)
+                            fmac2_row_bcast<S>(acc[r], acc[r + 1 < K ? r + 1 : r], R[2 + r], R[r + 1 < K ? 3 + r : 2 + r],
+                                               xq[S]);
+                        else
+                            fmac_row_bcast<S>(acc[r], R[2 + r], xq[S]);
+                    }
+                    if (__builtin_expect((fl >> S) & 1u, 0)) {       // out of line: most steps flush nothing
+                        const uint32_t f = row_bcast_nb<S>(R[1]);     // this row's flush word
+                        const uint32_t t = f >> 14;
 #pragma unroll
-                    for (int r = 0; r < K; ++r) {
-                        if (f & (1u << r)) {
-                            const uint32_t off = tb + (uint32_t)r * s4 + ((f >> (7 + r)) & 1u ? ks : 0u);
-                            unsafeAtomicAdd(reinterpret_cast<float *>(fb + (off + l4)), acc[r]);
-                            acc[r] = 0.f;
+                        for (int r = 0; r < K; ++r) {
+                            if (f & (1u << r)) {
+                                const uint32_t turn = t + ((f >> (7 + r)) & 1u);
+                                unsafeAtomicAdd(reinterpret_cast<float *>(fv + (__umul24(turn, ks) + vb[r])), acc[r]);
+                                acc[r] = 0.f;
+                            }
                         }
                     }
-                }
-            },
-            std::make_integer_sequence<int, TP>{});
-    };
+                },
+                std::make_integer_sequence<int, 16>{});
+        };
 
-    // three record buffers in rotation (no copies, so no early waits)
-    if (wave >= cnt) return;
-    uint32_t RA[NF][4], RB[NF][4], RC[NF][4];
-    load_records(view_of(wave), RA);
-    load_records(view_of(min(wave + FW, cnt - 1)), RB);
-    for (int it = wave; it < cnt; it += 3 * FW) {
-        walk_view(it, RA, RC);
-        if (it + FW >= cnt) break;
-        walk_view(it + FW, RB, RA);
-        if (it + 2 * FW >= cnt) break;
-        walk_view(it + 2 * FW, RC, RB);
+        // PD + 1 record buffers in rotation (no copies, so no early waits)
+        uint32_t RB0[NF], RB1[NF], RB2[NF], RB3[NF], RB4[NF];
+        // issued in order (no reordering across the barriers), so that the
+        // wait for a buffer never covers the loads of later ones
+        load_group(0, RB0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_group(1, RB1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_group(2, RB2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_group(3, RB3);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int gi = 0; gi < ng; gi += 5) {          // ng is a multiple of 5 (zero groups pad it)
+            walk_group(gi, RB0, RB4);
+            walk_group(gi + 1, RB1, RB0);
+            walk_group(gi + 2, RB2, RB1);
+            walk_group(gi + 3, RB3, RB2);
+            walk_group(gi + 4, RB4, RB3);
+        }
     }
 }
 
-// facc [V][cb][s64] (slices fastest, K - 1 guard channels each side) ->
+// facc [V][cb][s16] (slices fastest, K - 1 guard channels each side) ->
 // sino [V][R][C] (channels fastest), through a 64 x 64 LDS tile.
 __global__ __launch_bounds__(256) void par_unpack_kernel(const float *__restrict__ facc, float *__restrict__ sino,
                                                          int nr, int nc, int cb, int s64, int guard, int tn) {
@@ -292,7 +318,7 @@ __global__ __launch_bounds__(256) void par_unpack_kernel(const float *__restrict
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
         const int n = b + 4 * u;
-        t[n][a] = n0 + n < nc ? src[(int64_t)n * s64 + a] : 0.f;
+        t[n][a] = (n0 + n < nc && r0 + a < nr) ? src[(int64_t)n * s64 + a] : 0.f;
     }
     __syncthreads();
     float *dst = sino + ((int64_t)v * nr + r0) * nc + n0;
@@ -322,10 +348,11 @@ static hipError_t par_back_t(const Plan &p, const float *sino, float *recon, hip
 template <int K>
 static hipError_t par_fwd_t(const Plan &p, const float *recon, hipStream_t st) {
     const Geo &g = p.g;
-    const int tiles = ((g.nx + FTX - 1) / FTX) * ((g.ny + FTY - 1) / FTY);
-    const int chunks = (g.ns + 63) / 64;
-    hipLaunchKernelGGL((par_forward_kernel<K>), dim3(tiles, chunks, p.fwd_vsplit), dim3(FW * 64), 0, st, recon,
-                       p.facc, p.wrec, g, p.fwd_cb, p.fwd_s64, p.fwd_vsplit);
+    const int nrx = (g.nx + p.rsx - 1) / p.rsx, nry = (g.ny + p.rsy - 1) / p.rsy;
+    const int ng = fwd_groups(p.rsx, p.rsy);
+    hipLaunchKernelGGL((par_forward_kernel<K>), dim3(nrx * nry, (g.ns + 15) / 16, p.fwd_vsplit), dim3(FRW * 64),
+                       p.fwd_lds, st, recon, p.facc, p.wrec, g, p.fwd_cb, p.fwd_s16, p.rsx, p.rsy, nrx, nrx * nry, ng,
+                       p.fwd_vsplit);
     return hipGetLastError();
 }
 
@@ -356,7 +383,7 @@ hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, hipSt
 // unpack writes in full, so the sinogram needs no fill of its own).
 hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st) {
     const Geo &g = p.g;
-    hipError_t e = launch_fill_zero(p.facc, (int64_t)g.nv * p.fwd_cb * p.fwd_s64, st);
+    hipError_t e = launch_fill_zero(p.facc, (int64_t)g.nv * p.fwd_cb * p.fwd_s16, st);
     if (e != hipSuccess) return e;
     switch (p.ntap) {
     case 2: e = par_fwd_t<2>(p, recon, st); break;
@@ -370,8 +397,23 @@ hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hi
     if (e != hipSuccess) return e;
     const int tn = (g.nc + 63) / 64;
     hipLaunchKernelGGL(par_unpack_kernel, dim3((unsigned)(g.nv * tn), (g.nr + 63) / 64), dim3(256), 0, st, p.facc,
-                       sino, g.nr, g.nc, p.fwd_cb, p.fwd_s64, p.ntap - 1, tn);
+                       sino, g.nr, g.nc, p.fwd_cb, p.fwd_s16, p.ntap - 1, tn);
     return hipGetLastError();
+}
+
+// The region walk holds its voxels in more LDS than the default limit.
+hipError_t par_forward_allow_lds(int ntap, size_t bytes) {
+    const void *f = nullptr;
+    switch (ntap) {
+    case 2: f = (const void *)par_forward_kernel<2>; break;
+    case 3: f = (const void *)par_forward_kernel<3>; break;
+    case 4: f = (const void *)par_forward_kernel<4>; break;
+    case 5: f = (const void *)par_forward_kernel<5>; break;
+    case 6: f = (const void *)par_forward_kernel<6>; break;
+    case 7: f = (const void *)par_forward_kernel<7>; break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 }  // namespace bpamd

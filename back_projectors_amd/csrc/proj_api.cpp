@@ -210,13 +210,19 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         if (plan.back_nwcap > 64)
             return fail(PROJ_ERR_UNSUPPORTED, "back projection window wider than 64 channels (detector far finer than the voxels)");
         plan.back_ncg = plan.back_nwcap <= 32 ? 1 : 2;
-        plan.fwd_sl = 64;
-        plan.fwd_lds = (size_t)FTX * FTY * 64 * sizeof(float);
+        plan.fwd_sl = 16;
+        plan.rsx = (int)std::min<int64_t>(FRS, Nx);
+        plan.rsy = (int)std::min<int64_t>(FRS, Ny);
+        plan.fwd_lds = (size_t)plan.rsx * plan.rsy * 16 * sizeof(float);
         plan.fwd_cb = (int)C + 2 * (plan.ntap - 1);
-        plan.fwd_s64 = (int)(((S + 63) / 64) * 64);
-        // the walk addresses one view of the buffer with 32-bit byte offsets
-        if ((int64_t)(plan.fwd_cb + 2 * plan.ntap) * plan.fwd_s64 * 4 >= ((int64_t)1 << 31))
+        plan.fwd_s16 = (int)(((S + 15) / 16) * 16);
+        // the walk addresses the views of one workgroup with 32-bit byte offsets
+        if ((int64_t)(plan.fwd_cb + 2 * plan.ntap) * plan.fwd_s16 * 4 >= ((int64_t)1 << 30))
             return fail(PROJ_ERR_UNSUPPORTED, "forward accumulation buffer too large per view");
+        // walk-order sort bins: the first tap channels of a region span at most its window
+        plan.fwd_nbin = max_window(g, views, plan.rsx, plan.rsy, 64).nw + 2;
+        if (plan.fwd_nbin > 8192)
+            return fail(PROJ_ERR_UNSUPPORTED, "a forward region spans more than 8190 channels");
     } else {
         auto back_bytes = [&](int sl, int &nwcap, int &nrcap) {
             const WinMax w = max_window(g, views, BT, BT, sl);
@@ -260,12 +266,26 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
     const int64_t chunks_b = (S + plan.back_sl - 1) / plan.back_sl;
     const int64_t chunks_f = (S + plan.fwd_sl - 1) / plan.fwd_sl;
     if (chunks_b > 65535 || chunks_f > 65535) return fail(PROJ_ERR_UNSUPPORTED, "too many slices");
-    const int64_t ftiles = par ? ((Nx + FTX - 1) / FTX) * ((Ny + FTY - 1) / FTY)
-                               : ((Nx + CTX - 1) / CTX) * ((Ny + CTY - 1) / CTY);
-    // enough workgroups to fill 256 CUs a few times over; each split re-reads its tile
-    int64_t vs = (2048 + ftiles * chunks_f - 1) / (ftiles * chunks_f);
-    vs = std::max<int64_t>(1, std::min<int64_t>(vs, std::min<int64_t>(V, 64)));
-    plan.fwd_vsplit = (int)vs;
+    if (par) {
+        // one region workgroup per CU: a few per CU over the whole grid, each
+        // split keeping at least one view per row of every wave
+        const int64_t nreg = ((Nx + plan.rsx - 1) / plan.rsx) * ((Ny + plan.rsy - 1) / plan.rsy);
+        int64_t vs = (1024 + nreg * chunks_f - 1) / (nreg * chunks_f);
+        vs = std::max<int64_t>(1, std::min<int64_t>(vs, std::max<int64_t>(1, V / (FRW * 4))));
+        vs = std::min<int64_t>(vs, 64);
+        // and few enough views per workgroup for 32-bit offsets into the buffer
+        const int64_t view_bytes = (int64_t)(plan.fwd_cb + 2 * plan.ntap) * plan.fwd_s16 * 4;
+        const int64_t vmax = ((int64_t)1 << 31) / view_bytes;       // >= 2 by the check above
+        vs = std::max<int64_t>(vs, (V + vmax - 1) / vmax);
+        if (vs > 65535) return fail(PROJ_ERR_UNSUPPORTED, "too many views for the forward accumulation buffer");
+        plan.fwd_vsplit = (int)vs;
+    } else {
+        const int64_t ftiles = ((Nx + CTX - 1) / CTX) * ((Ny + CTY - 1) / CTY);
+        // enough workgroups to fill 256 CUs a few times over; each split re-reads its tile
+        int64_t vs = (2048 + ftiles * chunks_f - 1) / (ftiles * chunks_f);
+        vs = std::max<int64_t>(1, std::min<int64_t>(vs, std::min<int64_t>(V, 64)));
+        plan.fwd_vsplit = (int)vs;
+    }
     return ok();
 }
 
@@ -278,8 +298,8 @@ int describe(const Plan &p, int64_t table_bytes, char *buf, int len) {
         "slices/lane, window %d ch x %d rows, %zu B LDS | forward: %dx%d px tile, %s, %d slices, window %d ch x %d "
         "rows, %zu B LDS, %d view ranges | tables and buffers %lld B",
         par ? "parallel" : "cone_flat", g.nv, g.nr, g.nc, g.ny, g.nx, g.ns, g.radius, par ? p.ntap : 2 * g.radius + 1,
-        BT, BT, p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, par ? FTX : CTX, par ? FTY : CTY,
-        par ? "lanes=slices, wave per view, channel-ordered walk, ring accumulators"
+        BT, BT, p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, par ? p.rsx : CTX, par ? p.rsy : CTY,
+        par ? "lanes=16 slices x 4 views, channel-ordered region walk, ring accumulators"
             : "lanes=strided slices, wave per view, LDS window",
         p.fwd_sl,
         p.fwd_nwcap, par ? p.fwd_sl : p.fwd_nrcap, p.fwd_lds, p.fwd_vsplit, (long long)table_bytes);
@@ -392,15 +412,31 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(tap records)");
                 e = launch_par_taps(geo, h->d_views, h->d_rec, plan.ntap, nullptr);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "tap record pass");
-                constexpr int TP = FTX * FTY;
-                const int64_t ntiles = (int64_t)((geo.nx + FTX - 1) / FTX) * ((geo.ny + FTY - 1) / FTY);
-                const size_t wrec_bytes = (size_t)geo.nv * ntiles * TP * (2 + plan.ntap) * sizeof(uint32_t);
+                const int64_t nreg = (int64_t)((geo.nx + plan.rsx - 1) / plan.rsx) * ((geo.ny + plan.rsy - 1) / plan.rsy);
+                const int64_t per_view = nreg * fwd_groups(plan.rsx, plan.rsy) * (2 + plan.ntap) * 16;
+                // one more view of all-zero records for the rows of a wave past the last view
+                const size_t wrec_bytes = (size_t)(geo.nv + 1) * per_view * sizeof(uint32_t);
                 e = hipMalloc((void **)&h->d_wrec, wrec_bytes);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(walk records)");
-                e = launch_par_walk_records(geo, h->d_rec, h->d_wrec, plan.ntap, nullptr);
+                e = launch_fill_zero(reinterpret_cast<float *>(h->d_wrec) + (int64_t)geo.nv * per_view, per_view,
+                                     nullptr);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "zero fill");
+                e = launch_par_region_records(geo, h->d_rec, h->d_wrec, plan.ntap, plan.rsx, plan.rsy, plan.fwd_nbin,
+                                              nullptr);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "walk record pass");
                 rec_bytes += wrec_bytes;
-                const size_t facc_bytes = (size_t)geo.nv * plan.fwd_cb * plan.fwd_s64 * sizeof(float);
+                if (plan.fwd_lds > kMaxLds) {
+                    int lim = 0;
+                    e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, hip_device);
+                    if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipDeviceGetAttribute");
+                    if ((size_t)lim < plan.fwd_lds) {
+                        proj_destroy(h);
+                        return fail(PROJ_ERR_UNSUPPORTED, "device LDS per workgroup below the forward plan's need");
+                    }
+                    e = par_forward_allow_lds(plan.ntap, plan.fwd_lds);
+                    if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipFuncSetAttribute(LDS)");
+                }
+                const size_t facc_bytes = (size_t)geo.nv * plan.fwd_cb * plan.fwd_s16 * sizeof(float);
                 e = hipMalloc((void **)&h->d_facc, facc_bytes);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(forward accumulation buffer)");
                 rec_bytes += facc_bytes;
