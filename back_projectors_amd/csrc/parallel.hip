@@ -195,9 +195,19 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
     const int row = lane >> 4, sl = lane & 15;
     // wave index, made visibly uniform so that per-view control stays scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int region = (int)blockIdx.x;
+    // Workgroup L of a view range is assumed to run on XCD L mod 8 (the
+    // dispatch order): the slice chunks of one region get consecutive slots on
+    // one XCD, so that they read the region's records through one L2.  Any
+    // other placement is still correct, only slower.
+    const int nch = (g.ns + 15) / 16;
+    const int per_range = 8 * ((nreg + 7) / 8) * nch;
+    const int L = (int)(blockIdx.x % (unsigned)per_range);
+    const int vrange = (int)(blockIdx.x / (unsigned)per_range);
+    const int slot = L >> 3;
+    const int region = (slot / nch) * 8 + (L & 7);
+    if (region >= nreg) return;
     const int i0 = (region / nrx) * rsy, j0 = (region % nrx) * rsx;
-    const int k0 = (int)blockIdx.y * 16;
+    const int k0 = (slot % nch) * 16;
     const int rp = rsx * rsy;
 
     for (int e = (int)threadIdx.x; e < rp * 16; e += FRW * 64) {
@@ -210,7 +220,7 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
     __syncthreads();
 
     const int vper = (g.nv + vsplit - 1) / vsplit;
-    const int vbeg = (int)blockIdx.z * vper;
+    const int vbeg = vrange * vper;
     const int vend = min(g.nv, vbeg + vper);
     const char *xb = reinterpret_cast<const char *>(xr);
     char *fv = reinterpret_cast<char *>(facc + (int64_t)vbeg * cb * s16);
@@ -350,7 +360,8 @@ static hipError_t par_fwd_t(const Plan &p, const float *recon, hipStream_t st) {
     const Geo &g = p.g;
     const int nrx = (g.nx + p.rsx - 1) / p.rsx, nry = (g.ny + p.rsy - 1) / p.rsy;
     const int ng = fwd_groups(p.rsx, p.rsy);
-    hipLaunchKernelGGL((par_forward_kernel<K>), dim3(nrx * nry, (g.ns + 15) / 16, p.fwd_vsplit), dim3(FRW * 64),
+    const int64_t per_range = 8 * (int64_t)((nrx * nry + 7) / 8) * ((g.ns + 15) / 16);
+    hipLaunchKernelGGL((par_forward_kernel<K>), dim3((unsigned)(per_range * p.fwd_vsplit)), dim3(FRW * 64),
                        p.fwd_lds, st, recon, p.facc, p.wrec, g, p.fwd_cb, p.fwd_s16, p.rsx, p.rsy, nrx, nrx * nry, ng,
                        p.fwd_vsplit);
     return hipGetLastError();

@@ -277,7 +277,8 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         const int64_t view_bytes = (int64_t)(plan.fwd_cb + 2 * plan.ntap) * plan.fwd_s16 * 4;
         const int64_t vmax = ((int64_t)1 << 31) / view_bytes;       // >= 2 by the check above
         vs = std::max<int64_t>(vs, (V + vmax - 1) / vmax);
-        if (vs > 65535) return fail(PROJ_ERR_UNSUPPORTED, "too many views for the forward accumulation buffer");
+        if (vs * 8 * ((nreg + 7) / 8) * chunks_f >= ((int64_t)1 << 31))
+            return fail(PROJ_ERR_UNSUPPORTED, "too many forward workgroups");
         plan.fwd_vsplit = (int)vs;
     } else {
         const int64_t ftiles = ((Nx + CTX - 1) / CTX) * ((Ny + CTY - 1) / CTY);
