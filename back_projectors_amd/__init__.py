@@ -8,7 +8,8 @@ call raises.
 
 Names follow the C ABI: ``proj_create`` -> :class:`Projector`,
 ``proj_forward`` -> :meth:`Projector.forward`, ``proj_back`` ->
-:meth:`Projector.back`, ``proj_channel_index`` -> :meth:`Projector.channel_index`.
+:meth:`Projector.back`, ``proj_back_squared`` -> :meth:`Projector.back_squared`,
+``proj_channel_index`` -> :meth:`Projector.channel_index`.
 """
 from __future__ import annotations
 
@@ -34,8 +35,8 @@ STATUS = {
 }
 
 # Every entry point include/proj.h declares.
-EXPORTS = ("proj_create", "proj_forward", "proj_back", "proj_channel_index", "proj_plan_query",
-           "proj_destroy", "proj_status_string", "proj_last_error", "proj_describe")
+EXPORTS = ("proj_create", "proj_forward", "proj_back", "proj_back_squared", "proj_channel_index",
+           "proj_plan_query", "proj_destroy", "proj_status_string", "proj_last_error", "proj_describe")
 
 
 class ProjError(RuntimeError):
@@ -79,7 +80,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     i64x3 = P(ctypes.c_int64)
     lib.proj_create.argtypes = [P(_Geometry), i64x3, i64x3, ctypes.c_int, P(ctypes.c_void_p)]
     lib.proj_create.restype = ctypes.c_int
-    for name in ("proj_forward", "proj_back"):
+    for name in ("proj_forward", "proj_back", "proj_back_squared"):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         fn.restype = ctypes.c_int
@@ -208,6 +209,19 @@ class Projector:
             self._tensor(out, self.recon_shape, torch.float32, "out")
         _check(self._lib.proj_back(self._h, ctypes.c_void_p(sino.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                                    ctypes.c_void_p(_stream_ptr(torch, self.device, stream))), "proj_back")
+        return out
+
+    def back_squared(self, sino, out=None, stream=None):
+        """``proj_back_squared``: the back projection with every tap weight
+        squared (the Hessian-diagonal weighting), recon (Ny, Nx, S)."""
+        torch = self._torch
+        self._tensor(sino, self.sino_shape, torch.float32, "sino")
+        out = self._empty(self.recon_shape, torch.float32) if out is None else \
+            self._tensor(out, self.recon_shape, torch.float32, "out")
+        _check(self._lib.proj_back_squared(self._h, ctypes.c_void_p(sino.data_ptr()),
+                                           ctypes.c_void_p(out.data_ptr()),
+                                           ctypes.c_void_p(_stream_ptr(torch, self.device, stream))),
+               "proj_back_squared")
         return out
 
     def channel_index(self, out=None, stream=None):

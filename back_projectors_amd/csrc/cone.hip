@@ -48,7 +48,7 @@ __device__ __forceinline__ ConeVP cone_vp(const Geo &g, const ViewK &vk, double 
     return o;
 }
 
-template <int SL, int R>
+template <int SL, int R, int POW>
 __global__ __launch_bounds__(BT *BT) void cone_back_kernel(const float *__restrict__ sino,
                                                             float *__restrict__ recon,
                                                             const int32_t *__restrict__ idx,
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(BT *BT) void cone_back_kernel(const float *__restri
             tap_weights_d<R>(q.f, q.wch, hd);
             float h[NTAP];
 #pragma unroll
-            for (int t = 0; t < NTAP; ++t) h[t] = (float)hd[t];
+            for (int t = 0; t < NTAP; ++t) h[t] = POW == 2 ? (float)(hd[t] * hd[t]) : (float)hd[t];
             const float *col = win + (ncv - R - wd.n0) * nrp - wd.m0;
             const double wrow = q.mr * g.dv;
 #pragma unroll
@@ -121,7 +121,12 @@ __global__ __launch_bounds__(BT *BT) void cone_back_kernel(const float *__restri
                 if (k < nk && mk >= -R && mk <= g.nr - 1 + R) {
                     double gd[NTAP];
                     tap_weights_d<R>(wk - mk, wrow, gd);
-                    const float lk = (float)q.lsc * sqrtf((float)(q.r2 + dz * dz));
+                    float lk = (float)q.lsc * sqrtf((float)(q.r2 + dz * dz));
+                    if (POW == 2) {                 // squared weights: the Hessian-diagonal back projection
+                        lk = lk * lk;
+#pragma unroll
+                        for (int sg = 0; sg < NTAP; ++sg) gd[sg] = gd[sg] * gd[sg];
+                    }
                     const float *cell = col + ((int)mk - R);
                     float s = 0.f;
 #pragma unroll
@@ -274,12 +279,16 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
 }
 
 template <int SL, int R>
-static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, hipStream_t st) {
+static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, int power, hipStream_t st) {
     const Geo &g = p.g;
     const int tiles = ((g.nx + BT - 1) / BT) * ((g.ny + BT - 1) / BT);
     const int chunks = (g.ns + SL - 1) / SL;
-    hipLaunchKernelGGL((cone_back_kernel<SL, R>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino, recon,
-                       p.idx, p.views, p.bwin, g, p.back_nrcap);
+    if (power == 2)
+        hipLaunchKernelGGL((cone_back_kernel<SL, R, 2>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
+                           recon, p.idx, p.views, p.bwin, g, p.back_nrcap);
+    else
+        hipLaunchKernelGGL((cone_back_kernel<SL, R, 1>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
+                           recon, p.idx, p.views, p.bwin, g, p.back_nrcap);
     return hipGetLastError();
 }
 
@@ -312,11 +321,11 @@ static hipError_t cone_fwd_r(const Plan &p, const float *recon, float *sino, hip
     default: return hipErrorInvalidValue;                      \
     }
 
-hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, hipStream_t st) {
+hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st) {
     switch (p.back_sl) {
-    case 8: BPAMD_DISPATCH_R(cone_back_t, 8, p, sino, recon, st)
-    case 16: BPAMD_DISPATCH_R(cone_back_t, 16, p, sino, recon, st)
-    case 32: BPAMD_DISPATCH_R(cone_back_t, 32, p, sino, recon, st)
+    case 8: BPAMD_DISPATCH_R(cone_back_t, 8, p, sino, recon, power, st)
+    case 16: BPAMD_DISPATCH_R(cone_back_t, 16, p, sino, recon, power, st)
+    case 32: BPAMD_DISPATCH_R(cone_back_t, 32, p, sino, recon, power, st)
     default: return hipErrorInvalidValue;
     }
 }

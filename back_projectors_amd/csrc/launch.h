@@ -59,10 +59,11 @@ hipError_t launch_par_region_records(const Geo &g, const int32_t *rec, uint32_t 
                                     int nbin, hipStream_t st);
 hipError_t launch_fill_zero(float *buf, int64_t n, hipStream_t st);
 
-hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, hipStream_t st);
+// power 1: the adjoint of the forward; power 2: every tap weight squared
+hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st);
 hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
 hipError_t par_forward_allow_lds(int ntap, size_t bytes);
-hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, hipStream_t st);
+hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st);
 hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
 hipError_t cone_forward_allow_lds(int radius, int stride, size_t bytes);
 

@@ -32,7 +32,7 @@
 
 namespace bpamd {
 
-template <int SL, int NTAP, int NCG>
+template <int SL, int NTAP, int NCG, int POW>
 __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restrict__ sino,
                                                            float *__restrict__ recon,
                                                            const int32_t *__restrict__ rec,
@@ -90,7 +90,10 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
         const int32_t *r = rec + ((int64_t)v * np + p) * NREC;
         nf = valid ? r[0] : INT32_MAX;
 #pragma unroll
-        for (int t = 0; t < NTAP; ++t) w[t] = valid ? __int_as_float(r[1 + t]) : 0.f;
+        for (int t = 0; t < NTAP; ++t) {
+            const float wt = valid ? __int_as_float(r[1 + t]) : 0.f;
+            w[t] = POW == 2 ? wt * wt : wt;       // squared weights: the Hessian-diagonal back projection
+        }
     };
 
     float acc[SL];
@@ -341,17 +344,17 @@ __global__ __launch_bounds__(256) void par_unpack_kernel(const float *__restrict
     }
 }
 
-template <int SL, int NTAP>
+template <int SL, int NTAP, int POW>
 static hipError_t par_back_t(const Plan &p, const float *sino, float *recon, hipStream_t st) {
     const Geo &g = p.g;
     const int tiles = ((g.nx + BT - 1) / BT) * ((g.ny + BT - 1) / BT);
     const int chunks = (g.ns + SL - 1) / SL;
     if (p.back_ncg == 1)
-        hipLaunchKernelGGL((par_back_kernel<SL, NTAP, 1>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
-                           recon, p.rec, p.bwin, g, p.back_nwcap);
+        hipLaunchKernelGGL((par_back_kernel<SL, NTAP, 1, POW>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st,
+                           sino, recon, p.rec, p.bwin, g, p.back_nwcap);
     else
-        hipLaunchKernelGGL((par_back_kernel<SL, NTAP, 2>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
-                           recon, p.rec, p.bwin, g, p.back_nwcap);
+        hipLaunchKernelGGL((par_back_kernel<SL, NTAP, 2, POW>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st,
+                           sino, recon, p.rec, p.bwin, g, p.back_nwcap);
     return hipGetLastError();
 }
 
@@ -367,27 +370,32 @@ static hipError_t par_fwd_t(const Plan &p, const float *recon, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int SL>
+template <int SL, int POW>
 static hipError_t par_back_sl(const Plan &p, const float *sino, float *recon, hipStream_t st) {
     switch (p.ntap) {
-    case 2: return par_back_t<SL, 2>(p, sino, recon, st);
-    case 3: return par_back_t<SL, 3>(p, sino, recon, st);
-    case 4: return par_back_t<SL, 4>(p, sino, recon, st);
-    case 5: return par_back_t<SL, 5>(p, sino, recon, st);
-    case 6: return par_back_t<SL, 6>(p, sino, recon, st);
-    case 7: return par_back_t<SL, 7>(p, sino, recon, st);
+    case 2: return par_back_t<SL, 2, POW>(p, sino, recon, st);
+    case 3: return par_back_t<SL, 3, POW>(p, sino, recon, st);
+    case 4: return par_back_t<SL, 4, POW>(p, sino, recon, st);
+    case 5: return par_back_t<SL, 5, POW>(p, sino, recon, st);
+    case 6: return par_back_t<SL, 6, POW>(p, sino, recon, st);
+    case 7: return par_back_t<SL, 7, POW>(p, sino, recon, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, hipStream_t st) {
+template <int POW>
+static hipError_t par_back_pow(const Plan &p, const float *sino, float *recon, hipStream_t st) {
     switch (p.back_sl) {
-    case 8: return par_back_sl<8>(p, sino, recon, st);
-    case 16: return par_back_sl<16>(p, sino, recon, st);
-    case 32: return par_back_sl<32>(p, sino, recon, st);
-    case 64: return par_back_sl<64>(p, sino, recon, st);
+    case 8: return par_back_sl<8, POW>(p, sino, recon, st);
+    case 16: return par_back_sl<16, POW>(p, sino, recon, st);
+    case 32: return par_back_sl<32, POW>(p, sino, recon, st);
+    case 64: return par_back_sl<64, POW>(p, sino, recon, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st) {
+    return power == 2 ? par_back_pow<2>(p, sino, recon, st) : par_back_pow<1>(p, sino, recon, st);
 }
 
 // Zero the accumulation buffer, walk, then unpack into the sinogram (which the

@@ -529,7 +529,7 @@ proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev,
     return ok();
 }
 
-proj_status proj_back(proj_handle h, const float *sino_dev, float *recon_dev, void *hip_stream) {
+static proj_status back_power(proj_handle h, const float *sino_dev, float *recon_dev, int power, void *hip_stream) {
     if (!h) return fail(PROJ_ERR_INVALID_ARGUMENT, "null handle");
     if ((h->recon_elems > 0 && !recon_dev) || (h->sino_elems > 0 && !sino_dev))
         return fail(PROJ_ERR_INVALID_ARGUMENT, "null data pointer");
@@ -545,10 +545,18 @@ proj_status proj_back(proj_handle h, const float *sino_dev, float *recon_dev, vo
         if (e != hipSuccess) return device_fail(e, "zero fill");
         return ok();
     }
-    e = h->plan.g.kind == 0 ? launch_par_back(h->plan, sino_dev, recon_dev, st)
-                            : launch_cone_back(h->plan, sino_dev, recon_dev, st);
+    e = h->plan.g.kind == 0 ? launch_par_back(h->plan, sino_dev, recon_dev, power, st)
+                            : launch_cone_back(h->plan, sino_dev, recon_dev, power, st);
     if (e != hipSuccess) return device_fail(e, "back projection launch");
     return ok();
+}
+
+proj_status proj_back(proj_handle h, const float *sino_dev, float *recon_dev, void *hip_stream) {
+    return back_power(h, sino_dev, recon_dev, 1, hip_stream);
+}
+
+proj_status proj_back_squared(proj_handle h, const float *sino_dev, float *recon_dev, void *hip_stream) {
+    return back_power(h, sino_dev, recon_dev, 2, hip_stream);
 }
 
 proj_status proj_channel_index(proj_handle h, int32_t *index_dev, void *hip_stream) {

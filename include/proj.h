@@ -126,6 +126,18 @@ proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev,
 proj_status proj_back(proj_handle h, const float *sino_dev, float *recon_dev, void *hip_stream);
 
 /*
+ * proj_back_squared: recon[p][k] = sum over views and taps of w^2 *
+ * sino[v][row][n] -- the back projection with every tap weight squared, the
+ * one the diagonal of A^T A (a least-squares Hessian) needs.  The MBIRJAX
+ * "Projector kernels" page, "Gradient and Hessian can take different paths",
+ * calls the same kernels with the weights unchanged for the gradient and with
+ * coefficient power 2 for the Hessian diagonal.  Layouts, ownership, overlap
+ * rule and errors as proj_back; with sino = 1 everywhere it writes
+ * sum_i A_ij^2.  Asynchronous on hip_stream.
+ */
+proj_status proj_back_squared(proj_handle h, const float *sino_dev, float *recon_dev, void *hip_stream);
+
+/*
  * proj_channel_index: copy the handle's channel-index table n_c[V][Ny*Nx]
  * (int32, round half to even of the fp64 channel coordinate) into index_dev.
  * Asynchronous on hip_stream.

@@ -68,6 +68,8 @@ def _load():
         lib.orc_back.argtypes = [g, f32, f64, ctypes.c_void_p]
         lib.orc_forward_views.argtypes = [g, f32, ctypes.c_int32, i32, f64, ctypes.c_void_p]
         lib.orc_back_pixels.argtypes = [g, f32, ctypes.c_int32, i64, f64, ctypes.c_void_p]
+        lib.orc_back_power.argtypes = [g, f32, ctypes.c_int, f64, ctypes.c_void_p]
+        lib.orc_back_pixels_power.argtypes = [g, f32, ctypes.c_int, ctypes.c_int32, i64, f64, ctypes.c_void_p]
         lib.orc_voxel_taps.argtypes = [g, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        i32, i32, f64, ctypes.c_int]
         lib.orc_voxel_taps.restype = ctypes.c_int
@@ -143,11 +145,15 @@ def forward(g: Geometry, x, with_abs: bool = False):
     return (y, a) if with_abs else y
 
 
-def back(g: Geometry, y, with_abs: bool = False):
+def back(g: Geometry, y, with_abs: bool = False, power: int = 1):
+    """Back projection; power 2 squares every tap weight (the Hessian-diagonal
+    back projection)."""
+    if power not in (1, 2):
+        raise ValueError("power must be 1 or 2")
     y = _f32(y, g.sino_shape)
     x = np.empty(g.recon_shape, dtype=np.float64)
     a = np.empty(g.recon_shape, dtype=np.float64) if with_abs else None
-    _load().orc_back(g.ref, y, x, a.ctypes.data if with_abs else None)
+    _load().orc_back_power(g.ref, y, power, x, a.ctypes.data if with_abs else None)
     return (x, a) if with_abs else x
 
 
@@ -161,13 +167,15 @@ def forward_views(g: Geometry, x, views, with_abs: bool = False):
     return (y, a) if with_abs else y
 
 
-def back_pixels(g: Geometry, y, pixels, with_abs: bool = False):
+def back_pixels(g: Geometry, y, pixels, with_abs: bool = False, power: int = 1):
+    if power not in (1, 2):
+        raise ValueError("power must be 1 or 2")
     y = _f32(y, g.sino_shape)
     pixels = np.ascontiguousarray(pixels, dtype=np.int64)
     shape = (len(pixels), g.recon_shape[2])
     x = np.empty(shape, dtype=np.float64)
     a = np.empty(shape, dtype=np.float64) if with_abs else None
-    _load().orc_back_pixels(g.ref, y, len(pixels), pixels, x, a.ctypes.data if with_abs else None)
+    _load().orc_back_pixels_power(g.ref, y, power, len(pixels), pixels, x, a.ctypes.data if with_abs else None)
     return (x, a) if with_abs else x
 
 

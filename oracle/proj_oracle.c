@@ -252,8 +252,11 @@ static void forward_view(const orc_geom *g, const float *x, int32_t v, double *y
 }
 
 /* Back projection into one pixel's cylinder xp[S] (overwritten); views
- * ascending, then slices, then row taps, then channel taps. */
-static void back_pixel(const orc_geom *g, const float *y, int32_t i, int32_t j, double *xp, double *ap)
+ * ascending, then slices, then row taps, then channel taps.  With power 2
+ * every tap weight is squared: the back projection the Hessian diagonal of a
+ * least-squares fit uses ("Gradient and Hessian can take different paths",
+ * coefficient power 2). */
+static void back_pixel(const orc_geom *g, const float *y, int power, int32_t i, int32_t j, double *xp, double *ap)
 {
     const int64_t nrc = (int64_t)g->nr * g->nc;
     const int r = g->radius;
@@ -271,6 +274,7 @@ static void back_pixel(const orc_geom *g, const float *y, int32_t i, int32_t j, 
                     int32_t n = o.nc + tau;
                     if (n < 0 || n >= g->nc) continue;
                     double w = o.len * ov((double)n - o.u, o.w);
+                    if (power == 2) w = w * w;
                     double t = w * (double)yv[(int64_t)k * g->nc + n];
                     xp[k] += t;
                     if (ap) ap[k] += fabs(t);
@@ -288,6 +292,7 @@ static void back_pixel(const orc_geom *g, const float *y, int32_t i, int32_t j, 
                         if (n < 0 || n >= g->nc) continue;
                         double h = ov((double)n - o.u, o.w);
                         double w = lk * h * gw;
+                        if (power == 2) w = w * w;
                         double t = w * (double)yv[(int64_t)m * g->nc + n];
                         xp[k] += t;
                         if (ap) ap[k] += fabs(t);
@@ -317,27 +322,35 @@ void orc_forward_views(const orc_geom *g, const float *x, int32_t nsel, const in
         forward_view(g, x, views[q], y + q * nrc, ay ? ay + q * nrc : NULL);
 }
 
-/* Full back projection: x[Ny, Nx, S] (fp64, overwritten); threads split pixels. */
-void orc_back(const orc_geom *g, const float *y, double *x, double *ax)
+/* Full back projection: x[Ny, Nx, S] (fp64, overwritten); threads split
+ * pixels.  power is 1 (the adjoint) or 2 (every weight squared). */
+void orc_back_power(const orc_geom *g, const float *y, int power, double *x, double *ax)
 {
     const int64_t np = (int64_t)g->ny * g->nx;
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t p = 0; p < np; ++p) {
         int32_t i = (int32_t)(p / g->nx), j = (int32_t)(p % g->nx);
-        back_pixel(g, y, i, j, x + p * g->ns, ax ? ax + p * g->ns : NULL);
+        back_pixel(g, y, power, i, j, x + p * g->ns, ax ? ax + p * g->ns : NULL);
     }
 }
 
+void orc_back(const orc_geom *g, const float *y, double *x, double *ax) { orc_back_power(g, y, 1, x, ax); }
+
 /* Back projection of selected pixels only: x[nsel, S]. */
-void orc_back_pixels(const orc_geom *g, const float *y, int32_t nsel, const int64_t *pix,
-                     double *x, double *ax)
+void orc_back_pixels_power(const orc_geom *g, const float *y, int power, int32_t nsel, const int64_t *pix,
+                           double *x, double *ax)
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int32_t q = 0; q < nsel; ++q) {
         int64_t p = pix[q];
         int32_t i = (int32_t)(p / g->nx), j = (int32_t)(p % g->nx);
-        back_pixel(g, y, i, j, x + (int64_t)q * g->ns, ax ? ax + (int64_t)q * g->ns : NULL);
+        back_pixel(g, y, power, i, j, x + (int64_t)q * g->ns, ax ? ax + (int64_t)q * g->ns : NULL);
     }
+}
+
+void orc_back_pixels(const orc_geom *g, const float *y, int32_t nsel, const int64_t *pix, double *x, double *ax)
+{
+    orc_back_pixels_power(g, y, 1, nsel, pix, x, ax);
 }
 
 /* Every nonzero tap of one voxel (v, i, j, k): channel, row and weight.

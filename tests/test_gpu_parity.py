@@ -263,3 +263,39 @@ def test_full_adjoint_identity(bp, orc, name, full_cache):
     aty = host(proj.back(dev(y)))
     gap = adjoint_gap(ax, y, x, aty)
     assert gap < ADJOINT, f"{name}: adjoint gap {gap:.2e}"
+
+
+# ---------------------------------------------- squared-weight back ---
+@pytest.mark.parametrize("w", SMALL_CASES, ids=lambda w: w.name)
+def test_small_back_squared(bp, orc, w):
+    """proj_back_squared (every tap weight squared: the Hessian-diagonal back
+    projection) against the reference, every entry; and with a sinogram of
+    ones, sum_i A_ij^2 itself."""
+    note(f"small back squared {w.name}")
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    _, y = inputs(w)
+    xo, ax = orc.back(g, y, with_abs=True, power=2)
+    xg = host(proj.back_squared(dev(y)))
+    assert_close(xg, xo, ax, f"{w.name} back squared")
+    ones = np.ones(w.sino_shape, np.float32)
+    ho = orc.back(g, ones, power=2)
+    hg = host(proj.back_squared(dev(ones)))
+    assert_close(hg, ho, ho, f"{w.name} diagonal of A^T A")
+    # the plain adjoint is untouched by the squared path (same handle, after it)
+    xo1, ax1 = orc.back(g, y, with_abs=True)
+    assert_close(host(proj.back(dev(y))), xo1, ax1, f"{w.name} back after squared")
+    proj.close()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_back_squared_sampled_pixels(bp, orc, name, full_cache):
+    w, proj, g = full_setup(bp, orc, name, full_cache)
+    note(f"full back squared {name}")
+    y = w.sino_input()
+    xg = host(proj.back_squared(dev(y))).reshape(w.ny * w.nx, w.ns)
+    rng = np.random.default_rng(78)
+    pix = np.unique(np.concatenate([rng.integers(0, w.ny * w.nx, 300),
+                                    [0, w.ny * w.nx - 1, (w.ny // 2) * w.nx + w.nx // 2]]))
+    xo, ax = orc.back_pixels(g, y, pix, with_abs=True, power=2)
+    assert_close(xg[pix], xo, ax, f"{name} back squared pixels")

@@ -369,3 +369,51 @@ def test_tie_canaries_only_in_those_views(orc):
     u = orc.channel_coord(make(orc, w))
     assert np.array_equal(u, np.round(u))
     assert u.min() == 4.0 and u.max() == 1019.0
+
+
+# ------------------------------------------------- squared-weight back ---
+@pytest.mark.parametrize("w", [W.get(W.SMALL), SMALL_CONE, SMALL_HELIX, SMALL_TRANS],
+                         ids=lambda w: w.name)
+def test_squared_back_is_hessian_diagonal_weighting(orc, w):
+    """P-H: the back projection with squared weights at voxel j is
+    sum_i A_ij^2 y_i ("Gradient and Hessian can take different paths",
+    coefficient power 2).  A_ij is read off the forward scatter of the unit
+    voxel e_j -- a different loop from the back gather -- so a dropped square,
+    a wrong tap or a transposed index in either shows up."""
+    g = make(orc, w)
+    ny, nx, ns = w.recon_shape
+    rng = np.random.default_rng(21)
+    y = rng.standard_normal(w.sino_shape).astype(np.float32)
+    picks = [(ny // 2, nx // 2, ns // 2), (1, nx - 2, 0), (ny - 1, 0, ns - 1), (ny // 3, 2 * nx // 3, ns // 3)]
+    for (i, j, k) in picks:
+        e = np.zeros(w.recon_shape, np.float32)
+        e[i, j, k] = 1.0
+        col = orc.forward(g, e)                       # A e_j, fp64
+        expect = float((col * col * y.astype(np.float64)).sum())
+        got = orc.back_pixels(g, y, [i * nx + j], power=2)[0, k]
+        scale = float((col * col * np.abs(y.astype(np.float64))).sum())
+        assert scale > 0.0, (i, j, k)
+        assert abs(got - expect) <= 1e-12 * scale, (i, j, k, got, expect)
+        # and the plain adjoint on the same voxel is sum_i A_ij y_i
+        got1 = orc.back_pixels(g, y, [i * nx + j], power=1)[0, k]
+        assert abs(got1 - float((col * y.astype(np.float64)).sum())) <= 1e-12 * float(
+            (np.abs(col) * np.abs(y.astype(np.float64))).sum()), (i, j, k)
+
+
+def test_squared_back_single_voxel_axis_aligned(orc):
+    """P-H closed form: at theta = 0 with unit pitches a voxel centred on a
+    channel has one tap of weight dv/max(|cos|,|sin|) = 1, so its squared
+    back projection of y is y at that channel, and a voxel half a channel off
+    splits 1/2 + 1/2, whose squares sum to 1/2."""
+    geo = geom_dict(angles=(0.0,), dch=1.0)
+    g = orc.Geometry(geo, (1, 2, 1), (1, 1, 4))
+    y = np.array([[[1.0, 2.0, 4.0, 8.0]]], np.float32)
+    # Nx = 2: pixel centres at x = -0.5, +0.5; C = 4: channel centre 1.5, so
+    # u = x + 1.5 lands on channels 1 and 2 exactly
+    out = orc.back(g, y, power=2)
+    assert out[0, 0, 0] == 2.0 and out[0, 1, 0] == 4.0
+    g2 = orc.Geometry(dict(geo, det_channel_offset=0.5), (1, 2, 1), (1, 1, 4))
+    # u = x + 2: pixel 0 at 1.5 (half in channel 1, half in 2), pixel 1 at 2.5
+    out2 = orc.back(g2, y, power=2)
+    assert out2[0, 0, 0] == 0.25 * 2.0 + 0.25 * 4.0
+    assert out2[0, 1, 0] == 0.25 * 4.0 + 0.25 * 8.0
