@@ -48,15 +48,28 @@ __device__ __forceinline__ ConeVP cone_vp(const Geo &g, const ViewK &vk, double 
     return o;
 }
 
+// Back: lanes are the pixels of a BT x BT tile, each with SL slice
+// accumulators.  Per view the sinogram window the tile and slice chunk can reach
+// is staged in LDS, double buffered: view v + 1's cells are read into registers
+// (channels fastest, coalesced) while view v is gathered, then stored, with one
+// barrier per view.  The per-view constants and window travel as one register
+// (lanes 0-17 the view's 18 dwords, lanes 18-21 its window) fetched two views
+// ahead; the channel index of each lane's pixel one view ahead.  The row taps
+// run in fp32 (clamped edges by v_med3): a voxel's back projection sums the
+// taps of every view, so their 1e-7 absolute error is far below the
+// tolerance relative to that sum; the row itself is placed in fp64.
 template <int SL, int R, int POW>
-__global__ __launch_bounds__(BT *BT) void cone_back_kernel(const float *__restrict__ sino,
+__global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__restrict__ sino,
                                                             float *__restrict__ recon,
                                                             const int32_t *__restrict__ idx,
                                                             const ViewK *__restrict__ views,
-                                                            const int4 *__restrict__ wtab, Geo g, int nrp) {
+                                                            const int4 *__restrict__ wtab, Geo g, int nwcap,
+                                                            int nrp) {
     constexpr int NT = BT * BT;
     constexpr int NTAP = 2 * R + 1;
-    extern __shared__ float win[];        // [nwcap][nrp], rows fastest
+    constexpr int STG = CBSTG;            // staged cells per thread at most
+    extern __shared__ float win[];        // two windows of [nwcap][nrp], rows fastest
+    static_assert(sizeof(ViewK) == 72, "ViewK is read as 18 dwords");
 
     const int tiles_x = (g.nx + BT - 1) / BT;
     const int ntiles = tiles_x * ((g.ny + BT - 1) / BT);
@@ -65,9 +78,13 @@ __global__ __launch_bounds__(BT *BT) void cone_back_kernel(const float *__restri
     const int ti0 = (int)(blockIdx.x / tiles_x) * BT;
     const int k0 = (int)blockIdx.y * SL;
     const int nk = min(SL, g.ns - k0);
+    const int tid = (int)threadIdx.x;
+    const int wl = tid & 63;
+    const int wsz = nwcap * nrp;
+    const int stg = (wsz + NT - 1) / NT;  // <= STG by the plan
 
-    const int i = ti0 + (int)threadIdx.x / BT;
-    const int j = tj0 + (int)threadIdx.x % BT;
+    const int i = ti0 + tid / BT;
+    const int j = tj0 + tid % BT;
     const bool valid = (i < g.ny) && (j < g.nx);
     const int np = g.ny * g.nx;
     const int p = valid ? i * g.nx + j : 0;
@@ -77,68 +94,132 @@ __global__ __launch_bounds__(BT *BT) void cone_back_kernel(const float *__restri
 #pragma unroll
     for (int k = 0; k < SL; ++k) acc[k] = 0.f;
 
-    const int lane = (int)threadIdx.x & 31;
-    const int grp = (int)threadIdx.x >> 5;
-
-    for (int v = 0; v < g.nv; ++v) {
-        const int4 w4 = wtab[((int64_t)v * ntiles + blockIdx.x) * nch + blockIdx.y];
-        if (w4.y <= 0 || w4.w <= 0) continue;      // the tile misses the detector in this view
-        Window wd;
-        wd.n0 = w4.x;
-        wd.nw = w4.y;
-        wd.m0 = w4.z;
-        wd.nrw = w4.w;
-        const ViewK vk = views[v];
-        __syncthreads();
-        for (int m = grp; m < wd.nrw; m += NT / 32) {
-            const int row = wd.m0 + m;
-            const bool rok = row >= 0 && row < g.nr;
-            const float *srow = sino + ((int64_t)v * g.nr + (rok ? row : 0)) * g.nc;
-            for (int c = lane; c < wd.nw; c += 32) {
-                const int n = wd.n0 + c;
-                float val = 0.f;
-                if (rok && n >= 0 && n < g.nc) val = srow[n];
-                win[c * nrp + m] = val;
+    auto fetch_view = [&](int v, uint32_t &pv) {
+        const uint32_t *vkd = reinterpret_cast<const uint32_t *>(views + v);
+        const uint32_t *wd = reinterpret_cast<const uint32_t *>(wtab + ((int64_t)v * ntiles + blockIdx.x) * nch +
+                                                                 blockIdx.y);
+        pv = wl < 18 ? vkd[wl] : (wl < 22 ? wd[wl - 18] : 0u);
+    };
+    auto win_of = [](uint32_t pv) {
+        Window w;
+        w.n0 = __builtin_amdgcn_readlane((int)pv, 18);
+        w.nw = __builtin_amdgcn_readlane((int)pv, 19);
+        w.m0 = __builtin_amdgcn_readlane((int)pv, 20);
+        w.nrw = __builtin_amdgcn_readlane((int)pv, 21);
+        return w;
+    };
+    auto rd = [](uint32_t pv, int e) {
+        const int lo = __builtin_amdgcn_readlane((int)pv, 2 * e), hi = __builtin_amdgcn_readlane((int)pv, 2 * e + 1);
+        return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+    };
+    // window cells, flattened with channels fastest (coalesced reads)
+    auto stage_load = [&](int v, const Window &w, float (&st)[STG]) {
+        const float rnw = 1.0f / (float)max(w.nw, 1);
+#pragma unroll
+        for (int u = 0; u < STG; ++u) {
+            st[u] = 0.f;
+            if (u < stg) {
+                const int e = tid + NT * u;
+                const int m = (int)(((float)e + 0.5f) * rnw);   // exact: e < 2^22 and nw is small
+                const int c = e - m * w.nw;
+                const int row = w.m0 + m, n = w.n0 + c;
+                if (w.nw > 0 && m < w.nrw && row >= 0 && row < g.nr && n >= 0 && n < g.nc)
+                    st[u] = sino[((int64_t)v * g.nr + row) * g.nc + n];
             }
         }
+    };
+    auto stage_store = [&](float *buf, const Window &w, const float (&st)[STG]) {
+        const float rnw = 1.0f / (float)max(w.nw, 1);
+#pragma unroll
+        for (int u = 0; u < STG; ++u) {
+            if (u < stg) {
+                const int e = tid + NT * u;
+                const int m = (int)(((float)e + 0.5f) * rnw);
+                const int c = e - m * w.nw;
+                if (w.nw > 0 && m < w.nrw) buf[c * nrp + m] = st[u];
+            }
+        }
+    };
+
+    if (g.nv > 0) {
+        uint32_t pcur, pnext;
+        fetch_view(0, pcur);
+        fetch_view(min(1, g.nv - 1), pnext);
+        int ncur = valid ? idx[p] : INT32_MIN;
+        {
+            const Window w0 = win_of(pcur);
+            float st[STG];
+            stage_load(0, w0, st);
+            stage_store(win, w0, st);
+        }
         __syncthreads();
-        const int ncv = valid ? idx[(int64_t)v * np + p] : 0;
-        if (valid && ncv >= -R && ncv <= g.nc - 1 + R) {
-            const ConeVP q = cone_vp(g, vk, x, y, ncv);
-            double hd[NTAP];
-            tap_weights_d<R>(q.f, q.wch, hd);
-            float h[NTAP];
+        for (int v = 0; v < g.nv; ++v) {
+            const bool more = v + 1 < g.nv;
+            const Window wv = win_of(pcur);
+            const Window wn = win_of(pnext);
+            float st[STG];
+            int nnext = INT32_MIN;
+            uint32_t pafter = pnext;
+            if (more) {
+                stage_load(v + 1, wn, st);
+                nnext = valid ? idx[(int64_t)(v + 1) * np + p] : INT32_MIN;
+                fetch_view(min(v + 2, g.nv - 1), pafter);
+            }
+            if (wv.nw > 0 && wv.nrw > 0 && ncur >= -R && ncur <= g.nc - 1 + R) {
+                ViewK vk;
+                vk.c = rd(pcur, 0);
+                vk.s = rd(pcur, 1);
+                vk.shift = rd(pcur, 2);
+                vk.zsrc = rd(pcur, 3);
+                const ConeVP q = cone_vp(g, vk, x, y, ncur);
+                double hd[NTAP];
+                tap_weights_d<R>(q.f, q.wch, hd);
+                float h[NTAP];
 #pragma unroll
-            for (int t = 0; t < NTAP; ++t) h[t] = POW == 2 ? (float)(hd[t] * hd[t]) : (float)hd[t];
-            const float *col = win + (ncv - R - wd.n0) * nrp - wd.m0;
-            const double wrow = q.mr * g.dv;
+                for (int t = 0; t < NTAP; ++t) h[t] = POW == 2 ? (float)(hd[t] * hd[t]) : (float)hd[t];
+                const float *col = win + (v & 1) * wsz + (ncur - R - wv.n0) * nrp - wv.m0;
+                const float hrow = (float)(0.5 * (q.mr * g.dv));
+                const float lscf = (float)q.lsc;
 #pragma unroll
-            for (int k = 0; k < SL; ++k) {
-                const double dz = slice_z(g, k0 + k) - vk.zsrc;
-                const double t0 = q.mr * dz;
-                const double wk = t0 + g.crow;
-                const double mk = rint(wk);
-                if (k < nk && mk >= -R && mk <= g.nr - 1 + R) {
-                    double gd[NTAP];
-                    tap_weights_d<R>(wk - mk, wrow, gd);
-                    float lk = (float)q.lsc * sqrtf((float)(q.r2 + dz * dz));
-                    if (POW == 2) {                 // squared weights: the Hessian-diagonal back projection
-                        lk = lk * lk;
+                for (int k = 0; k < SL; ++k) {
+                    const double dz = slice_z(g, k0 + k) - vk.zsrc;
+                    const double t0 = q.mr * dz;
+                    const double wk = t0 + g.crow;
+                    const double mk = rint(wk);
+                    if (k < nk && mk >= -R && mk <= g.nr - 1 + R) {
+                        const float f = (float)(wk - mk);
+                        float gw[NTAP];
+                        float gp = __builtin_amdgcn_fmed3f(-0.5f - (float)R - f, -hrow, hrow);
 #pragma unroll
-                        for (int sg = 0; sg < NTAP; ++sg) gd[sg] = gd[sg] * gd[sg];
+                        for (int t = 0; t < NTAP; ++t) {
+                            const float gn = __builtin_amdgcn_fmed3f((float)t - (float)R + 0.5f - f, -hrow, hrow);
+                            gw[t] = gn - gp;
+                            gp = gn;
+                        }
+                        float lk = lscf * __builtin_amdgcn_sqrtf((float)(q.r2 + dz * dz));
+                        if (POW == 2) {             // squared weights: the Hessian-diagonal back projection
+                            lk = lk * lk;
+#pragma unroll
+                            for (int t = 0; t < NTAP; ++t) gw[t] = gw[t] * gw[t];
+                        }
+                        const float *cell = col + ((int)mk - R);
+                        float s = 0.f;
+#pragma unroll
+                        for (int sg = 0; sg < NTAP; ++sg) {
+                            float rv = 0.f;
+#pragma unroll
+                            for (int t = 0; t < NTAP; ++t) rv = fmaf(h[t], cell[t * nrp + sg], rv);
+                            s = fmaf(gw[sg], rv, s);
+                        }
+                        acc[k] = fmaf(lk, s, acc[k]);
                     }
-                    const float *cell = col + ((int)mk - R);
-                    float s = 0.f;
-#pragma unroll
-                    for (int sg = 0; sg < NTAP; ++sg) {
-                        float rv = 0.f;
-#pragma unroll
-                        for (int t = 0; t < NTAP; ++t) rv = fmaf(h[t], cell[t * nrp + sg], rv);
-                        s = fmaf(lk * (float)gd[sg], rv, s);
-                    }
-                    acc[k] += s;
                 }
             }
+            if (more) stage_store(win + ((v + 1) & 1) * wsz, wn, st);
+            __syncthreads();
+            pcur = pnext;
+            pnext = pafter;
+            ncur = nnext;
         }
     }
     if (valid) {
@@ -198,46 +279,95 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
     const int vend = min(g.nv, vbeg + vper);
     const int cnt = vend - vbeg;
     const int start = cnt > 0 ? (int)((blockIdx.x * 37u + blockIdx.y * 11u) % (unsigned)cnt) : 0;
+    auto view_of = [&](int it) {
+        const int v = vbeg + start + it;
+        return v >= vend ? v - cnt : v;
+    };
+    // this lane's pixel of the tile
+    const int il = ti0 + lane / CTX, jl = tj0 + lane % CTX;
+    const bool lin = il < g.ny && jl < g.nx;
+    const double xl = pix_x(g, jl), yl = pix_y(g, il);
 
-    for (int it = wave; it < cnt; it += CFW) {
-        int v = vbeg + start + it;
-        if (v >= vend) v -= cnt;
-        const int4 w4 = wtab[((int64_t)v * ntiles + blockIdx.x) * nch + blockIdx.y];
-        if (w4.y <= 0 || w4.w <= 0) continue;
+    // Per-view data, fetched two views ahead with vector loads: lanes 0-17
+    // hold the view's constants (ViewK, 18 dwords), lanes 18-21 its window,
+    // and every lane the channel index of its pixel.
+    static_assert(sizeof(ViewK) == 72, "ViewK is read as 18 dwords");
+    auto prefetch = [&](int it, uint32_t &pv, int &pn) {
+        const int v = view_of(min(it, cnt - 1));    // always issued, for a static wait count
+        const uint32_t *vkd = reinterpret_cast<const uint32_t *>(views + v);
+        const uint32_t *wd = reinterpret_cast<const uint32_t *>(wtab + ((int64_t)v * ntiles + blockIdx.x) * nch +
+                                                                 blockIdx.y);
+        pv = lane < 18 ? vkd[lane] : (lane < 22 ? wd[lane - 18] : 0u);
+        pn = lin ? idx[(int64_t)v * np + il * g.nx + jl] : INT32_MIN;
+    };
+    auto rl_d = [](double d, int q) {           // lane q's double, as a wave-uniform value
+        const long long b = __double_as_longlong(d);
+        const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), q);
+        const int hi = __builtin_amdgcn_readlane((int)(b >> 32), q);
+        return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+    };
+
+    auto walk_view = [&](int it, uint32_t pv, int pn) {
+        const int v = view_of(it);
+        ViewK vk;
+        {
+            double vd[9];
+#pragma unroll
+            for (int e = 0; e < 9; ++e) {
+                const int lo = __builtin_amdgcn_readlane((int)pv, 2 * e), hi = __builtin_amdgcn_readlane((int)pv, 2 * e + 1);
+                vd[e] = __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+            }
+            vk.c = vd[0]; vk.s = vd[1]; vk.shift = vd[2]; vk.zsrc = vd[3]; vk.cd = vd[4]; vk.sd = vd[5];
+            vk.u0 = vd[6]; vk.W = vd[7]; vk.L = vd[8];
+        }
         Window wd;
-        wd.n0 = w4.x;
-        wd.nw = w4.y;
-        wd.m0 = w4.z;
-        wd.nrw = w4.w;
-        const ViewK vk = views[v];
+        wd.n0 = __builtin_amdgcn_readlane((int)pv, 18);
+        wd.nw = __builtin_amdgcn_readlane((int)pv, 19);
+        wd.m0 = __builtin_amdgcn_readlane((int)pv, 20);
+        wd.nrw = __builtin_amdgcn_readlane((int)pv, 21);
+        if (wd.nw <= 0 || wd.nrw <= 0) return;
         // per-lane slice offsets of this view
         double dzs[P];
 #pragma unroll
         for (int ph = 0; ph < P; ++ph) dzs[ph] = slice_z(g, k0 + lane * P + ph) - vk.zsrc;
-        for (int q = 0; q < TP; ++q) {
-            const int i = ti0 + q / CTX, j = tj0 + q % CTX;
-            if (i >= g.ny || j >= g.nx) continue;
-            const int ncv = idx[(int64_t)v * np + i * g.nx + j];
-            if (ncv < -R || ncv > g.nc - 1 + R) continue;
-            const ConeVP cv = cone_vp(g, vk, pix_x(g, j), pix_y(g, i), ncv);
+        // this lane's pixel: channel taps and the per-(view, pixel) constants, fp64
+        const bool act = pn >= -R && pn <= g.nc - 1 + R;
+        float hq[NTAP];
+        double mrq = 0.0, lscq = 0.0, r2q = 0.0;
+#pragma unroll
+        for (int t = 0; t < NTAP; ++t) hq[t] = 0.f;
+        if (act) {
+            const ConeVP cv = cone_vp(g, vk, xl, yl, pn);
             double hd[NTAP];
             tap_weights_d<R>(cv.f, cv.wch, hd);
+#pragma unroll
+            for (int t = 0; t < NTAP; ++t) hq[t] = (float)hd[t];
+            mrq = cv.mr;
+            lscq = cv.lsc;
+            r2q = cv.r2;
+        }
+        uint64_t todo = __builtin_amdgcn_ballot_w64(act);
+        while (todo) {
+            const int q = (int)__builtin_ctzll(todo);
+            todo &= todo - 1;
+            const int ncv = __builtin_amdgcn_readlane(pn, q);
             float h[NTAP];
 #pragma unroll
-            for (int t = 0; t < NTAP; ++t) h[t] = (float)hd[t];
-            const double wrow = cv.mr * g.dv;
+            for (int t = 0; t < NTAP; ++t) h[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hq[t]), q));
+            const double mr = rl_d(mrq, q), lsc = rl_d(lscq, q), r2 = rl_d(r2q, q);
+            const double wrow = mr * g.dv;
             float *col = win + (ncv - R - wd.n0) * nrp - wd.m0;
 #pragma unroll
             for (int ph = 0; ph < P; ++ph) {
                 const int kk = lane * P + ph;
-                const double t0 = cv.mr * dzs[ph];
+                const double t0 = mr * dzs[ph];
                 const double wk = t0 + g.crow;
                 const double mk = rint(wk);
                 const bool ok = kk < nk && mk >= -R && mk <= g.nr - 1 + R;
                 double gd[NTAP];
                 tap_weights_d<R>(wk - mk, wrow, gd);
                 const float xv = xt[(q * P + ph) * 64 + lane];
-                const float lk = (float)cv.lsc * sqrtf((float)(cv.r2 + dzs[ph] * dzs[ph]));
+                const float lk = (float)lsc * sqrtf((float)(r2 + dzs[ph] * dzs[ph]));
                 float c[NTAP];
 #pragma unroll
                 for (int sg = 0; sg < NTAP; ++sg) c[sg] = lk * (float)gd[sg] * xv;
@@ -275,6 +405,24 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             if (val != 0.f && row >= 0 && row < g.nr && n >= 0 && n < g.nc)
                 unsafeAtomicAdd(&sino[((int64_t)v * g.nr + row) * g.nc + n], val);
         }
+    };
+
+    // three prefetch buffers in rotation: the view two turns ahead is loaded
+    // while this one is walked (no copies, so the waits stay narrow)
+    if (wave >= cnt) return;
+    uint32_t pvA, pvB, pvC;
+    int pnA, pnB, pnC;
+    prefetch(wave, pvA, pnA);
+    prefetch(wave + CFW, pvB, pnB);
+    for (int it = wave; it < cnt; it += 3 * CFW) {
+        prefetch(it + 2 * CFW, pvC, pnC);
+        walk_view(it, pvA, pnA);
+        if (it + CFW >= cnt) break;
+        prefetch(it + 3 * CFW, pvA, pnA);
+        walk_view(it + CFW, pvB, pnB);
+        if (it + 2 * CFW >= cnt) break;
+        prefetch(it + 4 * CFW, pvB, pnB);
+        walk_view(it + 2 * CFW, pvC, pnC);
     }
 }
 
@@ -285,10 +433,10 @@ static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, in
     const int chunks = (g.ns + SL - 1) / SL;
     if (power == 2)
         hipLaunchKernelGGL((cone_back_kernel<SL, R, 2>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
-                           recon, p.idx, p.views, p.bwin, g, p.back_nrcap);
+                           recon, p.idx, p.views, p.bwin, g, p.back_nwcap, p.back_nrcap);
     else
         hipLaunchKernelGGL((cone_back_kernel<SL, R, 1>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
-                           recon, p.idx, p.views, p.bwin, g, p.back_nrcap);
+                           recon, p.idx, p.views, p.bwin, g, p.back_nwcap, p.back_nrcap);
     return hipGetLastError();
 }
 

@@ -52,6 +52,7 @@ inline int fwd_groups(int rsx, int rsy) { return ((rsx * rsy + 79) / 80) * 5; }
 constexpr int CTX = 8;   // cone forward tile (pixels along x)
 constexpr int CTY = 8;   // cone forward tile (pixels along y)
 constexpr int CFW = 4;   // cone forward waves per workgroup (one view each at a time)
+constexpr int CBSTG = 8;  // cone back: staged window cells per thread at most (window <= 256 * CBSTG cells)
 
 hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
 hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st);

@@ -224,17 +224,20 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         if (plan.fwd_nbin > 8192)
             return fail(PROJ_ERR_UNSUPPORTED, "a forward region spans more than 8190 channels");
     } else {
+        // two staged windows (double buffer), each at most BT*BT*CBSTG cells
         auto back_bytes = [&](int sl, int &nwcap, int &nrcap) {
             const WinMax w = max_window(g, views, BT, BT, sl);
             nwcap = w.nw + 2;
             nrcap = (w.nr + 2) | 1;                 // odd pitch: conflict-free column strides
-            return (size_t)nwcap * nrcap * sizeof(float);
+            return 2 * (size_t)nwcap * nrcap * sizeof(float);
         };
         for (int sl = pick_chunk(S, {8, 16, 32});; sl /= 2) {
             plan.back_sl = sl;
             plan.back_lds = back_bytes(sl, plan.back_nwcap, plan.back_nrcap);
-            if (plan.back_lds <= kMaxLds || sl == 8) break;
+            if ((plan.back_lds <= kMaxLds && plan.back_nwcap * plan.back_nrcap <= BT * BT * CBSTG) || sl == 8) break;
         }
+        if (plan.back_nwcap * plan.back_nrcap > BT * BT * CBSTG)
+            return fail(PROJ_ERR_UNSUPPORTED, "cone back window larger than the staging allows (detector far finer than the voxels)");
         // smallest row magnification (rows per slice) over the whole scan: lanes
         // of one forward instruction take slices `stride` apart, so that their
         // rows differ
