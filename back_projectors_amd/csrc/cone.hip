@@ -367,7 +367,7 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                 double gd[NTAP];
                 tap_weights_d<R>(wk - mk, wrow, gd);
                 const float xv = xt[(q * P + ph) * 64 + lane];
-                const float lk = (float)lsc * sqrtf((float)(r2 + dzs[ph] * dzs[ph]));
+                const float lk = (float)lsc * __builtin_amdgcn_sqrtf((float)(r2 + dzs[ph] * dzs[ph]));
                 float c[NTAP];
 #pragma unroll
                 for (int sg = 0; sg < NTAP; ++sg) c[sg] = lk * (float)gd[sg] * xv;
