@@ -21,6 +21,9 @@ import numpy as np
 
 PROJ_PARALLEL = 0
 PROJ_CONE_FLAT = 1
+PROJ_FORWARD_AUTO = 0
+PROJ_FORWARD_TILE = 1
+PROJ_FORWARD_GATHER = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libbpamd.so")
@@ -62,6 +65,7 @@ class _Geometry(ctypes.Structure):
         ("det_channel_offset", ctypes.c_double),
         ("det_row_offset", ctypes.c_double),
         ("psf_radius", ctypes.c_int32),
+        ("forward_strategy", ctypes.c_int32),
     ]
 
 
@@ -136,7 +140,8 @@ class _GeomArgs:
             float(geometry.get("delta_voxel", 1.0)), float(geometry.get("delta_channel", 1.0)),
             float(geometry.get("delta_row", 1.0)), float(geometry.get("source_iso", 0.0)),
             float(geometry.get("source_detector", 0.0)), float(geometry.get("det_channel_offset", 0.0)),
-            float(geometry.get("det_row_offset", 0.0)), int(geometry.get("psf_radius", 1)))
+            float(geometry.get("det_row_offset", 0.0)), int(geometry.get("psf_radius", 1)),
+            int(geometry.get("forward_strategy", 0)))
         self.rs = (ctypes.c_int64 * 3)(*self.recon_shape)
         self.ss = (ctypes.c_int64 * 3)(*self.sino_shape)
 

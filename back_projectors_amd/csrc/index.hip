@@ -217,6 +217,81 @@ __global__ __launch_bounds__(256) void par_region_records_kernel(Geo g, const in
     }
 }
 
+// Gather strategy: per view, every pixel ordered by its first tap channel
+// (a counting sort, one workgroup per view; pixels of one channel keep an
+// arbitrary order).  Keys are n_f + NTAP - 1 in [0, C + NTAP - 2]; pixels with
+// no tap on the detector take key C + NTAP - 1 and sort last.  Dynamic LDS:
+// nbin = C + NTAP ints.
+__global__ __launch_bounds__(256) void par_view_sort_kernel(Geo g, const int32_t *__restrict__ rec,
+                                                            int32_t *__restrict__ order, int ntap, int nbin) {
+    extern __shared__ int bin[];
+    const int v = (int)blockIdx.x;
+    const int np = g.ny * g.nx;
+    const int t = (int)threadIdx.x;
+    auto key_of = [&](int p) {
+        const int nf = rec[((int64_t)v * np + p) * (1 + ntap)];
+        return nf == INT32_MAX ? nbin - 1 : nf + ntap - 1;
+    };
+    for (int e = t; e < nbin; e += 256) bin[e] = 0;
+    __syncthreads();
+    for (int p = t; p < np; p += 256) atomicAdd(&bin[key_of(p)], 1);
+    __syncthreads();
+    if (t == 0) {
+        int run = 0;
+        for (int e = 0; e < nbin; ++e) {
+            const int c = bin[e];
+            bin[e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    int32_t *o = order + (int64_t)v * np;
+    for (int p = t; p < np; p += 256) o[atomicAdd(&bin[key_of(p)], 1)] = p;
+}
+
+// The gather walk's records, in the region walk's format (see above) except
+// that field 0 is the byte offset of the pixel's voxel cylinder in the
+// volume, p * S * 4, a view's walk is all of its pixels, padded with zero
+// steps to ng groups of 16, and is cut into segments of segg groups, each
+// walked on its own: the last step of a segment flushes every accumulator.
+// One thread per (view, step).
+__global__ __launch_bounds__(256) void par_view_records_kernel(Geo g, const int32_t *__restrict__ rec,
+                                                               const int32_t *__restrict__ order,
+                                                               uint32_t *__restrict__ out, int ntap, int ng,
+                                                               int segg) {
+    const int np = g.ny * g.nx;
+    const int nstep = ng * 16;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)g.nv * nstep) return;
+    const int v = (int)(e / nstep);
+    const int q = (int)(e - (int64_t)v * nstep);
+    const int nf_ = 2 + ntap;
+    uint32_t *oq = out + ((int64_t)v * ng + (q >> 4)) * nf_ * 16 + (q & 15);   // field f: oq[f * 16]
+    const int32_t *ov = order + (int64_t)v * np;
+    auto nf_at = [&](int s) { return s < np ? rec[((int64_t)v * np + ov[s]) * (1 + ntap)] : (int)INT32_MAX; };
+    const int p = q < np ? ov[q] : 0;
+    oq[0] = (uint32_t)((int64_t)p * g.ns * 4);
+    oq[16] = 0u;
+    for (int r = 0; r < ntap; ++r) oq[(2 + r) * 16] = 0u;
+    const int nf = nf_at(q);
+    if (nf == INT32_MAX) return;
+    const int cm = ((nf % ntap) + ntap) % ntap;
+    const int turn = (nf - cm) / ntap + 1;
+    const int nx = nf_at(q + 1);
+    // the walk's last step, and the last step of every segment, flush all
+    const bool seg_end = (q + 1) % (segg * 16) == 0;
+    const int fin = (nx != INT32_MAX && !seg_end) ? min(nx - nf, ntap) : ntap;
+    uint32_t mask = 0, up = 0;
+    for (int d = 0; d < fin; ++d) {
+        const int rr = (cm + d) % ntap;
+        mask |= 1u << rr;
+        if (rr < cm) up |= 1u << rr;
+    }
+    if (mask) oq[16] = mask | (up << 7) | ((uint32_t)turn << 14);
+    const int32_t *rp_ = rec + ((int64_t)v * np + p) * (1 + ntap);
+    for (int rr = 0; rr < ntap; ++rr) oq[(2 + rr) * 16] = (uint32_t)rp_[1 + (rr - cm + ntap) % ntap];
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float4 *__restrict__ b4, float *__restrict__ tail,
                                                         int64_t n4, int ntail) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -253,6 +328,20 @@ hipError_t launch_par_region_records(const Geo &g, const int32_t *rec, uint32_t 
     const size_t lds = (size_t)(2 * rsx * rsy + nbin + 1) * sizeof(int);
     hipLaunchKernelGGL(par_region_records_kernel, dim3((unsigned)blocks), dim3(256), lds, st, g, rec, out, ntap, rsx,
                        rsy, nrx, nreg, ng, nbin);
+    return hipGetLastError();
+}
+
+hipError_t launch_par_view_records(const Geo &g, const int32_t *rec, int32_t *order, uint32_t *out, int ntap,
+                                  int ng, int segg, hipStream_t st) {
+    if (g.nv == 0) return hipSuccess;
+    const int nbin = g.nc + ntap;
+    hipLaunchKernelGGL(par_view_sort_kernel, dim3(g.nv), dim3(256), (size_t)nbin * sizeof(int), st, g, rec, order,
+                       ntap, nbin);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = (int64_t)g.nv * ng * 16;
+    hipLaunchKernelGGL(par_view_records_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, g, rec,
+                       order, out, ntap, ng, segg);
     return hipGetLastError();
 }
 

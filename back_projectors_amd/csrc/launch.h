@@ -22,6 +22,10 @@ struct Plan {
     int fwd_s16 = 0;                // parallel: slices of facc (S rounded up to 16)
     int rsx = 0, rsy = 0;           // parallel: forward region (pixels along x, y)
     int fwd_nbin = 0;               // parallel: bins of the walk-order sort (n_f span of a region + 2)
+    int fwd_strategy = 1;           // parallel: 1 tile (region walk), 2 gather (per-view sorted walk)
+    int gat_ng = 0;                 // gather: groups of 16 steps per view (all pixels, multiple of 4)
+    int gat_segg = 0;               // gather: groups per segment (multiple of 4)
+    int gat_nseg = 0;               // gather: segments per view
     const int4 *bwin = nullptr;     // back windows [V][tiles][chunks] (n0, nw, m0, nrw)
     const int4 *fwin = nullptr;     // cone forward windows [V][tiles][chunks]
     int ntap = 0;                   // parallel: taps per record
@@ -58,6 +62,8 @@ hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, 
 hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st);
 hipError_t launch_par_region_records(const Geo &g, const int32_t *rec, uint32_t *out, int ntap, int rsx, int rsy,
                                     int nbin, hipStream_t st);
+hipError_t launch_par_view_records(const Geo &g, const int32_t *rec, int32_t *order, uint32_t *out, int ntap,
+                                  int ng, int segg, hipStream_t st);
 hipError_t launch_fill_zero(float *buf, int64_t n, hipStream_t st);
 
 // power 1: the adjoint of the forward; power 2: every tap weight squared

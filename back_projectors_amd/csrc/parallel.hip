@@ -318,6 +318,125 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
     }
 }
 
+// Gather strategy walk.  Same lanes (16 slices x 4 rows, a view per row),
+// ring accumulators, records and flushes as the region walk, but a row walks
+// one segment of its view's sorted pixel list (all pixels of the image), and
+// reads each step's voxels from the volume with a vector load (64 bytes per
+// row, cached).  A workgroup takes 64 consecutive views at one (segment, slice
+// chunk): their segments cover nearly the same pixels, which then come from
+// the cache.  The last step of every segment flushes all accumulators, so a
+// channel split between two segments is added once by each.
+// The voxels of group g + 1 are loaded while group g is summed, the
+// records three groups ahead; two voxel buffers and four record buffers rotate
+// without copies (the walk is unrolled by four groups).
+template <int K>
+__global__ __launch_bounds__(FRW * 64) void par_gather_kernel(const float *__restrict__ recon,
+                                                               float *__restrict__ facc,
+                                                               const uint32_t *__restrict__ wrec, Geo g, int cb,
+                                                               int s16, int ng, int segg, int nseg) {
+    constexpr int NF = 2 + K;
+    constexpr int PD = 3;                 // record groups in flight ahead of their use
+    const int lane = (int)threadIdx.x & 63;
+    const int row = lane >> 4, sl = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int nvb = (g.nv + 63) / 64;
+    const int vb = (int)(blockIdx.x % (unsigned)nvb) * 64;
+    const int rest = (int)(blockIdx.x / (unsigned)nvb);
+    const int seg = rest % nseg, chunk = rest / nseg;
+    const int k0 = chunk * 16;
+    const int g0 = seg * segg, g1 = min(ng, g0 + segg);    // both multiples of 4
+    const int q0 = vb + wave * 4;
+    if (q0 >= g.nv) return;
+    // each row walks its own view; views past the end walk the zero records of view nv
+    const int vrow = q0 + row < g.nv ? q0 + row : g.nv;
+    const uint32_t *rb = wrec + (int64_t)vrow * ng * NF * 16 + sl;
+    // lanes past the last slice read slice k0 (a valid address) and drop it:
+    // the loads stay unpredicated, so every lane is active for the DPP
+    // broadcasts that form their addresses (a DPP read from an inactive lane
+    // returns nothing)
+    const bool kin = k0 + sl < g.ns;
+    const char *xb = reinterpret_cast<const char *>(recon);
+    const uint32_t xl = (uint32_t)(k0 + (kin ? sl : 0)) * 4u;     // + p * S * 4 from the records
+    const uint32_t s4 = (uint32_t)s16 * 4u;
+    const uint32_t ks = (uint32_t)K * s4;
+    char *fv = reinterpret_cast<char *>(facc + (int64_t)vb * cb * s16);
+    uint32_t vbo[K];
+#pragma unroll
+    for (int r = 0; r < K; ++r)
+        vbo[r] = (uint32_t)(((min(vrow, g.nv - 1) - vb) * cb + (K - 1)) * s16 + k0) * 4u + (uint32_t)sl * 4u + r * s4 - ks;
+    float acc[K];
+#pragma unroll
+    for (int r = 0; r < K; ++r) acc[r] = 0.f;
+
+    auto load_group = [&](int gi, uint32_t (&R)[NF]) {
+        const uint32_t *b = rb + (int64_t)gi * NF * 16;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) R[f] = b[f * 16];
+    };
+    auto load_x = [&](const uint32_t (&R)[NF], float (&X)[16]) {
+        static_for(
+            [&](auto SC) {
+                constexpr int S = decltype(SC)::value;
+                const float xv = *reinterpret_cast<const float *>(xb + (row_bcast<S>(R[0]) + xl));
+                X[S] = kin ? xv : 0.f;
+            },
+            std::make_integer_sequence<int, 16>{});
+    };
+    // one group: fetch the records PD groups ahead into P and the voxels of the
+    // next group (records RN) into XN, then sum this group (records R, voxels X)
+    auto walk_group = [&](int gi, const uint32_t (&R)[NF], const uint32_t (&RN)[NF], uint32_t (&P)[NF],
+                          const float (&X)[16], float (&XN)[16]) {
+        load_group(min(gi + PD, g1 - 1), P);
+        load_x(RN, XN);
+        uint64_t m = __builtin_amdgcn_ballot_w64(R[1] != 0u);
+        m |= m >> 32;
+        m |= m >> 16;
+        const uint32_t fl = (uint32_t)m & 0xffffu;
+        static_for(
+            [&](auto SC) {
+                constexpr int S = decltype(SC)::value;
+#pragma unroll
+                for (int r = 0; r < K; r += 2) {
+                    if (r + 1 < K)
+                        fmac2_row_bcast<S>(acc[r], acc[r + 1 < K ? r + 1 : r], R[2 + r], R[r + 1 < K ? 3 + r : 2 + r],
+                                           X[S]);
+                    else
+                        fmac_row_bcast<S>(acc[r], R[2 + r], X[S]);
+                }
+                if (__builtin_expect((fl >> S) & 1u, 0)) {
+                    const uint32_t f = row_bcast_nb<S>(R[1]);
+                    const uint32_t t = f >> 14;
+#pragma unroll
+                    for (int r = 0; r < K; ++r) {
+                        if (f & (1u << r)) {
+                            const uint32_t turn = t + ((f >> (7 + r)) & 1u);
+                            unsafeAtomicAdd(reinterpret_cast<float *>(fv + (__umul24(turn, ks) + vbo[r])), acc[r]);
+                            acc[r] = 0.f;
+                        }
+                    }
+                }
+            },
+            std::make_integer_sequence<int, 16>{});
+    };
+
+    uint32_t R0[NF], R1[NF], R2[NF], R3[NF];
+    float XA[16], XB[16];
+    load_group(g0, R0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_group(min(g0 + 1, g1 - 1), R1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_group(min(g0 + 2, g1 - 1), R2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(R0, XA);
+    for (int gi = g0; gi < g1; gi += 4) {
+        walk_group(gi, R0, R1, R3, XA, XB);
+        walk_group(gi + 1, R1, R2, R0, XB, XA);
+        walk_group(gi + 2, R2, R3, R1, XA, XB);
+        walk_group(gi + 3, R3, R0, R2, XB, XA);
+    }
+    // every segment's last step flushes all accumulators (the records say so)
+}
+
 // facc [V][cb][s16] (slices fastest, K - 1 guard channels each side) ->
 // sino [V][R][C] (channels fastest), through a 64 x 64 LDS tile.
 __global__ __launch_bounds__(256) void par_unpack_kernel(const float *__restrict__ facc, float *__restrict__ sino,
@@ -398,20 +517,42 @@ hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, int p
     return power == 2 ? par_back_pow<2>(p, sino, recon, st) : par_back_pow<1>(p, sino, recon, st);
 }
 
+template <int K>
+static hipError_t par_gather_t(const Plan &p, const float *recon, hipStream_t st) {
+    const Geo &g = p.g;
+    const int nvb = (g.nv + 63) / 64;
+    const int64_t blocks = (int64_t)nvb * p.gat_nseg * ((g.ns + 15) / 16);
+    hipLaunchKernelGGL((par_gather_kernel<K>), dim3((unsigned)blocks), dim3(FRW * 64), 0, st, recon, p.facc, p.wrec, g,
+                       p.fwd_cb, p.fwd_s16, p.gat_ng, p.gat_segg, p.gat_nseg);
+    return hipGetLastError();
+}
+
 // Zero the accumulation buffer, walk, then unpack into the sinogram (which the
 // unpack writes in full, so the sinogram needs no fill of its own).
 hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st) {
     const Geo &g = p.g;
     hipError_t e = launch_fill_zero(p.facc, (int64_t)g.nv * p.fwd_cb * p.fwd_s16, st);
     if (e != hipSuccess) return e;
-    switch (p.ntap) {
-    case 2: e = par_fwd_t<2>(p, recon, st); break;
-    case 3: e = par_fwd_t<3>(p, recon, st); break;
-    case 4: e = par_fwd_t<4>(p, recon, st); break;
-    case 5: e = par_fwd_t<5>(p, recon, st); break;
-    case 6: e = par_fwd_t<6>(p, recon, st); break;
-    case 7: e = par_fwd_t<7>(p, recon, st); break;
-    default: return hipErrorInvalidValue;
+    if (p.fwd_strategy == 2) {
+        switch (p.ntap) {
+        case 2: e = par_gather_t<2>(p, recon, st); break;
+        case 3: e = par_gather_t<3>(p, recon, st); break;
+        case 4: e = par_gather_t<4>(p, recon, st); break;
+        case 5: e = par_gather_t<5>(p, recon, st); break;
+        case 6: e = par_gather_t<6>(p, recon, st); break;
+        case 7: e = par_gather_t<7>(p, recon, st); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (p.ntap) {
+        case 2: e = par_fwd_t<2>(p, recon, st); break;
+        case 3: e = par_fwd_t<3>(p, recon, st); break;
+        case 4: e = par_fwd_t<4>(p, recon, st); break;
+        case 5: e = par_fwd_t<5>(p, recon, st); break;
+        case 6: e = par_fwd_t<6>(p, recon, st); break;
+        case 7: e = par_fwd_t<7>(p, recon, st); break;
+        default: return hipErrorInvalidValue;
+        }
     }
     if (e != hipSuccess) return e;
     const int tn = (g.nc + 63) / 64;

@@ -95,7 +95,23 @@ typedef struct {
     double det_channel_offset;   /* detector centre offset, channels (usually 0) */
     double det_row_offset;       /* detector centre offset, rows (usually 0) */
     int32_t psf_radius;          /* taps on each side of the centre channel (and row), 1..4 */
+    int32_t forward_strategy;    /* parallel beam: PROJ_FORWARD_AUTO (0, chosen from the shapes),
+                                    PROJ_FORWARD_TILE (1) or PROJ_FORWARD_GATHER (2); cone: 0 */
 } proj_geometry;
+
+/*
+ * Parallel-beam forward strategies (MBIRJAX "Projector kernels" page,
+ * "Forward scatters, back gathers": a per-voxel scatter, or a reduction over
+ * voxels sorted by channel).  Both walk voxels in the order of their first tap
+ * channel, so every channel is finished in registers before it is added out:
+ *   TILE   -- a region of pixels is held on chip and walked for every view;
+ *             each finished channel is added once per (view, region).
+ *   GATHER -- per view every pixel, sorted by channel at creation; walks read
+ *             the voxels from memory, each channel is added about once per view.
+ * AUTO takes the choice from the shapes alone; both give the same sinogram up
+ * to the order of fp32 additions.
+ */
+enum { PROJ_FORWARD_AUTO = 0, PROJ_FORWARD_TILE = 1, PROJ_FORWARD_GATHER = 2 };
 
 /*
  * proj_create: validate the geometry, copy it to the device, run the fp64

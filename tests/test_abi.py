@@ -93,7 +93,20 @@ BAD = [
     ("nan distance", base_geo(**dict(CONE, source_iso=math.nan)), (8, 8, 4), (4, 6, 16), -1),
     ("index table too large", base_geo(num_views=40000, angles=np.zeros(40000)), (256, 256, 1),
      (40000, 1, 16), -2),
+    ("forward strategy 3", base_geo(forward_strategy=3), (8, 8, 4), (4, 4, 16), -1),
+    ("forward strategy -1", base_geo(forward_strategy=-1), (8, 8, 4), (4, 4, 16), -1),
+    ("cone forward strategy", base_geo(**dict(CONE, forward_strategy=2)), (8, 8, 4), (4, 6, 16), -1),
 ]
+
+
+@pytest.mark.parametrize("strategy,word", [(1, "tile:"), (2, "gather:")])
+def test_forward_strategy_is_honoured(bp, strategy, word):
+    """A forced parallel forward strategy shows in the plan; AUTO picks one."""
+    w = W.get("parallel-512x512x64-720v")
+    desc = bp.plan_query(dict(w.geometry(), forward_strategy=strategy), w.recon_shape, w.sino_shape)
+    assert word in desc
+    auto = bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape)
+    assert ("tile:" in auto) != ("gather:" in auto)
 
 
 @pytest.mark.parametrize("case", BAD, ids=lambda c: c[0])

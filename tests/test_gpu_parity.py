@@ -299,3 +299,40 @@ def test_full_back_squared_sampled_pixels(bp, orc, name, full_cache):
                                     [0, w.ny * w.nx - 1, (w.ny // 2) * w.nx + w.nx // 2]]))
     xo, ax = orc.back_pixels(g, y, pix, with_abs=True, power=2)
     assert_close(xg[pix], xo, ax, f"{name} back squared pixels")
+
+
+# ------------------------------------------ forward strategies (a8) ---
+PAR_SMALL = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL]
+
+
+@pytest.mark.parametrize("strategy", [1, 2], ids=["tile", "gather"])
+@pytest.mark.parametrize("w", PAR_SMALL, ids=lambda w: w.name)
+def test_small_forward_strategies(bp, orc, w, strategy):
+    """Both parallel forward strategies, forced, against the reference."""
+    note(f"forward strategy {strategy} {w.name}")
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    proj = bp.Projector(dict(w.geometry(), forward_strategy=strategy), w.recon_shape, w.sino_shape)
+    assert ("gather:" if strategy == 2 else "tile:") in proj.describe()
+    x, y = inputs(w)
+    yo, ay = orc.forward(g, x, with_abs=True)
+    yg = host(proj.forward(dev(x)))
+    assert_close(yg, yo, ay, f"{w.name} forward strategy {strategy}")
+    gap = adjoint_gap(yg, y, x, host(proj.back(dev(y))))
+    assert gap < ADJOINT, f"adjoint gap {gap:.2e}"
+    proj.close()
+
+
+@pytest.mark.parametrize("name", ["parallel-512x512x64-720v", "translation-512x512x32-64v"])
+def test_full_forward_gather_sampled_views(bp, orc, name, full_cache):
+    full_cache.clear()
+    torch.cuda.empty_cache()
+    w = W.get(name)
+    note(f"full gather forward {name}")
+    proj = bp.Projector(dict(w.geometry(), forward_strategy=2), w.recon_shape, w.sino_shape)
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    x = w.recon_input()
+    yg = host(proj.forward(dev(x)))
+    views = sorted({0, w.nv // 4 + 1, w.nv // 2, w.nv - 1})
+    yo, ay = orc.forward_views(g, x, views, with_abs=True)
+    assert_close(yg[views], yo, ay, f"{name} gather forward views {views}")
+    proj.close()
