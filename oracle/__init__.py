@@ -168,15 +168,62 @@ def forward_views(g: Geometry, x, views, with_abs: bool = False):
 
 
 def back_pixels(g: Geometry, y, pixels, with_abs: bool = False, power: int = 1):
+    """Back projection at the listed flat pixel ids p = i*Nx + j: row q is
+    pixel pixels[q]'s column of ``back``.  An id outside [0, Ny*Nx) is batch
+    padding (MBIRJAX "Sharding Overview", "Why cone beam projects whole
+    cylinders": padding must stay inert) and its row is zero."""
     if power not in (1, 2):
         raise ValueError("power must be 1 or 2")
     y = _f32(y, g.sino_shape)
-    pixels = np.ascontiguousarray(pixels, dtype=np.int64)
-    shape = (len(pixels), g.recon_shape[2])
-    x = np.empty(shape, dtype=np.float64)
-    a = np.empty(shape, dtype=np.float64) if with_abs else None
-    _load().orc_back_pixels_power(g.ref, y, power, len(pixels), pixels, x, a.ctypes.data if with_abs else None)
+    pixels = np.asarray(pixels, dtype=np.int64).reshape(-1)
+    ny, nx, ns = g.recon_shape
+    keep = np.flatnonzero((pixels >= 0) & (pixels < ny * nx))
+    sel = np.ascontiguousarray(pixels[keep])
+    shape = (len(pixels), ns)
+    x = np.zeros(shape, dtype=np.float64)
+    a = np.zeros(shape, dtype=np.float64) if with_abs else None
+    xs = np.empty((len(sel), ns), dtype=np.float64)
+    as_ = np.empty((len(sel), ns), dtype=np.float64) if with_abs else None
+    if len(sel):
+        _load().orc_back_pixels_power(g.ref, y, power, len(sel), sel, xs, as_.ctypes.data if with_abs else None)
+    x[keep] = xs
+    if with_abs:
+        a[keep] = as_
     return (x, a) if with_abs else x
+
+
+def forward_pixels(g: Geometry, pixels, cylinders, with_abs: bool = False):
+    """Forward projection of a batch of voxel cylinders (MBIRJAX "Sharding
+    Overview", "Why cone beam projects whole cylinders"): A x for the volume x
+    that is zero except that pixel pixels[q] (flat id i*Nx + j) holds
+    cylinders[q] (S voxels).  Ids outside [0, Ny*Nx) are padding and add
+    nothing, whatever their cylinders hold.  A repeated id adds its cylinders:
+    the q-th occurrence of each id goes into volume number q, each volume is
+    projected on its own and the projections are summed in fp64, so no input
+    is rounded on the way."""
+    ny, nx, ns = g.recon_shape
+    pixels = np.asarray(pixels, dtype=np.int64).reshape(-1)
+    cylinders = np.asarray(cylinders, dtype=np.float32).reshape(len(pixels), ns)
+    keep = np.flatnonzero((pixels >= 0) & (pixels < ny * nx))
+    y = np.zeros(g.sino_shape, dtype=np.float64)
+    ay = np.zeros(g.sino_shape, dtype=np.float64) if with_abs else None
+    seen: dict = {}
+    layers: list = []
+    for q in keep:
+        p = int(pixels[q])
+        r = seen.get(p, 0)
+        seen[p] = r + 1
+        if r == len(layers):
+            layers.append(np.zeros((ny * nx, ns), dtype=np.float32))
+        layers[r][p] = cylinders[q]
+    for layer in layers:
+        out = forward(g, layer.reshape(ny, nx, ns), with_abs=with_abs)
+        if with_abs:
+            y += out[0]
+            ay += out[1]
+        else:
+            y += out
+    return (y, ay) if with_abs else y
 
 
 def voxel_taps(g: Geometry, v, i, j, k):

@@ -417,3 +417,103 @@ def test_squared_back_single_voxel_axis_aligned(orc):
     out2 = orc.back(g2, y, power=2)
     assert out2[0, 0, 0] == 0.25 * 2.0 + 0.25 * 4.0
     assert out2[0, 1, 0] == 0.25 * 4.0 + 0.25 * 8.0
+
+
+# ------------------------------------------------------- batches of cylinders ---
+def _centroid(w, axis):
+    idx = np.arange(w.shape[axis], dtype=np.float64)
+    shape = [1] * w.ndim
+    shape[axis] = -1
+    return float((w * idx.reshape(shape)).sum() / w.sum())
+
+
+def test_pixel_batch_parallel_centroid_and_mass(orc):
+    """P-B: one listed pixel in a batch padded with NaN cylinders.  Per view
+    and row, a parallel voxel's taps carry mass cyl[k] dv^2/dch (every tap on
+    the detector).  With dch = cos 0.3 and views where max(|cos t|, |sin t|)
+    = cos 0.3 the footprint box is exactly one channel wide; the cells it
+    overlaps then have their weighted mean at the box centre
+    u = (x cos t + y sin t)/dch + (C-1)/2, x = (j - (Nx-1)/2) dv,
+    y = (i - (Ny-1)/2) dv, p = i Nx + j (for a box of whole width the offset
+    of each point from its cell centre averages to zero).  Ny != Nx, so a
+    transposed id fails."""
+    ny, nx, ns, nc = 7, 9, 3, 40
+    dch = math.cos(0.3)
+    angles = (0.3, -0.3, math.pi / 2 - 0.3, math.pi + 0.3, 1.5 * math.pi + 0.3)
+    g = orc.Geometry(geom_dict(angles=angles, dch=dch), (ny, nx, ns), (len(angles), ns, nc))
+    i, j = 2, 6
+    pix = np.array([-1, i * nx + j, ny * nx, -(2 ** 31), ny * nx + 5], np.int64)
+    cyl = np.full((len(pix), ns), np.nan, np.float32)
+    cyl[1] = [1.0, 2.5, 0.75]
+    y = orc.forward_pixels(g, pix, cyl)
+    assert np.isfinite(y).all()
+    x0, y0 = (j - (nx - 1) / 2), (i - (ny - 1) / 2)
+    for v, t in enumerate(angles):
+        u = (x0 * math.cos(t) + y0 * math.sin(t)) / dch + (nc - 1) / 2
+        for k in range(ns):
+            row = y[v, k]
+            assert abs(row.sum() - float(cyl[1, k]) / dch) < 1e-13
+            assert abs(_centroid(row, 0) - u) < 1e-12
+
+
+@pytest.mark.parametrize("w", [SMALL_CONE, SMALL_HELIX], ids=lambda w: w.name)
+def test_pixel_batch_cone_is_the_scattered_volume(orc, w):
+    """P-B (cone), the definition of a batch: listing pixel p = i Nx + j with
+    cylinder c projects the volume that holds c at (i, j, 0..S-1) and zero
+    elsewhere; the entries with ids outside [0, Ny Nx) hold inf and must
+    change nothing.  Ny != Nx for the first workload, so a transposed id
+    fails."""
+    g = make(orc, w)
+    ny, nx, ns = w.recon_shape
+    rng = np.random.default_rng(8)
+    i, j = ny - 3, 2
+    c = rng.standard_normal(ns).astype(np.float32)
+    x = np.zeros(w.recon_shape, np.float32)
+    x[i, j] = c
+    cyl = np.full((3, ns), np.inf, np.float32)
+    cyl[1] = c
+    got = orc.forward_pixels(g, [ny * nx, i * nx + j, -1], cyl)
+    assert np.array_equal(got, orc.forward(g, x))
+
+
+@pytest.mark.parametrize("w", [W.get(W.SMALL), SMALL_CONE, SMALL_HELIX], ids=lambda w: w.name)
+def test_pixel_batch_adjoint_with_repeats_and_padding(orc, w):
+    """P1 on batches: <A_B c, y> = <c, A_B^T y> for a batch B with repeated
+    ids and padding; the forward runs through the per-view forward and the back
+    through the per-pixel gather, two separate code paths."""
+    g = make(orc, w)
+    ny, nx, ns = w.recon_shape
+    rng = np.random.default_rng(21)
+    pix = rng.integers(0, ny * nx, 40)
+    pix[5] = pix[9] = pix[30]            # a pixel listed three times
+    pix[[3, 17, 38]] = [-1, ny * nx, 10 ** 9]
+    cyl = rng.standard_normal((len(pix), ns)).astype(np.float32)
+    y = rng.standard_normal(w.sino_shape).astype(np.float32)
+    fwd = orc.forward_pixels(g, pix, cyl)
+    bck = orc.back_pixels(g, y, pix)
+    assert not bck[[3, 17, 38]].any()
+    keep = np.ones(len(pix), bool)
+    keep[[3, 17, 38]] = False
+    lhs = float((fwd * y.astype(np.float64)).sum())
+    rhs = float((cyl[keep].astype(np.float64) * bck[keep]).sum())
+    assert abs(lhs - rhs) < 1e-12 * np.linalg.norm(fwd) * np.linalg.norm(y)
+
+
+def test_pixel_batch_repeats_add_and_full_list_is_the_volume(orc):
+    """P2 on batches: a pixel listed twice adds its cylinders (values on a
+    1/16 grid, so the sum is exact in fp32), and listing every pixel once, in
+    any order, is the forward of the whole volume."""
+    w = W.get(W.SMALL)
+    g = make(orc, w)
+    ny, nx, ns = w.recon_shape
+    rng = np.random.default_rng(5)
+    c1 = (rng.integers(-64, 64, ns) / 16.0).astype(np.float32)
+    c2 = (rng.integers(-64, 64, ns) / 16.0).astype(np.float32)
+    p = 17 * nx + 40
+    twice = orc.forward_pixels(g, [p, p], np.stack([c1, c2]))
+    once = orc.forward_pixels(g, [p], (c1 + c2)[None])
+    assert np.allclose(twice, once, rtol=0, atol=1e-12)
+    x = w.recon_input()
+    perm = rng.permutation(ny * nx)
+    full = orc.forward_pixels(g, perm, x.reshape(ny * nx, ns)[perm])
+    assert np.array_equal(full, orc.forward(g, x))
