@@ -9,7 +9,9 @@ call raises.
 Names follow the C ABI: ``proj_create`` -> :class:`Projector`,
 ``proj_forward`` -> :meth:`Projector.forward`, ``proj_back`` ->
 :meth:`Projector.back`, ``proj_back_squared`` -> :meth:`Projector.back_squared`,
-``proj_channel_index`` -> :meth:`Projector.channel_index`.
+``proj_channel_index`` -> :meth:`Projector.channel_index`,
+``proj_forward_pixels`` -> :meth:`Projector.forward_pixels`,
+``proj_back_pixels`` -> :meth:`Projector.back_pixels`.
 """
 from __future__ import annotations
 
@@ -39,7 +41,7 @@ STATUS = {
 
 # Every entry point include/proj.h declares.
 EXPORTS = ("proj_create", "proj_forward", "proj_back", "proj_back_squared", "proj_channel_index",
-           "proj_plan_query", "proj_destroy", "proj_status_string", "proj_last_error", "proj_describe")
+           "proj_forward_pixels", "proj_back_pixels", "proj_plan_query", "proj_destroy", "proj_status_string", "proj_last_error", "proj_describe")
 
 
 class ProjError(RuntimeError):
@@ -89,6 +91,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         fn.restype = ctypes.c_int
     lib.proj_channel_index.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    vp = ctypes.c_void_p
+    lib.proj_forward_pixels.argtypes = [vp, vp, ctypes.c_int64, vp, vp, vp]
+    lib.proj_forward_pixels.restype = ctypes.c_int
+    lib.proj_back_pixels.argtypes = [vp, vp, vp, ctypes.c_int64, vp, vp]
+    lib.proj_back_pixels.restype = ctypes.c_int
     lib.proj_channel_index.restype = ctypes.c_int
     lib.proj_plan_query.argtypes = [P(_Geometry), i64x3, i64x3, ctypes.c_char_p, ctypes.c_int]
     lib.proj_plan_query.restype = ctypes.c_int
@@ -227,6 +234,37 @@ class Projector:
                                            ctypes.c_void_p(out.data_ptr()),
                                            ctypes.c_void_p(_stream_ptr(torch, self.device, stream))),
                "proj_back_squared")
+        return out
+
+    def forward_pixels(self, pixels, cylinders, out=None, stream=None):
+        """``proj_forward_pixels``: sinogram (V, R, C) of a volume that is zero
+        except at the listed pixels.  ``pixels`` int32 (n,) flat ids i*Nx + j,
+        ids outside [0, Ny*Nx) are inert padding; ``cylinders`` (n, S)."""
+        torch = self._torch
+        n = int(pixels.shape[0]) if isinstance(pixels, torch.Tensor) and pixels.dim() == 1 else -1
+        self._tensor(pixels, (n,), torch.int32, "pixels")
+        self._tensor(cylinders, (n, self.recon_shape[2]), torch.float32, "cylinders")
+        out = self._empty(self.sino_shape, torch.float32) if out is None else \
+            self._tensor(out, self.sino_shape, torch.float32, "out")
+        _check(self._lib.proj_forward_pixels(self._h, ctypes.c_void_p(pixels.data_ptr()), n,
+                                             ctypes.c_void_p(cylinders.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                             ctypes.c_void_p(_stream_ptr(torch, self.device, stream))),
+               "proj_forward_pixels")
+        return out
+
+    def back_pixels(self, sino, pixels, out=None, stream=None):
+        """``proj_back_pixels``: the cylinders (n, S) of A^T sinogram at the
+        listed pixels; a padding id (outside [0, Ny*Nx)) gets zeros."""
+        torch = self._torch
+        self._tensor(sino, self.sino_shape, torch.float32, "sino")
+        n = int(pixels.shape[0]) if isinstance(pixels, torch.Tensor) and pixels.dim() == 1 else -1
+        self._tensor(pixels, (n,), torch.int32, "pixels")
+        shape = (n, self.recon_shape[2])
+        out = self._empty(shape, torch.float32) if out is None else self._tensor(out, shape, torch.float32, "out")
+        _check(self._lib.proj_back_pixels(self._h, ctypes.c_void_p(sino.data_ptr()),
+                                          ctypes.c_void_p(pixels.data_ptr()), n, ctypes.c_void_p(out.data_ptr()),
+                                          ctypes.c_void_p(_stream_ptr(torch, self.device, stream))),
+               "proj_back_pixels")
         return out
 
     def channel_index(self, out=None, stream=None):

@@ -70,6 +70,13 @@ hipError_t launch_fill_zero(float *buf, int64_t n, hipStream_t st);
 hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st);
 hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
 hipError_t par_forward_allow_lds(int ntap, size_t bytes);
+// the slice-fastest accumulation buffer -> the sinogram (parallel beam)
+hipError_t launch_par_unpack(const Plan &p, float *sino, hipStream_t st);
+// batches of voxel cylinders (entries outside [0, Ny*Nx) are inert padding)
+hipError_t launch_back_pixels(const Plan &p, const float *sino, const int32_t *pix, int n, float *cyl,
+                              hipStream_t st);
+hipError_t launch_forward_pixels(const Plan &p, const int32_t *pix, int n, const float *cyl, float *sino,
+                                 hipStream_t st);
 hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st);
 hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
 hipError_t cone_forward_allow_lds(int radius, int stride, size_t bytes);

@@ -555,6 +555,11 @@ hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hi
         }
     }
     if (e != hipSuccess) return e;
+    return launch_par_unpack(p, sino, st);
+}
+
+hipError_t launch_par_unpack(const Plan &p, float *sino, hipStream_t st) {
+    const Geo &g = p.g;
     const int tn = (g.nc + 63) / 64;
     hipLaunchKernelGGL(par_unpack_kernel, dim3((unsigned)(g.nv * tn), (g.nr + 63) / 64), dim3(256), 0, st, p.facc,
                        sino, g.nr, g.nc, p.fwd_cb, p.fwd_s16, p.ntap - 1, tn);

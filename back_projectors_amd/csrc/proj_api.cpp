@@ -615,6 +615,66 @@ proj_status proj_back_squared(proj_handle h, const float *sino_dev, float *recon
     return back_power(h, sino_dev, recon_dev, 2, hip_stream);
 }
 
+static proj_status check_batch(proj_handle h, const int32_t *pix, int64_t n, const void *cyl, const void *sino) {
+    if (!h) return fail(PROJ_ERR_INVALID_ARGUMENT, "null handle");
+    const int64_t ns = h->plan.g.ns;
+    if (n < 0) return fail(PROJ_ERR_INVALID_ARGUMENT, "negative batch size");
+    if (ns > 0 && n > (kMaxElems - 1) / ns) return fail(PROJ_ERR_UNSUPPORTED, "batch of n*S elements above 2^31");
+    if (n > 0 && !pix) return fail(PROJ_ERR_INVALID_ARGUMENT, "null pixel list");
+    if ((n * ns > 0 && !cyl) || (h->sino_elems > 0 && !sino))
+        return fail(PROJ_ERR_INVALID_ARGUMENT, "null data pointer");
+    const int64_t cb = n * ns * 4, pb = n * 4, sb = h->sino_elems * 4;
+    if (overlaps(cyl, cb, sino, sb) || overlaps(pix, pb, cyl, cb) || overlaps(pix, pb, sino, sb))
+        return fail(PROJ_ERR_ALIAS, "pixel list, cylinders and sino buffers overlap");
+    return ok();
+}
+
+proj_status proj_forward_pixels(proj_handle h, const int32_t *pixels_dev, int64_t n, const float *cyl_dev,
+                                float *sino_dev, void *hip_stream) {
+    const proj_status s0 = check_batch(h, pixels_dev, n, cyl_dev, sino_dev);
+    if (s0 != PROJ_OK) return s0;
+    if (h->sino_elems == 0) return ok();
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return device_fail(dg.err, "hipSetDevice");
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipError_t e;
+    if (h->plan.back_sl == 0 || n == 0 || h->plan.g.ns == 0) {
+        e = launch_fill_zero(sino_dev, h->sino_elems, st);       // nothing to project
+        if (e != hipSuccess) return device_fail(e, "zero fill");
+        return ok();
+    }
+    if (h->plan.g.kind == 0) {
+        e = hipStreamWaitEvent(st, h->fwd_done, 0);
+        if (e != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
+    }
+    e = launch_forward_pixels(h->plan, pixels_dev, (int)n, cyl_dev, sino_dev, st);
+    if (e != hipSuccess) return device_fail(e, "batch forward projection launch");
+    if (h->plan.g.kind == 0) {
+        e = hipEventRecord(h->fwd_done, st);
+        if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+    }
+    return ok();
+}
+
+proj_status proj_back_pixels(proj_handle h, const float *sino_dev, const int32_t *pixels_dev, int64_t n,
+                             float *cyl_dev, void *hip_stream) {
+    const proj_status s0 = check_batch(h, pixels_dev, n, cyl_dev, sino_dev);
+    if (s0 != PROJ_OK) return s0;
+    if (n == 0 || h->plan.g.ns == 0) return ok();
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return device_fail(dg.err, "hipSetDevice");
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipError_t e;
+    if (h->plan.back_sl == 0) {
+        e = launch_fill_zero(cyl_dev, n * h->plan.g.ns, st);     // no views or empty detector
+        if (e != hipSuccess) return device_fail(e, "zero fill");
+        return ok();
+    }
+    e = launch_back_pixels(h->plan, sino_dev, pixels_dev, (int)n, cyl_dev, st);
+    if (e != hipSuccess) return device_fail(e, "batch back projection launch");
+    return ok();
+}
+
 proj_status proj_channel_index(proj_handle h, int32_t *index_dev, void *hip_stream) {
     if (!h) return fail(PROJ_ERR_INVALID_ARGUMENT, "null handle");
     if (h->index_elems == 0) return ok();

@@ -154,6 +154,39 @@ proj_status proj_back(proj_handle h, const float *sino_dev, float *recon_dev, vo
 proj_status proj_back_squared(proj_handle h, const float *sino_dev, float *recon_dev, void *hip_stream);
 
 /*
+ * Projection of a batch of voxel cylinders (a cylinder is the S voxels of one
+ * recon pixel, all slices).  The MBIRJAX "Sharding Overview" page, section
+ * "Why cone beam projects whole cylinders", has the owner of a group of views
+ * collect the full cylinders of a batch of pixels and project them; the same
+ * page asks that the zeros that pad a batch to a fixed size stay exactly
+ * inert.
+ *
+ *   pixels_dev   device int32 [n]: flat recon pixel ids p = i*Nx + j.  An id
+ *                outside [0, Ny*Nx) marks a padding entry.  Ids may repeat.
+ *   n            batch size, n >= 0, n*S below 2^31.
+ *   cyl_dev      device float [n][S], slices fastest: entry i is the cylinder
+ *                of pixel pixels_dev[i].
+ *   sino_dev     device float [V][R][C].
+ *
+ * proj_forward_pixels: sino = A x, where x is zero except that pixel
+ * pixels_dev[i] holds cylinder i (a repeated id adds its cylinders).  A
+ * padding entry adds nothing whatever its cylinder holds (NaN included).  sino
+ * is overwritten.
+ *
+ * proj_back_pixels: cylinder i = row pixels_dev[i] of A^T sino (the pixel's
+ * column of proj_back's output); a padding entry's cylinder is written as
+ * zeros.
+ *
+ * Both are exact adjoints of each other on the listed pixels.  No buffer may
+ * overlap another.  Asynchronous on hip_stream.  These serve batches: their
+ * cost grows with n*S*V, not with the volume.
+ */
+proj_status proj_forward_pixels(proj_handle h, const int32_t *pixels_dev, int64_t n, const float *cyl_dev,
+                                float *sino_dev, void *hip_stream);
+proj_status proj_back_pixels(proj_handle h, const float *sino_dev, const int32_t *pixels_dev, int64_t n,
+                             float *cyl_dev, void *hip_stream);
+
+/*
  * proj_channel_index: copy the handle's channel-index table n_c[V][Ny*Nx]
  * (int32, round half to even of the fp64 channel coordinate) into index_dev.
  * Asynchronous on hip_stream.

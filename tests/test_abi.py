@@ -131,6 +131,9 @@ def test_null_arguments(bp):
     assert lib.proj_forward(None, None, None, None) == -1
     assert lib.proj_back(None, None, None, None) == -1
     assert lib.proj_channel_index(None, None, None) == -1
+    assert lib.proj_back_squared(None, None, None, None) == -1
+    assert lib.proj_forward_pixels(None, None, 0, None, None, None) == -1
+    assert lib.proj_back_pixels(None, None, None, 0, None, None) == -1
     lib.proj_destroy(None)                           # ignored
     assert lib.proj_describe(None, None, 0) == -1
 

@@ -336,3 +336,149 @@ def test_full_forward_gather_sampled_views(bp, orc, name, full_cache):
     yo, ay = orc.forward_views(g, x, views, with_abs=True)
     assert_close(yg[views], yo, ay, f"{name} gather forward views {views}")
     proj.close()
+
+
+# ------------------------------------------------ batches of voxel cylinders ---
+PADDING_IDS = (-1, -(2 ** 31), 2 ** 31 - 1)
+
+
+def batch(w, n, seed, repeats=True):
+    """n listed pixels of w: random ids (one pixel three times when
+    `repeats`), the first and last pixel, and padding entries (ids outside
+    [0, Ny*Nx)) whose cylinders hold NaN, inf and huge values."""
+    rng = np.random.default_rng(seed)
+    np_ = w.ny * w.nx
+    pix = rng.integers(0, np_, n).astype(np.int32)
+    pix[0], pix[-1] = 0, np_ - 1
+    if repeats:
+        pix[4] = pix[11] = pix[n // 2]
+    pad = np.array([1, 7, n - 3, n // 3])
+    pix[pad] = [np_, PADDING_IDS[0], PADDING_IDS[1], PADDING_IDS[2]]
+    cyl = rng.standard_normal((n, w.ns)).astype(np.float32)
+    cyl[pad[0]] = np.nan
+    cyl[pad[1]] = np.inf
+    cyl[pad[2]] = -3e38
+    cyl[pad[3], ::2] = np.nan
+    return pix, cyl, pad
+
+
+@pytest.mark.parametrize("w", SMALL_CASES, ids=lambda w: w.name)
+def test_small_pixel_batches(bp, orc, w):
+    note(f"pixel batches {w.name}")
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    pix, cyl, pad = batch(w, 203, seed=w.seed_x)       # 203: ragged against the waves per workgroup
+    _, y = inputs(w)
+    yo, ay = orc.forward_pixels(g, pix, cyl, with_abs=True)
+    yg = host(proj.forward_pixels(dev(pix), dev(cyl)))
+    assert np.isfinite(yg).all(), "padding leaked into the forward"
+    assert_close(yg, yo, ay, f"{w.name} forward of a batch")
+    xo, ax = orc.back_pixels(g, y, pix, with_abs=True)
+    xg = host(proj.back_pixels(dev(y), dev(pix)))
+    assert not xg[pad].any(), "padding rows must be zero"
+    assert_close(xg, xo, ax, f"{w.name} back at a batch")
+    keep = np.ones(len(pix), bool)
+    keep[pad] = False
+    lhs = float((yg.astype(np.float64) * y).sum())
+    rhs = float((cyl[keep].astype(np.float64) * xg[keep]).sum())
+    gap = abs(lhs - rhs) / (np.linalg.norm(yg) * np.linalg.norm(y))
+    assert gap < ADJOINT, f"batch adjoint gap {gap:.2e}"
+    proj.close()
+
+
+@pytest.mark.parametrize("w", [PAR_RAGGED, CONE_RAGGED, HELIX_SMALL], ids=lambda w: w.name)
+def test_pixel_batch_poison_padding_bitwise(bp, w):
+    """Padding is exactly inert: a single listed voxel among poisoned padding
+    entries gives the same bits as the voxel listed alone and as a batch with
+    zero padding (each sinogram cell then receives one contribution, so no
+    summation order is involved)."""
+    note(f"poisoned padding {w.name}")
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    p = (w.ny // 2) * w.nx + w.nx // 3
+    k = w.ns // 2
+    one = np.zeros((1, w.ns), np.float32)
+    one[0, k] = 1.75
+    alone = host(proj.forward_pixels(dev(np.array([p], np.int32)), dev(one)))
+    assert np.count_nonzero(alone) > 0
+    pix = np.full(64, -1, np.int32)
+    pix[1::3] = w.ny * w.nx
+    pix[37] = p
+    clean = np.zeros((64, w.ns), np.float32)
+    clean[37] = one[0]
+    poison = np.full((64, w.ns), np.nan, np.float32)
+    poison[::2] = np.inf
+    poison[37] = one[0]
+    a = host(proj.forward_pixels(dev(pix), dev(clean)))
+    b = host(proj.forward_pixels(dev(pix), dev(poison)))
+    assert np.array_equal(a, alone) and np.array_equal(b, alone)
+    # the back: the listed pixel's row does not depend on its neighbours in the list
+    _, y = inputs(w)
+    r1 = host(proj.back_pixels(dev(y), dev(np.array([p], np.int32))))
+    r64 = host(proj.back_pixels(dev(y), dev(pix)))
+    assert np.array_equal(r64[37], r1[0]) and not np.delete(r64, 37, axis=0).any()
+    proj.close()
+
+
+@pytest.mark.parametrize("w", [PAR_RAGGED, CONE_R2], ids=lambda w: w.name)
+def test_pixel_batch_of_every_pixel_is_the_volume(bp, orc, w):
+    """Listing every pixel once (shuffled) is the whole-volume projection: the
+    batch path matches the reference forward and back of the volume."""
+    note(f"every pixel as a batch {w.name}")
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    x, y = inputs(w)
+    perm = np.random.default_rng(3).permutation(w.ny * w.nx).astype(np.int32)
+    cyl = x.reshape(-1, w.ns)[perm]
+    yo, ay = orc.forward(g, x, with_abs=True)
+    assert_close(host(proj.forward_pixels(dev(perm), dev(cyl))), yo, ay, f"{w.name} batch of every pixel")
+    xo, ax = orc.back(g, y, with_abs=True)
+    xg = host(proj.back_pixels(dev(y), dev(perm)))
+    assert_close(xg, xo.reshape(-1, w.ns)[perm], ax.reshape(-1, w.ns)[perm], f"{w.name} back of every pixel")
+    proj.close()
+
+
+def test_pixel_batch_empty_and_all_padding(bp):
+    note("empty and all-padding batches")
+    for w in (PAR_RAGGED, CONE_RAGGED):
+        proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+        empty_i = torch.zeros(0, dtype=torch.int32, device="cuda:0")
+        empty_c = torch.zeros((0, w.ns), dtype=torch.float32, device="cuda:0")
+        out = torch.full(w.sino_shape, float("nan"), device="cuda:0")
+        proj.forward_pixels(empty_i, empty_c, out=out)
+        assert not host(out).any()
+        assert host(proj.back_pixels(dev(inputs(w)[1]), empty_i)).shape == (0, w.ns)
+        pix = np.array([-5, w.ny * w.nx, -1], np.int32)
+        out.fill_(float("nan"))
+        proj.forward_pixels(dev(pix), dev(np.full((3, w.ns), np.nan, np.float32)), out=out)
+        assert not host(out).any()
+        cyl = torch.full((3, w.ns), float("nan"), device="cuda:0")
+        proj.back_pixels(dev(inputs(w)[1]), dev(pix), out=cyl)
+        assert not host(cyl).any()
+        proj.close()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_pixel_batch_sampled(bp, orc, name, full_cache):
+    """A batch of 1000 distinct pixels (plus padding) at the full sizes: the
+    forward on sampled views against the reference forward of the scattered
+    volume, the back on sampled rows of the batch."""
+    w, proj, g = full_setup(bp, orc, name, full_cache)
+    note(f"full pixel batch {name}")
+    rng = np.random.default_rng(91)
+    pix = rng.permutation(w.ny * w.nx)[:1000].astype(np.int32)
+    pix[[10, 500]] = [-1, w.ny * w.nx]
+    cyl = rng.standard_normal((len(pix), w.ns)).astype(np.float32)
+    cyl[[10, 500]] = np.nan
+    yg = host(proj.forward_pixels(dev(pix), dev(cyl)))
+    x = np.zeros((w.ny * w.nx, w.ns), np.float32)
+    keep = (pix >= 0) & (pix < w.ny * w.nx)
+    x[pix[keep]] = cyl[keep]
+    views = sorted({0, w.nv // 3, w.nv - 1})
+    yo, ay = orc.forward_views(g, x.reshape(w.recon_shape), views, with_abs=True)
+    assert_close(yg[views], yo, ay, f"{name} batch forward views {views}")
+    y = w.sino_input()
+    xg = host(proj.back_pixels(dev(y), dev(pix)))
+    rows = np.r_[0:40, 500, len(pix) - 40:len(pix)]
+    xo, ax = orc.back_pixels(g, y, pix[rows], with_abs=True)
+    assert_close(xg[rows], xo, ax, f"{name} batch back rows")
+    assert not xg[[10, 500]].any()
