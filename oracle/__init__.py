@@ -69,6 +69,8 @@ def _load():
         lib.orc_forward_views.argtypes = [g, f32, ctypes.c_int32, i32, f64, ctypes.c_void_p]
         lib.orc_back_pixels.argtypes = [g, f32, ctypes.c_int32, i64, f64, ctypes.c_void_p]
         lib.orc_back_power.argtypes = [g, f32, ctypes.c_int, f64, ctypes.c_void_p]
+        lib.orc_forward_f64.argtypes = [g, f64, f64]
+        lib.orc_back_f64.argtypes = [g, f64, f64]
         lib.orc_back_pixels_power.argtypes = [g, f32, ctypes.c_int, ctypes.c_int32, i64, f64, ctypes.c_void_p]
         lib.orc_voxel_taps.argtypes = [g, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        i32, i32, f64, ctypes.c_int]
@@ -155,6 +157,23 @@ def back(g: Geometry, y, with_abs: bool = False, power: int = 1):
     a = np.empty(g.recon_shape, dtype=np.float64) if with_abs else None
     _load().orc_back_power(g.ref, y, power, x, a.ctypes.data if with_abs else None)
     return (x, a) if with_abs else x
+
+
+def forward_f64(g: Geometry, x) -> np.ndarray:
+    """Forward projection of an fp64 volume, read without rounding to fp32
+    (for solver iterates); the arithmetic is ``forward``'s."""
+    x = np.ascontiguousarray(x, dtype=np.float64).reshape(g.recon_shape)
+    y = np.empty(g.sino_shape, dtype=np.float64)
+    _load().orc_forward_f64(g.ref, x, y)
+    return y
+
+
+def back_f64(g: Geometry, y) -> np.ndarray:
+    """Back projection of an fp64 sinogram, read without rounding to fp32."""
+    y = np.ascontiguousarray(y, dtype=np.float64).reshape(g.sino_shape)
+    x = np.empty(g.recon_shape, dtype=np.float64)
+    _load().orc_back_f64(g.ref, y, x)
+    return x
 
 
 def forward_views(g: Geometry, x, views, with_abs: bool = False):

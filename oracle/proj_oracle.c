@@ -204,7 +204,7 @@ void orc_channel_coord(const orc_geom *g, double *out)
 /* Forward projection of one view into yv[R, C] (overwritten), with the
  * absolute sums av[R, C] = sum |w * x| when av is not NULL.  Loop order: pixels
  * ascending, then slices, then row taps, then channel taps. */
-static void forward_view(const orc_geom *g, const float *x, int32_t v, double *yv, double *av)
+static void forward_view(const orc_geom *g, const float *x, const double *xd, int32_t v, double *yv, double *av)
 {
     const int64_t nrc = (int64_t)g->nr * g->nc;
     const int r = g->radius;
@@ -216,9 +216,9 @@ static void forward_view(const orc_geom *g, const float *x, int32_t v, double *y
         for (int32_t j = 0; j < g->nx; ++j) {
             orc_vp o;
             vp_geometry(g, c, s, v, i, j, &o);
-            const float *xp = x + ((int64_t)i * g->nx + j) * g->ns;
+            const int64_t xo = ((int64_t)i * g->nx + j) * g->ns;
             for (int32_t k = 0; k < g->ns; ++k) {
-                double val = (double)xp[k];
+                double val = xd ? xd[xo + k] : (double)x[xo + k];
                 if (g->kind == 0) {
                     for (int tau = -r; tau <= r; ++tau) {
                         int32_t n = o.nc + tau;
@@ -256,7 +256,8 @@ static void forward_view(const orc_geom *g, const float *x, int32_t v, double *y
  * every tap weight is squared: the back projection the Hessian diagonal of a
  * least-squares fit uses ("Gradient and Hessian can take different paths",
  * coefficient power 2). */
-static void back_pixel(const orc_geom *g, const float *y, int power, int32_t i, int32_t j, double *xp, double *ap)
+static void back_pixel(const orc_geom *g, const float *y, const double *yd, int power, int32_t i, int32_t j,
+                       double *xp, double *ap)
 {
     const int64_t nrc = (int64_t)g->nr * g->nc;
     const int r = g->radius;
@@ -267,7 +268,7 @@ static void back_pixel(const orc_geom *g, const float *y, int power, int32_t i, 
         orc_vp o;
         view_trig(g, v, &c, &s);
         vp_geometry(g, c, s, v, i, j, &o);
-        const float *yv = y + (int64_t)v * nrc;
+        const int64_t yo = (int64_t)v * nrc;
         for (int32_t k = 0; k < g->ns; ++k) {
             if (g->kind == 0) {
                 for (int tau = -r; tau <= r; ++tau) {
@@ -275,7 +276,8 @@ static void back_pixel(const orc_geom *g, const float *y, int power, int32_t i, 
                     if (n < 0 || n >= g->nc) continue;
                     double w = o.len * ov((double)n - o.u, o.w);
                     if (power == 2) w = w * w;
-                    double t = w * (double)yv[(int64_t)k * g->nc + n];
+                    const int64_t at = yo + (int64_t)k * g->nc + n;
+                    double t = w * (yd ? yd[at] : (double)y[at]);
                     xp[k] += t;
                     if (ap) ap[k] += fabs(t);
                 }
@@ -293,7 +295,8 @@ static void back_pixel(const orc_geom *g, const float *y, int power, int32_t i, 
                         double h = ov((double)n - o.u, o.w);
                         double w = lk * h * gw;
                         if (power == 2) w = w * w;
-                        double t = w * (double)yv[(int64_t)m * g->nc + n];
+                        const int64_t at = yo + (int64_t)m * g->nc + n;
+                        double t = w * (yd ? yd[at] : (double)y[at]);
                         xp[k] += t;
                         if (ap) ap[k] += fabs(t);
                     }
@@ -309,7 +312,7 @@ void orc_forward(const orc_geom *g, const float *x, double *y, double *ay)
     const int64_t nrc = (int64_t)g->nr * g->nc;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int32_t v = 0; v < g->nviews; ++v)
-        forward_view(g, x, v, y + v * nrc, ay ? ay + v * nrc : NULL);
+        forward_view(g, x, NULL, v, y + v * nrc, ay ? ay + v * nrc : NULL);
 }
 
 /* Forward of selected views only: y[nsel, R, C]. */
@@ -319,7 +322,7 @@ void orc_forward_views(const orc_geom *g, const float *x, int32_t nsel, const in
     const int64_t nrc = (int64_t)g->nr * g->nc;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int32_t q = 0; q < nsel; ++q)
-        forward_view(g, x, views[q], y + q * nrc, ay ? ay + q * nrc : NULL);
+        forward_view(g, x, NULL, views[q], y + q * nrc, ay ? ay + q * nrc : NULL);
 }
 
 /* Full back projection: x[Ny, Nx, S] (fp64, overwritten); threads split
@@ -330,11 +333,31 @@ void orc_back_power(const orc_geom *g, const float *y, int power, double *x, dou
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t p = 0; p < np; ++p) {
         int32_t i = (int32_t)(p / g->nx), j = (int32_t)(p % g->nx);
-        back_pixel(g, y, power, i, j, x + p * g->ns, ax ? ax + p * g->ns : NULL);
+        back_pixel(g, y, NULL, power, i, j, x + p * g->ns, ax ? ax + p * g->ns : NULL);
     }
 }
 
 void orc_back(const orc_geom *g, const float *y, double *x, double *ax) { orc_back_power(g, y, 1, x, ax); }
+
+/* The same forward and back with fp64 inputs, for iterates that are not fp32
+ * data (the reference solvers): the arithmetic is the one above, only the
+ * input is read without a rounding to fp32. */
+void orc_forward_f64(const orc_geom *g, const double *x, double *y)
+{
+    const int64_t nrc = (int64_t)g->nr * g->nc;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t v = 0; v < g->nviews; ++v) forward_view(g, NULL, x, v, y + v * nrc, NULL);
+}
+
+void orc_back_f64(const orc_geom *g, const double *y, double *x)
+{
+    const int64_t np = (int64_t)g->ny * g->nx;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < np; ++p) {
+        int32_t i = (int32_t)(p / g->nx), j = (int32_t)(p % g->nx);
+        back_pixel(g, NULL, y, 1, i, j, x + p * g->ns, NULL);
+    }
+}
 
 /* Back projection of selected pixels only: x[nsel, S]. */
 void orc_back_pixels_power(const orc_geom *g, const float *y, int power, int32_t nsel, const int64_t *pix,
@@ -344,7 +367,7 @@ void orc_back_pixels_power(const orc_geom *g, const float *y, int power, int32_t
     for (int32_t q = 0; q < nsel; ++q) {
         int64_t p = pix[q];
         int32_t i = (int32_t)(p / g->nx), j = (int32_t)(p % g->nx);
-        back_pixel(g, y, power, i, j, x + (int64_t)q * g->ns, ax ? ax + (int64_t)q * g->ns : NULL);
+        back_pixel(g, y, NULL, power, i, j, x + (int64_t)q * g->ns, ax ? ax + (int64_t)q * g->ns : NULL);
     }
 }
 
