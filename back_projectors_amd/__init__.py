@@ -11,13 +11,16 @@ Names follow the C ABI: ``proj_create`` -> :class:`Projector`,
 :meth:`Projector.back`, ``proj_back_squared`` -> :meth:`Projector.back_squared`,
 ``proj_channel_index`` -> :meth:`Projector.channel_index`,
 ``proj_forward_pixels`` -> :meth:`Projector.forward_pixels`,
-``proj_back_pixels`` -> :meth:`Projector.back_pixels`.
+``proj_back_pixels`` -> :meth:`Projector.back_pixels`, ``proj_cgls`` ->
+:meth:`Projector.cgls`, ``proj_sirt`` -> :meth:`Projector.sirt` (with
+``proj_solver_workspace_size`` for their workspace).
 """
 from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Sequence
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
 
 import numpy as np
 
@@ -41,7 +44,28 @@ STATUS = {
 
 # Every entry point include/proj.h declares.
 EXPORTS = ("proj_create", "proj_forward", "proj_back", "proj_back_squared", "proj_channel_index",
-           "proj_forward_pixels", "proj_back_pixels", "proj_plan_query", "proj_destroy", "proj_status_string", "proj_last_error", "proj_describe")
+           "proj_forward_pixels", "proj_back_pixels", "proj_solver_workspace_size", "proj_cgls", "proj_sirt",
+           "proj_plan_query", "proj_destroy", "proj_status_string", "proj_last_error", "proj_describe")
+
+
+class _SolverInfo(ctypes.Structure):
+    _fields_ = [("iterations", ctypes.c_int32), ("converged", ctypes.c_int32), ("reason", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+STOP_REASONS = ("converged", "iterations", "stationary", "breakdown")
+
+
+@dataclass
+class SolverResult:
+    """What ``Projector.cgls`` and ``Projector.sirt`` return: the last iterate
+    (a device tensor), completed iterations, the residual norms (initial, then
+    one per iteration), whether the stop rule held, and why the loop ended."""
+    volume: object
+    iterations: int
+    residual_history: List[float] = field(default_factory=list)
+    converged: bool = False
+    reason: str = "iterations"
 
 
 class ProjError(RuntimeError):
@@ -96,6 +120,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.proj_forward_pixels.restype = ctypes.c_int
     lib.proj_back_pixels.argtypes = [vp, vp, vp, ctypes.c_int64, vp, vp]
     lib.proj_back_pixels.restype = ctypes.c_int
+    lib.proj_solver_workspace_size.argtypes = [vp, P(ctypes.c_int64)]
+    lib.proj_solver_workspace_size.restype = ctypes.c_int
+    d, i32, i64 = ctypes.c_double, ctypes.c_int32, ctypes.c_int64
+    lib.proj_cgls.argtypes = [vp, vp, vp, vp, vp, i64, i32, d, d, P(d), P(_SolverInfo), vp]
+    lib.proj_cgls.restype = ctypes.c_int
+    lib.proj_sirt.argtypes = [vp, vp, vp, vp, vp, i64, i32, d, d, d, i32, P(d), P(_SolverInfo), vp]
+    lib.proj_sirt.restype = ctypes.c_int
     lib.proj_channel_index.restype = ctypes.c_int
     lib.proj_plan_query.argtypes = [P(_Geometry), i64x3, i64x3, ctypes.c_char_p, ctypes.c_int]
     lib.proj_plan_query.restype = ctypes.c_int
@@ -179,6 +210,7 @@ class Projector:
         self.recon_shape = self._ga.recon_shape
         self.sino_shape = self._ga.sino_shape
         self.device = int(device)
+        self._work = None          # solver workspace, allocated on first use
         h = ctypes.c_void_p()
         _check(self._lib.proj_create(ctypes.byref(self._ga.s), self._ga.rs, self._ga.ss, self.device,
                                      ctypes.byref(h)), "proj_create")
@@ -267,6 +299,40 @@ class Projector:
                "proj_back_pixels")
         return out
 
+    def _solve(self, name, sino, iterations, atol, rtol, x0, out, stream, extra):
+        torch = self._torch
+        self._tensor(sino, self.sino_shape, torch.float32, "sino")
+        if x0 is not None:
+            self._tensor(x0, self.recon_shape, torch.float32, "x0")
+        out = self._empty(self.recon_shape, torch.float32) if out is None else \
+            self._tensor(out, self.recon_shape, torch.float32, "out")
+        nbytes = ctypes.c_int64()
+        _check(self._lib.proj_solver_workspace_size(self._h, ctypes.byref(nbytes)), "proj_solver_workspace_size")
+        if self._work is None or self._work.numel() < nbytes.value:
+            self._work = torch.empty(nbytes.value, dtype=torch.uint8, device=f"cuda:{self.device}")
+        iterations = int(iterations)
+        hist = (ctypes.c_double * (max(iterations, 0) + 1))()
+        info = _SolverInfo()
+        fn = getattr(self._lib, name)
+        _check(fn(self._h, ctypes.c_void_p(sino.data_ptr()), ctypes.c_void_p(x0.data_ptr() if x0 is not None else 0),
+                  ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(self._work.data_ptr()), self._work.numel(),
+                  iterations, float(atol), float(rtol), *extra, hist, ctypes.byref(info),
+                  ctypes.c_void_p(_stream_ptr(torch, self.device, stream))), name)
+        return SolverResult(out, info.iterations, list(hist[:info.iterations + 1]), bool(info.converged),
+                            STOP_REASONS[info.reason])
+
+    def cgls(self, sino, iterations, atol=0.0, rtol=0.0, x0=None, out=None, stream=None) -> SolverResult:
+        """``proj_cgls``: least squares by conjugate gradients, stopping when
+        ||y - A x|| <= atol + rtol ||y|| (the initial iterate included)."""
+        return self._solve("proj_cgls", sino, iterations, atol, rtol, x0, out, stream, ())
+
+    def sirt(self, sino, iterations, atol=0.0, rtol=0.0, x0=None, relaxation=1.0, nonnegative=True, out=None,
+             stream=None) -> SolverResult:
+        """``proj_sirt``: x += relaxation * C A^T R (y - A x), clamped at 0 when
+        ``nonnegative``; the same stop rule as ``cgls``."""
+        return self._solve("proj_sirt", sino, iterations, atol, rtol, x0, out, stream,
+                           (float(relaxation), int(bool(nonnegative))))
+
     def channel_index(self, out=None, stream=None):
         """``proj_channel_index``: int32 (V, Ny*Nx) channel index table."""
         torch = self._torch
@@ -290,6 +356,7 @@ class Projector:
         if getattr(self, "_h", None) is not None and self._h.value:
             self._lib.proj_destroy(self._h)
             self._h = ctypes.c_void_p()
+        self._work = None
 
     def __del__(self):
         try:

@@ -77,6 +77,28 @@ hipError_t launch_back_pixels(const Plan &p, const float *sino, const int32_t *p
                               hipStream_t st);
 hipError_t launch_forward_pixels(const Plan &p, const int32_t *pix, int n, const float *cyl, float *sino,
                                  hipStream_t st);
+// Solver vector steps (csrc/solver.hip).  The elementwise steps:  d, a, b are vectors of n floats; `red` (when not
+// null) receives one fp64 partial sum per block of the squared values noted.
+enum VecOp : int {
+    V_FILL = 0,      // d = value
+    V_COPY,          // d = a
+    V_RECIP,         // d = d > 0 ? 1/d : 0
+    V_NORM,          // red += a^2
+    V_SUB_NORM,      // d = a - b, red += d^2
+    V_AXPY,          // d = d + c b, c = sign sc[num]/sc[den]; red += d^2 when asked
+    V_XPBY,          // d = a + c d, c = sc[num]/sc[den]
+    V_SIRT_RES,      // e = a - d (a = y, d = A x), red += e^2, d = b e (b = row weights)
+    V_SIRT_UPD,      // d = d + value b a (b = column weights, a = back projection), clamped at 0 when flag
+                     // (AXPY, XPBY and SIRT_UPD compute in fp64 and round once)
+};
+
+constexpr int kVecMaxBlocks = 1024;   // partial sums per reduction at most
+// One vector step over n floats; when `red` is given, the per-block partial
+// sums go there and, when sc_out >= 0, their total into sc_w[sc_out].
+hipError_t launch_vec(int op, float *d, const float *a, const float *b, const double *sc, int num, int den,
+                      double sign, double value, int flag, int64_t n, double *red, int sc_out, double *sc_w,
+                      hipStream_t st);
+
 hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st);
 hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
 hipError_t cone_forward_allow_lds(int radius, int stride, size_t bytes);

@@ -187,6 +187,72 @@ proj_status proj_back_pixels(proj_handle h, const float *sino_dev, const int32_t
                              float *cyl_dev, void *hip_stream);
 
 /*
+ * Iterative reconstruction around the pair: CGLS and SIRT.  What they return
+ * and when they stop follows the diffct page "Precision, training and
+ * reconstruction", section "Numerical solver API":
+ *   - stop when ||y - A x|| <= atol + rtol ||y||, tested on the initial
+ *     iterate too (then no iteration runs);
+ *   - the residual history holds ||y - A x0|| and then one value per
+ *     completed iteration;
+ *   - SIRT has a relaxation factor and a nonnegativity switch, and feeds the
+ *     last residual into the next update (one forward and one back projection
+ *     per iteration);
+ *   - CGLS reads its two norms of an iteration (the residual and A^T of it)
+ *     together.
+ * The iterations themselves are the textbook ones, in fp32 vectors with fp64
+ * norms:
+ *   CGLS (Bjorck's least-squares arrangement of conjugate gradients):
+ *     r = y - A x, s = A^T r, p = s, gamma = ||s||^2; per iteration
+ *     q = A p, alpha = gamma/||q||^2, x += alpha p, r -= alpha q,
+ *     s = A^T r, p = s + (||s||^2/gamma) p;
+ *   SIRT: x += relaxation * C A^T R (y - A x), R = 1/(row sums of A),
+ *     C = 1/(column sums of A), 0 where a sum is 0, then x = max(x, 0) when
+ *     nonnegative.  R and C are computed at the start of each call (one
+ *     forward and one back projection of ones).
+ *
+ *   sino_dev      device float [V][R][C], the data y (read only).
+ *   x0_dev        device float [Ny][Nx][S] initial iterate, or NULL for 0;
+ *                 it may be recon_dev itself (a warm start in place), else it
+ *                 must not overlap any other buffer and is left unchanged.
+ *   recon_dev     device float [Ny][Nx][S], receives the last iterate.
+ *   work_dev      device workspace, 256-byte aligned, at least
+ *                 proj_solver_workspace_size() bytes (two sinogram-sized and
+ *                 two volume-sized fp32 vectors and a few KiB of fp64
+ *                 scalars); its contents on entry do not matter.
+ *   iterations    most iterations to run, >= 0.
+ *   atol, rtol    finite, >= 0.
+ *   relaxation    SIRT only: finite, > 0 (1 is the usual choice).
+ *   residual_history  host double [iterations + 1] or NULL; entries past
+ *                 info->iterations + 1 are not written.
+ *   info          host, receives iterations, converged and the stop reason.
+ * The calls block: they synchronise hip_stream once per iteration to read
+ * the residual norm, and return with the last iterate written.  They allocate
+ * nothing.  No buffer may overlap another (except x0_dev == recon_dev).
+ */
+typedef enum {
+    PROJ_STOP_CONVERGED = 0,   /* the stop rule held */
+    PROJ_STOP_ITERATIONS = 1,  /* the iteration limit was reached */
+    PROJ_STOP_STATIONARY = 2,  /* CGLS: A^T r is exactly 0 (the least-squares equations hold) */
+    PROJ_STOP_BREAKDOWN = 3    /* CGLS: A p is exactly 0 */
+} proj_stop_reason;
+
+typedef struct {
+    int32_t iterations;  /* completed iterations */
+    int32_t converged;   /* 1 when the stop rule held */
+    int32_t reason;      /* proj_stop_reason */
+    int32_t reserved;
+} proj_solver_info;
+
+proj_status proj_solver_workspace_size(proj_handle h, int64_t *bytes);
+proj_status proj_cgls(proj_handle h, const float *sino_dev, const float *x0_dev, float *recon_dev,
+                      void *work_dev, int64_t work_bytes, int32_t iterations, double atol, double rtol,
+                      double *residual_history, proj_solver_info *info, void *hip_stream);
+proj_status proj_sirt(proj_handle h, const float *sino_dev, const float *x0_dev, float *recon_dev,
+                      void *work_dev, int64_t work_bytes, int32_t iterations, double atol, double rtol,
+                      double relaxation, int32_t nonnegative, double *residual_history, proj_solver_info *info,
+                      void *hip_stream);
+
+/*
  * proj_channel_index: copy the handle's channel-index table n_c[V][Ny*Nx]
  * (int32, round half to even of the fp64 channel coordinate) into index_dev.
  * Asynchronous on hip_stream.

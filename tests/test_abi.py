@@ -134,6 +134,10 @@ def test_null_arguments(bp):
     assert lib.proj_back_squared(None, None, None, None) == -1
     assert lib.proj_forward_pixels(None, None, 0, None, None, None) == -1
     assert lib.proj_back_pixels(None, None, None, 0, None, None) == -1
+    assert lib.proj_solver_workspace_size(None, None) == -1
+    info = bp._SolverInfo()
+    assert lib.proj_cgls(None, None, None, None, None, 0, 1, 0.0, 0.0, None, ctypes.byref(info), None) == -1
+    assert lib.proj_sirt(None, None, None, None, None, 0, 1, 0.0, 0.0, 1.0, 1, None, ctypes.byref(info), None) == -1
     lib.proj_destroy(None)                           # ignored
     assert lib.proj_describe(None, None, 0) == -1
 
