@@ -1,0 +1,63 @@
+// Internals shared by the C-ABI sources: the handle, and the error and
+// argument helpers every entry point uses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/proj.h"
+#include "launch.h"
+
+namespace bpamd {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;      // work arrays stay below 2^31 elements
+
+// Record `why` as the calling thread's last error and return `s`.
+proj_status fail(proj_status s, const std::string &why);
+// Clear the last error and return PROJ_OK.
+proj_status ok();
+
+inline bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return na > 0 && nb > 0 && pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool switched = false;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) {
+            err = hipSetDevice(dev);
+            switched = err == hipSuccess;
+        }
+    }
+    ~DeviceGuard() {
+        if (switched) (void)hipSetDevice(prev);
+    }
+};
+
+inline proj_status device_fail(hipError_t e, const char *what) {
+    return fail(e == hipErrorOutOfMemory ? PROJ_ERR_OUT_OF_MEMORY : PROJ_ERR_DEVICE,
+                std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace bpamd
+
+struct proj_handle_s {
+    int device = 0;
+    bpamd::Plan plan;
+    int64_t recon_elems = 0, sino_elems = 0, index_elems = 0;
+    bpamd::ViewK *d_views = nullptr;
+    int32_t *d_idx = nullptr;
+    int32_t *d_rec = nullptr;       // parallel tap records
+    uint32_t *d_wrec = nullptr;     // parallel forward walk steps
+    float *d_facc = nullptr;        // parallel forward accumulation buffer (slices fastest)
+    hipEvent_t fwd_done = nullptr;  // parallel: last forward on this handle, orders calls that share d_facc
+    bpamd::Window *d_bwin = nullptr;       // back projection windows per (view, tile, chunk)
+    bpamd::Window *d_fwin = nullptr;       // cone forward windows per (view, tile, chunk)
+    size_t table_bytes = 0;
+};
