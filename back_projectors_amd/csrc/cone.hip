@@ -15,6 +15,8 @@
 // scale L_k.  The sinogram window a tile and slice chunk can reach in one view
 // is staged in LDS (rows fastest); the forward adds into an LDS-private window
 // and flushes it with coalesced global atomics, exactly as the parallel pair.
+#include <type_traits>
+
 #include "launch.h"
 #include "taps.h"
 
@@ -346,6 +348,9 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             lscq = cv.lsc;
             r2q = cv.r2;
         }
+        double dz2[P];
+#pragma unroll
+        for (int ph = 0; ph < P; ++ph) dz2[ph] = dzs[ph] * dzs[ph];
         uint64_t todo = __builtin_amdgcn_ballot_w64(act);
         while (todo) {
             const int q = (int)__builtin_ctzll(todo);
@@ -354,44 +359,65 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             float h[NTAP];
 #pragma unroll
             for (int t = 0; t < NTAP; ++t) h[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hq[t]), q));
-            const double mr = rl_d(mrq, q), lsc = rl_d(lscq, q), r2 = rl_d(r2q, q);
-            const double wrow = mr * g.dv;
-            float *col = win + (ncv - R - wd.n0) * nrp - wd.m0;
+            const double mr = rl_d(mrq, q), r2 = rl_d(r2q, q);
+            const float lscf = (float)rl_d(lscq, q);
+            // the row box: width mr dv, as half widths computed (not negated) so
+            // the clamps below take canonical operands
+            const double hw = 0.5 * (mr * g.dv), nhw = -0.5 * (mr * g.dv);
+            // this pixel's 2R+1 window columns
+            float *colt[NTAP];
+            colt[0] = win + (ncv - R - wd.n0) * nrp - wd.m0 - R;
 #pragma unroll
-            for (int ph = 0; ph < P; ++ph) {
-                const int kk = lane * P + ph;
-                const double t0 = mr * dzs[ph];
-                const double wk = t0 + g.crow;
-                const double mk = rint(wk);
-                const bool ok = kk < nk && mk >= -R && mk <= g.nr - 1 + R;
-                double gd[NTAP];
-                tap_weights_d<R>(wk - mk, wrow, gd);
-                const float xv = xt[(q * P + ph) * 64 + lane];
-                const float lk = (float)lsc * __builtin_amdgcn_sqrtf((float)(r2 + dzs[ph] * dzs[ph]));
-                float c[NTAP];
+            for (int t = 1; t < NTAP; ++t) colt[t] = colt[t - 1] + nrp;
+            // One slice of this lane: row, row taps (fp64, the clamped-edge form;
+            // with a box no wider than the 2R+1 taps the outermost clamps are the
+            // box edges themselves, so they are skipped), chord, then the
+            // (2R+1)^2 taps as plain read-modify-writes, one row offset per round:
+            // within a round the active lanes hold distinct rows, and a lane's
+            // next row overlaps its neighbour's previous one, hence the ordering
+            // fence between rounds (LDS operations issue in order; the fence
+            // stops the compiler from hoisting the next round's reads).
+            auto slice = [&](auto narrow_c) {
+                constexpr bool NARROW = decltype(narrow_c)::value;
 #pragma unroll
-                for (int sg = 0; sg < NTAP; ++sg) c[sg] = lk * (float)gd[sg] * xv;
-                float *cell = col + (ok ? (int)mk - R : 0);
-                // One row offset at a time: within a round the active lanes hold
-                // distinct rows and the channel taps distinct columns, so plain
-                // read-modify-writes are race free.  A lane's next row overlaps its
-                // neighbour's previous one, hence the ordering fence between rounds
-                // (the wave issues LDS operations in order; the fence stops the
-                // compiler from hoisting the next round's reads).
+                for (int ph = 0; ph < P; ++ph) {
+                    const int kk = lane * P + ph;
+                    const double t0 = mr * dzs[ph];
+                    const double wk = t0 + g.crow;
+                    const double mk = rint(wk);
+                    const bool ok = kk < nk && mk >= -R && mk <= g.nr - 1 + R;
+                    const double f = wk - mk;
+                    double gd[NTAP];
+                    double gp = NARROW ? nhw : fmin(fmax((-0.5 - (double)R) - f, nhw), hw);
 #pragma unroll
-                for (int sg = 0; sg < NTAP; ++sg) {
-                    if (ok) {
-                        float old[NTAP];
-#pragma unroll
-                        for (int t = 0; t < NTAP; ++t)
-                            if (h[t] != 0.f) old[t] = cell[t * nrp + sg];
-#pragma unroll
-                        for (int t = 0; t < NTAP; ++t)
-                            if (h[t] != 0.f) cell[t * nrp + sg] = fmaf(h[t], c[sg], old[t]);
+                    for (int t = 0; t < NTAP; ++t) {
+                        const double gn = (NARROW && t == NTAP - 1) ? hw : fmin(fmax(((double)(t - R) + 0.5) - f, nhw), hw);
+                        gd[t] = gn - gp;
+                        gp = gn;
                     }
-                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    const float xv = xt[(q * P + ph) * 64 + lane];
+                    const float lkx = lscf * __builtin_amdgcn_sqrtf((float)(r2 + dz2[ph])) * xv;
+                    float c[NTAP];
+#pragma unroll
+                    for (int sg = 0; sg < NTAP; ++sg) c[sg] = lkx * (float)gd[sg];
+                    const int mo = ok ? (int)mk : R;
+#pragma unroll
+                    for (int sg = 0; sg < NTAP; ++sg) {
+                        if (ok) {
+                            float old[NTAP];
+#pragma unroll
+                            for (int t = 0; t < NTAP; ++t) old[t] = colt[t][mo + sg];
+#pragma unroll
+                            for (int t = 0; t < NTAP; ++t) colt[t][mo + sg] = fmaf(h[t], c[sg], old[t]);
+                        }
+                        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    }
                 }
-            }
+            };
+            if (hw <= (double)R)
+                slice(std::true_type{});
+            else
+                slice(std::false_type{});
         }
         // add the window to the sinogram: lanes along channels, coalesced
         const int total = wd.nw * wd.nrw;
