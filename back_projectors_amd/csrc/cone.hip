@@ -76,9 +76,11 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
     const int tiles_x = (g.nx + BT - 1) / BT;
     const int ntiles = tiles_x * ((g.ny + BT - 1) / BT);
     const int nch = (g.ns + SL - 1) / SL;
-    const int tj0 = (int)(blockIdx.x % tiles_x) * BT;
-    const int ti0 = (int)(blockIdx.x / tiles_x) * BT;
-    const int k0 = (int)blockIdx.y * SL;
+    int tile, chunk;
+    xcd_work_item((int)gridDim.x, (int)gridDim.y, tile, chunk);
+    const int tj0 = (tile % tiles_x) * BT;
+    const int ti0 = (tile / tiles_x) * BT;
+    const int k0 = chunk * SL;
     const int nk = min(SL, g.ns - k0);
     const int tid = (int)threadIdx.x;
     const int wl = tid & 63;
@@ -98,8 +100,7 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
 
     auto fetch_view = [&](int v, uint32_t &pv) {
         const uint32_t *vkd = reinterpret_cast<const uint32_t *>(views + v);
-        const uint32_t *wd = reinterpret_cast<const uint32_t *>(wtab + ((int64_t)v * ntiles + blockIdx.x) * nch +
-                                                                 blockIdx.y);
+        const uint32_t *wd = reinterpret_cast<const uint32_t *>(wtab + ((int64_t)v * ntiles + tile) * nch + chunk);
         pv = wl < 18 ? vkd[wl] : (wl < 22 ? wd[wl - 18] : 0u);
     };
     auto win_of = [](uint32_t pv) {

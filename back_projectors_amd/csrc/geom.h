@@ -127,4 +127,21 @@ __host__ __device__ inline Window tile_window(const Geo &g, const ViewK &vk, int
     return w;
 }
 
+// The (tile, chunk) work item of this workgroup in a gx x gy grid, ordered for
+// the L2 caches: workgroups are dispatched to the 8 XCDs in turn by linear id
+// (id mod 8), and each XCD has its own L2, so the ids one XCD receives are
+// mapped to a contiguous run of the chunk-major, row-major tile list.  Tiles
+// that run together on one XCD are then neighbours whose detector windows
+// overlap, and they read them through one L2.  A bijection of the grid: any
+// other placement by the hardware is still correct, only slower.
+__device__ inline void xcd_work_item(int gx, int gy, int &tile, int &chunk) {
+    const int n = gx * gy;
+    const int lin = (int)blockIdx.y * gx + (int)blockIdx.x;
+    const int xcd = lin & 7, slot = lin >> 3;
+    const int q = n >> 3, r = n & 7;
+    const int w = xcd * q + (xcd < r ? xcd : r) + slot;
+    tile = w % gx;
+    chunk = w / gx;
+}
+
 }  // namespace bpamd

@@ -44,10 +44,11 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
 
     const int tiles_x = (g.nx + BT - 1) / BT;
     const int ntiles = tiles_x * ((g.ny + BT - 1) / BT);
-    const int tile = (int)blockIdx.x;
+    int tile, chunk;
+    xcd_work_item((int)gridDim.x, (int)gridDim.y, tile, chunk);
     const int tj0 = (tile % tiles_x) * BT;
     const int ti0 = (tile / tiles_x) * BT;
-    const int k0 = (int)blockIdx.y * SL;
+    const int k0 = chunk * SL;
     const int nk = min(SL, g.ns - k0);
 
     const int i = ti0 + (int)threadIdx.x / BT;
