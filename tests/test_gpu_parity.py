@@ -161,15 +161,20 @@ def test_empty_and_degenerate_shapes(bp):
 
 
 def test_single_voxel_matches_hand_value(bp):
-    """One unit voxel at theta = 0 lands whole in its channel (dv = 1)."""
-    note("single voxel")
-    geo = dict(kind=0, num_views=1, angles=np.array([0.0]), delta_channel=1.0)
-    p = bp.Projector(geo, (1, 1, 1), (1, 1, 11))
-    y = host(p.forward(torch.ones((1, 1, 1), device="cuda:0")))
-    expect = np.zeros((1, 1, 11), np.float32)
-    expect[0, 0, 5] = 1.0
-    assert np.array_equal(y, expect)
-    p.close()
+    """One unit voxel, the hand-worked taps of tests/golden/single_voxel_taps.txt:
+    fp32 weights rounded once from the fp64 closed forms."""
+    from golden_io import single_voxel_taps
+    note("single voxel golden taps")
+    for (th, off), taps in single_voxel_taps().items():
+        geo = dict(kind=0, num_views=1, angles=np.array([np.radians(th)]), channel_shift=np.array([off]),
+                   delta_channel=1.0)
+        p = bp.Projector(geo, (1, 1, 1), (1, 1, 11))
+        y = host(p.forward(torch.ones((1, 1, 1), device="cuda:0")))
+        expect = np.zeros((1, 1, 11), np.float32)
+        for n, wgt in taps.items():
+            expect[0, 0, n] = np.float32(wgt)
+        assert np.max(np.abs(y - expect)) <= 1e-7, (th, off, y)
+        p.close()
 
 
 # ------------------------------------------------------------ full sizes ---

@@ -120,6 +120,20 @@ def test_single_voxel_45_degrees(orc, d, expect):
         assert abs(got[n] - v) < 1e-15
 
 
+def test_single_voxel_golden_fixture(orc):
+    """The hand-worked single-voxel taps of ``tests/golden/single_voxel_taps.txt``
+    (0, 45 and 180 degrees, centred, half and quarter channel off)."""
+    from golden_io import single_voxel_taps
+    cases = single_voxel_taps()
+    assert len(cases) == 7
+    for (th, off), taps in cases.items():
+        _, y = one_voxel(orc, math.radians(th), off)
+        expect = np.zeros_like(y)
+        for n, wgt in taps.items():
+            expect[n] = wgt
+        assert np.max(np.abs(y - expect)) < 1e-15, (th, off, y)
+
+
 def test_tap_count_bounded_by_footprint(orc):
     """With W <= 1 at most two adjacent channels receive weight; the chosen
     channel n_c = rint(u) always carries weight."""
