@@ -250,13 +250,11 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                                                                  const int4 *__restrict__ wtab, Geo g, int nwcap,
                                                                  int nrp, int vsplit) {
     constexpr int NTAP = 2 * R + 1;
-    constexpr int TP = CTX * CTY;
     constexpr int CH = 64 * P;            // slices per chunk
     extern __shared__ float lds[];
-    float *xt = lds;                                   // [TP][P][64]
     const int lane = (int)threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    float *win = lds + TP * CH + wave * nwcap * nrp;   // this wave's window [nwcap][nrp]
+    float *win = lds + wave * nwcap * nrp;             // this wave's window [nwcap][nrp]
 
     const int tiles_x = (g.nx + CTX - 1) / CTX;
     const int ntiles = tiles_x * ((g.ny + CTY - 1) / CTY);
@@ -267,15 +265,7 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
     const int nk = min(CH, g.ns - k0);
     const int np = g.ny * g.nx;
 
-    for (int e = (int)threadIdx.x; e < TP * CH; e += CFW * 64) {
-        const int q = e / CH, kk = e - q * CH;
-        const int i = ti0 + q / CTX, j = tj0 + q % CTX;
-        float val = 0.f;
-        if (i < g.ny && j < g.nx && kk < nk) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + kk];
-        xt[(q * P + kk % P) * 64 + kk / P] = val;
-    }
     for (int e = lane; e < nwcap * nrp; e += 64) win[e] = 0.f;
-    __syncthreads();
 
     const int vper = (g.nv + vsplit - 1) / vsplit;
     const int vbeg = (int)blockIdx.z * vper;
@@ -352,10 +342,8 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         double dz2[P];
 #pragma unroll
         for (int ph = 0; ph < P; ++ph) dz2[ph] = dzs[ph] * dzs[ph];
-        uint64_t todo = __builtin_amdgcn_ballot_w64(act);
-        while (todo) {
-            const int q = (int)__builtin_ctzll(todo);
-            todo &= todo - 1;
+        // one pixel of the tile, its cylinder's voxels in xv
+        auto pixel = [&](int q, const float (&xv)[P]) {
             const int ncv = __builtin_amdgcn_readlane(pn, q);
             float h[NTAP];
 #pragma unroll
@@ -396,8 +384,7 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                         gd[t] = gn - gp;
                         gp = gn;
                     }
-                    const float xv = xt[(q * P + ph) * 64 + lane];
-                    const float lkx = lscf * __builtin_amdgcn_sqrtf((float)(r2 + dz2[ph])) * xv;
+                    const float lkx = lscf * __builtin_amdgcn_sqrtf((float)(r2 + dz2[ph])) * xv[ph];
                     float c[NTAP];
 #pragma unroll
                     for (int sg = 0; sg < NTAP; ++sg) c[sg] = lkx * (float)gd[sg];
@@ -419,6 +406,39 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                 slice(std::true_type{});
             else
                 slice(std::false_type{});
+        };
+        // The voxels come from memory (L2: the tile's cylinders are read by
+        // every view), the next pixel's while this one is projected, in two
+        // alternating register buffers (no copies, so the loads are waited for
+        // only where used).  Lanes past the chunk's last slice load nothing.
+        auto load_px = [&](int q, float (&xv)[P]) {
+            const float *src = recon + (int64_t)((ti0 + q / CTX) * g.nx + tj0 + q % CTX) * g.ns + k0;
+#pragma unroll
+            for (int ph = 0; ph < P; ++ph) {
+                const int kk = lane * P + ph;
+                xv[ph] = kk < nk ? src[kk] : 0.f;
+            }
+        };
+        uint64_t todo = __builtin_amdgcn_ballot_w64(act);
+        if (todo) {
+            float xa[P], xb[P];
+            int q = (int)__builtin_ctzll(todo);
+            todo &= todo - 1;
+            load_px(q, xa);
+            for (;;) {
+                const int qb = todo ? (int)__builtin_ctzll(todo) : q;
+                load_px(qb, xb);
+                pixel(q, xa);
+                if (!todo) break;
+                todo &= todo - 1;
+                q = qb;
+                const int qa = todo ? (int)__builtin_ctzll(todo) : q;
+                load_px(qa, xa);
+                pixel(q, xb);
+                if (!todo) break;
+                todo &= todo - 1;
+                q = qa;
+            }
         }
         // add the window to the sinogram: lanes along channels, coalesced
         const int total = wd.nw * wd.nrw;

@@ -278,7 +278,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         const WinMax wf = max_window(g, views, CTX, CTY, plan.fwd_sl);
         plan.fwd_nwcap = wf.nw + 2;
         plan.fwd_nrcap = (wf.nr + 2) | 1;
-        plan.fwd_lds = ((size_t)CTX * CTY * plan.fwd_sl + (size_t)CFW * plan.fwd_nwcap * plan.fwd_nrcap) * sizeof(float);
+        plan.fwd_lds = (size_t)CFW * plan.fwd_nwcap * plan.fwd_nrcap * sizeof(float);
     }
     if (plan.back_lds > kMaxLds || plan.fwd_lds > kMaxLdsOptIn) {
         char buf[160];
