@@ -45,6 +45,20 @@ inline proj_status device_fail(hipError_t e, const char *what) {
                 std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// The parallel forward's accumulation buffer belongs to the handle, so a
+// forward first waits on the GPU for the handle's previous one (an event; no
+// host synchronisation) and then records its own end.  While `st` is being
+// captured into a graph neither happens: an event recorded outside a capture
+// cannot be waited on inside it, and within a graph the captured launches are
+// ordered by the graph itself (two forwards on one handle must then not run
+// concurrently, the caller's ordering).
+inline hipError_t stream_capturing(hipStream_t st, bool &capturing) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(st, &cs);
+    capturing = e == hipSuccess && cs != hipStreamCaptureStatusNone;
+    return e;
+}
+
 }  // namespace bpamd
 
 struct proj_handle_s {

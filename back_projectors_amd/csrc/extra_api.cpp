@@ -37,13 +37,18 @@ proj_status proj_forward_pixels(proj_handle h, const int32_t *pixels_dev, int64_
         if (e != hipSuccess) return device_fail(e, "zero fill");
         return ok();
     }
+    bool capturing = false;
     if (h->plan.g.kind == 0) {
-        e = hipStreamWaitEvent(st, h->fwd_done, 0);
-        if (e != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
+        e = stream_capturing(st, capturing);
+        if (e != hipSuccess) return device_fail(e, "hipStreamIsCapturing");
+        if (!capturing) {
+            e = hipStreamWaitEvent(st, h->fwd_done, 0);
+            if (e != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
+        }
     }
     e = launch_forward_pixels(h->plan, pixels_dev, (int)n, cyl_dev, sino_dev, st);
     if (e != hipSuccess) return device_fail(e, "batch forward projection launch");
-    if (h->plan.g.kind == 0) {
+    if (h->plan.g.kind == 0 && !capturing) {
         e = hipEventRecord(h->fwd_done, st);
         if (e != hipSuccess) return device_fail(e, "hipEventRecord");
     }

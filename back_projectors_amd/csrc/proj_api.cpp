@@ -535,12 +535,19 @@ proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev,
     if (h->plan.g.kind == 0) {
         // the accumulation buffer belongs to the handle: a call on another
         // stream waits on the GPU for the previous one
-        e = hipStreamWaitEvent(st, h->fwd_done, 0);
-        if (e != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
+        bool capturing = false;
+        e = stream_capturing(st, capturing);
+        if (e != hipSuccess) return device_fail(e, "hipStreamIsCapturing");
+        if (!capturing) {
+            e = hipStreamWaitEvent(st, h->fwd_done, 0);
+            if (e != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
+        }
         e = launch_par_forward(h->plan, recon_dev, sino_dev, st);
         if (e != hipSuccess) return device_fail(e, "forward projection launch");
-        e = hipEventRecord(h->fwd_done, st);
-        if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+        if (!capturing) {
+            e = hipEventRecord(h->fwd_done, st);
+            if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+        }
         return ok();
     }
     e = launch_cone_forward(h->plan, recon_dev, sino_dev, st);
