@@ -226,9 +226,17 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         if ((int64_t)(plan.fwd_cb + 2 * plan.ntap) * plan.fwd_s16 * 4 >= ((int64_t)1 << 30))
             return fail(PROJ_ERR_UNSUPPORTED, "forward accumulation buffer too large per view");
         // gather strategy: every pixel of a view, in groups of 16 steps padded to
-        // a multiple of 4 groups, walked in segments of up to 144 groups
+        // a multiple of 4 groups, walked in segments of up to 144 groups; small
+        // problems take shorter segments (multiples of 4 groups) so that the
+        // grid of (64-view block, segment, 16-slice chunk) workgroups still
+        // counts about 512 where it can
         plan.gat_ng = (int)(((Ny * Nx + 63) / 64) * 4);
-        plan.gat_segg = std::min(plan.gat_ng, 144);
+        {
+            const int64_t nvb = (V + 63) / 64, nchk = (S + 15) / 16;
+            const int64_t want = (plan.gat_ng * nvb * nchk + 511) / 512;
+            const int64_t segg = std::max<int64_t>(4, std::min<int64_t>(((want + 3) / 4) * 4, 144));
+            plan.gat_segg = (int)std::min<int64_t>(segg, plan.gat_ng);
+        }
         plan.gat_nseg = (plan.gat_ng + plan.gat_segg - 1) / plan.gat_segg;
         const bool gather_ok = Ny * Nx * S * 4 < ((int64_t)1 << 32) &&
                                64 * (int64_t)(plan.fwd_cb + 2 * plan.ntap) * plan.fwd_s16 * 4 < ((int64_t)1 << 31);
