@@ -93,10 +93,25 @@ BAD = [
     ("nan distance", base_geo(**dict(CONE, source_iso=math.nan)), (8, 8, 4), (4, 6, 16), -1),
     ("index table too large", base_geo(num_views=40000, angles=np.zeros(40000)), (256, 256, 1),
      (40000, 1, 16), -2),
+    ("recon of 2^31 elements", base_geo(), (2048, 2048, 512), (4, 512, 16), -2),
+    ("sinogram of 2^31 elements", base_geo(num_views=8192, angles=np.zeros(8192)), (4, 4, 16), (8192, 16, 16384),
+     -2),
+    ("16384 channels", base_geo(), (8, 8, 4), (4, 4, 16384), -2),
+    ("detector 10x finer than voxels", base_geo(delta_channel=0.1), (8, 8, 4), (4, 4, 160), -2),
+    ("cone detector 20x finer", base_geo(**dict(CONE, delta_channel=0.05, delta_row=0.05)), (8, 8, 4), (4, 200, 400),
+     -2),
     ("forward strategy 3", base_geo(forward_strategy=3), (8, 8, 4), (4, 4, 16), -1),
     ("forward strategy -1", base_geo(forward_strategy=-1), (8, 8, 4), (4, 4, 16), -1),
     ("cone forward strategy", base_geo(**dict(CONE, forward_strategy=2)), (8, 8, 4), (4, 6, 16), -1),
 ]
+
+
+def test_largest_shapes_plan(bp):
+    """Shapes just inside the limits plan (no allocation here): a recon of
+    2^31 - 2^20 elements, psf radius 4."""
+    desc = bp.plan_query(base_geo(), (2048, 2047, 512), (4, 512, 4096))
+    assert "Ny=2048 Nx=2047 S=512" in desc
+    assert "radius=4" in bp.plan_query(base_geo(psf_radius=4), (8, 8, 4), (4, 4, 16))
 
 
 @pytest.mark.parametrize("strategy,word", [(1, "tile:"), (2, "gather:")])
