@@ -487,3 +487,31 @@ def test_full_pixel_batch_sampled(bp, orc, name, full_cache):
     xo, ax = orc.back_pixels(g, y, pix[rows], with_abs=True)
     assert_close(xg[rows], xo, ax, f"{name} batch back rows")
     assert not xg[[10, 500]].any()
+
+
+def test_largest_volume_mass_and_back_of_ones(bp):
+    """The largest parallel volume the planner accepts, 2048 x 2047 x 512
+    (2^31 - 2^20 voxels, so every address above 2^31 bytes is exercised), 4
+    views, a 4096-channel detector that every tap lands on: per view and row
+    the forward carries the slice's mass (dv^2/dch = 1 per voxel), and the back
+    projection of ones is 4 (the view count) at every voxel."""
+    geo = dict(kind=0, num_views=4, angles=np.array([0.0, 0.4, 1.3, 2.2]), delta_channel=1.0)
+    rs, ss = (2048, 2047, 512), (4, 512, 4096)
+    note(f"largest volume {rs} sino {ss}")
+    proj = bp.Projector(geo, rs, ss)
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(11)
+    x = torch.rand(rs, device="cuda:0", generator=gen)
+    y = proj.forward(x)
+    slice_mass = torch.sum(x, dim=(0, 1), dtype=torch.float64)          # [S]
+    row_mass = torch.sum(y, dim=2, dtype=torch.float64)                 # [V, R]
+    err = float(torch.max(torch.abs(row_mass - slice_mass[None, :]) / slice_mass[None, :]))
+    assert err < 1e-5, f"mass per view and row off by {err:.2e}"
+    del x
+    torch.cuda.empty_cache()
+    b = proj.back(torch.ones(ss, device="cuda:0"))
+    dev_max = float(torch.max(torch.abs(b - 4.0)))
+    assert dev_max < 1e-5, f"back projection of ones deviates from 4 by {dev_max:.2e}"
+    del b, y
+    proj.close()
+    torch.cuda.empty_cache()
