@@ -73,5 +73,6 @@ struct proj_handle_s {
     hipEvent_t fwd_done = nullptr;  // parallel: last forward on this handle, orders calls that share d_facc
     bpamd::Window *d_bwin = nullptr;       // back projection windows per (view, tile, chunk)
     bpamd::Window *d_fwin = nullptr;       // cone forward windows per (view, tile, chunk)
+    bpamd::Window *d_fslab = nullptr;      // cone forward active slices per (view, tile, chunk)
     size_t table_bytes = 0;
 };

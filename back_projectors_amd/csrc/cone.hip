@@ -242,12 +242,13 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
 // same cell (float atomics in LDS are avoided: on gfx950 they cost tens of
 // times a plain update).  The finished window is added to the sinogram with
 // coalesced global atomics, one per cell per view and tile.
-template <int R, int P>
+template <int R, int P, bool U>
 __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__restrict__ recon,
                                                                  float *__restrict__ sino,
                                                                  const int32_t *__restrict__ idx,
                                                                  const ViewK *__restrict__ views,
-                                                                 const int4 *__restrict__ wtab, Geo g, int nwcap,
+                                                                 const int4 *__restrict__ wtab,
+                                                                 const int4 *__restrict__ stab, Geo g, int nwcap,
                                                                  int nrp, int vsplit) {
     constexpr int NTAP = 2 * R + 1;
     constexpr int CH = 64 * P;            // slices per chunk
@@ -283,14 +284,18 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
 
     // Per-view data, fetched two views ahead with vector loads: lanes 0-17
     // hold the view's constants (ViewK, 18 dwords), lanes 18-21 its window,
-    // and every lane the channel index of its pixel.
+    // lanes 22-25 its slab, and every lane the channel index of its pixel.
     static_assert(sizeof(ViewK) == 72, "ViewK is read as 18 dwords");
     auto prefetch = [&](int it, uint32_t &pv, int &pn) {
         const int v = view_of(min(it, cnt - 1));    // always issued, for a static wait count
         const uint32_t *vkd = reinterpret_cast<const uint32_t *>(views + v);
-        const uint32_t *wd = reinterpret_cast<const uint32_t *>(wtab + ((int64_t)v * ntiles + blockIdx.x) * nch +
-                                                                 blockIdx.y);
-        pv = lane < 18 ? vkd[lane] : (lane < 22 ? wd[lane - 18] : 0u);
+        const int64_t te = ((int64_t)v * ntiles + blockIdx.x) * nch + blockIdx.y;
+        const uint32_t *wd = reinterpret_cast<const uint32_t *>(wtab + te);
+        const uint32_t *sd = reinterpret_cast<const uint32_t *>(stab + te);
+        if (U)
+            pv = lane < 18 ? vkd[lane] : (lane < 22 ? wd[lane - 18] : (lane < 26 ? sd[lane - 22] : 0u));
+        else
+            pv = lane < 18 ? vkd[lane] : (lane < 22 ? wd[lane - 18] : 0u);
         pn = lin ? idx[(int64_t)v * np + il * g.nx + jl] : INT32_MIN;
     };
     auto rl_d = [](double d, int q) {           // lane q's double, as a wave-uniform value
@@ -319,10 +324,15 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         wd.m0 = __builtin_amdgcn_readlane((int)pv, 20);
         wd.nrw = __builtin_amdgcn_readlane((int)pv, 21);
         if (wd.nw <= 0 || wd.nrw <= 0) return;
-        // per-lane slice offsets of this view
-        double dzs[P];
-#pragma unroll
-        for (int ph = 0; ph < P; ++ph) dzs[ph] = slice_z(g, k0 + lane * P + ph) - vk.zsrc;
+        // The chunk's slices that can reach the detector rows in this view
+        // (the slab, from the creation pass): with `unit`, lanes take
+        // consecutive slices from the first one, in `nit` passes of 64;
+        // otherwise lane l takes slices l*P + ph over the whole chunk.
+        // (Without slabs, U false: every chunk walks all its slices with stride P.)
+        const int klo = U ? __builtin_amdgcn_readlane((int)pv, 22) : 0;
+        const int nit = U ? __builtin_amdgcn_readlane((int)pv, 23) : P;
+        const bool unit = U && __builtin_amdgcn_readlane((int)pv, 24) != 0;
+        if (nit <= 0) return;                                 // no slice reaches the detector
         // this lane's pixel: channel taps and the per-(view, pixel) constants, fp64
         const bool act = pn >= -R && pn <= g.nc - 1 + R;
         float hq[NTAP];
@@ -338,6 +348,13 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             mrq = cv.mr;
             lscq = cv.lsc;
             r2q = cv.r2;
+        }
+        int kkv[P];                                           // this lane's slice in each pass
+        double dzs[P];
+#pragma unroll
+        for (int ph = 0; ph < P; ++ph) {
+            kkv[ph] = unit ? klo + ph * 64 + lane : lane * P + ph;
+            dzs[ph] = slice_z(g, k0 + kkv[ph]) - vk.zsrc;
         }
         double dz2[P];
 #pragma unroll
@@ -370,7 +387,8 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                 constexpr bool NARROW = decltype(narrow_c)::value;
 #pragma unroll
                 for (int ph = 0; ph < P; ++ph) {
-                    const int kk = lane * P + ph;
+                    if (U && ph >= nit) break;                    // uniform
+                    const int kk = kkv[ph];
                     const double t0 = mr * dzs[ph];
                     const double wk = t0 + g.crow;
                     const double mk = rint(wk);
@@ -415,8 +433,8 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             const float *src = recon + (int64_t)((ti0 + q / CTX) * g.nx + tj0 + q % CTX) * g.ns + k0;
 #pragma unroll
             for (int ph = 0; ph < P; ++ph) {
-                const int kk = lane * P + ph;
-                xv[ph] = kk < nk ? src[kk] : 0.f;
+                const int kk = kkv[ph];
+                xv[ph] = ((!U || ph < nit) && kk < nk) ? src[kk] : 0.f;
             }
         };
         uint64_t todo = __builtin_amdgcn_ballot_w64(act);
@@ -487,14 +505,21 @@ static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, in
     return hipGetLastError();
 }
 
-template <int R, int P>
-static hipError_t cone_fwd_t(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+template <int R, int P, bool U>
+static hipError_t cone_fwd_u(const Plan &p, const float *recon, float *sino, hipStream_t st) {
     const Geo &g = p.g;
     const int tiles = ((g.nx + CTX - 1) / CTX) * ((g.ny + CTY - 1) / CTY);
     const int chunks = (g.ns + 64 * P - 1) / (64 * P);
-    hipLaunchKernelGGL((cone_forward_kernel<R, P>), dim3(tiles, chunks, p.fwd_vsplit), dim3(CFW * 64), p.fwd_lds,
-                       st, recon, sino, p.idx, p.views, p.fwin, g, p.fwd_nwcap, p.fwd_nrcap, p.fwd_vsplit);
+    hipLaunchKernelGGL((cone_forward_kernel<R, P, U>), dim3(tiles, chunks, p.fwd_vsplit), dim3(CFW * 64), p.fwd_lds,
+                       st, recon, sino, p.idx, p.views, p.fwin, p.fslab, g, p.fwd_nwcap, p.fwd_nrcap,
+                       p.fwd_vsplit);
     return hipGetLastError();
+}
+
+template <int R, int P>
+static hipError_t cone_fwd_t(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+    if (p.cone_unit) return cone_fwd_u<R, P, true>(p, recon, sino, st);
+    return cone_fwd_u<R, P, false>(p, recon, sino, st);
 }
 
 template <int R>
@@ -538,13 +563,19 @@ hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, h
 // Dynamic LDS above the default limit needs the opt-in attribute.
 hipError_t cone_forward_allow_lds(int radius, int stride, size_t bytes) {
     const void *f = nullptr;
-#define BPAMD_CF(RR, PP) \
-    if (radius == RR && stride == PP) f = (const void *)cone_forward_kernel<RR, PP>;
+    const void *fu = nullptr;
+#define BPAMD_CF(RR, PP)                                                                                      \
+    if (radius == RR && stride == PP) {                                                                       \
+        f = (const void *)cone_forward_kernel<RR, PP, false>;                                                 \
+        fu = (const void *)cone_forward_kernel<RR, PP, true>;                                                 \
+    }
     BPAMD_CF(1, 1) BPAMD_CF(1, 2) BPAMD_CF(1, 3) BPAMD_CF(2, 1) BPAMD_CF(2, 2) BPAMD_CF(2, 3)
     BPAMD_CF(3, 1) BPAMD_CF(3, 2) BPAMD_CF(3, 3) BPAMD_CF(4, 1) BPAMD_CF(4, 2) BPAMD_CF(4, 3)
 #undef BPAMD_CF
     if (!f) return hipErrorInvalidValue;
-    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(fu, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 }  // namespace bpamd

@@ -28,6 +28,7 @@ struct Plan {
     int gat_nseg = 0;               // gather: segments per view
     const int4 *bwin = nullptr;     // back windows [V][tiles][chunks] (n0, nw, m0, nrw)
     const int4 *fwin = nullptr;     // cone forward windows [V][tiles][chunks]
+    const int4 *fslab = nullptr;    // cone forward slabs [V][tiles][chunks] (first slice, passes, unit stride, 0)
     int ntap = 0;                   // parallel: taps per record
 
     // back projection: lanes = pixels of a BT x BT tile, SL slices per lane
@@ -44,6 +45,7 @@ struct Plan {
     size_t fwd_lds = 0;
     int fwd_vsplit = 1;             // view ranges per tile (grid z)
     int cone_stride = 1;            // cone forward: slices between the lanes of one instruction
+    int cone_unit = 0;              // cone forward: some slab saves work (the slab-reading kernel)
 };
 
 constexpr int BT = 16;   // back tile edge (pixels), 256 threads

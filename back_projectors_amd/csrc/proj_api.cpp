@@ -100,6 +100,61 @@ WinMax window_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int 
     return m;
 }
 
+// Cone forward slabs of every (view, tile, slice chunk), in the window
+// table's order: the chunk's slices whose rows can reach the detector in that
+// view, conservatively for every pixel of the tile (rows within half a row of
+// [-r, R - 1 + r], a slice of margin each side; the kernel still tests each
+// slice exactly), as (first slice, passes, unit stride, 0).  With the tile's
+// smallest row magnification at least one, consecutive slices fall on
+// distinct rows, and lanes may take consecutive slices from the first one;
+// that is used when it needs fewer passes than the planned stride.  Zero
+// passes: no slice of the chunk reaches the detector in that view.
+void slab_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_, int sl, int stride,
+                std::vector<Window> *out) {
+    const int ty = (g.ny + ty_ - 1) / ty_, tx = (g.nx + tx_ - 1) / tx_;
+    const int nch = (g.ns + sl - 1) / sl;
+    out->resize((size_t)g.nv * ty * tx * nch);
+    const double wlo = (-0.5 - g.radius) - g.crow, whi = (g.nr - 1 + g.radius + 0.5) - g.crow;
+    size_t e = 0;
+    for (int v = 0; v < g.nv; ++v)
+        for (int a = 0; a < ty; ++a)
+            for (int b = 0; b < tx; ++b) {
+                const int i0 = a * ty_, i1 = std::min(i0 + ty_, g.ny) - 1;
+                const int j0 = b * tx_, j1 = std::min(j0 + tx_, g.nx) - 1;
+                const ViewK &vk = views[v];
+                double dmin = 1e300, dmax = -1e300;
+                for (int ii : {i0, i1})
+                    for (int jj : {j0, j1}) {
+                        const double d = g.sid + (pix_y(g, ii) * vk.c - pix_x(g, jj) * vk.s);
+                        dmin = std::min(dmin, d);
+                        dmax = std::max(dmax, d);
+                    }
+                const double mlo = g.sdd / (dmax * g.drow), mhi = g.sdd / (dmin * g.drow);
+                const double dz[4] = {wlo / mlo, wlo / mhi, whi / mlo, whi / mhi};
+                const double zlo = *std::min_element(dz, dz + 4) + vk.zsrc;
+                const double zhi = *std::max_element(dz, dz + 4) + vk.zsrc;
+                const double kglo = std::floor(zlo / g.dv + g.cz) - 1.0, kghi = std::ceil(zhi / g.dv + g.cz) + 1.0;
+                for (int c = 0; c < nch; ++c, ++e) {
+                    const int k0 = c * sl, nk = std::min(sl, g.ns - k0);
+                    const double lo = std::max(kglo - k0, 0.0), hi = std::min(kghi - k0, (double)nk - 1.0);
+                    Window s;
+                    s.n0 = 0;
+                    s.nw = 0;
+                    s.m0 = 0;
+                    s.nrw = 0;
+                    if (hi >= lo) {
+                        const int klo = (int)lo, nact = (int)hi - klo + 1;
+                        const int nit_unit = (nact + 63) / 64;
+                        const bool unit = stride > 1 && mlo >= 1.0 + 1e-9 && nit_unit < stride;
+                        s.n0 = unit ? klo : 0;
+                        s.nw = unit ? nit_unit : stride;
+                        s.m0 = unit ? 1 : 0;
+                    }
+                    (*out)[e] = s;
+                }
+            }
+}
+
 WinMax max_window(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_, int sl) {
     return window_table(g, views, tx_, ty_, sl, nullptr);
 }
@@ -476,9 +531,15 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
         }
         if (plan.back_sl > 0) {
             // every (view, tile, chunk) window, from the same code that sized the plan
-            std::vector<Window> bw, fw;
+            std::vector<Window> bw, fw, fs;
             window_table(geo, views, BT, BT, plan.back_sl, &bw);
-            if (geo.kind != 0) window_table(geo, views, CTX, CTY, plan.fwd_sl, &fw);
+            if (geo.kind != 0) {
+                window_table(geo, views, CTX, CTY, plan.fwd_sl, &fw);
+                slab_table(geo, views, CTX, CTY, plan.fwd_sl, plan.cone_stride, &fs);
+                // the slab-reading kernel when some slab saves work (a unit-stride
+                // walk, or a chunk that misses the detector in a view)
+                for (const Window &w : fs) h->plan.cone_unit |= (w.m0 != 0 || w.nw == 0) ? 1 : 0;
+            }
             e = hipMalloc((void **)&h->d_bwin, bw.size() * sizeof(Window));
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(windows)");
             e = hipMemcpy(h->d_bwin, bw.data(), bw.size() * sizeof(Window), hipMemcpyHostToDevice);
@@ -488,8 +549,12 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(windows)");
                 e = hipMemcpy(h->d_fwin, fw.data(), fw.size() * sizeof(Window), hipMemcpyHostToDevice);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(windows)");
+                e = hipMalloc((void **)&h->d_fslab, fs.size() * sizeof(Window));
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(slabs)");
+                e = hipMemcpy(h->d_fslab, fs.data(), fs.size() * sizeof(Window), hipMemcpyHostToDevice);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMemcpy(slabs)");
             }
-            rec_bytes += (bw.size() + fw.size()) * sizeof(Window);
+            rec_bytes += (bw.size() + fw.size() + fs.size()) * sizeof(Window);
         }
         if (geo.kind != 0 && plan.fwd_sl > 0 && plan.fwd_lds > kMaxLds) {
             int lim = 0;
@@ -510,6 +575,7 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
         h->plan.facc = h->d_facc;
         h->plan.bwin = reinterpret_cast<const int4 *>(h->d_bwin);
         h->plan.fwin = reinterpret_cast<const int4 *>(h->d_fwin);
+        h->plan.fslab = reinterpret_cast<const int4 *>(h->d_fslab);
         if (std::getenv("PROJ_LOG")) {
             char buf[512];
             describe(h->plan, (int64_t)h->table_bytes, buf, sizeof buf);
@@ -618,6 +684,7 @@ void proj_destroy(proj_handle h) {
         if (h->fwd_done) (void)hipEventDestroy(h->fwd_done);
         if (h->d_bwin) (void)hipFree(h->d_bwin);
         if (h->d_fwin) (void)hipFree(h->d_fwin);
+        if (h->d_fslab) (void)hipFree(h->d_fslab);
         if (h->d_views) (void)hipFree(h->d_views);
     }
     delete h;
