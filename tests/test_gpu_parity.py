@@ -58,7 +58,16 @@ CONE_R2 = W.Workload("cone-20x24x18-11v-r2", W.CONE_FLAT, 20, 24, 18, 11, 30, 50
 HELIX_SMALL = W.Workload("helical-36x36x40-47v", W.CONE_FLAT, 36, 36, 40, 47, 12, 60, dch=11 / 6,
                          drow=11 / 6, sid=45.0, sdd=82.5, angle_step=2 * math.pi / 20, zsrc_step=0.6,
                          seed_x=33, seed_y=34)
-SMALL_CASES = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, CONE_RAGGED, CONE_R2, HELIX_SMALL]
+# larger psf radii: 4 channel taps on a fine parallel detector; cone radii 3
+# and 4 (their outer taps carry no weight here, the code paths are what counts)
+PAR_R4 = W.Workload("parallel-30x26x11-19v-fine-r4", W.PARALLEL, 30, 26, 11, 19, 11, 120, dch=0.45, radius=4,
+                    seed_x=41, seed_y=42)
+CONE_R3 = W.Workload("cone-22x26x20-13v-r3", W.CONE_FLAT, 22, 26, 20, 13, 40, 70, dch=1.0, drow=1.0, sid=50.0,
+                     sdd=80.0, radius=3, seed_x=43, seed_y=44)
+CONE_R4 = W.Workload("cone-22x26x20-13v-r4", W.CONE_FLAT, 22, 26, 20, 13, 40, 70, dch=1.5, drow=1.5, sid=50.0,
+                     sdd=80.0, radius=4, seed_x=45, seed_y=46)
+SMALL_CASES = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, PAR_R4, CONE_RAGGED, CONE_R2, CONE_R3,
+               CONE_R4, HELIX_SMALL]
 
 
 def inputs(w):
