@@ -105,8 +105,9 @@ WinMax window_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int 
 // view, conservatively for every pixel of the tile (rows within half a row of
 // [-r, R - 1 + r], a slice of margin each side; the kernel still tests each
 // slice exactly), as (first slice, passes, unit stride, 0).  With the tile's
-// smallest row magnification at least one, consecutive slices fall on
-// distinct rows, and lanes may take consecutive slices from the first one;
+// smallest row advance per slice (magnification times the voxel pitch) at
+// least one, consecutive slices fall on distinct rows, and lanes may take
+// consecutive slices from the first one;
 // that is used when it needs fewer passes than the planned stride.  Zero
 // passes: no slice of the chunk reaches the detector in that view.
 void slab_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_, int sl, int stride,
@@ -145,7 +146,8 @@ void slab_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_,
                     if (hi >= lo) {
                         const int klo = (int)lo, nact = (int)hi - klo + 1;
                         const int nit_unit = (nact + 63) / 64;
-                        const bool unit = stride > 1 && mlo >= 1.0 + 1e-9 && nit_unit < stride;
+                        // consecutive slices are dv apart: their rows differ by mr dv
+                        const bool unit = stride > 1 && mlo * g.dv >= 1.0 + 1e-9 && nit_unit < stride;
                         s.n0 = unit ? klo : 0;
                         s.nw = unit ? nit_unit : stride;
                         s.m0 = unit ? 1 : 0;

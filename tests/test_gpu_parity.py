@@ -559,3 +559,31 @@ def test_largest_volume_mass_and_back_of_ones(bp):
     del b, y
     proj.close()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("w,dv", [(CONE_RAGGED, 1.25), (HELIX_SMALL, 0.9), (PAR_RAGGED, 0.8)],
+                         ids=["cone", "helical", "parallel"])
+def test_offsets_shifts_and_voxel_pitch(bp, orc, w, dv):
+    """Geometry parameters the workloads leave at their defaults: a voxel pitch
+    other than 1, detector channel and row offsets, and a lateral detector
+    shift per view."""
+    note(f"offsets {w.name} dv={dv}")
+    rng = np.random.default_rng(51)
+    geo = dict(w.geometry(), delta_voxel=dv, det_channel_offset=2.3,
+               det_row_offset=-1.7 if w.kind == W.CONE_FLAT else 0.0,
+               channel_shift=rng.uniform(-3.0, 3.0, w.nv))
+    if w.kind == W.PARALLEL:
+        geo["delta_row"] = dv                      # parallel: one row per slice
+    g = orc.Geometry(geo, w.recon_shape, w.sino_shape)
+    proj = bp.Projector(geo, w.recon_shape, w.sino_shape)
+    x, y = inputs(w)
+    assert np.array_equal(host(proj.channel_index()), orc.channel_index(g))
+    yo, ay = orc.forward(g, x, with_abs=True)
+    yg = host(proj.forward(dev(x)))
+    assert_close(yg, yo, ay, f"{w.name} forward with offsets")
+    xo, ax = orc.back(g, y, with_abs=True)
+    xg = host(proj.back(dev(y)))
+    assert_close(xg, xo, ax, f"{w.name} back with offsets")
+    gap = adjoint_gap(yg, y, x, xg)
+    assert gap < ADJOINT, f"adjoint gap {gap:.2e}"
+    proj.close()
