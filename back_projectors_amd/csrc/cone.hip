@@ -56,10 +56,10 @@ __device__ __forceinline__ ConeVP cone_vp(const Geo &g, const ViewK &vk, double 
 // (channels fastest, coalesced) while view v is gathered, then stored, with one
 // barrier per view.  The per-view constants and window travel as one register
 // (lanes 0-17 the view's 18 dwords, lanes 18-21 its window) fetched two views
-// ahead; the channel index of each lane's pixel one view ahead.  The row taps
-// run in fp32 (clamped edges by v_med3): a voxel's back projection sums the
-// taps of every view, so their 1e-7 absolute error is far below the
-// tolerance relative to that sum; the row itself is placed in fp64.
+// ahead; the channel index of each lane's pixel one view ahead.  The row is
+// placed in fp64; its taps run in fp32 (clamped edges by v_med3), and where a
+// tap cell lies off the detector's top or bottom edge they are formed as
+// interval overlaps from fp32 pairs, accurate for thin edge taps.
 template <int SL, int R, int POW>
 __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__restrict__ sino,
                                                             float *__restrict__ recon,
@@ -181,23 +181,52 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
 #pragma unroll
                 for (int t = 0; t < NTAP; ++t) h[t] = POW == 2 ? (float)(hd[t] * hd[t]) : (float)hd[t];
                 const float *col = win + (v & 1) * wsz + (ncur - R - wv.n0) * nrp - wv.m0;
-                const float hrow = (float)(0.5 * (q.mr * g.dv));
+                const double wrow = q.mr * g.dv;        // footprint width in rows
+                const double hrowd = 0.5 * wrow;
+                const float hrow = (float)hrowd, wcap = fminf(1.f, (float)wrow);
                 const float lscf = (float)q.lsc;
+                // slice k sits dz0 + k dv above the source; its row advances by
+                // mr dv per slice (fp64 fma, no re-placement from the slice index)
+                const double dz0 = slice_z(g, k0) - vk.zsrc;
 #pragma unroll
                 for (int k = 0; k < SL; ++k) {
-                    const double dz = slice_z(g, k0 + k) - vk.zsrc;
-                    const double t0 = q.mr * dz;
-                    const double wk = t0 + g.crow;
+                    const double dz = fma((double)k, g.dv, dz0);
+                    const double wk = fma(q.mr, dz, g.crow);
                     const double mk = rint(wk);
                     if (k < nk && mk >= -R && mk <= g.nr - 1 + R) {
-                        const float f = (float)(wk - mk);
                         float gw[NTAP];
-                        float gp = __builtin_amdgcn_fmed3f(-0.5f - (float)R - f, -hrow, hrow);
+                        if (mk < R || mk > g.nr - 1 - R) {
+                            // a tap cell lies off the top or bottom detector
+                            // edge: a voxel whose rows graze that edge in every
+                            // view sums nothing but thin edge taps, so each tap
+                            // is the overlap min(1, b_t - lo, hi - b_(t-1),
+                            // hi - lo) of its cell [b_(t-1), b_t] with the
+                            // footprint [lo, hi], with lo and hi carried as
+                            // fp32 pairs: a thin tap is then an exact difference
+                            // of nearby numbers plus the low part
+                            const double fd = wk - mk;
+                            const double lod = fd - hrowd, hid = fd + hrowd;
+                            const float loh = (float)lod, lol = (float)(lod - (double)loh);
+                            const float hih = (float)hid, hil = (float)(hid - (double)hih);
 #pragma unroll
-                        for (int t = 0; t < NTAP; ++t) {
-                            const float gn = __builtin_amdgcn_fmed3f((float)t - (float)R + 0.5f - f, -hrow, hrow);
-                            gw[t] = gn - gp;
-                            gp = gn;
+                            for (int t = 0; t < NTAP; ++t) {
+                                const float bt = (float)t - (float)R + 0.5f;
+                                const float xa = (bt - loh) - lol;
+                                const float ya = (hih - (bt - 1.f)) + hil;
+                                gw[t] = __builtin_amdgcn_fmed3f(fminf(xa, ya), 0.f, wcap);
+                            }
+                        } else {
+                            // inside the detector every footprint keeps its
+                            // full width, and the 1e-7 absolute error of fp32
+                            // clamps (v_med3) stays far below the tolerance
+                            const float f = (float)(wk - mk);
+                            float gp = __builtin_amdgcn_fmed3f(-0.5f - (float)R - f, -hrow, hrow);
+#pragma unroll
+                            for (int t = 0; t < NTAP; ++t) {
+                                const float gn = __builtin_amdgcn_fmed3f((float)t - (float)R + 0.5f - f, -hrow, hrow);
+                                gw[t] = gn - gp;
+                                gp = gn;
+                            }
                         }
                         float lk = lscf * __builtin_amdgcn_sqrtf((float)(q.r2 + dz * dz));
                         if (POW == 2) {             // squared weights: the Hessian-diagonal back projection
