@@ -11,9 +11,10 @@
 // a BT x BT pixel tile and a chunk of SL slices; lanes are pixels, each with
 // SL register accumulators.  Per view the sinogram cells the tile can reach
 // (a channel window of SL rows) are staged in LDS, channel-major with slices
-// fastest, by coalesced reads; each lane then reads its NTAP taps per slice
-// (adjacent channels, so pairs come in one ds_read2) and accumulates.  Every
-// voxel is written once and nothing collides.
+// fastest, by coalesced reads; each lane then reads each of its NTAP taps four
+// slices at a time (one 16-byte LDS read, which gfx950 serves at about twice
+// the bytes per clock of paired 4-byte reads) and accumulates.  Every voxel is
+// written once and nothing collides.
 //
 // Forward (scatter with no colliding LDS or register updates): a workgroup
 // owns an FTX x FTY pixel tile and a chunk of 64 slices; lanes are slices and
@@ -37,7 +38,11 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
                                                            float *__restrict__ recon,
                                                            const int32_t *__restrict__ rec,
                                                            const int4 *__restrict__ wtab, Geo g, int nwcap) {
-    constexpr int SLP = SL + 1;           // LDS pitch of one channel column
+    // LDS pitch of one channel column: a multiple of four floats, so a lane
+    // reads four slices of a tap with one 16-byte read; SLP / 4 is odd, so
+    // 16 lanes on consecutive channels hit 16 distinct bank groups
+    constexpr int SLP = SL + 4;
+    static_assert(SL % 4 == 0 && (SLP / 4) % 2 == 1, "16-byte column reads need SL a multiple of 4");
     constexpr int NREC = 1 + NTAP;
     constexpr int RPT = (SL + 7) / 8;     // staged rows per thread: 8 row groups of 32 lanes
     extern __shared__ float lds[];        // two windows of [nwcap][SLP], slices fastest
@@ -124,13 +129,24 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
             load_taps(v + 1, nnf, nw);
         }
         if (nf != INT32_MAX && wcur.y > 0) {
-            const float *col = buf + (nf - wcur.x) * SLP;
+            const float4 *col = reinterpret_cast<const float4 *>(buf + (nf - wcur.x) * SLP);
 #pragma unroll
-            for (int k = 0; k < SL; ++k) {
-                float sacc = acc[k];
+            for (int q = 0; q < SL / 4; ++q) {
+                float4 c[NTAP];
 #pragma unroll
-                for (int t = 0; t < NTAP; ++t) sacc = fmaf(w[t], col[t * SLP + k], sacc);
-                acc[k] = sacc;
+                for (int t = 0; t < NTAP; ++t) c[t] = col[t * (SLP / 4) + q];
+                float s0 = acc[4 * q], s1 = acc[4 * q + 1], s2 = acc[4 * q + 2], s3 = acc[4 * q + 3];
+#pragma unroll
+                for (int t = 0; t < NTAP; ++t) {
+                    s0 = fmaf(w[t], c[t].x, s0);
+                    s1 = fmaf(w[t], c[t].y, s1);
+                    s2 = fmaf(w[t], c[t].z, s2);
+                    s3 = fmaf(w[t], c[t].w, s3);
+                }
+                acc[4 * q] = s0;
+                acc[4 * q + 1] = s1;
+                acc[4 * q + 2] = s2;
+                acc[4 * q + 3] = s3;
             }
         }
         if (more) {

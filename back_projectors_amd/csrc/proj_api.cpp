@@ -267,7 +267,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
             const WinMax w = max_window(g, views, BT, BT, sl);
             plan.back_sl = sl;
             plan.back_nwcap = w.nw + 2;
-            plan.back_lds = 2 * (size_t)plan.back_nwcap * (sl + 1) * sizeof(float);
+            plan.back_lds = 2 * (size_t)plan.back_nwcap * (sl + 4) * sizeof(float);   // pitch: par_back_kernel
             if (plan.back_lds <= kMaxLds || sl == 8) break;
         }
         if (plan.back_nwcap > 64)
