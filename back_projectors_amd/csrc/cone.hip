@@ -54,23 +54,37 @@ __device__ __forceinline__ ConeVP cone_vp(const Geo &g, const ViewK &vk, double 
 // accumulators.  Per view the sinogram window the tile and slice chunk can reach
 // is staged in LDS, double buffered: view v + 1's cells are read into registers
 // (channels fastest, coalesced) while view v is gathered, then stored, with one
-// barrier per view.  The per-view constants and window travel as one register
-// (lanes 0-17 the view's 18 dwords, lanes 18-21 its window) fetched two views
-// ahead; the channel index of each lane's pixel one view ahead.  The row is
-// placed in fp64; its taps run in fp32 (clamped edges by v_med3), and where a
-// tap cell lies off the detector's top or bottom edge they are formed as
-// interval overlaps from fp32 pairs, accurate for thin edge taps.
-template <int SL, int R, int POW>
+// barrier per view.  The window's row pitch NRP is odd and fixed at compile
+// time, so the (2R+1)^2 tap reads of a slice share one address with immediate
+// offsets, and lanes on one row but different channels hit different banks.
+// The per-view constants and window travel as one register (lanes 0-17 the
+// view's 18 dwords, lanes 18-21 its window) fetched two views ahead; the
+// channel index of each lane's pixel one view ahead.
+//
+// Per (view, pixel) the row coordinate w_k = Mr dz_k + c_row is affine in the
+// slice index, so it is carried in 32.32 fixed point (from the fp64 value at
+// the chunk's first slice, advanced by one 64-bit add per slice, about 4e-9 of
+// a row off after 32 slices): the high word is the tap row m_k = floor(w_k +
+// 1/2) (offset by R) and the low word the position inside it.  A row chosen
+// differently at an exact half (round half up here, half to even in the
+// model) moves no weight while the footprint is no wider than 2R rows: every
+// tap is the overlap of one cell with the footprint.  The row taps run in fp32
+// (clamped edges by v_med3); where a tap cell lies off the detector's top or
+// bottom edge they are formed as interval overlaps from fp32 pairs, accurate
+// for thin edge taps.  The chord scale sqrt(d^2 + a^2 + dz^2) runs in fp32,
+// with the per-pixel factor dv / M folded into the channel taps.
+template <int SL, int R, int POW, int NRP>
 __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__restrict__ sino,
                                                             float *__restrict__ recon,
                                                             const int32_t *__restrict__ idx,
                                                             const ViewK *__restrict__ views,
                                                             const int4 *__restrict__ wtab, Geo g, int nwcap,
-                                                            int nrp) {
+                                                            int nrcap) {
     constexpr int NT = BT * BT;
     constexpr int NTAP = 2 * R + 1;
     constexpr int STG = CBSTG;            // staged cells per thread at most
-    extern __shared__ float win[];        // two windows of [nwcap][nrp], rows fastest
+    static_assert(NRP % 2 == 1, "odd row pitch");
+    extern __shared__ float win[];        // two windows of [nwcap][NRP], rows fastest
     static_assert(sizeof(ViewK) == 72, "ViewK is read as 18 dwords");
 
     const int tiles_x = (g.nx + BT - 1) / BT;
@@ -84,8 +98,12 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
     const int nk = min(SL, g.ns - k0);
     const int tid = (int)threadIdx.x;
     const int wl = tid & 63;
-    const int wsz = nwcap * nrp;
-    const int stg = (wsz + NT - 1) / NT;  // <= STG by the plan
+    const int wsz = nwcap * NRP;          // floats per window
+    const int stg = (nwcap * nrcap + NT - 1) / NT;  // staged cells per thread, <= STG by the plan
+    // rows m with m + R in [0, nr - 1 + 2R] have a tap on the detector; those
+    // with m + R in [2R, nr - 1] have every tap on it (none if ib < 0)
+    const unsigned rlim = (unsigned)(g.nr - 1 + 2 * R);
+    const int ib = g.nr - 1 - 2 * R;
 
     const int i = ti0 + tid / BT;
     const int j = tj0 + tid % BT;
@@ -139,7 +157,7 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                 const int e = tid + NT * u;
                 const int m = (int)(((float)e + 0.5f) * rnw);
                 const int c = e - m * w.nw;
-                if (w.nw > 0 && m < w.nrw) buf[c * nrp + m] = st[u];
+                if (w.nw > 0 && m < w.nrw) buf[c * NRP + m] = st[u];
             }
         }
     };
@@ -177,33 +195,68 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                 const ConeVP q = cone_vp(g, vk, x, y, ncur);
                 double hd[NTAP];
                 tap_weights_d<R>(q.f, q.wch, hd);
+                // channel taps with the chord factor dv / M folded in (squared
+                // for the Hessian-diagonal back projection)
                 float h[NTAP];
 #pragma unroll
-                for (int t = 0; t < NTAP; ++t) h[t] = POW == 2 ? (float)(hd[t] * hd[t]) : (float)hd[t];
-                const float *col = win + (v & 1) * wsz + (ncur - R - wv.n0) * nrp - wv.m0;
-                const double wrow = q.mr * g.dv;        // footprint width in rows
+                for (int t = 0; t < NTAP; ++t)
+                    h[t] = POW == 2 ? (float)((hd[t] * hd[t]) * (q.lsc * q.lsc)) : (float)(hd[t] * q.lsc);
+                // window cell of row offset sg, channel tap t at slice k:
+                // col[(m_k + R) + t NRP + sg]
+                const float *col = win + (v & 1) * wsz + (ncur - R - wv.n0) * NRP - wv.m0 - 2 * R;
+                const double wrow = q.mr * g.dv;        // footprint width in rows = row advance per slice
                 const double hrowd = 0.5 * wrow;
                 const float hrow = (float)hrowd, wcap = fminf(1.f, (float)wrow);
-                const float lscf = (float)q.lsc;
-                // slice k sits dz0 + k dv above the source; its row advances by
-                // mr dv per slice (fp64 fma, no re-placement from the slice index)
+                // slice k0 sits dz0 above the source; w + R + 1/2 in 32.32 fixed point
                 const double dz0 = slice_z(g, k0) - vk.zsrc;
+                const double t0 = (q.mr * dz0 + g.crow) + (0.5 + (double)R);
+                const double fl0 = floor(t0);
+                uint64_t wfx = ((uint64_t)(uint32_t)(int)fl0 << 32) | (uint64_t)(uint32_t)((t0 - fl0) * 4294967296.0);
+                const uint64_t afx = (uint64_t)(wrow * 4294967296.0 + 0.5);
+                const float r2f = (float)q.r2, dvf = (float)g.dv;
+                float dzf = (float)dz0;
+                // the slice count, re-read per view so that the per-slice tests
+                // stay scalar compares instead of 32 hoisted lane masks,
+                int nkv, k0v;
+                asm volatile("s_mov_b32 %0, %1" : "=s"(nkv) : "s"(nk));
+                // and the chunk's first slice, so that the edge branch's slice
+                // heights are not hoisted out of the view loop into registers
+                asm volatile("s_mov_b32 %0, %1" : "=s"(k0v) : "s"(k0));
 #pragma unroll
                 for (int k = 0; k < SL; ++k) {
-                    const double dz = fma((double)k, g.dv, dz0);
-                    const double wk = fma(q.mr, dz, g.crow);
-                    const double mk = rint(wk);
-                    if (k < nk && mk >= -R && mk <= g.nr - 1 + R) {
+                    const int hk = (int)(wfx >> 32);            // m_k + R
+                    const uint32_t fr = (uint32_t)wfx;          // (w_k - m_k + 1/2) 2^32
+                    const float dzk = dzf;
+                    wfx += afx;
+                    dzf += dvf;
+                    // slices past the chunk's last one get an empty row range
+                    // (a uniform bound, so the test stays one compare); the
+                    // range is one row wider each side than the taps need, and
+                    // the edge branch below decides those rows in fp64
+                    const unsigned rl1 = k < nkv ? rlim + 3u : 0u;
+                    if ((unsigned)(hk + 1) < rl1) {
                         float gw[NTAP];
-                        if (mk < R || mk > g.nr - 1 - R) {
+                        int hr = hk;                            // tap centre row + R
+                        bool ok = true;
+                        if (ib < 0 || (unsigned)(hk - 2 * R) > (unsigned)ib) {
                             // a tap cell lies off the top or bottom detector
-                            // edge: a voxel whose rows graze that edge in every
-                            // view sums nothing but thin edge taps, so each tap
-                            // is the overlap min(1, b_t - lo, hi - b_(t-1),
-                            // hi - lo) of its cell [b_(t-1), b_t] with the
-                            // footprint [lo, hi], with lo and hi carried as
-                            // fp32 pairs: a thin tap is then an exact difference
-                            // of nearby numbers plus the low part
+                            // edge: the row is placed in fp64 in the model's
+                            // operation order, so that a footprint edge on a cell
+                            // boundary gives an exactly empty tap there (a
+                            // voxel that only grazes the detector then adds
+                            // exactly nothing).  A voxel whose rows graze
+                            // that edge in every view sums nothing but thin
+                            // edge taps, so each tap is the overlap min(1,
+                            // b_t - lo, hi - b_(t-1), hi - lo) of its cell
+                            // [b_(t-1), b_t] with the footprint [lo, hi], with
+                            // lo and hi carried as fp32 pairs: a thin tap is
+                            // then an exact difference of nearby numbers plus
+                            // the low part
+                            const double dz = slice_z(g, k0v + k) - vk.zsrc;
+                            const double wk = q.mr * dz + g.crow;    // product, then sum (no contraction)
+                            const double mk = rint(wk);
+                            ok = mk >= -R && mk <= g.nr - 1 + R;
+                            hr = ok ? (int)mk + R : R;
                             const double fd = wk - mk;
                             const double lod = fd - hrowd, hid = fd + hrowd;
                             const float loh = (float)lod, lol = (float)(lod - (double)loh);
@@ -217,33 +270,41 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                             }
                         } else {
                             // inside the detector every footprint keeps its
-                            // full width, and the 1e-7 absolute error of fp32
-                            // clamps (v_med3) stays far below the tolerance
-                            const float f = (float)(wk - mk);
-                            float gp = __builtin_amdgcn_fmed3f(-0.5f - (float)R - f, -hrow, hrow);
+                            // full width; cell edges sit at (j - R) - phi with
+                            // phi = fr 2^-32 = w_k - m_k + 1/2, and the 1e-7
+                            // absolute error of fp32 clamps stays far below
+                            // the tolerance
+                            const float phr = (float)fr;
+                            float gp = __builtin_amdgcn_fmed3f(fmaf(phr, -0x1p-32f, -(float)R), -hrow, hrow);
 #pragma unroll
                             for (int t = 0; t < NTAP; ++t) {
-                                const float gn = __builtin_amdgcn_fmed3f((float)t - (float)R + 0.5f - f, -hrow, hrow);
+                                const float gn =
+                                    __builtin_amdgcn_fmed3f(fmaf(phr, -0x1p-32f, (float)(t + 1 - R)), -hrow, hrow);
                                 gw[t] = gn - gp;
                                 gp = gn;
                             }
                         }
-                        float lk = lscf * __builtin_amdgcn_sqrtf((float)(q.r2 + dz * dz));
-                        if (POW == 2) {             // squared weights: the Hessian-diagonal back projection
-                            lk = lk * lk;
+                        if (ok) {
+                            const float qk = fmaf(dzk, dzk, r2f);   // d^2 + a^2 + dz^2
+                            float lk;
+                            if (POW == 2) {             // squared weights: the Hessian-diagonal back projection
+                                lk = qk;
 #pragma unroll
-                            for (int t = 0; t < NTAP; ++t) gw[t] = gw[t] * gw[t];
+                                for (int t = 0; t < NTAP; ++t) gw[t] = gw[t] * gw[t];
+                            } else {
+                                lk = __builtin_amdgcn_sqrtf(qk);
+                            }
+                            const float *cell = col + hr;
+                            float s = 0.f;
+#pragma unroll
+                            for (int sg = 0; sg < NTAP; ++sg) {
+                                float rv = 0.f;
+#pragma unroll
+                                for (int t = 0; t < NTAP; ++t) rv = fmaf(h[t], cell[t * NRP + sg], rv);
+                                s = fmaf(gw[sg], rv, s);
+                            }
+                            acc[k] = fmaf(lk, s, acc[k]);
                         }
-                        const float *cell = col + ((int)mk - R);
-                        float s = 0.f;
-#pragma unroll
-                        for (int sg = 0; sg < NTAP; ++sg) {
-                            float rv = 0.f;
-#pragma unroll
-                            for (int t = 0; t < NTAP; ++t) rv = fmaf(h[t], cell[t * nrp + sg], rv);
-                            s = fmaf(gw[sg], rv, s);
-                        }
-                        acc[k] = fmaf(lk, s, acc[k]);
                     }
                 }
             }
@@ -520,18 +581,28 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
     }
 }
 
-template <int SL, int R>
-static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, int power, hipStream_t st) {
+template <int SL, int R, int NRP>
+static hipError_t cone_back_n(const Plan &p, const float *sino, float *recon, int power, hipStream_t st) {
     const Geo &g = p.g;
     const int tiles = ((g.nx + BT - 1) / BT) * ((g.ny + BT - 1) / BT);
     const int chunks = (g.ns + SL - 1) / SL;
     if (power == 2)
-        hipLaunchKernelGGL((cone_back_kernel<SL, R, 2>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
-                           recon, p.idx, p.views, p.bwin, g, p.back_nwcap, p.back_nrcap);
+        hipLaunchKernelGGL((cone_back_kernel<SL, R, 2, NRP>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st,
+                           sino, recon, p.idx, p.views, p.bwin, g, p.back_nwcap, p.back_nrcap);
     else
-        hipLaunchKernelGGL((cone_back_kernel<SL, R, 1>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st, sino,
-                           recon, p.idx, p.views, p.bwin, g, p.back_nwcap, p.back_nrcap);
+        hipLaunchKernelGGL((cone_back_kernel<SL, R, 1, NRP>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st,
+                           sino, recon, p.idx, p.views, p.bwin, g, p.back_nwcap, p.back_nrcap);
     return hipGetLastError();
+}
+
+template <int SL, int R>
+static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, int power, hipStream_t st) {
+    switch (p.back_nrp) {
+    case 33: return cone_back_n<SL, R, 33>(p, sino, recon, power, st);
+    case 65: return cone_back_n<SL, R, 65>(p, sino, recon, power, st);
+    case 129: return cone_back_n<SL, R, 129>(p, sino, recon, power, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int R, int P, bool U>

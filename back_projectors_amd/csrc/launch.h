@@ -35,6 +35,7 @@ struct Plan {
     int back_sl = 0;                // slices per chunk (accumulators per lane)
     int back_nwcap = 0;             // window channels capacity
     int back_nrcap = 0;             // window rows capacity (cone)
+    int back_nrp = 0;               // cone back LDS row pitch: 33, 65 or 129 (odd, compile-time in the kernel)
     size_t back_lds = 0;            // dynamic LDS bytes
     int back_ncg = 1;               // parallel back: 32-channel staging groups (1 or 2)
 
