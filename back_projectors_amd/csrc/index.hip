@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256) void par_taps_kernel(Geo g, const ViewK *__res
 // touches every accumulator exactly once and nothing is ever moved between
 // registers.  Steps are grouped by 16; per (view, region, group) the records
 // are 2 + NTAP fields of 16 dwords, one dword per step:
-//   field 0: LDS byte offset of the step's voxel row (pixel-in-region * 64);
+//   field 0: LDS byte offset of the step's voxel row (pixel-in-region times
+//            the bytes of one pixel's slices in the region copy, 64 or 128);
 //   field 1: 0 when nothing is flushed after this step; else bits 0-6 = the
 //            accumulators to flush, bits 7-13 = those among them below
 //            n_f mod NTAP (their channel lies one ring turn up), bits 14-31 =
@@ -124,7 +125,8 @@ __global__ __launch_bounds__(256) void par_taps_kernel(Geo g, const ViewK *__res
 // Dynamic LDS: 2 * RSX * RSY + nbin + 1 ints.
 __global__ __launch_bounds__(256) void par_region_records_kernel(Geo g, const int32_t *__restrict__ rec,
                                                                  uint32_t *__restrict__ out, int ntap, int rsx,
-                                                                 int rsy, int nrx, int nreg, int ng, int nbin) {
+                                                                 int rsy, int nrx, int nreg, int ng, int nbin,
+                                                                 uint32_t pxb) {
     extern __shared__ int sh[];
     const int rp = rsx * rsy;
     int *key = sh;                      // [rp] n_f - min n_f, or nbin - 1 for "no tap on the detector"
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(256) void par_region_records_kernel(Geo g, const in
     for (int q = t; q < ng * 16; q += 256) {
         uint32_t *oq = o + (q >> 4) * nf_ * 16 + (q & 15);     // field f of this step: oq[f * 16]
         const int p = q < rp ? perm[q] : 0;
-        oq[0] = (uint32_t)p * 64u;
+        oq[0] = (uint32_t)p * pxb;                        // the pixel's voxel row in the region's LDS copy
         oq[16] = 0u;
         for (int r = 0; r < ntap; ++r) oq[(2 + r) * 16] = 0u;
         if (q >= nvalid) continue;
@@ -319,7 +321,7 @@ hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int n
 }
 
 hipError_t launch_par_region_records(const Geo &g, const int32_t *rec, uint32_t *out, int ntap, int rsx, int rsy,
-                                    int nbin, hipStream_t st) {
+                                    int nbin, int spl, hipStream_t st) {
     const int nrx = (g.nx + rsx - 1) / rsx, nry = (g.ny + rsy - 1) / rsy;
     const int nreg = nrx * nry;
     const int ng = fwd_groups(rsx, rsy);
@@ -327,7 +329,7 @@ hipError_t launch_par_region_records(const Geo &g, const int32_t *rec, uint32_t 
     if (blocks == 0) return hipSuccess;
     const size_t lds = (size_t)(2 * rsx * rsy + nbin + 1) * sizeof(int);
     hipLaunchKernelGGL(par_region_records_kernel, dim3((unsigned)blocks), dim3(256), lds, st, g, rec, out, ntap, rsx,
-                       rsy, nrx, nreg, ng, nbin);
+                       rsy, nrx, nreg, ng, nbin, (uint32_t)(64 * spl));
     return hipGetLastError();
 }
 

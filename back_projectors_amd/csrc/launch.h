@@ -19,7 +19,8 @@ struct Plan {
     const uint32_t *wrec = nullptr; // parallel: forward walk records [V + 1][regions][groups][2 + ntap][16]
     float *facc = nullptr;          // parallel: forward accumulation buffer [V][fwd_cb][fwd_s16]
     int fwd_cb = 0;                 // parallel: channels of facc (C plus ntap - 1 guards each side)
-    int fwd_s16 = 0;                // parallel: slices of facc (S rounded up to 16)
+    int fwd_s16 = 0;                // parallel: slices of facc (S rounded up to 16 * fwd_spl)
+    int fwd_spl = 1;                // parallel region walk: adjacent slices per lane (1 or 2)
     int rsx = 0, rsy = 0;           // parallel: forward region (pixels along x, y)
     int fwd_nbin = 0;               // parallel: bins of the walk-order sort (n_f span of a region + 2)
     int fwd_strategy = 1;           // parallel: 1 tile (region walk), 2 gather (per-view sorted walk)
@@ -52,6 +53,7 @@ struct Plan {
 constexpr int BT = 16;   // back tile edge (pixels), 256 threads
 constexpr int FRW = 16;  // parallel forward waves per workgroup (four views each at a time)
 constexpr int FRS = 48;  // parallel forward region edge (pixels): 48 * 48 voxels of 16 slices = 144 KiB of LDS
+constexpr int FRS2 = 32; // the same with two slices per lane: 32 * 32 voxels of 32 slices = 128 KiB of LDS
 
 // Groups of 16 walk steps per (view, region): every pixel of the region, then
 // zero steps up to a multiple of 5 groups (the walk rotates five record buffers).
@@ -64,7 +66,7 @@ constexpr int CBSTG = 8;  // cone back: staged window cells per thread at most (
 hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
 hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st);
 hipError_t launch_par_region_records(const Geo &g, const int32_t *rec, uint32_t *out, int ntap, int rsx, int rsy,
-                                    int nbin, hipStream_t st);
+                                    int nbin, int spl, hipStream_t st);
 hipError_t launch_par_view_records(const Geo &g, const int32_t *rec, int32_t *order, uint32_t *out, int ntap,
                                   int ng, int segg, hipStream_t st);
 hipError_t launch_fill_zero(float *buf, int64_t n, hipStream_t st);
@@ -72,7 +74,7 @@ hipError_t launch_fill_zero(float *buf, int64_t n, hipStream_t st);
 // power 1: the adjoint of the forward; power 2: every tap weight squared
 hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st);
 hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
-hipError_t par_forward_allow_lds(int ntap, size_t bytes);
+hipError_t par_forward_allow_lds(int ntap, int spl, size_t bytes);
 // the slice-fastest accumulation buffer -> the sinogram (parallel beam)
 hipError_t launch_par_unpack(const Plan &p, float *sino, hipStream_t st);
 // batches of voxel cylinders (entries outside [0, Ny*Nx) are inert padding)

@@ -27,6 +27,7 @@
 // sinogram with coalesced global atomics, one per cell per view and tile.
 // Float atomics in LDS are avoided on purpose: on gfx950 they cost tens of
 // times a plain read-modify-write.
+#include <type_traits>
 #include <utility>
 
 #include "launch.h"
@@ -196,13 +197,32 @@ __device__ __forceinline__ void fmac2_row_bcast(float &a0, float &a1, uint32_t w
         : "v"(w0), "v"(w1), "v"(x), "n"(N));
 }
 
+template <int N>
+__device__ __forceinline__ void fmac4_row_bcast(float &a0, float &a1, float &b0, float &b1, uint32_t w0, uint32_t w1,
+                                                float x, float y) {
+    asm("s_nop 1\n\tv_fmac_f32_dpp %0, %4, %6 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %6 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %4, %7 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %5, %7 row_newbcast:%8 row_mask:0xf bank_mask:0xf"
+        : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1)
+        : "v"(w0), "v"(w1), "v"(x), "v"(y), "n"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void fmac2xy_row_bcast(float &a0, float &a1, uint32_t w, float x, float y) {
+    asm("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %3 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+        : "+v"(a0), "+v"(a1)
+        : "v"(w), "v"(x), "v"(y), "n"(N));
+}
+
 // Lane N of each 16-lane row, broadcast to its row, without a prior value.
 template <int N>
 __device__ __forceinline__ uint32_t row_bcast_nb(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + N, 0xf, 0xf, true);
 }
 
-template <int K>
+template <int K, int SPL>
 __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__restrict__ recon,
                                                                 float *__restrict__ facc,
                                                                 const uint32_t *__restrict__ wrec, Geo g, int cb,
@@ -210,7 +230,10 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
                                                                 int vsplit) {
     constexpr int NF = 2 + K;             // record fields per step
     constexpr int D = 4;                  // voxel reads in flight ahead of the step using them
-    extern __shared__ float xr[];         // the region's voxels, [pixel][16 slices]
+    constexpr int CS = 16 * SPL;          // slices of a chunk: SPL per lane, 16 apart
+    static_assert(SPL == 1 || SPL == 2, "one or two slices per lane");
+    using XV = typename std::conditional<SPL == 2, float2, float>::type;   // a lane's voxels of one step
+    extern __shared__ float xr[];         // the region's voxels, [pixel][CS slices]
     const int lane = (int)threadIdx.x & 63;
     const int row = lane >> 4, sl = lane & 15;
     // wave index, made visibly uniform so that per-view control stays scalar
@@ -219,7 +242,7 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
     // dispatch order): the slice chunks of one region get consecutive slots on
     // one XCD, so that they read the region's records through one L2.  Any
     // other placement is still correct, only slower.
-    const int nch = (g.ns + 15) / 16;
+    const int nch = (g.ns + CS - 1) / CS;
     const int per_range = 8 * ((nreg + 7) / 8) * nch;
     const int L = (int)(blockIdx.x % (unsigned)per_range);
     const int vrange = (int)(blockIdx.x / (unsigned)per_range);
@@ -227,11 +250,11 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
     const int region = (slot / nch) * 8 + (L & 7);
     if (region >= nreg) return;
     const int i0 = (region / nrx) * rsy, j0 = (region % nrx) * rsx;
-    const int k0 = (slot % nch) * 16;
+    const int k0 = (slot % nch) * CS;
     const int rp = rsx * rsy;
 
-    for (int e = (int)threadIdx.x; e < rp * 16; e += FRW * 64) {
-        const int p = e >> 4, k = e & 15;
+    for (int e = (int)threadIdx.x; e < rp * CS; e += FRW * 64) {
+        const int p = e / CS, k = e % CS;
         const int i = i0 + p / rsx, j = j0 + p % rsx;
         float val = 0.f;
         if (i < g.ny && j < g.nx && k0 + k < g.ns) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + k];
@@ -244,7 +267,9 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
     const int vend = min(g.nv, vbeg + vper);
     const char *xb = reinterpret_cast<const char *>(xr);
     char *fv = reinterpret_cast<char *>(facc + (int64_t)vbeg * cb * s16);
-    const uint32_t l4 = (uint32_t)sl * 4u;
+    // lane sl holds slices sl and sl + 16 of the chunk: one paired LDS read per
+    // step, and a flush covers 16 consecutive slices (64 bytes) per atomic
+    const uint32_t l4 = (uint32_t)sl * 4u;          // this lane's first slice, bytes
     const uint32_t s4 = (uint32_t)s16 * 4u;         // bytes between channels of the accumulation buffer
     const uint32_t ks = (uint32_t)K * s4;           // bytes per ring turn
     const int64_t gstride = (int64_t)NF * 16;       // dwords per group of 16 steps
@@ -256,15 +281,17 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
         const int vrow = q0 + row < vend ? q0 + row : g.nv;
         const uint32_t *rb = wrec + ((int64_t)vrow * nreg + region) * ng * gstride + sl;
         // byte offset from fv (this workgroup's first view) of ring turn 0,
-        // accumulator r, for this lane: turn T, accumulator r is at
-        // vb[r] + T * ks (modulo 2^32; the sum itself stays below 2^31)
+        // accumulator r, for this lane's first slice: turn T, accumulator r is
+        // at vb[r] + T * ks (modulo 2^32; the sum itself stays below 2^31)
         uint32_t vb[K];
 #pragma unroll
         for (int r = 0; r < K; ++r)
             vb[r] = (uint32_t)(((min(vrow, g.nv - 1) - vbeg) * cb + (K - 1)) * s16 + k0) * 4u + l4 + r * s4 - ks;
-        float acc[K];
+        float acc[SPL][K];
 #pragma unroll
-        for (int r = 0; r < K; ++r) acc[r] = 0.f;
+        for (int s = 0; s < SPL; ++s)
+#pragma unroll
+            for (int r = 0; r < K; ++r) acc[s][r] = 0.f;
 
         auto load_group = [&](int gi, uint32_t (&R)[NF]) {
             const uint32_t *b = rb + (int64_t)gi * gstride;
@@ -279,23 +306,39 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
             m |= m >> 32;
             m |= m >> 16;
             const uint32_t fl = (uint32_t)m & 0xffffu;      // steps after which some row flushes
-            float xq[16];
+            XV xq[16];
             auto read_x = [&](auto SC) {
                 constexpr int S = decltype(SC)::value;
-                xq[S] = *reinterpret_cast<const float *>(xb + (row_bcast<S>(R[0]) + l4));
+                const float *xs = reinterpret_cast<const float *>(xb + (row_bcast<S>(R[0]) + l4));
+                if constexpr (SPL == 2)
+                    xq[S] = make_float2(xs[0], xs[16]);
+                else
+                    xq[S] = xs[0];
             };
             static_for(read_x, std::make_integer_sequence<int, D>{});
             static_for(
                 [&](auto SC) {
                     constexpr int S = decltype(SC)::value;
                     if constexpr (S + D < 16) read_x(std::integral_constant<int, S + D>{});
+                    if constexpr (SPL == 2) {
 #pragma unroll
-                    for (int r = 0; r < K; r += 2) {
-                        if (r + 1 < K)
-                            fmac2_row_bcast<S>(acc[r], acc[r + 1 < K ? r + 1 : r], R[2 + r], R[r + 1 < K ? 3 + r : 2 + r],
-                                               xq[S]);
-                        else
-                            fmac_row_bcast<S>(acc[r], R[2 + r], xq[S]);
+                        for (int r = 0; r < K; r += 2) {
+                            if (r + 1 < K)
+                                fmac4_row_bcast<S>(acc[0][r], acc[0][r + 1 < K ? r + 1 : r], acc[SPL - 1][r],
+                                                   acc[SPL - 1][r + 1 < K ? r + 1 : r], R[2 + r],
+                                                   R[r + 1 < K ? 3 + r : 2 + r], xq[S].x, xq[S].y);
+                            else
+                                fmac2xy_row_bcast<S>(acc[0][r], acc[SPL - 1][r], R[2 + r], xq[S].x, xq[S].y);
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < K; r += 2) {
+                            if (r + 1 < K)
+                                fmac2_row_bcast<S>(acc[0][r], acc[0][r + 1 < K ? r + 1 : r], R[2 + r],
+                                                   R[r + 1 < K ? 3 + r : 2 + r], xq[S]);
+                            else
+                                fmac_row_bcast<S>(acc[0][r], R[2 + r], xq[S]);
+                        }
                     }
                     if (__builtin_expect((fl >> S) & 1u, 0)) {       // out of line: most steps flush nothing
                         const uint32_t f = row_bcast_nb<S>(R[1]);     // this row's flush word
@@ -304,8 +347,12 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
                         for (int r = 0; r < K; ++r) {
                             if (f & (1u << r)) {
                                 const uint32_t turn = t + ((f >> (7 + r)) & 1u);
-                                unsafeAtomicAdd(reinterpret_cast<float *>(fv + (__umul24(turn, ks) + vb[r])), acc[r]);
-                                acc[r] = 0.f;
+                                float *dst = reinterpret_cast<float *>(fv + (__umul24(turn, ks) + vb[r]));
+#pragma unroll
+                                for (int s = 0; s < SPL; ++s) {
+                                    unsafeAtomicAdd(dst + 16 * s, acc[s][r]);
+                                    acc[s][r] = 0.f;
+                                }
                             }
                         }
                     }
@@ -494,16 +541,21 @@ static hipError_t par_back_t(const Plan &p, const float *sino, float *recon, hip
     return hipGetLastError();
 }
 
-template <int K>
-static hipError_t par_fwd_t(const Plan &p, const float *recon, hipStream_t st) {
+template <int K, int SPL>
+static hipError_t par_fwd_s(const Plan &p, const float *recon, hipStream_t st) {
     const Geo &g = p.g;
     const int nrx = (g.nx + p.rsx - 1) / p.rsx, nry = (g.ny + p.rsy - 1) / p.rsy;
     const int ng = fwd_groups(p.rsx, p.rsy);
-    const int64_t per_range = 8 * (int64_t)((nrx * nry + 7) / 8) * ((g.ns + 15) / 16);
-    hipLaunchKernelGGL((par_forward_kernel<K>), dim3((unsigned)(per_range * p.fwd_vsplit)), dim3(FRW * 64),
+    const int64_t per_range = 8 * (int64_t)((nrx * nry + 7) / 8) * ((g.ns + 16 * SPL - 1) / (16 * SPL));
+    hipLaunchKernelGGL((par_forward_kernel<K, SPL>), dim3((unsigned)(per_range * p.fwd_vsplit)), dim3(FRW * 64),
                        p.fwd_lds, st, recon, p.facc, p.wrec, g, p.fwd_cb, p.fwd_s16, p.rsx, p.rsy, nrx, nrx * nry, ng,
                        p.fwd_vsplit);
     return hipGetLastError();
+}
+
+template <int K>
+static hipError_t par_fwd_t(const Plan &p, const float *recon, hipStream_t st) {
+    return p.fwd_spl == 2 ? par_fwd_s<K, 2>(p, recon, st) : par_fwd_s<K, 1>(p, recon, st);
 }
 
 template <int SL, int POW>
@@ -584,17 +636,15 @@ hipError_t launch_par_unpack(const Plan &p, float *sino, hipStream_t st) {
 }
 
 // The region walk holds its voxels in more LDS than the default limit.
-hipError_t par_forward_allow_lds(int ntap, size_t bytes) {
+hipError_t par_forward_allow_lds(int ntap, int spl, size_t bytes) {
     const void *f = nullptr;
+#define BPAMD_PF(KK)                                                                                          \
+    case KK: f = spl == 2 ? (const void *)par_forward_kernel<KK, 2> : (const void *)par_forward_kernel<KK, 1>; break;
     switch (ntap) {
-    case 2: f = (const void *)par_forward_kernel<2>; break;
-    case 3: f = (const void *)par_forward_kernel<3>; break;
-    case 4: f = (const void *)par_forward_kernel<4>; break;
-    case 5: f = (const void *)par_forward_kernel<5>; break;
-    case 6: f = (const void *)par_forward_kernel<6>; break;
-    case 7: f = (const void *)par_forward_kernel<7>; break;
+    BPAMD_PF(2) BPAMD_PF(3) BPAMD_PF(4) BPAMD_PF(5) BPAMD_PF(6) BPAMD_PF(7)
     default: return hipErrorInvalidValue;
     }
+#undef BPAMD_PF
     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 

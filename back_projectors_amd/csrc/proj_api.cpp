@@ -273,12 +273,17 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         if (plan.back_nwcap > 64)
             return fail(PROJ_ERR_UNSUPPORTED, "back projection window wider than 64 channels (detector far finer than the voxels)");
         plan.back_ncg = plan.back_nwcap <= 32 ? 1 : 2;
-        plan.fwd_sl = 16;
-        plan.rsx = (int)std::min<int64_t>(FRS, Nx);
-        plan.rsy = (int)std::min<int64_t>(FRS, Ny);
-        plan.fwd_lds = (size_t)plan.rsx * plan.rsy * 16 * sizeof(float);
+        // region walk: two slices per lane, 16 apart (one paired LDS read per
+        // step for 32 slices of four views) unless the volume has 16 slices or
+        // fewer, which one slice per lane covers without idle lanes
+        plan.fwd_spl = S > 16 ? 2 : 1;
+        plan.fwd_sl = 16 * plan.fwd_spl;
+        const int frs = plan.fwd_spl == 2 ? FRS2 : FRS;
+        plan.rsx = (int)std::min<int64_t>(frs, Nx);
+        plan.rsy = (int)std::min<int64_t>(frs, Ny);
+        plan.fwd_lds = (size_t)plan.rsx * plan.rsy * 16 * plan.fwd_spl * sizeof(float);
         plan.fwd_cb = (int)C + 2 * (plan.ntap - 1);
-        plan.fwd_s16 = (int)(((S + 15) / 16) * 16);
+        plan.fwd_s16 = (int)(((S + 16 * plan.fwd_spl - 1) / (16 * plan.fwd_spl)) * 16 * plan.fwd_spl);
         // the walk addresses the views of one workgroup with 32-bit byte offsets
         if ((int64_t)(plan.fwd_cb + 2 * plan.ntap) * plan.fwd_s16 * 4 >= ((int64_t)1 << 30))
             return fail(PROJ_ERR_UNSUPPORTED, "forward accumulation buffer too large per view");
@@ -510,7 +515,7 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                                          nullptr);
                     if (e != hipSuccess) return cleanup(PROJ_OK, e, "zero fill");
                     e = launch_par_region_records(geo, h->d_rec, h->d_wrec, plan.ntap, plan.rsx, plan.rsy, plan.fwd_nbin,
-                                                  nullptr);
+                                                  plan.fwd_spl, nullptr);
                     if (e != hipSuccess) return cleanup(PROJ_OK, e, "walk record pass");
                     rec_bytes += wrec_bytes;
                     if (plan.fwd_lds > kMaxLds) {
@@ -521,7 +526,7 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                             proj_destroy(h);
                             return fail(PROJ_ERR_UNSUPPORTED, "device LDS per workgroup below the forward plan's need");
                         }
-                        e = par_forward_allow_lds(plan.ntap, plan.fwd_lds);
+                        e = par_forward_allow_lds(plan.ntap, plan.fwd_spl, plan.fwd_lds);
                         if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipFuncSetAttribute(LDS)");
                     }
                 }
