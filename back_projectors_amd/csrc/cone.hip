@@ -69,10 +69,13 @@ __device__ __forceinline__ ConeVP cone_vp(const Geo &g, const ViewK &vk, double 
 // differently at an exact half (round half up here, half to even in the
 // model) moves no weight while the footprint is no wider than 2R rows: every
 // tap is the overlap of one cell with the footprint.  The row taps run in fp32
-// (clamped edges by v_med3); where a tap cell lies off the detector's top or
-// bottom edge they are formed as interval overlaps from fp32 pairs, accurate
-// for thin edge taps.  The chord scale sqrt(d^2 + a^2 + dz^2) runs in fp32,
-// with the per-pixel factor dv / M folded into the channel taps.
+// (clamped edges by v_med3).  Two cases take the row in fp64, in the model's
+// operation order, with the taps formed as interval overlaps from fp32 pairs
+// (accurate for thin taps): a tap cell off the detector's top or bottom edge,
+// and a footprint wider than 2R rows (its outermost taps cut it, so the tap
+// row must be the model's even at an exact half).  The chord scale
+// sqrt(d^2 + a^2 + dz^2) runs in fp32, with the per-pixel factor dv / M folded
+// into the channel taps.
 template <int SL, int R, int POW, int NRP>
 __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__restrict__ sino,
                                                             float *__restrict__ recon,
@@ -207,6 +210,11 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                 const double wrow = q.mr * g.dv;        // footprint width in rows = row advance per slice
                 const double hrowd = 0.5 * wrow;
                 const float hrow = (float)hrowd, wcap = fminf(1.f, (float)wrow);
+                // a footprint wider than the 2R + 1 tap rows loses a sliver to the
+                // outermost taps, which one it loses depends on the tap row, so
+                // that row must be the model's own rounding even at an exact
+                // half: such pixels take the fp64 placement for every slice
+                const bool wide = wrow > 2.0 * R;
                 // slice k0 sits dz0 above the source; w + R + 1/2 in 32.32 fixed point
                 const double dz0 = slice_z(g, k0) - vk.zsrc;
                 const double t0 = (q.mr * dz0 + g.crow) + (0.5 + (double)R);
@@ -238,13 +246,14 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                         float gw[NTAP];
                         int hr = hk;                            // tap centre row + R
                         bool ok = true;
-                        if (ib < 0 || (unsigned)(hk - 2 * R) > (unsigned)ib) {
-                            // a tap cell lies off the top or bottom detector
-                            // edge: the row is placed in fp64 in the model's
-                            // operation order, so that a footprint edge on a cell
-                            // boundary gives an exactly empty tap there (a
-                            // voxel that only grazes the detector then adds
-                            // exactly nothing).  A voxel whose rows graze
+                        if (wide || ib < 0 || (unsigned)(hk - 2 * R) > (unsigned)ib) {
+                            // a footprint wider than the taps, or a tap cell off
+                            // the top or bottom detector edge: the row is placed
+                            // in fp64 in the model's operation order, so that
+                            // the tap row is the model's at an exact half, and a
+                            // footprint edge on a cell boundary gives an exactly
+                            // empty tap there (a voxel that only grazes the
+                            // detector then adds exactly nothing).  A voxel whose rows graze
                             // that edge in every view sums nothing but thin
                             // edge taps, so each tap is the overlap min(1,
                             // b_t - lo, hi - b_(t-1), hi - lo) of its cell

@@ -66,8 +66,12 @@ CONE_R3 = W.Workload("cone-22x26x20-13v-r3", W.CONE_FLAT, 22, 26, 20, 13, 40, 70
                      sdd=80.0, radius=3, seed_x=43, seed_y=44)
 CONE_R4 = W.Workload("cone-22x26x20-13v-r4", W.CONE_FLAT, 22, 26, 20, 13, 40, 70, dch=1.5, drow=1.5, sid=50.0,
                      sdd=80.0, radius=4, seed_x=45, seed_y=46)
+# rows much finer than the voxels (about 2 rows per slice): the cone back's
+# window of a 32-slice chunk spans about 70 rows, its widest LDS row pitch
+CONE_TALL = W.Workload("cone-30x34x64-17v-tallrows", W.CONE_FLAT, 30, 34, 64, 17, 128, 40, dch=2.0, drow=0.45,
+                       sid=60.0, sdd=70.0, seed_x=47, seed_y=48)
 SMALL_CASES = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, PAR_R4, CONE_RAGGED, CONE_R2, CONE_R3,
-               CONE_R4, HELIX_SMALL]
+               CONE_R4, HELIX_SMALL, CONE_TALL]
 
 
 def inputs(w):
