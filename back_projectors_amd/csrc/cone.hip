@@ -278,17 +278,21 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                                 gw[t] = __builtin_amdgcn_fmed3f(fminf(xa, ya), 0.f, wcap);
                             }
                         } else {
-                            // inside the detector every footprint keeps its
-                            // full width; cell edges sit at (j - R) - phi with
-                            // phi = fr 2^-32 = w_k - m_k + 1/2, and the 1e-7
+                            // inside the detector, a footprint no wider than
+                            // 2R rows: cell edges sit at (j - R) - phi with phi
+                            // = fr 2^-32 = w_k - m_k + 1/2, the outermost ones
+                            // (j = 0 and 2R + 1) beyond the footprint, so their
+                            // clamps are the footprint's own edges; the 1e-7
                             // absolute error of fp32 clamps stays far below
                             // the tolerance
                             const float phr = (float)fr;
-                            float gp = __builtin_amdgcn_fmed3f(fmaf(phr, -0x1p-32f, -(float)R), -hrow, hrow);
+                            float gp = -hrow;
 #pragma unroll
                             for (int t = 0; t < NTAP; ++t) {
                                 const float gn =
-                                    __builtin_amdgcn_fmed3f(fmaf(phr, -0x1p-32f, (float)(t + 1 - R)), -hrow, hrow);
+                                    t == NTAP - 1
+                                        ? hrow
+                                        : __builtin_amdgcn_fmed3f(fmaf(phr, -0x1p-32f, (float)(t + 1 - R)), -hrow, hrow);
                                 gw[t] = gn - gp;
                                 gp = gn;
                             }

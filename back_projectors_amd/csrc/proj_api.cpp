@@ -399,7 +399,8 @@ int describe(const Plan &p, int64_t table_bytes, char *buf, int len) {
         BT, BT, p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, par ? p.rsx : CTX, par ? p.rsy : CTY,
         par ? (p.fwd_strategy == PROJ_FORWARD_GATHER
                    ? "gather: per-view sorted walk of all pixels, lanes=16 slices x 4 views, voxels from memory"
-                   : "tile: channel-ordered region walk, lanes=16 slices x 4 views, ring accumulators")
+                   : (p.fwd_spl == 2 ? "tile: channel-ordered region walk, lanes=16 x 4 views with 2 slices each, ring accumulators"
+                                     : "tile: channel-ordered region walk, lanes=16 slices x 4 views, ring accumulators"))
             : "lanes=strided slices, wave per view, LDS window",
         p.fwd_sl,
         p.fwd_nwcap, par ? p.fwd_sl : p.fwd_nrcap, p.fwd_lds, p.fwd_vsplit, (long long)table_bytes);
