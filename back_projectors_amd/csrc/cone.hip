@@ -380,9 +380,10 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         const int v = vbeg + start + it;
         return v >= vend ? v - cnt : v;
     };
-    // this lane's pixel of the tile
+    // this lane's pixel of the tile (lanes past the tile's CTX * CTY pixels
+    // hold none)
     const int il = ti0 + lane / CTX, jl = tj0 + lane % CTX;
-    const bool lin = il < g.ny && jl < g.nx;
+    const bool lin = lane < CTX * CTY && il < g.ny && jl < g.nx;
     const double xl = pix_x(g, jl), yl = pix_y(g, il);
 
     // Per-view data, fetched two views ahead with vector loads: lanes 0-17

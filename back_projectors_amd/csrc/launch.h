@@ -59,7 +59,8 @@ constexpr int FRS2 = 32; // the same with two slices per lane: 32 * 32 voxels of
 // zero steps up to a multiple of 5 groups (the walk rotates five record buffers).
 inline int fwd_groups(int rsx, int rsy) { return ((rsx * rsy + 79) / 80) * 5; }
 constexpr int CTX = 8;   // cone forward tile (pixels along x)
-constexpr int CTY = 8;   // cone forward tile (pixels along y)
+constexpr int CTY = 4;   // cone forward tile (pixels along y); half a wave of pixels: the
+                         // narrower detector window per wave lets four workgroups share a CU
 constexpr int CFW = 4;   // cone forward waves per workgroup (one view each at a time)
 constexpr int CBSTG = 8;  // cone back: staged window cells per thread at most (window <= 256 * CBSTG cells)
 
