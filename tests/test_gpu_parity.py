@@ -70,8 +70,15 @@ CONE_R4 = W.Workload("cone-22x26x20-13v-r4", W.CONE_FLAT, 22, 26, 20, 13, 40, 70
 # window of a 32-slice chunk spans about 70 rows, its widest LDS row pitch
 CONE_TALL = W.Workload("cone-30x34x64-17v-tallrows", W.CONE_FLAT, 30, 34, 64, 17, 128, 40, dch=2.0, drow=0.45,
                        sid=60.0, sdd=70.0, seed_x=47, seed_y=48)
+# channels finer than the voxels at radius 1: footprints up to about 2.6
+# channels wide are cut by the three taps (parallel, and cone with a row pitch
+# close to the voxels')
+PAR_TRUNC = W.Workload("parallel-26x30x18-21v-fine-r1", W.PARALLEL, 26, 30, 18, 21, 18, 90, dch=0.55, radius=1,
+                       seed_x=61, seed_y=62)
+CONE_FINECH = W.Workload("cone-24x28x20-15v-finech", W.CONE_FLAT, 24, 28, 20, 15, 30, 110, dch=0.45, drow=1.2,
+                         sid=50.0, sdd=75.0, seed_x=63, seed_y=64)
 SMALL_CASES = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, PAR_R4, CONE_RAGGED, CONE_R2, CONE_R3,
-               CONE_R4, HELIX_SMALL, CONE_TALL]
+               CONE_R4, HELIX_SMALL, CONE_TALL, PAR_TRUNC, CONE_FINECH]
 
 
 def inputs(w):
@@ -355,7 +362,7 @@ def test_full_back_squared_sampled_pixels(bp, orc, name, full_cache):
 
 
 # ------------------------------------------ forward strategies (a8) ---
-PAR_SMALL = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL]
+PAR_SMALL = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, PAR_TRUNC]
 
 
 @pytest.mark.parametrize("strategy", [1, 2], ids=["tile", "gather"])
