@@ -439,8 +439,11 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         if (nit <= 0) return;                                 // no slice reaches the detector
         // this lane's pixel: channel taps and the per-(view, pixel) constants, fp64
         const bool act = pn >= -R && pn <= g.nc - 1 + R;
+        // (the chord factor dv / M and d^2 + a^2 only ever enter the fp32
+        // chord, so they are carried in fp32)
         float hq[NTAP];
-        double mrq = 0.0, lscq = 0.0, r2q = 0.0;
+        double mrq = 0.0;
+        float lscq = 0.f, r2q = 0.f;
 #pragma unroll
         for (int t = 0; t < NTAP; ++t) hq[t] = 0.f;
         if (act) {
@@ -450,8 +453,8 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
 #pragma unroll
             for (int t = 0; t < NTAP; ++t) hq[t] = (float)hd[t];
             mrq = cv.mr;
-            lscq = cv.lsc;
-            r2q = cv.r2;
+            lscq = (float)cv.lsc;
+            r2q = (float)cv.r2;
         }
         int kkv[P];                                           // this lane's slice in each pass
         double dzs[P];
@@ -460,20 +463,20 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             kkv[ph] = unit ? klo + ph * 64 + lane : lane * P + ph;
             dzs[ph] = slice_z(g, k0 + kkv[ph]) - vk.zsrc;
         }
-        double dz2[P];
+        float dz2[P];
 #pragma unroll
-        for (int ph = 0; ph < P; ++ph) dz2[ph] = dzs[ph] * dzs[ph];
+        for (int ph = 0; ph < P; ++ph) dz2[ph] = (float)(dzs[ph] * dzs[ph]);
         // one pixel of the tile, its cylinder's voxels in xv
         auto pixel = [&](int q, const float (&xv)[P]) {
             const int ncv = __builtin_amdgcn_readlane(pn, q);
             float h[NTAP];
 #pragma unroll
             for (int t = 0; t < NTAP; ++t) h[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hq[t]), q));
-            const double mr = rl_d(mrq, q), r2 = rl_d(r2q, q);
-            const float lscf = (float)rl_d(lscq, q);
-            // the row box: width mr dv, as half widths computed (not negated) so
-            // the clamps below take canonical operands
-            const double hw = 0.5 * (mr * g.dv), nhw = -0.5 * (mr * g.dv);
+            const double mr = rl_d(mrq, q);
+            const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r2q), q));
+            const float lscf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lscq), q));
+            // the row box: half width mr dv / 2 (its negation is an operand modifier)
+            const double hw = 0.5 * (mr * g.dv), nhw = -hw;
             // this pixel's 2R+1 window columns
             float *colt[NTAP];
             colt[0] = win + (ncv - R - wd.n0) * nrp - wd.m0 - R;
@@ -506,7 +509,7 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                         gd[t] = gn - gp;
                         gp = gn;
                     }
-                    const float lkx = lscf * __builtin_amdgcn_sqrtf((float)(r2 + dz2[ph])) * xv[ph];
+                    const float lkx = lscf * __builtin_amdgcn_sqrtf(r2 + dz2[ph]) * xv[ph];
                     float c[NTAP];
 #pragma unroll
                     for (int sg = 0; sg < NTAP; ++sg) c[sg] = lkx * (float)gd[sg];
