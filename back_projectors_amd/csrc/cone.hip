@@ -217,10 +217,12 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                 const bool wide = wrow > 2.0 * R;
                 // slice k0 sits dz0 above the source; w + R + 1/2 in 32.32 fixed point
                 const double dz0 = slice_z(g, k0) - vk.zsrc;
-                const double t0 = (q.mr * dz0 + g.crow) + (0.5 + (double)R);
+                // (clamped into the integer range first: a row that far off is off
+                // the detector for every slice of the chunk either way)
+                const double t0 = fmin(fmax((q.mr * dz0 + g.crow) + (0.5 + (double)R), -1e9), 1e9);
                 const double fl0 = floor(t0);
                 uint64_t wfx = ((uint64_t)(uint32_t)(int)fl0 << 32) | (uint64_t)(uint32_t)((t0 - fl0) * 4294967296.0);
-                const uint64_t afx = (uint64_t)(wrow * 4294967296.0 + 0.5);
+                const uint64_t afx = (uint64_t)(fmin(wrow, 1e6) * 4294967296.0 + 0.5);
                 const float r2f = (float)q.r2, dvf = (float)g.dv;
                 float dzf = (float)dz0;
                 // the slice count, re-read per view so that the per-slice tests
@@ -240,9 +242,10 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                     // slices past the chunk's last one get an empty row range
                     // (a uniform bound, so the test stays one compare); the
                     // range is one row wider each side than the taps need, and
-                    // the edge branch below decides those rows in fp64
+                    // the edge branch below decides those rows in fp64, as it
+                    // decides every slice of a wide footprint
                     const unsigned rl1 = k < nkv ? rlim + 3u : 0u;
-                    if ((unsigned)(hk + 1) < rl1) {
+                    if ((unsigned)(hk + 1) < rl1 || (wide && k < nkv)) {
                         float gw[NTAP];
                         int hr = hk;                            // tap centre row + R
                         bool ok = true;
