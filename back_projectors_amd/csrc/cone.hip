@@ -246,7 +246,28 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                     // decides every slice of a wide footprint
                     const unsigned rl1 = k < nkv ? rlim + 3u : 0u;
                     if ((unsigned)(hk + 1) < rl1 || (wide && k < nkv)) {
+                        // inside the detector, a footprint no wider than 2R
+                        // rows: cell edges sit at (j - R) - phi with phi = fr
+                        // 2^-32 = w_k - m_k + 1/2, the outermost ones (j = 0 and
+                        // 2R + 1) beyond the footprint, so their clamps are the
+                        // footprint's own edges; the 1e-7 absolute error of fp32
+                        // clamps stays far below the tolerance.  Formed for
+                        // every lane (straight-line code); the branch below
+                        // replaces it where it does not apply.
                         float gw[NTAP];
+                        {
+                            const float phr = (float)fr;
+                            float gp = -hrow;
+#pragma unroll
+                            for (int t = 0; t < NTAP; ++t) {
+                                const float gn =
+                                    t == NTAP - 1
+                                        ? hrow
+                                        : __builtin_amdgcn_fmed3f(fmaf(phr, -0x1p-32f, (float)(t + 1 - R)), -hrow, hrow);
+                                gw[t] = gn - gp;
+                                gp = gn;
+                            }
+                        }
                         int hr = hk;                            // tap centre row + R
                         bool ok = true;
                         if (wide || ib < 0 || (unsigned)(hk - 2 * R) > (unsigned)ib) {
@@ -256,14 +277,13 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                             // the tap row is the model's at an exact half, and a
                             // footprint edge on a cell boundary gives an exactly
                             // empty tap there (a voxel that only grazes the
-                            // detector then adds exactly nothing).  A voxel whose rows graze
-                            // that edge in every view sums nothing but thin
-                            // edge taps, so each tap is the overlap min(1,
+                            // detector then adds exactly nothing).  A voxel whose
+                            // rows graze that edge in every view sums nothing but
+                            // thin edge taps, so each tap is the overlap min(1,
                             // b_t - lo, hi - b_(t-1), hi - lo) of its cell
-                            // [b_(t-1), b_t] with the footprint [lo, hi], with
-                            // lo and hi carried as fp32 pairs: a thin tap is
-                            // then an exact difference of nearby numbers plus
-                            // the low part
+                            // [b_(t-1), b_t] with the footprint [lo, hi], with lo
+                            // and hi carried as fp32 pairs: a thin tap is then an
+                            // exact difference of nearby numbers plus the low part
                             const double dz = slice_z(g, k0v + k) - vk.zsrc;
                             const double wk = q.mr * dz + g.crow;    // product, then sum (no contraction)
                             const double mk = rint(wk);
@@ -279,25 +299,6 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                                 const float xa = (bt - loh) - lol;
                                 const float ya = (hih - (bt - 1.f)) + hil;
                                 gw[t] = __builtin_amdgcn_fmed3f(fminf(xa, ya), 0.f, wcap);
-                            }
-                        } else {
-                            // inside the detector, a footprint no wider than
-                            // 2R rows: cell edges sit at (j - R) - phi with phi
-                            // = fr 2^-32 = w_k - m_k + 1/2, the outermost ones
-                            // (j = 0 and 2R + 1) beyond the footprint, so their
-                            // clamps are the footprint's own edges; the 1e-7
-                            // absolute error of fp32 clamps stays far below
-                            // the tolerance
-                            const float phr = (float)fr;
-                            float gp = -hrow;
-#pragma unroll
-                            for (int t = 0; t < NTAP; ++t) {
-                                const float gn =
-                                    t == NTAP - 1
-                                        ? hrow
-                                        : __builtin_amdgcn_fmed3f(fmaf(phr, -0x1p-32f, (float)(t + 1 - R)), -hrow, hrow);
-                                gw[t] = gn - gp;
-                                gp = gn;
                             }
                         }
                         if (ok) {
