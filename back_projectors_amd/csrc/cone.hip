@@ -517,17 +517,19 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                     float c[NTAP];
 #pragma unroll
                     for (int sg = 0; sg < NTAP; ++sg) c[sg] = lkx * (float)gd[sg];
-                    const int mo = ok ? (int)mk : R;
+                    // one exec mask for the 2R + 1 rounds (the lanes of a round
+                    // are the same in every round)
+                    if (ok) {
+                        const int mo = (int)mk;
 #pragma unroll
-                    for (int sg = 0; sg < NTAP; ++sg) {
-                        if (ok) {
+                        for (int sg = 0; sg < NTAP; ++sg) {
                             float old[NTAP];
 #pragma unroll
                             for (int t = 0; t < NTAP; ++t) old[t] = colt[t][mo + sg];
 #pragma unroll
                             for (int t = 0; t < NTAP; ++t) colt[t][mo + sg] = fmaf(h[t], c[sg], old[t]);
+                            __atomic_signal_fence(__ATOMIC_SEQ_CST);
                         }
-                        __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     }
                 }
             };
