@@ -479,8 +479,10 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             const double mr = rl_d(mrq, q);
             const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r2q), q));
             const float lscf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lscq), q));
-            // the row box: half width mr dv / 2 (its negation is an operand modifier)
-            const double hw = 0.5 * (mr * g.dv), nhw = -hw;
+            // the row box: width mr dv, half width hw (its negation is an operand
+            // modifier)
+            const double wbox = mr * g.dv;
+            const double hw = 0.5 * wbox, nhw = -hw;
             // this pixel's 2R+1 window columns
             float *colt[NTAP];
             colt[0] = win + (ncv - R - wd.n0) * nrp - wd.m0 - R;
@@ -506,12 +508,28 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                     const bool ok = kk < nk && mk >= -R && mk <= g.nr - 1 + R;
                     const double f = wk - mk;
                     double gd[NTAP];
-                    double gp = NARROW ? nhw : fmin(fmax((-0.5 - (double)R) - f, nhw), hw);
+                    if constexpr (R == 1 && NARROW) {
+                        // the box [-h, h] and the cells around it, whose inner
+                        // edges sit at -(1/2 + f) and 1/2 - f (both exact): the
+                        // outer taps are max(h - (1/2 + f), 0) and
+                        // max(h - (1/2 - f), 0), each one rounding of the exact
+                        // value, as the model's overlap gives it (a tap of a
+                        // footprint that only touches its cell can be 1e-15 and
+                        // alone in its sinogram cell); the middle one is never
+                        // thin (at least min(h, 1/2)), so the box width minus
+                        // the outer two is accurate
+                        gd[0] = fmax(hw - (0.5 + f), 0.0);
+                        gd[2] = fmax(hw - (0.5 - f), 0.0);
+                        gd[1] = (wbox - gd[0]) - gd[2];
+                    } else {
+                        double gp = NARROW ? nhw : fmin(fmax((-0.5 - (double)R) - f, nhw), hw);
 #pragma unroll
-                    for (int t = 0; t < NTAP; ++t) {
-                        const double gn = (NARROW && t == NTAP - 1) ? hw : fmin(fmax(((double)(t - R) + 0.5) - f, nhw), hw);
-                        gd[t] = gn - gp;
-                        gp = gn;
+                        for (int t = 0; t < NTAP; ++t) {
+                            const double gn =
+                                (NARROW && t == NTAP - 1) ? hw : fmin(fmax(((double)(t - R) + 0.5) - f, nhw), hw);
+                            gd[t] = gn - gp;
+                            gp = gn;
+                        }
                     }
                     const float lkx = lscf * __builtin_amdgcn_sqrtf(r2 + dz2[ph]) * xv[ph];
                     float c[NTAP];
