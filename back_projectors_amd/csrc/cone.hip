@@ -136,33 +136,31 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
         const int lo = __builtin_amdgcn_readlane((int)pv, 2 * e), hi = __builtin_amdgcn_readlane((int)pv, 2 * e + 1);
         return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
     };
-    // window cells, flattened with channels fastest (coalesced reads)
-    auto stage_load = [&](int v, const Window &w, float (&st)[STG]) {
+    // window cells, flattened with channels fastest (coalesced reads); each
+    // cell's LDS offset is kept from the load for the store (-1: none)
+    auto stage_load = [&](int v, const Window &w, float (&st)[STG], int (&sa)[STG]) {
         const float rnw = 1.0f / (float)max(w.nw, 1);
 #pragma unroll
         for (int u = 0; u < STG; ++u) {
             st[u] = 0.f;
+            sa[u] = -1;
             if (u < stg) {
                 const int e = tid + NT * u;
                 const int m = (int)(((float)e + 0.5f) * rnw);   // exact: e < 2^22 and nw is small
                 const int c = e - m * w.nw;
                 const int row = w.m0 + m, n = w.n0 + c;
-                if (w.nw > 0 && m < w.nrw && row >= 0 && row < g.nr && n >= 0 && n < g.nc)
-                    st[u] = sino[((int64_t)v * g.nr + row) * g.nc + n];
+                if (w.nw > 0 && m < w.nrw) {
+                    sa[u] = c * NRP + m;
+                    if (row >= 0 && row < g.nr && n >= 0 && n < g.nc)
+                        st[u] = sino[((int64_t)v * g.nr + row) * g.nc + n];
+                }
             }
         }
     };
-    auto stage_store = [&](float *buf, const Window &w, const float (&st)[STG]) {
-        const float rnw = 1.0f / (float)max(w.nw, 1);
+    auto stage_store = [&](float *buf, const float (&st)[STG], const int (&sa)[STG]) {
 #pragma unroll
-        for (int u = 0; u < STG; ++u) {
-            if (u < stg) {
-                const int e = tid + NT * u;
-                const int m = (int)(((float)e + 0.5f) * rnw);
-                const int c = e - m * w.nw;
-                if (w.nw > 0 && m < w.nrw) buf[c * NRP + m] = st[u];
-            }
-        }
+        for (int u = 0; u < STG; ++u)
+            if (u < stg && sa[u] >= 0) buf[sa[u]] = st[u];
     };
 
     if (g.nv > 0) {
@@ -173,8 +171,9 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
         {
             const Window w0 = win_of(pcur);
             float st[STG];
-            stage_load(0, w0, st);
-            stage_store(win, w0, st);
+            int sa[STG];
+            stage_load(0, w0, st, sa);
+            stage_store(win, st, sa);
         }
         __syncthreads();
         for (int v = 0; v < g.nv; ++v) {
@@ -182,10 +181,11 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
             const Window wv = win_of(pcur);
             const Window wn = win_of(pnext);
             float st[STG];
+            int sa[STG];
             int nnext = INT32_MIN;
             uint32_t pafter = pnext;
             if (more) {
-                stage_load(v + 1, wn, st);
+                stage_load(v + 1, wn, st, sa);
                 nnext = valid ? idx[(int64_t)(v + 1) * np + p] : INT32_MIN;
                 fetch_view(min(v + 2, g.nv - 1), pafter);
             }
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                     }
                 }
             }
-            if (more) stage_store(win + ((v + 1) & 1) * wsz, wn, st);
+            if (more) stage_store(win + ((v + 1) & 1) * wsz, st, sa);
             __syncthreads();
             pcur = pnext;
             pnext = pafter;
