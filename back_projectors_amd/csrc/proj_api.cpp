@@ -278,9 +278,8 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         // fewer, which one slice per lane covers without idle lanes
         plan.fwd_spl = S > 16 ? 2 : 1;
         plan.fwd_sl = 16 * plan.fwd_spl;
-        const int frs = plan.fwd_spl == 2 ? FRS2 : FRS;
-        plan.rsx = (int)std::min<int64_t>(frs, Nx);
-        plan.rsy = (int)std::min<int64_t>(frs, Ny);
+        plan.rsx = (int)std::min<int64_t>(plan.fwd_spl == 2 ? FRS2X : FRS, Nx);
+        plan.rsy = (int)std::min<int64_t>(plan.fwd_spl == 2 ? FRS2Y : FRS, Ny);
         plan.fwd_lds = (size_t)plan.rsx * plan.rsy * 16 * plan.fwd_spl * sizeof(float);
         plan.fwd_cb = (int)C + 2 * (plan.ntap - 1);
         plan.fwd_s16 = (int)(((S + 16 * plan.fwd_spl - 1) / (16 * plan.fwd_spl)) * 16 * plan.fwd_spl);

@@ -116,11 +116,11 @@ def test_largest_shapes_plan(bp):
 
 @pytest.mark.parametrize("slices,words", [
     (16, ("48x48 px tile", "lanes=16 slices x 4 views", ", 16 slices,")),
-    (17, ("32x32 px tile", "lanes=16 x 4 views with 2 slices each", ", 32 slices,")),
-    (64, ("32x32 px tile", "lanes=16 x 4 views with 2 slices each", ", 32 slices,")),
+    (17, ("40x32 px tile", "lanes=16 x 4 views with 2 slices each", ", 32 slices,")),
+    (64, ("40x32 px tile", "lanes=16 x 4 views with 2 slices each", ", 32 slices,")),
 ])
 def test_region_walk_slices_per_lane(bp, slices, words):
-    """The tile forward walks two slices per lane (32-slice chunks over 32x32
+    """The tile forward walks two slices per lane (32-slice chunks over 40x32
     regions) unless the volume has 16 slices or fewer (one slice per lane,
     16-slice chunks over 48x48 regions)."""
     desc = bp.plan_query(base_geo(num_views=720, angles=np.arange(720) * np.pi / 720, forward_strategy=1),
