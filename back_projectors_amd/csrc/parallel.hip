@@ -17,16 +17,20 @@
 // written once and nothing collides.
 //
 // Forward (scatter with no colliding LDS or register updates): a workgroup
-// owns an FTX x FTY pixel tile and a chunk of 64 slices; lanes are slices and
-// each wave works on one view at a time.  The tile's voxels sit in LDS.  A
-// wave walks the tile's pixels in the order of their first tap channel, which
-// the creation pass fixed per (view, tile) together with how far the walk's
-// channel window moves after each pixel, so the walk has no comparisons: NTAP
-// registers hold the current channels and a channel the walk leaves behind is
-// stored once into the wave's own LDS window.  The window is then added to the
-// sinogram with coalesced global atomics, one per cell per view and tile.
-// Float atomics in LDS are avoided on purpose: on gfx950 they cost tens of
-// times a plain read-modify-write.
+// holds a region of pixels (40 x 32, or 48 x 48 when the volume has 16 slices
+// or fewer) and a chunk of 32 (16) slices in LDS and walks every view of its
+// view range over it.  Each 16-lane row of a wave walks one view, its lanes
+// holding two slices (16 apart) or one; the creation pass sorted the region's
+// pixels by first tap channel per view (paragraph "Forward scatters, back
+// gathers": the sort by channel, done once per geometry) and stored the walk
+// as records that reach the lanes by DPP row broadcasts.  A view's NTAP
+// current channels live in ring accumulators (channel n in accumulator n mod
+// NTAP), so a step touches each exactly once; a channel the walk has passed is
+// added once, with a global atomic of 16 slices per row, to a slice-fastest
+// accumulation buffer, which a second kernel transposes into the sinogram.
+// The gather strategy walks each view's list of all pixels the same way,
+// reading the voxels from memory.  Float atomics in LDS are avoided on
+// purpose: on gfx950 they cost tens of times a plain read-modify-write.
 #include <type_traits>
 #include <utility>
 
