@@ -77,8 +77,13 @@ PAR_TRUNC = W.Workload("parallel-26x30x18-21v-fine-r1", W.PARALLEL, 26, 30, 18, 
                        seed_x=61, seed_y=62)
 CONE_FINECH = W.Workload("cone-24x28x20-15v-finech", W.CONE_FLAT, 24, 28, 20, 15, 30, 110, dch=0.45, drow=1.2,
                          sid=50.0, sdd=75.0, seed_x=63, seed_y=64)
+# the same at radius 3: a batch forward's detector band (64 slices at up to
+# about 4.2 rows each, 7 channel taps) outgrows the band the LDS holds in the
+# high-magnification views, which then take the direct form
+CONE_TALL_R3 = W.Workload("cone-30x34x64-17v-tallrows-r3", W.CONE_FLAT, 30, 34, 64, 17, 128, 40, dch=2.0, drow=0.45,
+                          sid=60.0, sdd=70.0, radius=3, seed_x=49, seed_y=50)
 SMALL_CASES = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, PAR_R4, CONE_RAGGED, CONE_R2, CONE_R3,
-               CONE_R4, HELIX_SMALL, CONE_TALL, PAR_TRUNC, CONE_FINECH]
+               CONE_R4, HELIX_SMALL, CONE_TALL, PAR_TRUNC, CONE_FINECH, CONE_TALL_R3]
 
 
 def inputs(w):
