@@ -161,9 +161,11 @@ __global__ __launch_bounds__(SW * 64) void cone_back_pixels_kernel(const float *
 // Cone forward of a batch: per view the wave first adds its slices' taps into
 // an LDS band of the detector (the rows its 64 slices reach times the 2R + 1
 // channel taps; a slice's row never decreases with the slice, so the rows in
-// range form one band, from the first to the last lane in range), with LDS
-// float atomics because two slices can share a row, and then adds the band
-// to the sinogram, one global atomic per touched cell, the channels of a row
+// range form one band, from the first to the last lane in range), as plain
+// read-modify-writes in `stride` passes of the lanes whose slice is that
+// pass's modulo (the plan's stride makes the rows of one pass distinct, as in
+// the full cone forward; LDS float atomics cost tens of times more), and then
+// adds the band to the sinogram, one global atomic per touched cell, the channels of a row
 // adjacent (about 66 requests per view at 256^3 against 9 per slice when
 // every tap is its own global atomic).  A band taller than the LDS holds
 // (magnification far above one) takes the direct form.
@@ -174,7 +176,8 @@ __global__ __launch_bounds__(SW * 64) void cone_forward_pixels_kernel(const int3
                                                                       const float *__restrict__ cyl,
                                                                       float *__restrict__ sino,
                                                                       const int32_t *__restrict__ idx,
-                                                                      const ViewK *__restrict__ views, Geo g) {
+                                                                      const ViewK *__restrict__ views, Geo g,
+                                                                      int stride) {
     constexpr int NTAP = 2 * R + 1;
     constexpr int PROW = CPB_CELLS / NTAP;      // band rows at most
     __shared__ float band_all[SW * CPB_CELLS];
@@ -221,16 +224,24 @@ __global__ __launch_bounds__(SW * 64) void cone_forward_pixels_kernel(const int3
             }
             continue;
         }
-        if (ok) {
+        for (int ph = 0; ph < stride; ++ph) {        // uniform
+            if (ok && lane % stride == ph) {
 #pragma unroll
-            for (int sg = 0; sg < NTAP; ++sg) {
-                const int m = mk - R + sg;
-                if (m < lo || m > hi) continue;
-                const float c = lk * (float)gd[sg] * xv;
+                for (int sg = 0; sg < NTAP; ++sg) {
+                    const int m = mk - R + sg;
+                    if (m >= lo && m <= hi) {
+                        const float c = lk * (float)gd[sg] * xv;
+                        float *cell = band + (m - lo) * NTAP;
 #pragma unroll
-                for (int t = 0; t < NTAP; ++t)
-                    if (h[t] != 0.f) atomicAdd(&band[(m - lo) * NTAP + t], h[t] * c);
+                        for (int t = 0; t < NTAP; ++t) cell[t] = fmaf(h[t], c, cell[t]);
+                    }
+                    // a lane's next row is its neighbour's (in the pass) current
+                    // one: LDS operations of a wave run in order, and the fence
+                    // keeps the compiler from moving the next round up
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                }
             }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
         }
         // the band's adds are done (LDS operations of a wave complete in
         // order; the fence keeps the compiler from moving the reads up)
@@ -297,7 +308,8 @@ hipError_t launch_forward_pixels(const Plan &p, const int32_t *pix, int n, const
     hipError_t e = launch_fill_zero(sino, (int64_t)g.nv * g.nr * g.nc, st);
     if (e != hipSuccess || n == 0) return e;
     const dim3 grid((unsigned)((n + SW - 1) / SW), (unsigned)((g.ns + 63) / 64));
-    BPAMD_SUBSET_R(cone_forward_pixels_kernel, grid, dim3(SW * 64), 0, st, pix, n, cyl, sino, p.idx, p.views, g)
+    BPAMD_SUBSET_R(cone_forward_pixels_kernel, grid, dim3(SW * 64), 0, st, pix, n, cyl, sino, p.idx, p.views, g,
+                   p.cone_stride)
     return hipGetLastError();
 }
 
