@@ -146,8 +146,11 @@ void slab_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_,
                     if (hi >= lo) {
                         const int klo = (int)lo, nact = (int)hi - klo + 1;
                         const int nit_unit = (nact + 63) / 64;
-                        // consecutive slices are dv apart: their rows differ by mr dv
-                        const bool unit = stride > 1 && mlo * g.dv >= 1.0 + 1e-9 && nit_unit < stride;
+                        // consecutive slices are dv apart: their rows differ by mr dv.
+                        // Unit stride also where it takes as many passes: the rows
+                        // of one instruction then sit about mr apart instead of
+                        // stride * mr, which spreads them over more LDS banks
+                        const bool unit = stride > 1 && mlo * g.dv >= 1.0 + 1e-9 && nit_unit <= stride;
                         s.n0 = unit ? klo : 0;
                         s.nw = unit ? nit_unit : stride;
                         s.m0 = unit ? 1 : 0;
