@@ -82,8 +82,14 @@ CONE_FINECH = W.Workload("cone-24x28x20-15v-finech", W.CONE_FLAT, 24, 28, 20, 15
 # high-magnification views, which then take the direct form
 CONE_TALL_R3 = W.Workload("cone-30x34x64-17v-tallrows-r3", W.CONE_FLAT, 30, 34, 64, 17, 128, 40, dch=2.0, drow=0.45,
                           sid=60.0, sdd=70.0, radius=3, seed_x=49, seed_y=50)
+# a short source distance: the planned stride is 2 (row magnification down to
+# 0.73), while the tiles nearest the source (magnification at least 1) walk
+# consecutive slices, over 64 of them, in as many passes as the stride; 128
+# rows cut the longest cylinders
+CONE_UNIT = W.Workload("cone-20x24x100-12v-unitwalk", W.CONE_FLAT, 20, 24, 100, 12, 128, 48, dch=1.5, drow=1.5,
+                       sid=40.0, sdd=60.0, seed_x=65, seed_y=66)
 SMALL_CASES = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, PAR_R4, CONE_RAGGED, CONE_R2, CONE_R3,
-               CONE_R4, HELIX_SMALL, CONE_TALL, PAR_TRUNC, CONE_FINECH, CONE_TALL_R3]
+               CONE_R4, HELIX_SMALL, CONE_TALL, PAR_TRUNC, CONE_FINECH, CONE_TALL_R3, CONE_UNIT]
 
 
 def inputs(w):
