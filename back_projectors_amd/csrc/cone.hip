@@ -618,17 +618,41 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                 q = qa;
             }
         }
-        // add the window to the sinogram: lanes along channels, coalesced
-        const int total = wd.nw * wd.nrw;
-        const float rnw = 1.0f / (float)wd.nw;
-        for (int e = lane; e < total; e += 64) {
-            const int m = (int)(((float)e + 0.5f) * rnw);
-            const int c = e - m * wd.nw;
-            const float val = win[c * nrp + m];
-            win[c * nrp + m] = 0.f;
-            const int row = wd.m0 + m, n = wd.n0 + c;
-            if (val != 0.f && row >= 0 && row < g.nr && n >= 0 && n < g.nc)
-                unsafeAtomicAdd(&sino[((int64_t)v * g.nr + row) * g.nc + n], val);
+        // add the window to the sinogram: lanes along channels, coalesced.
+        // A window of at most 64 channels goes dm = 64 / nw rows per step,
+        // each lane keeping one channel (lanes past dm * nw idle), so the LDS
+        // offset, the sinogram offset and the row advance by uniform steps;
+        // a wider one walks its cells in order, 64 per step.  (The view's
+        // sinogram is under 2^31 cells.)
+        const int nw = wd.nw, nrw = wd.nrw;
+        float *sv = sino + (int64_t)v * g.nr * g.nc;
+        if (nw <= 64) {
+            const int dm = 64 / nw;
+            const int m1 = (int)(((float)lane + 0.5f) * (1.0f / (float)nw));
+            if (m1 < dm) {
+                const int c = lane - m1 * nw;
+                const int n = wd.n0 + c;
+                const bool nok = (unsigned)n < (unsigned)g.nc;
+                int row = wd.m0 + m1, lo = c * nrp + m1, go = row * g.nc + n;
+                const int rend = wd.m0 + nrw, gs = dm * g.nc;
+                for (; row < rend; row += dm, lo += dm, go += gs) {
+                    const float val = win[lo];
+                    win[lo] = 0.f;
+                    if (val != 0.f && nok && (unsigned)row < (unsigned)g.nr) unsafeAtomicAdd(sv + go, val);
+                }
+            }
+        } else {
+            const int total = nw * nrw;
+            const float rnw = 1.0f / (float)nw;
+            for (int e = lane; e < total; e += 64) {
+                const int m = (int)(((float)e + 0.5f) * rnw);
+                const int c = e - m * nw;
+                const float val = win[c * nrp + m];
+                win[c * nrp + m] = 0.f;
+                const int row = wd.m0 + m, n = wd.n0 + c;
+                if (val != 0.f && (unsigned)row < (unsigned)g.nr && (unsigned)n < (unsigned)g.nc)
+                    unsafeAtomicAdd(sv + (row * g.nc + n), val);
+            }
         }
     };
 
