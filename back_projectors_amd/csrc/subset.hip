@@ -162,13 +162,13 @@ __global__ __launch_bounds__(SW * 64) void cone_back_pixels_kernel(const float *
 // an LDS band of the detector (the rows its 64 slices reach times the 2R + 1
 // channel taps; a slice's row never decreases with the slice, so the rows in
 // range form one band, from the first to the last lane in range), as plain
-// read-modify-writes in `stride` passes of the lanes whose slice is that
-// pass's modulo (the plan's stride makes the rows of one pass distinct, as in
-// the full cone forward; LDS float atomics cost tens of times more), and then
-// adds the band to the sinogram, one global atomic per touched cell, the channels of a row
-// adjacent (about 66 requests per view at 256^3 against 9 per slice when
-// every tap is its own global atomic).  A band taller than the LDS holds
-// (magnification far above one) takes the direct form.
+// read-modify-writes in `stride` passes, each taking the lanes whose slice is
+// that pass's residue (the plan's stride puts the rows of one pass on distinct
+// rows, as in the full cone forward; LDS float atomics cost tens of times
+// more).  Then it adds the band to the sinogram, one global atomic per touched
+// cell, the channels of a row adjacent (about 66 requests per view at 256^3
+// against 9 per slice when every tap is its own global atomic).  A band taller
+// than the LDS holds (magnification far above one) takes the direct form.
 constexpr int CPB_CELLS = 1536;         // LDS band cells per wave (rows x taps)
 
 template <int R>
