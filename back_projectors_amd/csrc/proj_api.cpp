@@ -348,7 +348,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         int stride = 1;
         while (stride * amin < 1.0 + 1e-9 && stride <= 3) ++stride;
         if (stride > 3)
-            return fail(PROJ_ERR_UNSUPPORTED, "row magnification below 1/3 (detector rows far finer than the voxels)");
+            return fail(PROJ_ERR_UNSUPPORTED, "row magnification below 1/3 (detector rows far coarser than the voxels)");
         plan.cone_stride = stride;
         plan.fwd_sl = 64 * stride;
         const WinMax wf = max_window(g, views, CTX, CTY, plan.fwd_sl);

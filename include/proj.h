@@ -121,7 +121,13 @@ enum { PROJ_FORWARD_AUTO = 0, PROJ_FORWARD_TILE = 1, PROJ_FORWARD_GATHER = 2 };
  *   sino_shape   {V, R, C}, each >= 0; parallel beam requires R == S
  *   hip_device   HIP device ordinal the handle lives on
  *   out          receives the handle (NULL on error)
- * Limits: V*Ny*Nx, Ny*Nx*S and V*R*C below 2^31 elements.
+ * Limits: V*Ny*Nx, Ny*Nx*S and V*R*C below 2^31 elements.  Geometries the
+ * kernels cannot hold return PROJ_ERR_UNSUPPORTED, the reason in
+ * proj_last_error(): more than 7 channel taps per voxel, a detector window
+ * too large for the on-chip staging (channels or rows far finer than the
+ * voxels), or, for the cone, a row magnification below 1/3 anywhere in the
+ * scan (rows more than three voxel pitches apart, so that three slices can
+ * share a row).
  * Synchronises the device once (creation is not on the hot path).
  */
 proj_status proj_create(const proj_geometry *g, const int64_t recon_shape[3],

@@ -100,6 +100,7 @@ BAD = [
     ("detector 10x finer than voxels", base_geo(delta_channel=0.1), (8, 8, 4), (4, 4, 160), -2),
     ("cone detector 20x finer", base_geo(**dict(CONE, delta_channel=0.05, delta_row=0.05)), (8, 8, 4), (4, 200, 400),
      -2),
+    ("cone rows 8x coarser", base_geo(**dict(CONE, delta_row=8.0)), (8, 8, 4), (4, 6, 16), -2),
     ("forward strategy 3", base_geo(forward_strategy=3), (8, 8, 4), (4, 4, 16), -1),
     ("forward strategy -1", base_geo(forward_strategy=-1), (8, 8, 4), (4, 4, 16), -1),
     ("cone forward strategy", base_geo(**dict(CONE, forward_strategy=2)), (8, 8, 4), (4, 6, 16), -1),
@@ -127,6 +128,23 @@ def test_region_walk_slices_per_lane(bp, slices, words):
                          (256, 256, slices), (720, slices, 384))
     for word in words:
         assert word in desc, (word, desc)
+
+
+@pytest.mark.parametrize("w,stride", [
+    (W.scaled(W.get("cone-256x256x256-360v"), "cone-22x26x30-13v-coarserows", ny=22, nx=26, ns=30, nv=13, nr=24,
+              nc=40, dch=1.5, drow=3.0, sid=40.0, sdd=60.0), 3),
+    (W.scaled(W.get("cone-256x256x256-360v"), "cone-20x24x100-12v-unitwalk", ny=20, nx=24, ns=100, nv=12, nr=128,
+              nc=48, dch=1.5, drow=1.5, sid=40.0, sdd=60.0), 2),
+    (W.scaled(W.get("cone-256x256x256-360v"), "cone-20x24x18-11v", ny=20, nx=24, ns=18, nv=11, nr=24, nc=48,
+              dch=1.5, drow=0.9, sid=40.0, sdd=60.0), 1),
+], ids=lambda v: v if isinstance(v, int) else v.name)
+def test_cone_forward_slice_stride(bp, w, stride):
+    """Lanes of one cone forward instruction take slices `stride` apart, the
+    smallest stride at which the smallest row magnification over the scan
+    (rows per slice, at the volume's corners) puts them on distinct rows: the
+    chunk is 64 * stride slices."""
+    desc = bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape)
+    assert f"LDS window, {64 * stride} slices," in desc.split("forward:")[1], desc
 
 
 @pytest.mark.parametrize("strategy,word", [(1, "tile:"), (2, "gather:")])

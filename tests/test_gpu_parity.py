@@ -88,8 +88,12 @@ CONE_TALL_R3 = W.Workload("cone-30x34x64-17v-tallrows-r3", W.CONE_FLAT, 30, 34, 
 # rows cut the longest cylinders
 CONE_UNIT = W.Workload("cone-20x24x100-12v-unitwalk", W.CONE_FLAT, 20, 24, 100, 12, 128, 48, dch=1.5, drow=1.5,
                        sid=40.0, sdd=60.0, seed_x=65, seed_y=66)
+# detector rows coarser than the voxels (row magnification 0.38 to 0.74): the
+# cone forwards (full and batch) take slices three apart per instruction
+CONE_COARSE = W.Workload("cone-22x26x30-13v-coarserows", W.CONE_FLAT, 22, 26, 30, 13, 24, 40, dch=1.5, drow=3.0,
+                         sid=40.0, sdd=60.0, seed_x=67, seed_y=68)
 SMALL_CASES = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, PAR_R4, CONE_RAGGED, CONE_R2, CONE_R3,
-               CONE_R4, HELIX_SMALL, CONE_TALL, PAR_TRUNC, CONE_FINECH, CONE_TALL_R3, CONE_UNIT]
+               CONE_R4, HELIX_SMALL, CONE_TALL, PAR_TRUNC, CONE_FINECH, CONE_TALL_R3, CONE_UNIT, CONE_COARSE]
 
 
 def inputs(w):
