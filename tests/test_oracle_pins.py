@@ -7,6 +7,7 @@ linearity, partition of unity, symmetry), the physics of a voxel's projection,
 or limits where one geometry reduces to another.
 """
 import math
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -47,6 +48,14 @@ SMALL_HELIX = W.Workload("helical-20x20x10-23v", W.CONE_FLAT, 20, 20, 10, 23, 8,
                          angle_step=2 * math.pi / 10, zsrc_step=0.4, seed_x=9, seed_y=10)
 SMALL_TRANS = W.Workload("translation-16x24x4-9v", W.PARALLEL, 16, 24, 4, 9, 4, 64,
                          shift_step=3.0, seed_x=11, seed_y=12)
+
+# A cone whose channel and row pitches differ, with a source close enough that
+# off-centre pixels see the central ray at 5-25 degrees: the in-plane ray
+# direction theta - gamma and theta + gamma then give clearly different box
+# widths, and a magnification built from the wrong pitch moves every voxel.
+PITCH_CONE = W.Workload("cone-20x24x10-9v-pitch", W.CONE_FLAT, 20, 24, 10, 9, 32, 120,
+                        dch=1.3, drow=1.1, sid=40.0, sdd=70.0,
+                        angle_step=0.61, seed_x=31, seed_y=32)
 
 
 # --------------------------------------------------------------------- ov ---
@@ -259,7 +268,8 @@ def _box_cell_quadrature(d, a, q=20000):
     return float(np.mean(np.abs(t) <= a / 2))
 
 
-@pytest.mark.parametrize("w", [W.get("cone-256x256x256-360v"), SMALL_HELIX], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [W.get("cone-256x256x256-360v"), SMALL_HELIX, PITCH_CONE],
+                         ids=lambda w: w.name)
 def test_cone_rows_follow_perspective(orc, w):
     """The row profile of a voxel is its magnified height (SDD/D * dv) centred
     on the perspective projection of its centre onto the flat detector.  Row
@@ -293,6 +303,151 @@ def test_cone_rows_follow_perspective(orc, w):
             assert abs(rows.get(r_, 0.0) - expect) < 3e-4
         checked += 1
     assert checked > 50
+
+
+def _pixel_chords(src, ea, eb, cch, dch, sdd, sid, px, py, dv, t):
+    """Length of the in-plane ray from the source to the detector point at
+    channel coordinate t inside the square pixel centred at (px, py): slab
+    clipping against the pixel's four edges, exact for straight rays."""
+    q = ((t - cch) * dch)[:, None] * ea[None, :] + (sdd - sid) * eb[None, :]
+    d = q - src[None, :]
+    lo = np.array([px - dv / 2, py - dv / 2])
+    hi = np.array([px + dv / 2, py + dv / 2])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t0 = (lo[None, :] - src[None, :]) / d
+        t1 = (hi[None, :] - src[None, :]) / d
+    enter = np.minimum(t0, t1).max(axis=1)
+    leave = np.maximum(t0, t1).min(axis=1)
+    return np.maximum(leave - enter, 0.0) * np.linalg.norm(d, axis=1)
+
+
+def _half_max_window(t, prof):
+    """Peak value and the two half-maximum crossings of a sampled profile
+    (linear interpolation between samples)."""
+    pk = float(prof.max())
+    half = pk / 2
+    above = np.flatnonzero(prof >= half)
+    i0, i1 = above[0], above[-1]
+    tl = t[i0 - 1] + (half - prof[i0 - 1]) * (t[i0] - t[i0 - 1]) / (prof[i0] - prof[i0 - 1])
+    tr = t[i1] + (half - prof[i1]) * (t[i1 + 1] - t[i1]) / (prof[i1 + 1] - prof[i1])
+    return pk, tl, tr
+
+
+def cone_inplane_shadow_errors(vp_params, w: W.Workload, min_gamma_deg=5.0):
+    """For every (view, pixel) of a cone workload whose centre sees the central
+    ray at |gamma| >= min_gamma_deg, the exact in-plane shadow of the square
+    pixel on the flat detector: chord lengths of the rays from the source
+    through the pixel, sampled over the span of its four projected corners.
+    Returns the worst deviations of the reference's box from that shadow:
+    centre (channels) against the half-maximum window's midpoint, width
+    (relative) against the full width at half maximum, and height (relative)
+    against the longest chord.  vp_params(v, i, j) returns the reference's
+    per-(view, pixel) parameters."""
+    ang = w.angles()
+    cch = (w.nc - 1) / 2
+    worst = dict(centre=0.0, width=0.0, height=0.0, n=0)
+    for v, th in enumerate(ang):
+        ea = np.array([math.cos(th), math.sin(th)])
+        eb = np.array([-math.sin(th), math.cos(th)])
+        src = -w.sid * eb
+        for i in range(w.ny):
+            for j in range(w.nx):
+                p = np.array([(j - (w.nx - 1) / 2) * w.dv, (i - (w.ny - 1) / 2) * w.dv])
+                if abs(math.degrees(math.atan2(float(p @ ea), w.sid + float(p @ eb)))) < min_gamma_deg:
+                    continue
+                corners = np.array([[p[0] + sx * w.dv / 2, p[1] + sy * w.dv / 2]
+                                    for sx in (-1, 1) for sy in (-1, 1)])
+                tc = w.sdd * (corners @ ea) / (w.sid + corners @ eb) / w.dch + cch
+                t = np.linspace(tc.min() - 0.05, tc.max() + 0.05, 4001)
+                prof = _pixel_chords(src, ea, eb, cch, w.dch, w.sdd, w.sid, p[0], p[1], w.dv, t)
+                pk, tl, tr = _half_max_window(t, prof)
+                prm = vp_params(v, i, j)
+                worst["centre"] = max(worst["centre"], abs((tl + tr) / 2 - prm["u"]))
+                worst["width"] = max(worst["width"], abs((tr - tl) - prm["W"]) / prm["W"])
+                worst["height"] = max(worst["height"], abs(pk - prm["L"]) / prm["L"])
+                worst["n"] += 1
+    return worst
+
+
+# The shadow is the box only up to the perspective across one pixel: the
+# deviations grow like dv / D (D between 24 and 56 voxels here).
+INPLANE_TOL = dict(centre=0.02, width=0.01, height=0.01)
+
+
+@pytest.mark.parametrize("w", [PITCH_CONE, SMALL_HELIX], ids=lambda w: w.name)
+def test_cone_inplane_footprint_is_the_pixel_shadow(orc, w):
+    """B3/P8 in the plane: the cone's channel box (centre u, width W_ch,
+    height L_xy) is the pixel's shadow on the flat detector, traced from the
+    source through the pixel's square.  The centre is where the shadow's
+    half-maximum window sits, the width its full width at half maximum, the
+    height its longest chord.  This fixes the in-plane ray direction used for
+    the box (a sign slip in theta -/+ gamma changes the width and height by up
+    to 40% here), the 1/cos(gamma) obliquity of the flat detector and the
+    channel magnification's pitch (the channel pitch differs from the row
+    pitch in the first geometry)."""
+    g = make(orc, w)
+    worst = cone_inplane_shadow_errors(lambda v, i, j: orc.vp_params(g, v, i, j), w)
+    assert worst["n"] > 300
+    for key, tol in INPLANE_TOL.items():
+        assert worst[key] < tol, (key, worst)
+
+
+def _mutant(orc, tmp_path, old, new):
+    """A copy of the reference built on the CPU from its own source with one
+    line changed, exposing the per-(view, pixel) parameters and the voxel taps
+    through the same interface as the reference module."""
+    import ctypes
+    import subprocess
+    import types
+    src = open(os.path.join(os.path.dirname(orc.__file__), "proj_oracle.c")).read()
+    assert src.count(old) == 1, "the planted line no longer matches the reference's source"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", *orc.CFLAGS, "-o", lib_path, str(path), "-lm"], check=True)
+    lib = ctypes.CDLL(lib_path)
+    f64 = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+    i32 = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+    lib.orc_vp_params.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, f64]
+    lib.orc_voxel_taps.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 4 + [i32, i32, f64, ctypes.c_int]
+    lib.orc_voxel_taps.restype = ctypes.c_int
+
+    def vp_params(g, v, i, j):
+        out = np.zeros(7, np.float64)
+        lib.orc_vp_params(ctypes.addressof(g.s), v, i, j, out)
+        return dict(u=out[0], nc=int(out[1]), W=out[2], L=out[3], Mr=out[4], rho=out[5], Wrow=out[6])
+
+    def voxel_taps(g, v, i, j, k):
+        cap = (2 * g.s.radius + 1) ** 2
+        rows, chans, w = np.zeros(cap, np.int32), np.zeros(cap, np.int32), np.zeros(cap, np.float64)
+        n = lib.orc_voxel_taps(ctypes.addressof(g.s), v, i, j, k, rows, chans, w, cap)
+        return [(int(rows[q]), int(chans[q]), float(w[q])) for q in range(n)]
+
+    return types.SimpleNamespace(Geometry=orc.Geometry, vp_params=vp_params, voxel_taps=voxel_taps)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("old,new", [
+    ("double alpha = g->angles[v] - gam;", "double alpha = g->angles[v] + gam;"),
+    ("double mc = g->sdd / dc;", "double mc = g->sdd / drw;"),
+    ("o->w = mc * g->dv * m / cos(gam);", "o->w = mc * g->dv * m;"),
+    ("double mr = g->sdd / drw;", "double mr = g->sdd / dc;"),
+], ids=["theta_plus_gamma", "mc_from_row_pitch", "no_obliquity", "mr_from_channel_pitch"])
+def test_cone_footprint_pins_catch_planted_mistakes(orc, tmp_path, old, new):
+    """The cone footprint pins reject a copy of the reference with one
+    plausible mistake planted in its footprint: the in-plane shadow pin or
+    the perspective row pin fails on the geometry whose pitches differ."""
+    mut = _mutant(orc, tmp_path, old, new)
+    w = PITCH_CONE
+    g = make(mut, w)
+    worst = cone_inplane_shadow_errors(lambda v, i, j: mut.vp_params(g, v, i, j), w)
+    inplane_caught = any(worst[k] > 2 * tol for k, tol in INPLANE_TOL.items())
+    try:
+        test_cone_rows_follow_perspective(mut, w)
+        rows_caught = False
+    except AssertionError:
+        rows_caught = True
+    assert inplane_caught or rows_caught, worst
 
 
 # ---------------------------------------------------------------- symmetry ---
