@@ -147,6 +147,26 @@ def test_cone_forward_slice_stride(bp, w, stride):
     assert f"LDS window, {64 * stride} slices," in desc.split("forward:")[1], desc
 
 
+def test_cone_forward_window_wider_than_a_flush_step(bp):
+    """Channels far finer than the magnified voxels: the cone forward's
+    detector window spans more than the 64 lanes of one flush step, which
+    then walks the window's cells in order (the GPU parity case of this
+    geometry runs that flush)."""
+    geo = dict(kind=1, num_views=5, angles=-0.05 + 0.025 * np.arange(5), delta_voxel=1.0, delta_channel=0.14,
+               delta_row=4.0, source_iso=200.0, source_detector=300.0, psf_radius=1)
+    desc = bp.plan_query(geo, (20, 24, 16), (5, 12, 300))
+    nw = int(re.search(r"forward: .*? window (\d+) ch", desc).group(1))
+    assert nw > 64, desc
+
+
+def test_helical_radius2_plans(bp):
+    """The helical scan at psf radius 2 (no truncated footprint) plans with
+    5x5 taps."""
+    w = W.scaled(W.get("helical-512x512x96-1338v"), "helical-r2", radius=2)
+    desc = bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape)
+    assert "radius=2 taps=5" in desc, desc
+
+
 @pytest.mark.parametrize("strategy,word", [(1, "tile:"), (2, "gather:")])
 def test_forward_strategy_is_honoured(bp, strategy, word):
     """A forced parallel forward strategy shows in the plan; AUTO picks one."""

@@ -92,8 +92,18 @@ CONE_UNIT = W.Workload("cone-20x24x100-12v-unitwalk", W.CONE_FLAT, 20, 24, 100, 
 # cone forwards (full and batch) take slices three apart per instruction
 CONE_COARSE = W.Workload("cone-22x26x30-13v-coarserows", W.CONE_FLAT, 22, 26, 30, 13, 24, 40, dch=1.5, drow=3.0,
                          sid=40.0, sdd=60.0, seed_x=67, seed_y=68)
+# channels about 11 times finer than the magnified voxels and rows 2.7 times
+# coarser, near-frontal views: the cone forward's detector window spans 89
+# channels, over the 64 lanes of a flush step (the flush then walks the
+# window's cells in order, 64 per step)
+CONE_WIDEWIN = W.Workload("cone-20x24x16-5v-widewindow", W.CONE_FLAT, 20, 24, 16, 5, 12, 300, dch=0.14, drow=4.0,
+                          sid=200.0, sdd=300.0, angle_step=0.025, angle_start=-0.05, seed_x=69, seed_y=70)
+# the small helical scan at psf radius 2: its footprints near the source are
+# up to 2.6 channels wide, which radius 1 truncates and radius 2 keeps whole
+HELIX_R2 = W.scaled(HELIX_SMALL, "helical-36x36x40-47v-r2", radius=2, seed_x=71, seed_y=72)
 SMALL_CASES = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, PAR_R4, CONE_RAGGED, CONE_R2, CONE_R3,
-               CONE_R4, HELIX_SMALL, CONE_TALL, PAR_TRUNC, CONE_FINECH, CONE_TALL_R3, CONE_UNIT, CONE_COARSE]
+               CONE_R4, HELIX_SMALL, CONE_TALL, PAR_TRUNC, CONE_FINECH, CONE_TALL_R3, CONE_UNIT, CONE_COARSE,
+               CONE_WIDEWIN, HELIX_R2]
 
 
 def inputs(w):
@@ -127,10 +137,10 @@ def test_small_parity(bp, orc, w):
     proj.close()
 
 
-def test_outputs_fully_overwritten_and_guards_untouched(bp, orc):
+@pytest.mark.parametrize("w", [PAR_RAGGED, CONE_RAGGED, HELIX_SMALL], ids=lambda w: w.name)
+def test_outputs_fully_overwritten_and_guards_untouched(bp, orc, w):
     """NaN-prefilled outputs come back fully written; canaries just outside
     the output ranges keep their values (adapted poison-the-padding test)."""
-    w = PAR_RAGGED
     note(f"guard bands {w.name}")
     proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
     x, y = inputs(w)
@@ -153,6 +163,49 @@ def test_outputs_fully_overwritten_and_guards_untouched(bp, orc):
     g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
     yo, ay = orc.forward(g, x, with_abs=True)
     assert_close(s[pad:-pad].reshape(w.sino_shape), yo, ay, "forward into a view")
+    xo, ax = orc.back(g, y, with_abs=True)
+    assert_close(r[pad:-pad].reshape(w.recon_shape), xo, ax, "back into a view")
+    proj.close()
+
+
+def test_overlapping_buffers_rejected_before_any_write(bp):
+    """Every call that takes two caller buffers returns PROJ_ERR_ALIAS when
+    they overlap, through the C ABI, and leaves both untouched (the check runs
+    before any launch).  (proj_channel_index's alias check guards the
+    handle's own table, whose address the ABI never hands out.)"""
+    import ctypes
+    w = CONE_RAGGED
+    note(f"alias checks {w.name}")
+    lib = bp.load_library()
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    h = proj._h
+    nr, ns = int(np.prod(w.recon_shape)), int(np.prod(w.sino_shape))
+    buf = torch.full((nr + ns,), 3.0, device="cuda:0")
+    base = buf.data_ptr()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    # recon and sinogram sharing their last/first 4 bytes, or fully the same memory
+    for rec, sino in ((base, base + 4 * (nr - 1)), (base, base)):
+        assert lib.proj_forward(h, ctypes.c_void_p(rec), ctypes.c_void_p(sino), stream) == -3
+        assert lib.proj_back(h, ctypes.c_void_p(sino), ctypes.c_void_p(rec), stream) == -3
+        assert lib.proj_back_squared(h, ctypes.c_void_p(sino), ctypes.c_void_p(rec), stream) == -3
+    # batches: pixel list, cylinders and sinogram, pairwise overlapping
+    n = 8
+    pix = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+    cyl = torch.full((n, w.ns), 3.0, device="cuda:0")
+    sino = torch.full(w.sino_shape, 3.0, device="cuda:0")
+    P = lambda t, off=0: ctypes.c_void_p(t.data_ptr() + off)
+    for pp, cc, ss in ((pix, cyl, cyl), (pix, pix, sino), (cyl, cyl, sino)):
+        st_f = lib.proj_forward_pixels(h, P(pp), ctypes.c_int64(n), P(cc), P(ss), stream)
+        st_b = lib.proj_back_pixels(h, P(ss), P(pp), ctypes.c_int64(n), P(cc), stream)
+        assert st_f == -3 and st_b == -3, (st_f, st_b)
+    assert "overlap" in lib.proj_last_error().decode()
+    torch.cuda.synchronize()
+    assert bool(torch.all(buf == 3.0)) and bool(torch.all(cyl == 3.0)) and bool(torch.all(sino == 3.0))
+    # disjoint buffers still work on the same handle afterwards
+    x, _ = inputs(w)
+    out = proj.forward(dev(x))
+    assert np.isfinite(host(out)).all()
     proj.close()
 
 
@@ -314,6 +367,20 @@ def test_full_forward_sampled_views(bp, orc, name, full_cache):
     assert_close(yg[views], yo, ay, f"{name} forward views {views}")
 
 
+@pytest.mark.parametrize("name", ["cone-256x256x256-360v", "helical-512x512x96-1338v"])
+def test_full_forward_dense_sampled_views(bp, orc, name, full_cache):
+    """The cone forward of a dense N(0,1) volume (every solver iterate is
+    dense; the phantom leaves most of each tile's detector window at zero and
+    skips those cells' flushes) on sampled views, against the reference."""
+    w, proj, g = full_setup(bp, orc, name, full_cache)
+    note(f"full dense forward {name}")
+    x = np.random.default_rng(101).standard_normal(w.recon_shape).astype(np.float32)
+    yg = host(proj.forward(dev(x)))
+    views = sorted({1, w.nv // 3, (2 * w.nv) // 3 + 1, w.nv - 2})
+    yo, ay = orc.forward_views(g, x, views, with_abs=True)
+    assert_close(yg[views], yo, ay, f"{name} dense forward views {views}")
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_back_sampled_pixels(bp, orc, name, full_cache):
     w, proj, g = full_setup(bp, orc, name, full_cache)
@@ -338,6 +405,43 @@ def test_full_adjoint_identity(bp, orc, name, full_cache):
     aty = host(proj.back(dev(y)))
     gap = adjoint_gap(ax, y, x, aty)
     assert gap < ADJOINT, f"{name}: adjoint gap {gap:.2e}"
+
+
+def test_full_helical_radius2(bp, orc, full_cache):
+    """The helical scan at psf radius 2, where no footprint is truncated (the
+    widest, near the source, span about 2.5 channels): bit-exact index on
+    sampled views, forward of the phantom and of a dense volume on sampled
+    views, back on sampled pixels, adjoint identity."""
+    full_cache.clear()
+    torch.cuda.empty_cache()
+    base = W.get("helical-512x512x96-1338v")
+    w = W.scaled(base, "helical-512x512x96-1338v-r2", radius=2)
+    note(f"full helical radius 2 {w.name}")
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    assert "radius=2 taps=5" in proj.describe()
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    views = [0, 335, 668, 1001, w.nv - 1]
+    geo = w.geometry()
+    sub = dict(geo, num_views=len(views), angles=geo["angles"][views], source_z=geo["source_z"][views])
+    gs = orc.Geometry(sub, w.recon_shape, (len(views), w.nr, w.nc))
+    assert np.array_equal(host(proj.channel_index())[views], orc.channel_index(gs))
+    for label, x in (("phantom", w.recon_input()),
+                     ("dense", np.random.default_rng(103).standard_normal(w.recon_shape).astype(np.float32))):
+        yg = host(proj.forward(dev(x)))
+        yo, ay = orc.forward_views(g, x, views, with_abs=True)
+        assert_close(yg[views], yo, ay, f"{w.name} forward of the {label} on views {views}")
+    y = w.sino_input()
+    xg = host(proj.back(dev(y))).reshape(w.ny * w.nx, w.ns)
+    rng = np.random.default_rng(79)
+    pix = np.unique(np.concatenate([rng.integers(0, w.ny * w.nx, 300), [0, w.ny * w.nx - 1,
+                                                                         (w.ny // 2) * w.nx + w.nx // 2]]))
+    xo, ax = orc.back_pixels(g, y, pix, with_abs=True)
+    assert_close(xg[pix], xo, ax, f"{w.name} back pixels")
+    x = w.recon_input()
+    gap = adjoint_gap(host(proj.forward(dev(x))), y, x, xg.reshape(w.recon_shape))
+    assert gap < ADJOINT, f"adjoint gap {gap:.2e}"
+    proj.close()
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------- squared-weight back ---

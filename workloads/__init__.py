@@ -57,6 +57,7 @@ class Workload:
     seed_y: int = 0                # 0 -> the back input is the forward of x
     dv: float = 1.0
     radius: int = 1
+    angle_start: float = 0.0       # first view angle when angle_step is given
 
     # ----------------------------------------------------------- geometry ---
     def angles(self) -> np.ndarray:
@@ -64,7 +65,7 @@ class Workload:
         if self.shift_step != 0.0:
             return np.zeros(self.nv, dtype=np.float64)
         if self.angle_step is not None:
-            return v * self.angle_step
+            return self.angle_start + v * self.angle_step
         span = math.pi if self.kind == PARALLEL else 2.0 * math.pi
         return v * span / self.nv
 
