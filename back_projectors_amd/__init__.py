@@ -7,7 +7,8 @@ the library has not been built, or a tensor is not on the handle's GPU, the
 call raises.
 
 Names follow the C ABI: ``proj_create`` -> :class:`Projector`,
-``proj_forward`` -> :meth:`Projector.forward`, ``proj_back`` ->
+``proj_forward`` -> :meth:`Projector.forward`, ``proj_forward_noalloc`` ->
+:meth:`Projector.forward_noalloc`, ``proj_back`` ->
 :meth:`Projector.back`, ``proj_back_squared`` -> :meth:`Projector.back_squared`,
 ``proj_channel_index`` -> :meth:`Projector.channel_index`,
 ``proj_forward_pixels`` -> :meth:`Projector.forward_pixels`,
@@ -43,7 +44,7 @@ STATUS = {
 }
 
 # Every entry point include/proj.h declares.
-EXPORTS = ("proj_create", "proj_forward", "proj_back", "proj_back_squared", "proj_channel_index",
+EXPORTS = ("proj_create", "proj_forward", "proj_forward_noalloc", "proj_back", "proj_back_squared", "proj_channel_index",
            "proj_forward_pixels", "proj_back_pixels", "proj_solver_workspace_size", "proj_cgls", "proj_sirt",
            "proj_plan_query", "proj_destroy", "proj_status_string", "proj_last_error", "proj_describe")
 
@@ -110,7 +111,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     i64x3 = P(ctypes.c_int64)
     lib.proj_create.argtypes = [P(_Geometry), i64x3, i64x3, ctypes.c_int, P(ctypes.c_void_p)]
     lib.proj_create.restype = ctypes.c_int
-    for name in ("proj_forward", "proj_back", "proj_back_squared"):
+    for name in ("proj_forward", "proj_forward_noalloc", "proj_back", "proj_back_squared"):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         fn.restype = ctypes.c_int
@@ -243,6 +244,22 @@ class Projector:
             self._tensor(out, self.sino_shape, torch.float32, "out")
         _check(self._lib.proj_forward(self._h, ctypes.c_void_p(recon.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                                       ctypes.c_void_p(_stream_ptr(torch, self.device, stream))), "proj_forward")
+        return out
+
+    def forward_noalloc(self, recon, out=None, stream=None):
+        """``proj_forward_noalloc``: the same sinogram as :meth:`forward`, with
+        the parallel walk's partial sums in the library's fixed device scratch
+        (at most 144 MiB, shared by every call on the GPU) instead of the
+        handle's buffer.  The call itself allocates nothing; pass ``out`` to
+        keep the whole call allocation-free."""
+        torch = self._torch
+        self._tensor(recon, self.recon_shape, torch.float32, "recon")
+        out = self._empty(self.sino_shape, torch.float32) if out is None else \
+            self._tensor(out, self.sino_shape, torch.float32, "out")
+        _check(self._lib.proj_forward_noalloc(self._h, ctypes.c_void_p(recon.data_ptr()),
+                                              ctypes.c_void_p(out.data_ptr()),
+                                              ctypes.c_void_p(_stream_ptr(torch, self.device, stream))),
+               "proj_forward_noalloc")
         return out
 
     def back(self, sino, out=None, stream=None):

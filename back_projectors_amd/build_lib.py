@@ -19,7 +19,8 @@ OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libbpamd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["index.hip", "parallel.hip", "cone.hip", "subset.hip", "solver.hip", "proj_api.cpp", "extra_api.cpp"]
+SOURCES = ["index.hip", "parallel.hip", "cone.hip", "subset.hip", "solver.hip", "noalloc.hip", "proj_api.cpp",
+           "extra_api.cpp"]
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -150,6 +150,26 @@ proj_status proj_create(const proj_geometry *g, const int64_t recon_shape[3],
 proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev, void *hip_stream);
 
 /*
+ * proj_forward_noalloc: proj_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * allocation).  Same operation, layouts, overlap rule and errors as
+ * proj_forward, and the same kernels; it allocates nothing.  Parallel beam
+ * adds its partial sums into a fixed device array of the library, at most
+ * 144 MiB (one copy per GPU, held until the process ends), instead of the
+ * handle's accumulation buffer; the buffer needs V * (C + 2 (taps - 1)) *
+ * (S rounded up to 16 or 32) * 4 bytes (142 MB for 512x512x64 at 720 views),
+ * and a handle that needs more returns PROJ_ERR_UNSUPPORTED before any
+ * write.  Cone beam needs no scratch.
+ * Every call on one GPU shares that array: two calls that can overlap in time
+ * on one GPU (other streams, a replayed graph beside an eager call, any
+ * handles) race and must be ordered by the caller.  Calls of proj_forward on
+ * the same handle do not touch the array.  The first call on each GPU looks
+ * up the array's device address; make it outside a graph capture.
+ * Asynchronous on hip_stream.
+ */
+proj_status proj_forward_noalloc(proj_handle h, const float *recon_dev, float *sino_dev, void *hip_stream);
+
+/*
  * proj_back: recon = A^T sino, the exact adjoint of proj_forward.  sino_dev is
  * read, recon_dev is overwritten.  The two buffers must not overlap.
  * Asynchronous on hip_stream.
