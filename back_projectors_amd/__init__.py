@@ -30,6 +30,8 @@ PROJ_CONE_FLAT = 1
 PROJ_FORWARD_AUTO = 0
 PROJ_FORWARD_TILE = 1
 PROJ_FORWARD_GATHER = 2
+PROJ_FORWARD_CONE_TILE_8X4 = 3
+PROJ_FORWARD_CONE_TILE_8X8 = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libbpamd.so")

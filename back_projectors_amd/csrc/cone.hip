@@ -370,15 +370,30 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
 }
 
 // Forward: a workgroup owns a CTX x CTY pixel tile and a chunk of 64*P slices;
-// each wave works on one view at a time into its own LDS window (channels x
-// rows, rows fastest).  Lane l takes slices l*P + ph, ph = 0..P-1, and P is
-// chosen at creation so that P times the smallest row magnification is at
-// least one: the slices of one instruction then fall on distinct detector
-// rows, so every tap is a plain read-modify-write with no two lanes on the
-// same cell (float atomics in LDS are avoided: on gfx950 they cost tens of
-// times a plain update).  The finished window is added to the sinogram with
-// coalesced global atomics, one per cell per view and tile.
-template <int R, int P, bool U>
+// each wave works on one view at a time.  The 3x3 (generally (2R+1)^2) tap
+// block of a voxel is the product of its row taps and its channel taps, so a
+// pixel's cylinder is projected in two steps:
+//   1. slices -> rows.  Lanes are slices (lane l takes slices l*P + ph, or
+//      consecutive slices where the slab allows); each computes its row w_k
+//      (fp64, the model's operation order), its 2R+1 row taps and the chord,
+//      and adds L_k x_k g_sg into a one-column row profile of the window in
+//      LDS, one row offset per round.  P is chosen at creation so that the
+//      slices of one instruction fall on distinct rows: every add is a plain
+//      read-modify-write with no two lanes on one cell (float atomics in LDS
+//      cost tens of times a plain update on gfx950).
+//   2. rows -> channels.  Lanes are rows of the window (64 per pass); each
+//      reads and clears its profile cell and adds h_t times it into 2R+1
+//      register accumulators, one per channel of the pixel's taps.  The tile's
+//      pixels are walked in the order of their channel index, so a channel is
+//      finished once the walk has passed it: it is written into its window
+//      column once (rows of the pass) and the accumulators shift down by one
+//      channel (slot t holds channel lo + t, so every register index is
+//      fixed at compile time).
+// The window is then added to the sinogram with coalesced global atomics, one
+// per cell per (view, tile, chunk).  Per voxel-view this does 2R+1 LDS
+// read-modify-writes on one column instead of (2R+1)^2 on the block, and the
+// (2R+1)^2 products become 2R+1 per slice and 2R+1 per row.
+template <int R, int P, bool U, int TY>
 __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__restrict__ recon,
                                                                  float *__restrict__ sino,
                                                                  const int32_t *__restrict__ idx,
@@ -388,21 +403,26 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                                                                  int nrp, int vsplit) {
     constexpr int NTAP = 2 * R + 1;
     constexpr int CH = 64 * P;            // slices per chunk
+    constexpr int NPG = 3;                // row passes of 64 held in registers (one row group)
+    constexpr int NPX = CTX * TY;         // pixels per tile (at most one per lane)
+    static_assert(NPX <= 64, "one pixel per lane");
     extern __shared__ float lds[];
     const int lane = (int)threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    float *win = lds + wave * nwcap * nrp;             // this wave's window [nwcap][nrp]
+    float *win = lds + wave * cone_fwd_wave_words(nwcap, nrp);   // this wave's window [nwcap][nrp]
+    float *prof = win + nwcap * nrp;                             // and row profile [nrp]
 
     const int tiles_x = (g.nx + CTX - 1) / CTX;
-    const int ntiles = tiles_x * ((g.ny + CTY - 1) / CTY);
+    const int ntiles = tiles_x * ((g.ny + TY - 1) / TY);
     const int nch = (g.ns + CH - 1) / CH;
     const int tj0 = (int)(blockIdx.x % tiles_x) * CTX;
-    const int ti0 = (int)(blockIdx.x / tiles_x) * CTY;
+    const int ti0 = (int)(blockIdx.x / tiles_x) * TY;
     const int k0 = (int)blockIdx.y * CH;
     const int nk = min(CH, g.ns - k0);
     const int np = g.ny * g.nx;
 
-    for (int e = lane; e < nwcap * nrp; e += 64) win[e] = 0.f;
+    // the profile starts at zero; the second step clears every cell it reads
+    for (int e = lane; e < nrp; e += 64) prof[e] = 0.f;
 
     const int vper = (g.nv + vsplit - 1) / vsplit;
     const int vbeg = (int)blockIdx.z * vper;
@@ -413,10 +433,10 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         const int v = vbeg + start + it;
         return v >= vend ? v - cnt : v;
     };
-    // this lane's pixel of the tile (lanes past the tile's CTX * CTY pixels
+    // this lane's pixel of the tile (lanes past the tile's CTX * TY pixels
     // hold none)
     const int il = ti0 + lane / CTX, jl = tj0 + lane % CTX;
-    const bool lin = lane < CTX * CTY && il < g.ny && jl < g.nx;
+    const bool lin = lane < NPX && il < g.ny && jl < g.nx;
     const double xl = pix_x(g, jl), yl = pix_y(g, il);
 
     // Per-view data, fetched two views ahead with vector loads: lanes 0-17
@@ -472,6 +492,8 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         if (nit <= 0) return;                                 // no slice reaches the detector
         // this lane's pixel: channel taps and the per-(view, pixel) constants, fp64
         const bool act = pn >= -R && pn <= g.nc - 1 + R;
+        const uint64_t actb = __builtin_amdgcn_ballot_w64(act);
+        if (!actb) return;
         // (the chord factor dv / M and d^2 + a^2 only ever enter the fp32
         // chord, so they are carried in fp32)
         float hq[NTAP];
@@ -489,6 +511,39 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             lscq = (float)cv.lsc;
             r2q = (float)cv.r2;
         }
+        // Walk order: the active pixels by channel index, then by pixel.  The
+        // rank of each comes from counting over the channel keys; the lanes
+        // of the order are filled by a forward permute (inactive lanes take
+        // the ranks after the active ones).
+        const int kq = act ? pn : INT32_MAX;
+        int kmin = INT32_MAX, kmax = INT32_MIN;
+        {
+            uint64_t rest = actb;
+            while (rest) {
+                const int q = (int)__builtin_ctzll(rest);
+                rest &= rest - 1;
+                const int kk2 = __builtin_amdgcn_readlane(kq, q);
+                kmin = min(kmin, kk2);
+                kmax = max(kmax, kk2);
+            }
+        }
+        const int npix = (int)__builtin_popcountll(actb);
+        int rank = npix + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(~actb >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)~actb, 0u));
+        {
+            int base = 0;
+            for (int c = kmin; c <= kmax; ++c) {
+                const uint64_t b = __builtin_amdgcn_ballot_w64(kq == c);
+                if (!b) continue;
+                const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+                if (kq == c) rank = base + below;
+                base += (int)__builtin_popcountll(b);
+            }
+        }
+        const int order = __builtin_amdgcn_ds_permute(rank * 4, lane);   // lane r: the pixel of rank r
+        const int korder = __builtin_amdgcn_ds_permute(rank * 4, kq);    // and its channel index
+
         int kkv[P];                                           // this lane's slice in each pass
         double dzs[P];
 #pragma unroll
@@ -497,147 +552,211 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             dzs[ph] = slice_z(g, k0 + kkv[ph]) - vk.zsrc;
         }
         float dz2[P];
+        bool kok[P];                                          // slice inside the chunk
+        int kkc[P];                                           // and clamped into it, for the loads
 #pragma unroll
-        for (int ph = 0; ph < P; ++ph) dz2[ph] = (float)(dzs[ph] * dzs[ph]);
-        // one pixel of the tile, its cylinder's voxels in xv
-        auto pixel = [&](int q, const float (&xv)[P]) {
-            const int ncv = __builtin_amdgcn_readlane(pn, q);
-            float h[NTAP];
-#pragma unroll
-            for (int t = 0; t < NTAP; ++t) h[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hq[t]), q));
+        for (int ph = 0; ph < P; ++ph) {
+            dz2[ph] = (float)(dzs[ph] * dzs[ph]);
+            kok[ph] = kkv[ph] < nk && (!U || ph < nit);
+            kkc[ph] = min(kkv[ph], nk - 1);
+        }
+
+        const int nrw = wd.nrw;
+        const int npass = (nrw + 63) >> 6;                   // row passes of 64 lanes
+        const int cbase = kmin - R;                          // first channel of the walk
+        const int clast = kmax + R;                          // last channel of the walk
+        float *const colb = win + (cbase - wd.n0) * nrp + lane;   // this lane's row of the first column
+
+        // Step 1 for one pixel: its cylinder's slices into the row profile.
+        // Per slice: the row (fp64, bit-exact with the model), the row taps
+        // (fp64; with a box no wider than the 2R+1 taps the outermost clamps
+        // are the box edges themselves, so they are skipped), the chord, then
+        // 2R+1 read-modify-writes, one row offset per round: within a round
+        // the active lanes hold distinct rows, and a lane's next row may be
+        // its neighbour's previous one, hence the ordering fence between
+        // rounds (LDS operations of a wave issue in order; the fence keeps
+        // the compiler from hoisting the next round's reads).
+        auto to_rows = [&](int q, const float (&xv)[P]) {
             const double mr = rl_d(mrq, q);
             const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r2q), q));
             const float lscf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lscq), q));
-            // the row box: width mr dv, half width hw (its negation is an operand
-            // modifier)
             const double wbox = mr * g.dv;
             const double hw = 0.5 * wbox, nhw = -hw;
-            // this pixel's 2R+1 window columns
-            float *colt[NTAP];
-            colt[0] = win + (ncv - R - wd.n0) * nrp - wd.m0 - R;
-#pragma unroll
-            for (int t = 1; t < NTAP; ++t) colt[t] = colt[t - 1] + nrp;
-            // One slice of this lane: row, row taps (fp64, the clamped-edge form;
-            // with a box no wider than the 2R+1 taps the outermost clamps are the
-            // box edges themselves, so they are skipped), chord, then the
-            // (2R+1)^2 taps as plain read-modify-writes, one row offset per round:
-            // within a round the active lanes hold distinct rows, and a lane's
-            // next row overlaps its neighbour's previous one, hence the ordering
-            // fence between rounds (LDS operations issue in order; the fence
-            // stops the compiler from hoisting the next round's reads).
-            auto slice = [&](auto narrow_c) {
+            const double hwm = hw - 0.5;                      // exact for hw in [1/4, 1] (Sterbenz)
+            const float wboxf = (float)wbox;
+            float *const pr = prof - wd.m0 - R;               // pr[mk + sg]: row offset sg - R of row mk
+            auto slices = [&](auto narrow_c) {
                 constexpr bool NARROW = decltype(narrow_c)::value;
 #pragma unroll
                 for (int ph = 0; ph < P; ++ph) {
                     if (U && ph >= nit) break;                    // uniform
-                    const int kk = kkv[ph];
                     const double t0 = mr * dzs[ph];
                     const double wk = t0 + g.crow;
                     const double mk = rint(wk);
-                    const bool ok = kk < nk && mk >= -R && mk <= g.nr - 1 + R;
+                    const int mi = (int)mk;                       // saturates far off the detector
+                    const bool ok = kok[ph] && (unsigned)mi + (unsigned)R <= (unsigned)(g.nr - 1 + 2 * R);
                     const double f = wk - mk;
-                    double gd[NTAP];
+                    float gf[NTAP];
                     if constexpr (R == 1 && NARROW) {
                         // the box [-h, h] and the cells around it, whose inner
-                        // edges sit at -(1/2 + f) and 1/2 - f (both exact): the
-                        // outer taps are max(h - (1/2 + f), 0) and
-                        // max(h - (1/2 - f), 0), each one rounding of the exact
-                        // value, as the model's overlap gives it (a tap of a
-                        // footprint that only touches its cell can be 1e-15 and
-                        // alone in its sinogram cell); the middle one is never
-                        // thin (at least min(h, 1/2)), so the box width minus
-                        // the outer two is accurate
-                        gd[0] = fmax(hw - (0.5 + f), 0.0);
-                        gd[2] = fmax(hw - (0.5 - f), 0.0);
-                        gd[1] = (wbox - gd[0]) - gd[2];
+                        // edges sit at -(1/2 + f) and 1/2 - f: the outer taps
+                        // are max((h - 1/2) - f, 0) and max((h - 1/2) + f, 0),
+                        // each one rounding of the exact value (h - 1/2 is
+                        // exact for h >= 1/4), as the model's overlap gives it
+                        // (a tap of a footprint that only touches its cell can
+                        // be 1e-15 and alone in its sinogram cell); the middle
+                        // one is never thin (at least min(2h, 1) minus the
+                        // outer two), so the box width minus the outer two in
+                        // fp32 is accurate
+                        gf[0] = (float)fmax(hwm - f, 0.0);
+                        gf[2] = (float)fmax(hwm + f, 0.0);
+                        gf[1] = (wboxf - gf[0]) - gf[2];
                     } else {
                         double gp = NARROW ? nhw : fmin(fmax((-0.5 - (double)R) - f, nhw), hw);
 #pragma unroll
                         for (int t = 0; t < NTAP; ++t) {
                             const double gn =
                                 (NARROW && t == NTAP - 1) ? hw : fmin(fmax(((double)(t - R) + 0.5) - f, nhw), hw);
-                            gd[t] = gn - gp;
+                            gf[t] = (float)(gn - gp);
                             gp = gn;
                         }
                     }
                     const float lkx = lscf * __builtin_amdgcn_sqrtf(r2 + dz2[ph]) * xv[ph];
-                    float c[NTAP];
-#pragma unroll
-                    for (int sg = 0; sg < NTAP; ++sg) c[sg] = lkx * (float)gd[sg];
                     // one exec mask for the 2R + 1 rounds (the lanes of a round
                     // are the same in every round)
                     if (ok) {
-                        const int mo = (int)mk;
+                        float *const cell = pr + mi;
 #pragma unroll
                         for (int sg = 0; sg < NTAP; ++sg) {
-                            float old[NTAP];
-#pragma unroll
-                            for (int t = 0; t < NTAP; ++t) old[t] = colt[t][mo + sg];
-#pragma unroll
-                            for (int t = 0; t < NTAP; ++t) colt[t][mo + sg] = fmaf(h[t], c[sg], old[t]);
+                            cell[sg] = fmaf(lkx, gf[sg], cell[sg]);
                             __atomic_signal_fence(__ATOMIC_SEQ_CST);
                         }
                     }
                 }
             };
-            if (hw <= (double)R)
-                slice(std::true_type{});
+            if (R == 1 ? (hw <= 1.0 && hw >= 0.25) : hw <= (double)R)
+                slices(std::true_type{});
             else
-                slice(std::false_type{});
+                slices(std::false_type{});
         };
+
         // The voxels come from memory (L2: the tile's cylinders are read by
         // every view), the next pixel's while this one is projected, in two
         // alternating register buffers (no copies, so the loads are waited for
-        // only where used).  Lanes past the chunk's last slice load nothing.
+        // only where used).  Every lane loads, from its slice clamped into the
+        // chunk: lanes past the chunk's last slice never use the value, and
+        // loads that are all unconditional let the compiler wait for the
+        // current pixel's alone, not for the prefetch behind them.
         auto load_px = [&](int q, float (&xv)[P]) {
             const float *src = recon + (int64_t)((ti0 + q / CTX) * g.nx + tj0 + q % CTX) * g.ns + k0;
 #pragma unroll
-            for (int ph = 0; ph < P; ++ph) {
-                const int kk = kkv[ph];
-                xv[ph] = ((!U || ph < nit) && kk < nk) ? src[kk] : 0.f;
-            }
+            for (int ph = 0; ph < P; ++ph) xv[ph] = src[kkc[ph]];
         };
-        uint64_t todo = __builtin_amdgcn_ballot_w64(act);
-        if (todo) {
-            float xa[P], xb[P];
-            int q = (int)__builtin_ctzll(todo);
-            todo &= todo - 1;
-            load_px(q, xa);
-            for (;;) {
-                const int qb = todo ? (int)__builtin_ctzll(todo) : q;
-                load_px(qb, xb);
-                pixel(q, xa);
-                if (!todo) break;
-                todo &= todo - 1;
-                q = qb;
-                const int qa = todo ? (int)__builtin_ctzll(todo) : q;
-                load_px(qa, xa);
-                pixel(q, xb);
-                if (!todo) break;
-                todo &= todo - 1;
-                q = qa;
+
+        // Row groups of NPG passes: the ring accumulators of one group live
+        // in registers; a window taller than 64 * NPG rows walks the pixels
+        // once per group (the profile is cleared in full every time).
+        for (int grp = 0; grp * NPG < npass; ++grp) {
+            float acc[NPG][NTAP];
+#pragma unroll
+            for (int ps = 0; ps < NPG; ++ps)
+#pragma unroll
+                for (int s = 0; s < NTAP; ++s) acc[ps][s] = 0.f;
+            bool rowok[NPG];
+#pragma unroll
+            for (int ps = 0; ps < NPG; ++ps) rowok[ps] = (grp * NPG + ps) * 64 + lane < nrw;
+            int lo = cbase;                                   // channel of ring slot 0
+            // write channel lo's accumulators into its window column and
+            // shift the ring down by one channel (slot t holds channel lo + t)
+            auto finish = [&]() {
+                float *col = colb + (lo - cbase) * nrp + grp * NPG * 64;
+#pragma unroll
+                for (int ps = 0; ps < NPG; ++ps) {
+                    if (grp * NPG + ps < npass) {
+                        if (rowok[ps]) col[ps * 64] = acc[ps][0];
+#pragma unroll
+                        for (int t = 0; t + 1 < NTAP; ++t) acc[ps][t] = acc[ps][t + 1];
+                        acc[ps][NTAP - 1] = 0.f;
+                    }
+                }
+                ++lo;
+            };
+            // Step 2 for one pixel, whose taps cover channels lo .. lo + 2R:
+            // every profile row of the window is read, cleared and added into
+            // the ring.
+            auto to_channels = [&](int q) {
+                float h[NTAP];
+#pragma unroll
+                for (int t = 0; t < NTAP; ++t)
+                    h[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hq[t]), q));
+#pragma unroll
+                for (int ps = 0; ps < NPG; ++ps) {
+                    const int pp = grp * NPG + ps;
+                    if (pp < npass) {
+                        float *cell = prof + pp * 64 + lane;
+                        float r = 0.f;
+                        if (rowok[ps]) {
+                            r = *cell;
+                            *cell = 0.f;
+                        }
+#pragma unroll
+                        for (int t = 0; t < NTAP; ++t) acc[ps][t] = fmaf(h[t], r, acc[ps][t]);
+                    }
+                }
+                if (npass > NPG) {                            // the other groups' rows: cleared only
+                    for (int pp = 0; pp < npass; ++pp)
+                        if (pp / NPG != grp && pp * 64 + lane < nrw) prof[pp * 64 + lane] = 0.f;
+                }
+            };
+            auto visit = [&](int i, const float (&xv)[P]) {
+                const int q = __builtin_amdgcn_readlane(order, i);
+                const int n = __builtin_amdgcn_readlane(korder, i);
+                while (lo < n - R) finish();                  // channels the walk has passed
+                to_rows(q, xv);
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                to_channels(q);
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            };
+            {
+                float xa[P], xb[P];
+                int i = 0;
+                // (the prefetch is always issued, the last pixel's again at
+                // the end, so that the wait counts stay static)
+                load_px(__builtin_amdgcn_readlane(order, 0), xa);
+                for (;;) {
+                    load_px(__builtin_amdgcn_readlane(order, min(i + 1, npix - 1)), xb);
+                    visit(i, xa);
+                    if (++i >= npix) break;
+                    load_px(__builtin_amdgcn_readlane(order, min(i + 1, npix - 1)), xa);
+                    visit(i, xb);
+                    if (++i >= npix) break;
+                }
             }
+            while (lo <= clast) finish();
         }
-        // add the window to the sinogram: lanes along channels, coalesced.
-        // A window of at most 64 channels goes dm = 64 / nw rows per step,
-        // each lane keeping one channel (lanes past dm * nw idle), so the LDS
-        // offset, the sinogram offset and the row advance by uniform steps;
-        // a wider one walks its cells in order, 64 per step.  (The view's
-        // sinogram is under 2^31 cells.)
-        const int nw = wd.nw, nrw = wd.nrw;
+
+        // add the walked columns of the window to the sinogram: lanes along
+        // channels, coalesced.  A span of at most 64 channels goes dm = 64 /
+        // nw rows per step, each lane keeping one channel (lanes past dm * nw
+        // idle), so the LDS offset, the sinogram offset and the row advance by
+        // uniform steps; a wider one walks its cells in order, 64 per step.
+        // (The view's sinogram is under 2^31 cells.)  Every cell of these
+        // columns was written by the walk, so nothing needs clearing.
+        const int nw = clast - cbase + 1;
+        const int n0 = cbase;
+        const float *wsrc = win + (cbase - wd.n0) * nrp;
         float *sv = sino + (int64_t)v * g.nr * g.nc;
         if (nw <= 64) {
             const int dm = 64 / nw;
             const int m1 = (int)(((float)lane + 0.5f) * (1.0f / (float)nw));
             if (m1 < dm) {
                 const int c = lane - m1 * nw;
-                const int n = wd.n0 + c;
+                const int n = n0 + c;
                 const bool nok = (unsigned)n < (unsigned)g.nc;
-                int row = wd.m0 + m1, lo = c * nrp + m1, go = row * g.nc + n;
+                int row = wd.m0 + m1, lo2 = c * nrp + m1, go = row * g.nc + n;
                 const int rend = wd.m0 + nrw, gs = dm * g.nc;
-                for (; row < rend; row += dm, lo += dm, go += gs) {
-                    const float val = win[lo];
-                    win[lo] = 0.f;
+                for (; row < rend; row += dm, lo2 += dm, go += gs) {
+                    const float val = wsrc[lo2];
                     if (val != 0.f && nok && (unsigned)row < (unsigned)g.nr) unsafeAtomicAdd(sv + go, val);
                 }
             }
@@ -647,9 +766,8 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             for (int e = lane; e < total; e += 64) {
                 const int m = (int)(((float)e + 0.5f) * rnw);
                 const int c = e - m * nw;
-                const float val = win[c * nrp + m];
-                win[c * nrp + m] = 0.f;
-                const int row = wd.m0 + m, n = wd.n0 + c;
+                const float val = wsrc[c * nrp + m];
+                const int row = wd.m0 + m, n = n0 + c;
                 if (val != 0.f && (unsigned)row < (unsigned)g.nr && (unsigned)n < (unsigned)g.nc)
                     unsafeAtomicAdd(sv + (row * g.nc + n), val);
             }
@@ -699,21 +817,25 @@ static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, in
     }
 }
 
-template <int R, int P, bool U>
+template <int R, int P, bool U, int TY>
 static hipError_t cone_fwd_u(const Plan &p, const float *recon, float *sino, hipStream_t st) {
     const Geo &g = p.g;
-    const int tiles = ((g.nx + CTX - 1) / CTX) * ((g.ny + CTY - 1) / CTY);
+    const int tiles = ((g.nx + CTX - 1) / CTX) * ((g.ny + TY - 1) / TY);
     const int chunks = (g.ns + 64 * P - 1) / (64 * P);
-    hipLaunchKernelGGL((cone_forward_kernel<R, P, U>), dim3(tiles, chunks, p.fwd_vsplit), dim3(CFW * 64), p.fwd_lds,
-                       st, recon, sino, p.idx, p.views, p.fwin, p.fslab, g, p.fwd_nwcap, p.fwd_nrcap,
+    hipLaunchKernelGGL((cone_forward_kernel<R, P, U, TY>), dim3(tiles, chunks, p.fwd_vsplit), dim3(CFW * 64),
+                       p.fwd_lds, st, recon, sino, p.idx, p.views, p.fwin, p.fslab, g, p.fwd_nwcap, p.fwd_nrcap,
                        p.fwd_vsplit);
     return hipGetLastError();
 }
 
 template <int R, int P>
 static hipError_t cone_fwd_t(const Plan &p, const float *recon, float *sino, hipStream_t st) {
-    if (p.cone_unit) return cone_fwd_u<R, P, true>(p, recon, sino, st);
-    return cone_fwd_u<R, P, false>(p, recon, sino, st);
+    if (p.cone_ty == 8) {
+        if (p.cone_unit) return cone_fwd_u<R, P, true, 8>(p, recon, sino, st);
+        return cone_fwd_u<R, P, false, 8>(p, recon, sino, st);
+    }
+    if (p.cone_unit) return cone_fwd_u<R, P, true, 4>(p, recon, sino, st);
+    return cone_fwd_u<R, P, false, 4>(p, recon, sino, st);
 }
 
 template <int R>
@@ -755,13 +877,15 @@ hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, h
 }
 
 // Dynamic LDS above the default limit needs the opt-in attribute.
-hipError_t cone_forward_allow_lds(int radius, int stride, size_t bytes) {
+hipError_t cone_forward_allow_lds(int radius, int stride, int ty, size_t bytes) {
     const void *f = nullptr;
     const void *fu = nullptr;
 #define BPAMD_CF(RR, PP)                                                                                      \
     if (radius == RR && stride == PP) {                                                                       \
-        f = (const void *)cone_forward_kernel<RR, PP, false>;                                                 \
-        fu = (const void *)cone_forward_kernel<RR, PP, true>;                                                 \
+        f = ty == 8 ? (const void *)cone_forward_kernel<RR, PP, false, 8>                                     \
+                    : (const void *)cone_forward_kernel<RR, PP, false, 4>;                                    \
+        fu = ty == 8 ? (const void *)cone_forward_kernel<RR, PP, true, 8>                                     \
+                     : (const void *)cone_forward_kernel<RR, PP, true, 4>;                                    \
     }
     BPAMD_CF(1, 1) BPAMD_CF(1, 2) BPAMD_CF(1, 3) BPAMD_CF(2, 1) BPAMD_CF(2, 2) BPAMD_CF(2, 3)
     BPAMD_CF(3, 1) BPAMD_CF(3, 2) BPAMD_CF(3, 3) BPAMD_CF(4, 1) BPAMD_CF(4, 2) BPAMD_CF(4, 3)

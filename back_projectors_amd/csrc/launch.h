@@ -48,6 +48,7 @@ struct Plan {
     int fwd_vsplit = 1;             // view ranges per tile (grid z)
     int cone_stride = 1;            // cone forward: slices between the lanes of one instruction
     int cone_unit = 0;              // cone forward: some slab saves work (the slab-reading kernel)
+    int cone_ty = 4;                // cone forward: tile rows (CTX x cone_ty pixels, 4 or 8)
 };
 
 constexpr int BT = 16;   // back tile edge (pixels), 256 threads
@@ -62,13 +63,11 @@ constexpr int FRS2Y = 32;
 // Groups of 16 walk steps per (view, region): every pixel of the region, then
 // zero steps up to a multiple of 5 groups (the walk rotates five record buffers).
 inline int fwd_groups(int rsx, int rsy) { return ((rsx * rsy + 79) / 80) * 5; }
-constexpr int CTX = 8;   // cone forward tile (pixels along x)
-constexpr int CTY = 4;   // cone forward tile (pixels along y); half a wave of pixels: the
-                         // narrower detector window per wave lets four workgroups share a CU,
-                         // while a smaller tile multiplies the windows and so the flush atomics,
-                         // one per nonzero cell (256^3 forward of a dense volume: 14.9 ms at
-                         // 8 x 8, 14.5 ms at 8 x 4, 25.8 ms at 4 x 4)
+constexpr int CTX = 8;   // cone forward tile (pixels along x); 4 or 8 rows of them (Plan::cone_ty)
 constexpr int CFW = 4;   // cone forward waves per workgroup (one view each at a time)
+// LDS floats of one cone forward wave: its detector window [nwcap][nrp] and a
+// one-column row profile [nrp] (rows of the window, the first projection step)
+__host__ __device__ inline int cone_fwd_wave_words(int nwcap, int nrp) { return (nwcap + 1) * nrp; }
 constexpr int CBSTG = 8;  // cone back: staged window cells per thread at most (window <= 256 * CBSTG cells)
 
 hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
@@ -114,6 +113,6 @@ hipError_t launch_vec(int op, float *d, const float *a, const float *b, const do
 
 hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st);
 hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
-hipError_t cone_forward_allow_lds(int radius, int stride, size_t bytes);
+hipError_t cone_forward_allow_lds(int radius, int stride, int ty, size_t bytes);
 
 }  // namespace bpamd

@@ -100,64 +100,114 @@ WinMax window_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int 
     return m;
 }
 
-// Cone forward slabs of every (view, tile, slice chunk), in the window
-// table's order: the chunk's slices whose rows can reach the detector in that
-// view, conservatively for every pixel of the tile (rows within half a row of
-// [-r, R - 1 + r], a slice of margin each side; the kernel still tests each
-// slice exactly), as (first slice, passes, unit stride, 0).  With the tile's
-// smallest row advance per slice (magnification times the voxel pitch) at
-// least one, consecutive slices fall on distinct rows, and lanes may take
-// consecutive slices from the first one;
-// that is used when it needs fewer passes than the planned stride.  Zero
-// passes: no slice of the chunk reaches the detector in that view.
+// Cone forward slab of one (view, tile, slice chunk): the chunk's slices
+// whose rows can reach the detector in that view, conservatively for every
+// pixel of the tile (rows within half a row of [-r, R - 1 + r], a slice of
+// margin each side; the kernel still tests each slice exactly), as (first
+// slice, passes, unit stride, 0).  With the tile's smallest row advance per
+// slice (magnification times the voxel pitch) at least one, consecutive
+// slices fall on distinct rows, and lanes may take consecutive slices from
+// the first one; that is used when it needs no more passes than the planned
+// stride.  Zero passes: no slice of the chunk reaches the detector in that view.
+struct SlabRange {
+    double kglo, kghi;   // the tile's slices that can reach the detector (all chunks)
+    double mlo;          // the tile's smallest row magnification
+};
+
+SlabRange slab_range(const Geo &g, const ViewK &vk, int i0, int i1, int j0, int j1) {
+    const double wlo = (-0.5 - g.radius) - g.crow, whi = (g.nr - 1 + g.radius + 0.5) - g.crow;
+    double dmin = 1e300, dmax = -1e300;
+    for (int ii : {i0, i1})
+        for (int jj : {j0, j1}) {
+            const double d = g.sid + (pix_y(g, ii) * vk.c - pix_x(g, jj) * vk.s);
+            dmin = std::min(dmin, d);
+            dmax = std::max(dmax, d);
+        }
+    const double mlo = g.sdd / (dmax * g.drow), mhi = g.sdd / (dmin * g.drow);
+    const double dz[4] = {wlo / mlo, wlo / mhi, whi / mlo, whi / mhi};
+    const double zlo = *std::min_element(dz, dz + 4) + vk.zsrc;
+    const double zhi = *std::max_element(dz, dz + 4) + vk.zsrc;
+    return {std::floor(zlo / g.dv + g.cz) - 1.0, std::ceil(zhi / g.dv + g.cz) + 1.0, mlo};
+}
+
+Window slab_of(const Geo &g, const SlabRange &sr, int k0, int nk, int stride) {
+    Window s;
+    s.n0 = 0;
+    s.nw = 0;
+    s.m0 = 0;
+    s.nrw = 0;
+    const double lo = std::max(sr.kglo - k0, 0.0), hi = std::min(sr.kghi - k0, (double)nk - 1.0);
+    if (hi >= lo) {
+        const int klo = (int)lo, nact = (int)hi - klo + 1;
+        const int nit_unit = (nact + 63) / 64;
+        // consecutive slices are dv apart: their rows differ by mr dv.
+        // Unit stride also where it takes as many passes: the rows of one
+        // instruction then sit about mr apart instead of stride * mr
+        const bool unit = stride > 1 && sr.mlo * g.dv >= 1.0 + 1e-9 && nit_unit <= stride;
+        s.n0 = unit ? klo : 0;
+        s.nw = unit ? nit_unit : stride;
+        s.m0 = unit ? 1 : 0;
+    }
+    return s;
+}
+
+// Slabs of every (view, tile, slice chunk), in the window table's order.
 void slab_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_, int sl, int stride,
                 std::vector<Window> *out) {
     const int ty = (g.ny + ty_ - 1) / ty_, tx = (g.nx + tx_ - 1) / tx_;
     const int nch = (g.ns + sl - 1) / sl;
     out->resize((size_t)g.nv * ty * tx * nch);
-    const double wlo = (-0.5 - g.radius) - g.crow, whi = (g.nr - 1 + g.radius + 0.5) - g.crow;
     size_t e = 0;
     for (int v = 0; v < g.nv; ++v)
         for (int a = 0; a < ty; ++a)
             for (int b = 0; b < tx; ++b) {
                 const int i0 = a * ty_, i1 = std::min(i0 + ty_, g.ny) - 1;
                 const int j0 = b * tx_, j1 = std::min(j0 + tx_, g.nx) - 1;
-                const ViewK &vk = views[v];
-                double dmin = 1e300, dmax = -1e300;
-                for (int ii : {i0, i1})
-                    for (int jj : {j0, j1}) {
-                        const double d = g.sid + (pix_y(g, ii) * vk.c - pix_x(g, jj) * vk.s);
-                        dmin = std::min(dmin, d);
-                        dmax = std::max(dmax, d);
-                    }
-                const double mlo = g.sdd / (dmax * g.drow), mhi = g.sdd / (dmin * g.drow);
-                const double dz[4] = {wlo / mlo, wlo / mhi, whi / mlo, whi / mhi};
-                const double zlo = *std::min_element(dz, dz + 4) + vk.zsrc;
-                const double zhi = *std::max_element(dz, dz + 4) + vk.zsrc;
-                const double kglo = std::floor(zlo / g.dv + g.cz) - 1.0, kghi = std::ceil(zhi / g.dv + g.cz) + 1.0;
+                const SlabRange sr = slab_range(g, views[v], i0, i1, j0, j1);
                 for (int c = 0; c < nch; ++c, ++e) {
                     const int k0 = c * sl, nk = std::min(sl, g.ns - k0);
-                    const double lo = std::max(kglo - k0, 0.0), hi = std::min(kghi - k0, (double)nk - 1.0);
-                    Window s;
-                    s.n0 = 0;
-                    s.nw = 0;
-                    s.m0 = 0;
-                    s.nrw = 0;
-                    if (hi >= lo) {
-                        const int klo = (int)lo, nact = (int)hi - klo + 1;
-                        const int nit_unit = (nact + 63) / 64;
-                        // consecutive slices are dv apart: their rows differ by mr dv.
-                        // Unit stride also where it takes as many passes: the rows
-                        // of one instruction then sit about mr apart instead of
-                        // stride * mr, which spreads them over more LDS banks
-                        const bool unit = stride > 1 && mlo * g.dv >= 1.0 + 1e-9 && nit_unit <= stride;
-                        s.n0 = unit ? klo : 0;
-                        s.nw = unit ? nit_unit : stride;
-                        s.m0 = unit ? 1 : 0;
-                    }
-                    (*out)[e] = s;
+                    (*out)[e] = slab_of(g, sr, k0, nk, stride);
                 }
             }
+}
+
+// Estimated time of a cone forward call with CTX x ty tiles, from the same
+// windows and slabs the call uses, on a sample of at most about 64 views:
+// the slice-to-row work (tile pixels times slab passes, about 0.12 ns each
+// on gfx950) and the window flush of a dense volume (64-byte atomic requests:
+// window rows on the detector times the cache lines their channels span,
+// about 21.6 G per second).  The two overlap, so the call takes about the
+// larger; the 8 x 8 tiles cost about 5% more work per pass (measured: the
+// 256^3 cone forward of a dense volume 15.0 ms at 8 x 4, flush-bound, and
+// 11.3 ms at 8 x 8; the 512^2 x 96 helical scan 61.5 ms at 8 x 4,
+// work-bound, and 66.9 ms at 8 x 8).
+double cone_forward_cost(const Geo &g, const std::vector<ViewK> &views, int ty_, int sl, int stride) {
+    const int ty = (g.ny + ty_ - 1) / ty_, tx = (g.nx + CTX - 1) / CTX;
+    const int nch = (g.ns + sl - 1) / sl;
+    const int step = std::max(1, g.nv / 64);
+    double pixpass = 0.0, lines = 0.0;
+    int nsample = 0;
+    for (int v = 0; v < g.nv; v += step, ++nsample)
+        for (int a = 0; a < ty; ++a)
+            for (int b = 0; b < tx; ++b) {
+                const int i0 = a * ty_, i1 = std::min(i0 + ty_, g.ny) - 1;
+                const int j0 = b * CTX, j1 = std::min(j0 + CTX, g.nx) - 1;
+                const double npx = (double)(i1 - i0 + 1) * (j1 - j0 + 1);
+                const SlabRange sr = slab_range(g, views[v], i0, i1, j0, j1);
+                for (int c = 0; c < nch; ++c) {
+                    const int k0 = c * sl, nk = std::min(sl, g.ns - k0);
+                    const Window w = tile_window(g, views[v], i0, i1, j0, j1, k0, k0 + nk - 1);
+                    if (w.nw <= 0 || w.nrw <= 0) continue;
+                    pixpass += npx * slab_of(g, sr, k0, nk, stride).nw;
+                    const int r0 = std::max(w.m0, 0), r1 = std::min(w.m0 + w.nrw - 1, g.nr - 1);
+                    const int c0 = std::max(w.n0, 0), c1 = std::min(w.n0 + w.nw - 1, g.nc - 1);
+                    if (r1 >= r0 && c1 >= c0) lines += (double)(r1 - r0 + 1) * (c1 / 16 - c0 / 16 + 1);
+                }
+            }
+    const double scale = nsample > 0 ? (double)g.nv / nsample : 0.0;
+    const double work = pixpass * scale * 0.12e-9 * (ty_ == 8 ? 1.05 : 1.0);
+    const double flush = lines * scale / 21.6e9;
+    return std::max(work, flush);
 }
 
 WinMax max_window(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_, int sl) {
@@ -204,10 +254,11 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         return fail(PROJ_ERR_INVALID_ARGUMENT, "non-finite detector offset");
     if (gp->psf_radius < 1 || gp->psf_radius > 4)
         return fail(PROJ_ERR_INVALID_ARGUMENT, "psf_radius must be in [1, 4]");
-    if (gp->forward_strategy < PROJ_FORWARD_AUTO || gp->forward_strategy > PROJ_FORWARD_GATHER)
-        return fail(PROJ_ERR_INVALID_ARGUMENT, "forward_strategy must be PROJ_FORWARD_AUTO, _TILE or _GATHER");
-    if (gp->kind != PROJ_PARALLEL && gp->forward_strategy != PROJ_FORWARD_AUTO)
-        return fail(PROJ_ERR_INVALID_ARGUMENT, "forward_strategy is for parallel beam only");
+    if (gp->kind == PROJ_PARALLEL && (gp->forward_strategy < PROJ_FORWARD_AUTO || gp->forward_strategy > PROJ_FORWARD_GATHER))
+        return fail(PROJ_ERR_INVALID_ARGUMENT, "parallel forward_strategy must be PROJ_FORWARD_AUTO, _TILE or _GATHER");
+    if (gp->kind != PROJ_PARALLEL && gp->forward_strategy != PROJ_FORWARD_AUTO &&
+        gp->forward_strategy != PROJ_FORWARD_CONE_TILE_8X4 && gp->forward_strategy != PROJ_FORWARD_CONE_TILE_8X8)
+        return fail(PROJ_ERR_INVALID_ARGUMENT, "cone forward_strategy must be PROJ_FORWARD_AUTO, _CONE_TILE_8X4 or _8X8");
     const double half_diag = 0.5 * std::sqrt((double)Nx * Nx + (double)Ny * Ny) * dv;
     if (gp->kind == PROJ_PARALLEL) {
         if (R != S) return fail(PROJ_ERR_INVALID_ARGUMENT, "parallel beam needs one detector row per slice (R == S)");
@@ -351,10 +402,21 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
             return fail(PROJ_ERR_UNSUPPORTED, "row magnification below 1/3 (detector rows far coarser than the voxels)");
         plan.cone_stride = stride;
         plan.fwd_sl = 64 * stride;
-        const WinMax wf = max_window(g, views, CTX, CTY, plan.fwd_sl);
-        plan.fwd_nwcap = wf.nw + 2;
-        plan.fwd_nrcap = (wf.nr + 2) | 1;
-        plan.fwd_lds = (size_t)CFW * plan.fwd_nwcap * plan.fwd_nrcap * sizeof(float);
+        // tile rows: 8 x 4 pixels, or 8 x 8 where the flush of the narrower
+        // tiles' windows would bound the call (forced by forward_strategy)
+        if (gp->forward_strategy == PROJ_FORWARD_CONE_TILE_8X4)
+            plan.cone_ty = 4;
+        else if (gp->forward_strategy == PROJ_FORWARD_CONE_TILE_8X8)
+            plan.cone_ty = 8;
+        else
+            plan.cone_ty = cone_forward_cost(g, views, 8, plan.fwd_sl, stride) <
+                                   cone_forward_cost(g, views, 4, plan.fwd_sl, stride)
+                               ? 8
+                               : 4;
+        const WinMax wf = max_window(g, views, CTX, plan.cone_ty, plan.fwd_sl);
+        plan.fwd_nwcap = wf.nw;
+        plan.fwd_nrcap = wf.nr | 1;
+        plan.fwd_lds = (size_t)CFW * cone_fwd_wave_words(plan.fwd_nwcap, plan.fwd_nrcap) * sizeof(float);
     }
     if (plan.back_lds > kMaxLds || plan.fwd_lds > kMaxLdsOptIn) {
         char buf[160];
@@ -380,7 +442,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
             return fail(PROJ_ERR_UNSUPPORTED, "too many forward workgroups");
         plan.fwd_vsplit = (int)vs;
     } else {
-        const int64_t ftiles = ((Nx + CTX - 1) / CTX) * ((Ny + CTY - 1) / CTY);
+        const int64_t ftiles = ((Nx + CTX - 1) / CTX) * ((Ny + plan.cone_ty - 1) / plan.cone_ty);
         // enough workgroups to fill 256 CUs a few times over; each split re-reads its tile
         int64_t vs = (2048 + ftiles * chunks_f - 1) / (ftiles * chunks_f);
         vs = std::max<int64_t>(1, std::min<int64_t>(vs, std::min<int64_t>(V, 64)));
@@ -398,12 +460,12 @@ int describe(const Plan &p, int64_t table_bytes, char *buf, int len) {
         "slices/lane, window %d ch x %d rows, %zu B LDS | forward: %dx%d px tile, %s, %d slices, window %d ch x %d "
         "rows, %zu B LDS, %d view ranges | tables and buffers %lld B",
         par ? "parallel" : "cone_flat", g.nv, g.nr, g.nc, g.ny, g.nx, g.ns, g.radius, par ? p.ntap : 2 * g.radius + 1,
-        BT, BT, p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, par ? p.rsx : CTX, par ? p.rsy : CTY,
+        BT, BT, p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, par ? p.rsx : CTX, par ? p.rsy : p.cone_ty,
         par ? (p.fwd_strategy == PROJ_FORWARD_GATHER
                    ? "gather: per-view sorted walk of all pixels, lanes=16 slices x 4 views, voxels from memory"
                    : (p.fwd_spl == 2 ? "tile: channel-ordered region walk, lanes=16 x 4 views with 2 slices each, ring accumulators"
                                      : "tile: channel-ordered region walk, lanes=16 slices x 4 views, ring accumulators"))
-            : "lanes=strided slices, wave per view, LDS window",
+            : "wave per view: lanes=strided slices into a row profile, then lanes=rows into channel ring accumulators",
         p.fwd_sl,
         p.fwd_nwcap, par ? p.fwd_sl : p.fwd_nrcap, p.fwd_lds, p.fwd_vsplit, (long long)table_bytes);
 }
@@ -548,8 +610,8 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
             std::vector<Window> bw, fw, fs;
             window_table(geo, views, BT, BT, plan.back_sl, &bw);
             if (geo.kind != 0) {
-                window_table(geo, views, CTX, CTY, plan.fwd_sl, &fw);
-                slab_table(geo, views, CTX, CTY, plan.fwd_sl, plan.cone_stride, &fs);
+                window_table(geo, views, CTX, plan.cone_ty, plan.fwd_sl, &fw);
+                slab_table(geo, views, CTX, plan.cone_ty, plan.fwd_sl, plan.cone_stride, &fs);
                 // the slab-reading kernel when some slab saves work (a unit-stride
                 // walk, or a chunk that misses the detector in a view)
                 for (const Window &w : fs) h->plan.cone_unit |= (w.m0 != 0 || w.nw == 0) ? 1 : 0;
@@ -578,7 +640,7 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                 proj_destroy(h);
                 return fail(PROJ_ERR_UNSUPPORTED, "device LDS per workgroup below the forward plan's need");
             }
-            e = cone_forward_allow_lds(geo.radius, plan.cone_stride, plan.fwd_lds);
+            e = cone_forward_allow_lds(geo.radius, plan.cone_stride, plan.cone_ty, plan.fwd_lds);
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipFuncSetAttribute(LDS)");
         }
         h->table_bytes = (size_t)h->index_elems * sizeof(int32_t) + views.size() * sizeof(ViewK) + rec_bytes;

@@ -95,8 +95,9 @@ typedef struct {
     double det_channel_offset;   /* detector centre offset, channels (usually 0) */
     double det_row_offset;       /* detector centre offset, rows (usually 0) */
     int32_t psf_radius;          /* taps on each side of the centre channel (and row), 1..4 */
-    int32_t forward_strategy;    /* parallel beam: PROJ_FORWARD_AUTO (0, chosen from the shapes),
-                                    PROJ_FORWARD_TILE (1) or PROJ_FORWARD_GATHER (2); cone: 0 */
+    int32_t forward_strategy;    /* PROJ_FORWARD_AUTO (0): chosen from the shapes; parallel beam:
+                                    PROJ_FORWARD_TILE (1) or PROJ_FORWARD_GATHER (2); cone beam:
+                                    PROJ_FORWARD_CONE_TILE_8X4 (3) or _8X8 (4) */
 } proj_geometry;
 
 /*
@@ -110,8 +111,20 @@ typedef struct {
  *             the voxels from memory, each channel is added about once per view.
  * AUTO takes the choice from the shapes alone; both give the same sinogram up
  * to the order of fp32 additions.
+ * Cone-beam forward tiles: a workgroup holds 8 x 4 or 8 x 8 pixels and adds
+ * a detector window per view to the sinogram with one global atomic per
+ * cell; larger tiles flush fewer cells per voxel, smaller ones skip more
+ * slices that miss the detector.  AUTO estimates both from the windows and
+ * takes the faster; CONE_TILE_8X4 / _8X8 force one.  The sinogram is the
+ * same up to the order of fp32 additions.
  */
-enum { PROJ_FORWARD_AUTO = 0, PROJ_FORWARD_TILE = 1, PROJ_FORWARD_GATHER = 2 };
+enum {
+    PROJ_FORWARD_AUTO = 0,
+    PROJ_FORWARD_TILE = 1,
+    PROJ_FORWARD_GATHER = 2,
+    PROJ_FORWARD_CONE_TILE_8X4 = 3,
+    PROJ_FORWARD_CONE_TILE_8X8 = 4
+};
 
 /*
  * proj_create: validate the geometry, copy it to the device, run the fp64

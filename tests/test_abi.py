@@ -104,6 +104,8 @@ BAD = [
     ("forward strategy 3", base_geo(forward_strategy=3), (8, 8, 4), (4, 4, 16), -1),
     ("forward strategy -1", base_geo(forward_strategy=-1), (8, 8, 4), (4, 4, 16), -1),
     ("cone forward strategy", base_geo(**dict(CONE, forward_strategy=2)), (8, 8, 4), (4, 6, 16), -1),
+    ("cone forward strategy 5", base_geo(**dict(CONE, forward_strategy=5)), (8, 8, 4), (4, 6, 16), -1),
+    ("parallel with a cone tile", base_geo(forward_strategy=3), (8, 8, 4), (4, 4, 16), -1),
 ]
 
 
@@ -144,7 +146,7 @@ def test_cone_forward_slice_stride(bp, w, stride):
     (rows per slice, at the volume's corners) puts them on distinct rows: the
     chunk is 64 * stride slices."""
     desc = bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape)
-    assert f"LDS window, {64 * stride} slices," in desc.split("forward:")[1], desc
+    assert f"channel ring accumulators, {64 * stride} slices," in desc.split("forward:")[1], desc
 
 
 def test_cone_forward_window_wider_than_a_flush_step(bp):
@@ -165,6 +167,20 @@ def test_helical_radius2_plans(bp):
     w = W.scaled(W.get("helical-512x512x96-1338v"), "helical-r2", radius=2)
     desc = bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape)
     assert "radius=2 taps=5" in desc, desc
+
+
+@pytest.mark.parametrize("name,tile", [("cone-256x256x256-360v", "8x8"), ("helical-512x512x96-1338v", "8x4")])
+def test_cone_forward_tile_choice(bp, name, tile):
+    """The cone forward's tile from the planner's estimate: the 256^3 cone,
+    whose dense flush of 8 x 4 windows would bound the call, takes 8 x 8
+    tiles; the helical scan, bound by its slice work, keeps 8 x 4.  Either can
+    be forced."""
+    w = W.get(name)
+    fwd = lambda d: d.split("forward:")[1]
+    assert f"{tile} px tile" in fwd(bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape))
+    for code, forced in ((3, "8x4"), (4, "8x8")):
+        desc = bp.plan_query(dict(w.geometry(), forward_strategy=code), w.recon_shape, w.sino_shape)
+        assert f"{forced} px tile" in fwd(desc), desc
 
 
 @pytest.mark.parametrize("strategy,word", [(1, "tile:"), (2, "gather:")])

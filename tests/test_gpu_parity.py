@@ -501,6 +501,46 @@ def test_small_forward_strategies(bp, orc, w, strategy):
     proj.close()
 
 
+CONE_SMALL = [w for w in SMALL_CASES if w.kind == W.CONE_FLAT]
+
+
+@pytest.mark.parametrize("tile", [3, 4], ids=["8x4", "8x8"])
+@pytest.mark.parametrize("w", CONE_SMALL, ids=lambda w: w.name)
+def test_small_cone_forward_tiles(bp, orc, w, tile):
+    """Both cone forward tiles (8 x 4 and 8 x 8 pixels), forced, against the
+    reference: forward of the whole sinogram and the adjoint identity."""
+    note(f"cone forward tile {tile} {w.name}")
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    proj = bp.Projector(dict(w.geometry(), forward_strategy=tile), w.recon_shape, w.sino_shape)
+    assert ("8x4 px tile" if tile == 3 else "8x8 px tile") in proj.describe().split("forward:")[1]
+    x, y = inputs(w)
+    yo, ay = orc.forward(g, x, with_abs=True)
+    yg = host(proj.forward(dev(x)))
+    assert_close(yg, yo, ay, f"{w.name} forward tile {tile}")
+    gap = adjoint_gap(yg, y, x, host(proj.back(dev(y))))
+    assert gap < ADJOINT, f"adjoint gap {gap:.2e}"
+    proj.close()
+
+
+@pytest.mark.parametrize("name,tile", [("cone-256x256x256-360v", 3), ("helical-512x512x96-1338v", 4)],
+                         ids=["cone-8x4", "helical-8x8"])
+def test_full_cone_forward_other_tile(bp, orc, name, tile, full_cache):
+    """The full-size cone workloads with the tile the planner does not pick
+    for them, dense volume, sampled views against the reference."""
+    full_cache.clear()
+    torch.cuda.empty_cache()
+    w = W.get(name)
+    note(f"full cone forward tile {tile} {name}")
+    proj = bp.Projector(dict(w.geometry(), forward_strategy=tile), w.recon_shape, w.sino_shape)
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    x = np.random.default_rng(105).standard_normal(w.recon_shape).astype(np.float32)
+    yg = host(proj.forward(dev(x)))
+    views = sorted({2, w.nv // 2, w.nv - 3})
+    yo, ay = orc.forward_views(g, x, views, with_abs=True)
+    assert_close(yg[views], yo, ay, f"{name} forward tile {tile} views {views}")
+    proj.close()
+
+
 @pytest.mark.parametrize("name", ["parallel-512x512x64-720v", "translation-512x512x32-64v"])
 def test_full_forward_gather_sampled_views(bp, orc, name, full_cache):
     full_cache.clear()
