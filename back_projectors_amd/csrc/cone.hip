@@ -393,7 +393,7 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
 // per cell per (view, tile, chunk).  Per voxel-view this does 2R+1 LDS
 // read-modify-writes on one column instead of (2R+1)^2 on the block, and the
 // (2R+1)^2 products become 2R+1 per slice and 2R+1 per row.
-template <int R, int P, bool U, int TY>
+template <int R, int P, bool U, int TY, int NPG>
 __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__restrict__ recon,
                                                                  float *__restrict__ sino,
                                                                  const int32_t *__restrict__ idx,
@@ -403,7 +403,6 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                                                                  int nrp, int vsplit) {
     constexpr int NTAP = 2 * R + 1;
     constexpr int CH = 64 * P;            // slices per chunk
-    constexpr int NPG = 3;                // row passes of 64 held in registers (one row group)
     constexpr int NPX = CTX * TY;         // pixels per tile (at most one per lane)
     static_assert(NPX <= 64, "one pixel per lane");
     extern __shared__ float lds[];
@@ -670,14 +669,14 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             // shift the ring down by one channel (slot t holds channel lo + t)
             auto finish = [&]() {
                 float *col = colb + (lo - cbase) * nrp + grp * NPG * 64;
+                // (a pass past the window's rows has no lane with rowok and
+                // only ever adds zeros, so no pass needs a guard of its own)
 #pragma unroll
                 for (int ps = 0; ps < NPG; ++ps) {
-                    if (grp * NPG + ps < npass) {
-                        if (rowok[ps]) col[ps * 64] = acc[ps][0];
+                    if (rowok[ps]) col[ps * 64] = acc[ps][0];
 #pragma unroll
-                        for (int t = 0; t + 1 < NTAP; ++t) acc[ps][t] = acc[ps][t + 1];
-                        acc[ps][NTAP - 1] = 0.f;
-                    }
+                    for (int t = 0; t + 1 < NTAP; ++t) acc[ps][t] = acc[ps][t + 1];
+                    acc[ps][NTAP - 1] = 0.f;
                 }
                 ++lo;
             };
@@ -691,17 +690,14 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                     h[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hq[t]), q));
 #pragma unroll
                 for (int ps = 0; ps < NPG; ++ps) {
-                    const int pp = grp * NPG + ps;
-                    if (pp < npass) {
-                        float *cell = prof + pp * 64 + lane;
-                        float r = 0.f;
-                        if (rowok[ps]) {
-                            r = *cell;
-                            *cell = 0.f;
-                        }
-#pragma unroll
-                        for (int t = 0; t < NTAP; ++t) acc[ps][t] = fmaf(h[t], r, acc[ps][t]);
+                    float *cell = prof + (grp * NPG + ps) * 64 + lane;
+                    float r = 0.f;
+                    if (rowok[ps]) {
+                        r = *cell;
+                        *cell = 0.f;
                     }
+#pragma unroll
+                    for (int t = 0; t < NTAP; ++t) acc[ps][t] = fmaf(h[t], r, acc[ps][t]);
                 }
                 if (npass > NPG) {                            // the other groups' rows: cleared only
                     for (int pp = 0; pp < npass; ++pp)
@@ -817,25 +813,40 @@ static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, in
     }
 }
 
-template <int R, int P, bool U, int TY>
+// Row passes of 64 lanes held in registers per row group: 2 where the
+// windows have at most 128 rows (radius 1), else 3.
+template <int R>
+constexpr int cone_fwd_npg(int nrcap) {
+    return (R == 1 && nrcap <= 128) ? 2 : 3;
+}
+
+template <int R, int P, bool U, int TY, int NPG>
 static hipError_t cone_fwd_u(const Plan &p, const float *recon, float *sino, hipStream_t st) {
     const Geo &g = p.g;
     const int tiles = ((g.nx + CTX - 1) / CTX) * ((g.ny + TY - 1) / TY);
     const int chunks = (g.ns + 64 * P - 1) / (64 * P);
-    hipLaunchKernelGGL((cone_forward_kernel<R, P, U, TY>), dim3(tiles, chunks, p.fwd_vsplit), dim3(CFW * 64),
+    hipLaunchKernelGGL((cone_forward_kernel<R, P, U, TY, NPG>), dim3(tiles, chunks, p.fwd_vsplit), dim3(CFW * 64),
                        p.fwd_lds, st, recon, sino, p.idx, p.views, p.fwin, p.fslab, g, p.fwd_nwcap, p.fwd_nrcap,
                        p.fwd_vsplit);
     return hipGetLastError();
 }
 
+template <int R, int P, int NPG>
+static hipError_t cone_fwd_n(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+    if (p.cone_ty == 8) {
+        if (p.cone_unit) return cone_fwd_u<R, P, true, 8, NPG>(p, recon, sino, st);
+        return cone_fwd_u<R, P, false, 8, NPG>(p, recon, sino, st);
+    }
+    if (p.cone_unit) return cone_fwd_u<R, P, true, 4, NPG>(p, recon, sino, st);
+    return cone_fwd_u<R, P, false, 4, NPG>(p, recon, sino, st);
+}
+
 template <int R, int P>
 static hipError_t cone_fwd_t(const Plan &p, const float *recon, float *sino, hipStream_t st) {
-    if (p.cone_ty == 8) {
-        if (p.cone_unit) return cone_fwd_u<R, P, true, 8>(p, recon, sino, st);
-        return cone_fwd_u<R, P, false, 8>(p, recon, sino, st);
+    if constexpr (R == 1) {
+        if (cone_fwd_npg<R>(p.fwd_nrcap) == 2) return cone_fwd_n<R, P, 2>(p, recon, sino, st);
     }
-    if (p.cone_unit) return cone_fwd_u<R, P, true, 4>(p, recon, sino, st);
-    return cone_fwd_u<R, P, false, 4>(p, recon, sino, st);
+    return cone_fwd_n<R, P, 3>(p, recon, sino, st);
 }
 
 template <int R>
@@ -877,19 +888,27 @@ hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, h
 }
 
 // Dynamic LDS above the default limit needs the opt-in attribute.
-hipError_t cone_forward_allow_lds(int radius, int stride, int ty, size_t bytes) {
+hipError_t cone_forward_allow_lds(int radius, int stride, int ty, int nrcap, size_t bytes) {
     const void *f = nullptr;
     const void *fu = nullptr;
+#define BPAMD_CFN(RR, PP, NN)                                                                                 \
+    {                                                                                                         \
+        f = ty == 8 ? (const void *)cone_forward_kernel<RR, PP, false, 8, NN>                                 \
+                    : (const void *)cone_forward_kernel<RR, PP, false, 4, NN>;                                \
+        fu = ty == 8 ? (const void *)cone_forward_kernel<RR, PP, true, 8, NN>                                 \
+                     : (const void *)cone_forward_kernel<RR, PP, true, 4, NN>;                                \
+    }
 #define BPAMD_CF(RR, PP)                                                                                      \
     if (radius == RR && stride == PP) {                                                                       \
-        f = ty == 8 ? (const void *)cone_forward_kernel<RR, PP, false, 8>                                     \
-                    : (const void *)cone_forward_kernel<RR, PP, false, 4>;                                    \
-        fu = ty == 8 ? (const void *)cone_forward_kernel<RR, PP, true, 8>                                     \
-                     : (const void *)cone_forward_kernel<RR, PP, true, 4>;                                    \
+        if constexpr (RR == 1) {                                                                              \
+            if (cone_fwd_npg<RR>(nrcap) == 2) BPAMD_CFN(RR, PP, 2) else BPAMD_CFN(RR, PP, 3)                  \
+        } else                                                                                                \
+            BPAMD_CFN(RR, PP, 3)                                                                              \
     }
     BPAMD_CF(1, 1) BPAMD_CF(1, 2) BPAMD_CF(1, 3) BPAMD_CF(2, 1) BPAMD_CF(2, 2) BPAMD_CF(2, 3)
     BPAMD_CF(3, 1) BPAMD_CF(3, 2) BPAMD_CF(3, 3) BPAMD_CF(4, 1) BPAMD_CF(4, 2) BPAMD_CF(4, 3)
 #undef BPAMD_CF
+#undef BPAMD_CFN
     if (!f) return hipErrorInvalidValue;
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e != hipSuccess) return e;
