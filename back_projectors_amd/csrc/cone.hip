@@ -169,11 +169,13 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
     // cell's LDS offset is kept from the load for the store (-1: none)
     auto stage_load = [&](int v, const Window &w, float (&st)[STG], int (&sa)[STG]) {
         const float rnw = 1.0f / (float)max(w.nw, 1);
+        // this view's window cells per thread (at most stg, the plan's largest)
+        const int stgv = w.nw > 0 && w.nrw > 0 ? (w.nw * w.nrw + NT - 1) / NT : 0;
 #pragma unroll
         for (int u = 0; u < STG; ++u) {
             st[u] = 0.f;
             sa[u] = -1;
-            if (u < stg) {
+            if (u < stgv) {
                 const int e = tid + NT * u;
                 const int m = (int)(((float)e + 0.5f) * rnw);   // exact: e < 2^22 and nw is small
                 const int c = e - m * w.nw;
