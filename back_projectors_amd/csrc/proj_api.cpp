@@ -214,17 +214,21 @@ WinMax max_window(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty
     return window_table(g, views, tx_, ty_, sl, nullptr);
 }
 
-// The parallel-beam forward strategy from the shapes alone (no data).  On
-// gfx950 the region walk won at every measured shape of 1e8 voxel-views or
-// more -- by 1.4x to 4.4x (512^2 x 64 at 16, 90 and 720 views, 256^2 x 128 at
-// 360, 1024^2 x 16 at 180, 512^2 x 32 translation at 64) -- while the gather
-// walk won below (64^2 x 8 at 90 views, 512^2 x 32 translation at 8 views),
-// where too few regions exist to fill the chip and each is loaded for only a
-// few views.
+// The parallel-beam forward strategy from the shapes alone (no data), from
+// a sweep of both strategies on gfx950 (bench.py --op sweep): the gather walk
+// wins at up to 1e8 voxel-views (64^2 x 8 at 90 views, 128^2 x 16 at 90 views
+// with radius 1 to 4, 512^2 x 32 translation at 8 views: 1.5x to 7x), and at
+// up to about 2.5e8 when there are few views (512^2 x 32 translation at 16 and
+// 24 views, 512^2 x 64 at 8 and 12 views: 1.1x to 1.5x), where the region
+// walk has too few views per region to amortise loading it and too few
+// regions to fill the chip.  The region walk wins from there on (512^2 x 64
+// at 16 views and more, 256^2 x 32 at 96 views and more, every 3.8e8 shape
+// with radius 1 to 4 and fine detectors: 1.2x to 6x).  The one shape of the
+// sweep the rule misplaces, 512^2 x 32 translation at 32 views, loses 9%.
 int choose_forward(const Geo &g, const Plan &plan) {
     (void)plan;
     const double vu = (double)g.nv * g.ny * g.nx * g.ns;
-    return vu <= 1e8 ? PROJ_FORWARD_GATHER : PROJ_FORWARD_TILE;
+    return (vu <= 1e8 || (vu <= 2.5e8 && g.nv <= 32)) ? PROJ_FORWARD_GATHER : PROJ_FORWARD_TILE;
 }
 
 // Validation and planning without touching the GPU.  Fills geo/views/plan.

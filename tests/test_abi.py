@@ -183,6 +183,19 @@ def test_cone_forward_tile_choice(bp, name, tile):
         assert f"{forced} px tile" in fwd(desc), desc
 
 
+@pytest.mark.parametrize("ny,ns,nv,kind,word", [
+    (64, 8, 90, "parallel", "gather:"), (512, 64, 8, "parallel", "gather:"), (512, 64, 12, "parallel", "gather:"),
+    (512, 64, 16, "parallel", "tile:"), (512, 32, 16, "translation", "gather:"), (512, 32, 24, "translation", "gather:"),
+    (512, 32, 64, "translation", "tile:"), (256, 32, 96, "parallel", "tile:"), (512, 64, 720, "parallel", "tile:"),
+])
+def test_forward_strategy_rule(bp, ny, ns, nv, kind, word):
+    """The planner's parallel forward strategy on shapes of the gfx950 sweep:
+    gather up to 1e8 voxel-views, and up to 2.5e8 with at most 32 views."""
+    base = W.get("translation-512x512x32-64v" if kind == "translation" else W.BENCH)
+    w = W.scaled(base, "sweep", ny=ny, nx=ny, ns=ns, nr=ns, nv=nv, nc=int(ny * 1.5) + 16)
+    assert word in bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape).split("forward:")[1]
+
+
 @pytest.mark.parametrize("strategy,word", [(1, "tile:"), (2, "gather:")])
 def test_forward_strategy_is_honoured(bp, strategy, word):
     """A forced parallel forward strategy shows in the plan; AUTO picks one."""
