@@ -154,11 +154,14 @@ proj_status proj_create(const proj_geometry *g, const int64_t recon_shape[3],
  * Graph capture: proj_forward, proj_back, proj_back_squared,
  * proj_forward_pixels and proj_back_pixels allocate, copy and synchronise
  * nothing and use no memset, so they can be captured into a HIP graph.  Outside
- * a capture, parallel-beam forwards on one handle are ordered on the GPU (they
- * share the handle's accumulation buffer); inside a capture that ordering is
- * the graph's, so two captured forwards on one handle must not run
- * concurrently.  The solvers (proj_cgls, proj_sirt) synchronise and cannot be
- * captured.
+ * a capture, parallel-beam forwards on one handle (proj_forward and
+ * proj_forward_pixels) are ordered on the GPU (they share the handle's
+ * accumulation buffer); inside a capture that ordering is the graph's.  So two
+ * captured forwards on one handle must not run concurrently, and a replayed
+ * graph holding a parallel forward must be ordered by the caller against
+ * every other parallel forward of the same handle on another stream (an
+ * event after the replay, a stream wait before the next one).  The solvers
+ * (proj_cgls, proj_sirt) synchronise and cannot be captured.
  */
 proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev, void *hip_stream);
 

@@ -71,6 +71,49 @@ def test_forward_back_graph_replays(bp, w, strategy):
     proj.close()
 
 
+@pytest.mark.parametrize("strategy", [1, 2], ids=["tile", "gather"])
+def test_replay_and_eager_forward_on_other_streams(bp, strategy):
+    """A replayed parallel forward and an eager one on another stream share
+    the handle's accumulation buffer, and inside a graph the library cannot
+    order them: the caller does, with an event after the replay and a stream
+    wait before the next replay.  Done that way, replay / eager / replay on
+    alternating streams all give the eager result."""
+    w = PAR_RAGGED
+    note(f"replay then eager on another stream {w.name} strategy={strategy}")
+    proj = bp.Projector(_geometry(w, strategy), w.recon_shape, w.sino_shape)
+    x, _ = inputs(w)
+    xs, x2 = dev(x), dev(3.0 * x)
+    ref = host(proj.forward(xs))
+    out_g = torch.empty(w.sino_shape, device="cuda:0")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        proj.forward(xs, out=out_g, stream=s1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s1):
+        proj.forward(xs, out=out_g, stream=s1)
+    outs = [torch.empty(w.sino_shape, device="cuda:0") for _ in range(3)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            g.replay()
+            done = torch.cuda.Event()
+            done.record(s1)
+        s2.wait_event(done)                        # the caller orders the eager forward after the replay
+        with torch.cuda.stream(s2):
+            proj.forward(x2, out=outs[rep], stream=s2)
+        s1.wait_stream(s2)                         # and the next replay after the eager forward
+        if rep == 1:
+            torch.cuda.synchronize()
+            assert rel_l2(host(out_g), ref) < 1e-6, "replay result"
+    torch.cuda.synchronize()
+    assert rel_l2(host(out_g), ref) < 1e-6
+    for rep in range(3):
+        assert rel_l2(host(outs[rep]), 3.0 * ref) < 1e-6, f"eager forward {rep} on the second stream"
+    proj.close()
+
+
 def test_pixel_batch_graph_replays(bp):
     w = PAR_RAGGED
     note(f"graph capture of batches {w.name}")
