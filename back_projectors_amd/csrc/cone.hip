@@ -24,6 +24,16 @@
 
 namespace bpamd {
 
+// Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle,
+// no index stride (the loads below address bytes directly).
+constexpr int kRawDwordRsrc = 0x00020000;
+// A byte offset past any buffer range the back sets up (each is one view of
+// the sinogram, below 2^31 bytes): the range check makes its load a zero.
+constexpr unsigned kOffRange = 0x80000000u;
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima):
+// every global load of this wave, the direct global-to-LDS ones included, done.
+constexpr int kWaitVm0 = 0x0F70;
+
 // Per (view, pixel) quantities of the flat cone.
 struct ConeVP {
     double f;      // u - n_c
@@ -81,10 +91,12 @@ __device__ __forceinline__ ConeVPB cone_vp_back(const Geo &g, const ViewK &vk, d
 
 // Back: lanes are the pixels of a BT x BT tile, each with SL slice
 // accumulators.  Per view the sinogram window the tile and slice chunk can reach
-// is staged in LDS, double buffered: view v + 1's cells are read into registers
-// (channels fastest, coalesced) while view v is gathered, then stored, with one
-// barrier per view.  The window's row pitch NRP is odd and fixed at compile
-// time, so the (2R+1)^2 tap reads of a slice share one address with immediate
+// is staged in LDS, double buffered: view v + 1's window rows are copied from
+// the sinogram straight into LDS (one direct global-to-LDS load per window row
+// and 64 channels, no registers held) while view v is gathered, and one wait
+// and barrier per view publishes them.  The window keeps the sinogram's
+// layout, channels fastest, with an odd channel pitch PC fixed at compile time,
+// so the (2R+1)^2 tap reads of a slice share one address with immediate
 // offsets, and lanes on one row but different channels hit different banks.
 // The per-view constants and window travel as one register (lanes 0-17 the
 // view's 18 dwords, lanes 18-21 its window) fetched two views ahead; the
@@ -105,18 +117,16 @@ __device__ __forceinline__ ConeVPB cone_vp_back(const Geo &g, const ViewK &vk, d
 // row must be the model's even at an exact half).  The chord scale
 // sqrt(d^2 + a^2 + dz^2) runs in fp32, with the per-pixel factor dv / M folded
 // into the channel taps.
-template <int SL, int R, int POW, int NRP>
+template <int SL, int R, int POW, int PC>
 __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__restrict__ sino,
                                                             float *__restrict__ recon,
                                                             const int32_t *__restrict__ idx,
                                                             const ViewK *__restrict__ views,
-                                                            const int4 *__restrict__ wtab, Geo g, int nwcap,
-                                                            int nrcap) {
+                                                            const int4 *__restrict__ wtab, Geo g, int nrcap) {
     constexpr int NT = BT * BT;
     constexpr int NTAP = 2 * R + 1;
-    constexpr int STG = CBSTG;            // staged cells per thread at most
-    static_assert(NRP % 2 == 1, "odd row pitch");
-    extern __shared__ float win[];        // two windows of [nwcap][NRP], rows fastest
+    static_assert(PC % 2 == 1, "odd channel pitch");
+    extern __shared__ float win[];        // two windows of [nrcap][PC], channels fastest
     static_assert(sizeof(ViewK) == 72, "ViewK is read as 18 dwords");
 
     const int tiles_x = (g.nx + BT - 1) / BT;
@@ -130,8 +140,8 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
     const int nk = min(SL, g.ns - k0);
     const int tid = (int)threadIdx.x;
     const int wl = tid & 63;
-    const int wsz = nwcap * NRP;          // floats per window
-    const int stg = (nwcap * nrcap + NT - 1) / NT;  // staged cells per thread, <= STG by the plan
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wsz = nrcap * PC;           // floats per window
     // rows m with m + R in [0, nr - 1 + 2R] have a tap on the detector; those
     // with m + R in [2R, nr - 1] have every tap on it (none if ib < 0)
     const unsigned rlim = (unsigned)(g.nr - 1 + 2 * R);
@@ -165,33 +175,29 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
         const int lo = __builtin_amdgcn_readlane((int)pv, 2 * e), hi = __builtin_amdgcn_readlane((int)pv, 2 * e + 1);
         return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
     };
-    // window cells, flattened with channels fastest (coalesced reads); each
-    // cell's LDS offset is kept from the load for the store (-1: none)
-    auto stage_load = [&](int v, const Window &w, float (&st)[STG], int (&sa)[STG]) {
-        const float rnw = 1.0f / (float)max(w.nw, 1);
-        // this view's window cells per thread (at most stg, the plan's largest)
-        const int stgv = w.nw > 0 && w.nrw > 0 ? (w.nw * w.nrw + NT - 1) / NT : 0;
-#pragma unroll
-        for (int u = 0; u < STG; ++u) {
-            st[u] = 0.f;
-            sa[u] = -1;
-            if (u < stgv) {
-                const int e = tid + NT * u;
-                const int m = (int)(((float)e + 0.5f) * rnw);   // exact: e < 2^22 and nw is small
-                const int c = e - m * w.nw;
-                const int row = w.m0 + m, n = w.n0 + c;
-                if (w.nw > 0 && m < w.nrw) {
-                    sa[u] = c * NRP + m;
-                    if (row >= 0 && row < g.nr && n >= 0 && n < g.nc)
-                        st[u] = sino[((int64_t)v * g.nr + row) * g.nc + n];
+    // View v's window into buf: wave w copies window rows w, w + 4, ..., each
+    // as direct global-to-LDS loads of 64 channels (lane c: channel n0 + c to
+    // LDS cell [row][c]).  A cell off the detector gets an offset past the
+    // view's buffer range, which the range check turns into a zero; lanes past
+    // the window's width write nothing (no tap reads there).
+    const int64_t vfl = (int64_t)g.nr * g.nc;    // floats per view (bytes below 2^31, checked by the plan)
+    auto stage = [&](int v, const Window &w, float *buf) {
+        if (w.nw <= 0 || w.nrw <= 0) return;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(sino + (int64_t)v * vfl), (short)0, (int)(vfl * 4), kRawDwordRsrc);
+        for (int c0 = 0; c0 < w.nw; c0 += 64) {
+            const int c = c0 + wl, n = w.n0 + c;
+            const bool nok = (unsigned)n < (unsigned)g.nc;
+            if (c < w.nw) {
+                for (int m = wave; m < w.nrw; m += NT / 64) {
+                    const int row = w.m0 + m;
+                    const unsigned off =
+                        nok && (unsigned)row < (unsigned)g.nr ? (unsigned)(row * g.nc + n) * 4u : kOffRange;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(buf + m * PC + c0),
+                                                             4, off, 0, 0, 0);
                 }
             }
         }
-    };
-    auto stage_store = [&](float *buf, const float (&st)[STG], const int (&sa)[STG]) {
-#pragma unroll
-        for (int u = 0; u < STG; ++u)
-            if (u < stg && sa[u] >= 0) buf[sa[u]] = st[u];
     };
 
     if (g.nv > 0) {
@@ -199,24 +205,17 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
         fetch_view(0, pcur);
         fetch_view(min(1, g.nv - 1), pnext);
         int ncur = valid ? idx[p] : INT32_MIN;
-        {
-            const Window w0 = win_of(pcur);
-            float st[STG];
-            int sa[STG];
-            stage_load(0, w0, st, sa);
-            stage_store(win, st, sa);
-        }
+        stage(0, win_of(pcur), win);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
         for (int v = 0; v < g.nv; ++v) {
             const bool more = v + 1 < g.nv;
             const Window wv = win_of(pcur);
             const Window wn = win_of(pnext);
-            float st[STG];
-            int sa[STG];
             int nnext = INT32_MIN;
             uint32_t pafter = pnext;
             if (more) {
-                stage_load(v + 1, wn, st, sa);
+                stage(v + 1, wn, win + ((v + 1) & 1) * wsz);
                 nnext = valid ? idx[(int64_t)(v + 1) * np + p] : INT32_MIN;
                 fetch_view(min(v + 2, g.nv - 1), pafter);
             }
@@ -236,8 +235,8 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                 for (int t = 0; t < NTAP; ++t)
                     h[t] = POW == 2 ? ((float)(hd[t] * hd[t]) * (q.lsc * q.lsc)) : ((float)hd[t] * q.lsc);
                 // window cell of row offset sg, channel tap t at slice k:
-                // col[(m_k + R) + t NRP + sg]
-                const float *col = win + (v & 1) * wsz + (ncur - R - wv.n0) * NRP - wv.m0 - 2 * R;
+                // col[(m_k + R) PC + sg PC + t]
+                const float *col = win + (v & 1) * wsz + (ncur - R - wv.n0) - (wv.m0 + 2 * R) * PC;
                 const double wrow = q.mr * g.dv;        // footprint width in rows = row advance per slice
                 const double hrowd = 0.5 * wrow;
                 const float hrow = (float)hrowd, wcap = fminf(1.f, (float)wrow);
@@ -342,13 +341,13 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                             } else {
                                 lk = __builtin_amdgcn_sqrtf(qk);
                             }
-                            const float *cell = col + hr;
+                            const float *cell = col + hr * PC;
                             float s = 0.f;
 #pragma unroll
                             for (int sg = 0; sg < NTAP; ++sg) {
                                 float rv = 0.f;
 #pragma unroll
-                                for (int t = 0; t < NTAP; ++t) rv = fmaf(h[t], cell[t * NRP + sg], rv);
+                                for (int t = 0; t < NTAP; ++t) rv = fmaf(h[t], cell[sg * PC + t], rv);
                                 s = fmaf(gw[sg], rv, s);
                             }
                             acc[k] = fmaf(lk, s, acc[k]);
@@ -356,7 +355,7 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                     }
                 }
             }
-            if (more) stage_store(win + ((v + 1) & 1) * wsz, st, sa);
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the next window has landed in LDS
             __syncthreads();
             pcur = pnext;
             pnext = pafter;
@@ -791,26 +790,27 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
     }
 }
 
-template <int SL, int R, int NRP>
+template <int SL, int R, int PC>
 static hipError_t cone_back_n(const Plan &p, const float *sino, float *recon, int power, hipStream_t st) {
     const Geo &g = p.g;
     const int tiles = ((g.nx + BT - 1) / BT) * ((g.ny + BT - 1) / BT);
     const int chunks = (g.ns + SL - 1) / SL;
     if (power == 2)
-        hipLaunchKernelGGL((cone_back_kernel<SL, R, 2, NRP>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st,
-                           sino, recon, p.idx, p.views, p.bwin, g, p.back_nwcap, p.back_nrcap);
+        hipLaunchKernelGGL((cone_back_kernel<SL, R, 2, PC>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st,
+                           sino, recon, p.idx, p.views, p.bwin, g, p.back_nrcap);
     else
-        hipLaunchKernelGGL((cone_back_kernel<SL, R, 1, NRP>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st,
-                           sino, recon, p.idx, p.views, p.bwin, g, p.back_nwcap, p.back_nrcap);
+        hipLaunchKernelGGL((cone_back_kernel<SL, R, 1, PC>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st,
+                           sino, recon, p.idx, p.views, p.bwin, g, p.back_nrcap);
     return hipGetLastError();
 }
 
 template <int SL, int R>
 static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, int power, hipStream_t st) {
-    switch (p.back_nrp) {
+    switch (p.back_pc) {
     case 33: return cone_back_n<SL, R, 33>(p, sino, recon, power, st);
     case 65: return cone_back_n<SL, R, 65>(p, sino, recon, power, st);
     case 129: return cone_back_n<SL, R, 129>(p, sino, recon, power, st);
+    case 257: return cone_back_n<SL, R, 257>(p, sino, recon, power, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -36,7 +36,7 @@ struct Plan {
     int back_sl = 0;                // slices per chunk (accumulators per lane)
     int back_nwcap = 0;             // window channels capacity
     int back_nrcap = 0;             // window rows capacity (cone)
-    int back_nrp = 0;               // cone back LDS row pitch: 33, 65 or 129 (odd, compile-time in the kernel)
+    int back_pc = 0;                // cone back LDS channel pitch: 33, 65, 129 or 257 (odd, compile-time in the kernel)
     size_t back_lds = 0;            // dynamic LDS bytes
     int back_ncg = 1;               // parallel back: 32-channel staging groups (1 or 2)
 
@@ -68,7 +68,6 @@ constexpr int CFW = 4;   // cone forward waves per workgroup (one view each at a
 // LDS floats of one cone forward wave: its detector window [nwcap][nrp] and a
 // one-column row profile [nrp] (rows of the window, the first projection step)
 __host__ __device__ inline int cone_fwd_wave_words(int nwcap, int nrp) { return (nwcap + 1) * nrp; }
-constexpr int CBSTG = 8;  // cone back: staged window cells per thread at most (window <= 256 * CBSTG cells)
 
 hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
 hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st);

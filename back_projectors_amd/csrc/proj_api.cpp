@@ -371,24 +371,26 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
             return fail(PROJ_ERR_UNSUPPORTED, "a forward region spans more than 8190 channels");
         if (plan.fwd_strategy == PROJ_FORWARD_GATHER) plan.fwd_lds = 0;
     } else {
-        // two staged windows (double buffer), each at most BT*BT*CBSTG cells,
-        // laid out with an odd row pitch of 33, 65 or 129 floats (a
-        // compile-time constant of the kernel)
-        auto back_bytes = [&](int sl, int &nwcap, int &nrcap, int &nrp) {
+        // two windows (double buffer) of [rows][channels], channels fastest with
+        // an odd pitch of 33, 65, 129 or 257 floats (a compile-time constant of the
+        // kernel); the window rows are copied from one view of the sinogram
+        // with 32-bit byte offsets below 2^31
+        if ((int64_t)R * C * 4 >= ((int64_t)1 << 31))
+            return fail(PROJ_ERR_UNSUPPORTED, "cone back: one view of the sinogram is 2 GiB or more");
+        auto back_bytes = [&](int sl, int &nwcap, int &nrcap, int &pc) {
             const WinMax w = max_window(g, views, BT, BT, sl);
             nwcap = w.nw + 2;
             nrcap = w.nr + 2;
-            nrp = nrcap <= 33 ? 33 : (nrcap <= 65 ? 65 : 129);
-            return 2 * (size_t)nwcap * nrp * sizeof(float);
+            pc = nwcap <= 33 ? 33 : (nwcap <= 65 ? 65 : (nwcap <= 129 ? 129 : 257));
+            return 2 * (size_t)nrcap * pc * sizeof(float);
         };
         for (int sl = pick_chunk(S, {8, 16, 32});; sl /= 2) {
             plan.back_sl = sl;
-            plan.back_lds = back_bytes(sl, plan.back_nwcap, plan.back_nrcap, plan.back_nrp);
-            if ((plan.back_lds <= kMaxLds && plan.back_nwcap * plan.back_nrcap <= BT * BT * CBSTG &&
-                 plan.back_nrcap <= 129) || sl == 8) break;
+            plan.back_lds = back_bytes(sl, plan.back_nwcap, plan.back_nrcap, plan.back_pc);
+            if ((plan.back_lds <= kMaxLds && plan.back_nwcap <= 257) || sl == 8) break;
         }
-        if (plan.back_nwcap * plan.back_nrcap > BT * BT * CBSTG || plan.back_nrcap > 129)
-            return fail(PROJ_ERR_UNSUPPORTED, "cone back window larger than the staging allows (detector far finer than the voxels)");
+        if (plan.back_nwcap > 257)
+            return fail(PROJ_ERR_UNSUPPORTED, "cone back window wider than 257 channels (detector far finer than the voxels)");
         // smallest row magnification (rows per slice) over the whole scan: lanes
         // of one forward instruction take slices `stride` apart, so that their
         // rows differ
