@@ -401,7 +401,7 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                                                                  const ViewK *__restrict__ views,
                                                                  const int4 *__restrict__ wtab,
                                                                  const int4 *__restrict__ stab, Geo g, int nwcap,
-                                                                 int nrp, int vsplit) {
+                                                                 int nrp, int ncol, int vsplit) {
     constexpr int NTAP = 2 * R + 1;
     constexpr int CH = 64 * P;            // slices per chunk
     constexpr int NPX = CTX * TY;         // pixels per tile (at most one per lane)
@@ -409,8 +409,8 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
     extern __shared__ float lds[];
     const int lane = (int)threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    float *win = lds + wave * cone_fwd_wave_words(nwcap, nrp);   // this wave's window [nwcap][nrp]
-    float *prof = win + nwcap * nrp;                             // and row profile [nrp]
+    float *win = lds + wave * cone_fwd_wave_words(nwcap, nrp, ncol);   // this wave's window [nwcap][nrp]
+    float *prof = win + nwcap * nrp;                                   // and row profile columns [ncol][nrp]
 
     const int tiles_x = (g.nx + CTX - 1) / CTX;
     const int ntiles = tiles_x * ((g.ny + TY - 1) / TY);
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
     const int np = g.ny * g.nx;
 
     // the profile starts at zero; the second step clears every cell it reads
-    for (int e = lane; e < nrp; e += 64) prof[e] = 0.f;
+    for (int e = lane; e < ncol * nrp; e += 64) prof[e] = 0.f;
 
     const int vper = (g.nv + vsplit - 1) / vsplit;
     const int vbeg = (int)blockIdx.z * vper;
@@ -438,6 +438,12 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
     const int il = ti0 + lane / CTX, jl = tj0 + lane % CTX;
     const bool lin = lane < NPX && il < g.ny && jl < g.nx;
     const double xl = pix_x(g, jl), yl = pix_y(g, il);
+    // this lane's voxel cylinder in the chunk (clamped into the volume for
+    // lanes without a pixel, which are never walked), as two dwords the walk
+    // reads out per pixel
+    const uint64_t cyl = reinterpret_cast<uint64_t>(
+        recon + ((int64_t)min(il, g.ny - 1) * g.nx + min(jl, g.nx - 1)) * g.ns + k0);
+    const int cyl_lo = (int)(uint32_t)cyl, cyl_hi = (int)(uint32_t)(cyl >> 32);
 
     // Per-view data, fetched two views ahead with vector loads: lanes 0-17
     // hold the view's constants (ViewK, 18 dwords), lanes 18-21 its window,
@@ -483,13 +489,19 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         if (wd.nw <= 0 || wd.nrw <= 0) return;
         // The chunk's slices that can reach the detector rows in this view
         // (the slab, from the creation pass): with `unit`, lanes take
-        // consecutive slices from the first one, in `nit` passes of 64;
-        // otherwise lane l takes slices l*P + ph over the whole chunk.
-        // (Without slabs, U false: every chunk walks all its slices with stride P.)
+        // consecutive slices from the first one, in `nit` passes of 64, and
+        // with `inter` as well lane l adds into profile column l mod P (its
+        // slices are P apart, so on distinct rows; only where the plan gave
+        // the wave P columns); otherwise lane l takes
+        // slices l*P + ph over the whole chunk.  (Without slabs, U false:
+        // every chunk walks all its slices with stride P.)
         const int klo = U ? __builtin_amdgcn_readlane((int)pv, 22) : 0;
         const int nit = U ? __builtin_amdgcn_readlane((int)pv, 23) : P;
-        const bool unit = U && __builtin_amdgcn_readlane((int)pv, 24) != 0;
+        const int smode = U ? __builtin_amdgcn_readlane((int)pv, 24) : 0;
+        const bool unit = smode != 0;
+        const bool inter = P > 1 && smode == 2;
         if (nit <= 0) return;                                 // no slice reaches the detector
+        const int pcol = inter ? (lane % P) * nrp : 0;        // this lane's profile column
         // this lane's pixel: channel taps and the per-(view, pixel) constants, fp64
         const bool act = pn >= -R && pn <= g.nc - 1 + R;
         const uint64_t actb = __builtin_amdgcn_ballot_w64(act);
@@ -584,7 +596,7 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
             const double hw = 0.5 * wbox, nhw = -hw;
             const double hwm = hw - 0.5;                      // exact for hw in [1/4, 1] (Sterbenz)
             const float wboxf = (float)wbox;
-            float *const pr = prof - wd.m0 - R;               // pr[mk + sg]: row offset sg - R of row mk
+            float *const pr = prof + pcol - wd.m0 - R;        // pr[mk + sg]: row offset sg - R of row mk
             auto slices = [&](auto narrow_c) {
                 constexpr bool NARROW = decltype(narrow_c)::value;
 #pragma unroll
@@ -648,89 +660,111 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         // loads that are all unconditional let the compiler wait for the
         // current pixel's alone, not for the prefetch behind them.
         auto load_px = [&](int q, float (&xv)[P]) {
-            const float *src = recon + (int64_t)((ti0 + q / CTX) * g.nx + tj0 + q % CTX) * g.ns + k0;
+            const float *src = reinterpret_cast<const float *>(
+                ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(cyl_hi, q) << 32) |
+                (uint64_t)(uint32_t)__builtin_amdgcn_readlane(cyl_lo, q));
 #pragma unroll
             for (int ph = 0; ph < P; ++ph) xv[ph] = src[kkc[ph]];
         };
 
         // Row groups of NPG passes: the ring accumulators of one group live
         // in registers; a window taller than 64 * NPG rows walks the pixels
-        // once per group (the profile is cleared in full every time).
-        for (int grp = 0; grp * NPG < npass; ++grp) {
-            float acc[NPG][NTAP];
+        // once per group (the profile is cleared in full every time).  Row
+        // passes that lie inside the profile column and the window column
+        // whatever this view's window (a single group, and passes below the
+        // plan's row pitch nrp) read, clear and write without a row guard:
+        // rows past this view's window hold zeros in the profile and are never
+        // flushed from the window.  The last pass of a group is guarded.
+        auto walk_groups = [&](auto full_c) {
+            constexpr bool FULL = decltype(full_c)::value;
+            for (int grp = 0; grp * NPG < npass; ++grp) {
+                float acc[NPG][NTAP];
 #pragma unroll
-            for (int ps = 0; ps < NPG; ++ps)
+                for (int ps = 0; ps < NPG; ++ps)
 #pragma unroll
-                for (int s = 0; s < NTAP; ++s) acc[ps][s] = 0.f;
-            bool rowok[NPG];
+                    for (int s = 0; s < NTAP; ++s) acc[ps][s] = 0.f;
+                bool rowok[NPG];
 #pragma unroll
-            for (int ps = 0; ps < NPG; ++ps) rowok[ps] = (grp * NPG + ps) * 64 + lane < nrw;
-            int lo = cbase;                                   // channel of ring slot 0
-            // write channel lo's accumulators into its window column and
-            // shift the ring down by one channel (slot t holds channel lo + t)
-            auto finish = [&]() {
-                float *col = colb + (lo - cbase) * nrp + grp * NPG * 64;
-                // (a pass past the window's rows has no lane with rowok and
-                // only ever adds zeros, so no pass needs a guard of its own)
+                for (int ps = 0; ps < NPG; ++ps) rowok[ps] = (FULL && ps + 1 < NPG) || (grp * NPG + ps) * 64 + lane < nrw;
+                int lo = cbase;                                   // channel of ring slot 0
+                // write channel lo's accumulators into its window column and
+                // shift the ring down by one channel (slot t holds channel lo + t)
+                auto finish = [&]() {
+                    float *col = colb + (lo - cbase) * nrp + grp * NPG * 64;
+                    // (a pass past the window's rows has no lane with rowok and
+                    // only ever adds zeros, so no pass needs a guard of its own)
 #pragma unroll
-                for (int ps = 0; ps < NPG; ++ps) {
-                    if (rowok[ps]) col[ps * 64] = acc[ps][0];
+                    for (int ps = 0; ps < NPG; ++ps) {
+                        if (rowok[ps]) col[ps * 64] = acc[ps][0];
 #pragma unroll
-                    for (int t = 0; t + 1 < NTAP; ++t) acc[ps][t] = acc[ps][t + 1];
-                    acc[ps][NTAP - 1] = 0.f;
-                }
-                ++lo;
-            };
-            // Step 2 for one pixel, whose taps cover channels lo .. lo + 2R:
-            // every profile row of the window is read, cleared and added into
-            // the ring.
-            auto to_channels = [&](int q) {
-                float h[NTAP];
-#pragma unroll
-                for (int t = 0; t < NTAP; ++t)
-                    h[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hq[t]), q));
-#pragma unroll
-                for (int ps = 0; ps < NPG; ++ps) {
-                    float *cell = prof + (grp * NPG + ps) * 64 + lane;
-                    float r = 0.f;
-                    if (rowok[ps]) {
-                        r = *cell;
-                        *cell = 0.f;
+                        for (int t = 0; t + 1 < NTAP; ++t) acc[ps][t] = acc[ps][t + 1];
+                        acc[ps][NTAP - 1] = 0.f;
                     }
+                    ++lo;
+                };
+                // Step 2 for one pixel, whose taps cover channels lo .. lo + 2R:
+                // every profile row of the window is read, cleared and added into
+                // the ring.
+                auto to_channels = [&](int q) {
+                    float h[NTAP];
 #pragma unroll
-                    for (int t = 0; t < NTAP; ++t) acc[ps][t] = fmaf(h[t], r, acc[ps][t]);
+                    for (int t = 0; t < NTAP; ++t)
+                        h[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hq[t]), q));
+#pragma unroll
+                    for (int ps = 0; ps < NPG; ++ps) {
+                        float *cell = prof + (grp * NPG + ps) * 64 + lane;
+                        float r = 0.f;
+                        if (rowok[ps]) {
+                            r = *cell;
+                            *cell = 0.f;
+                            if (inter) {
+#pragma unroll
+                                for (int c = 1; c < P; ++c) {
+                                    r += cell[c * nrp];
+                                    cell[c * nrp] = 0.f;
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int t = 0; t < NTAP; ++t) acc[ps][t] = fmaf(h[t], r, acc[ps][t]);
+                    }
+                    if (!FULL && npass > NPG) {                   // the other groups' rows: cleared only
+                        for (int pp = 0; pp < npass; ++pp)
+                            if (pp / NPG != grp && pp * 64 + lane < nrw)
+                                for (int c = 0; c < (inter ? P : 1); ++c) prof[c * nrp + pp * 64 + lane] = 0.f;
+                    }
+                };
+                auto visit = [&](int i, const float (&xv)[P]) {
+                    const int q = __builtin_amdgcn_readlane(order, i);
+                    const int n = __builtin_amdgcn_readlane(korder, i);
+                    while (lo < n - R) finish();                  // channels the walk has passed
+                    to_rows(q, xv);
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    to_channels(q);
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                };
+                {
+                    float xa[P], xb[P];
+                    int i = 0;
+                    // (the prefetch is always issued, the last pixel's again at
+                    // the end, so that the wait counts stay static)
+                    load_px(__builtin_amdgcn_readlane(order, 0), xa);
+                    for (;;) {
+                        load_px(__builtin_amdgcn_readlane(order, min(i + 1, npix - 1)), xb);
+                        visit(i, xa);
+                        if (++i >= npix) break;
+                        load_px(__builtin_amdgcn_readlane(order, min(i + 1, npix - 1)), xa);
+                        visit(i, xb);
+                        if (++i >= npix) break;
+                    }
                 }
-                if (npass > NPG) {                            // the other groups' rows: cleared only
-                    for (int pp = 0; pp < npass; ++pp)
-                        if (pp / NPG != grp && pp * 64 + lane < nrw) prof[pp * 64 + lane] = 0.f;
-                }
-            };
-            auto visit = [&](int i, const float (&xv)[P]) {
-                const int q = __builtin_amdgcn_readlane(order, i);
-                const int n = __builtin_amdgcn_readlane(korder, i);
-                while (lo < n - R) finish();                  // channels the walk has passed
-                to_rows(q, xv);
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                to_channels(q);
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            };
-            {
-                float xa[P], xb[P];
-                int i = 0;
-                // (the prefetch is always issued, the last pixel's again at
-                // the end, so that the wait counts stay static)
-                load_px(__builtin_amdgcn_readlane(order, 0), xa);
-                for (;;) {
-                    load_px(__builtin_amdgcn_readlane(order, min(i + 1, npix - 1)), xb);
-                    visit(i, xa);
-                    if (++i >= npix) break;
-                    load_px(__builtin_amdgcn_readlane(order, min(i + 1, npix - 1)), xa);
-                    visit(i, xb);
-                    if (++i >= npix) break;
-                }
+                while (lo <= clast) finish();
             }
-            while (lo <= clast) finish();
-        }
+        };
+        if (npass <= NPG && nrp >= (NPG - 1) * 64)
+            walk_groups(std::true_type{});
+        else
+            walk_groups(std::false_type{});
 
         // add the walked columns of the window to the sinogram: lanes along
         // channels, coalesced.  A span of at most 64 channels goes dm = 64 /
@@ -829,7 +863,7 @@ static hipError_t cone_fwd_u(const Plan &p, const float *recon, float *sino, hip
     const int chunks = (g.ns + 64 * P - 1) / (64 * P);
     hipLaunchKernelGGL((cone_forward_kernel<R, P, U, TY, NPG>), dim3(tiles, chunks, p.fwd_vsplit), dim3(CFW * 64),
                        p.fwd_lds, st, recon, sino, p.idx, p.views, p.fwin, p.fslab, g, p.fwd_nwcap, p.fwd_nrcap,
-                       p.fwd_vsplit);
+                       p.cone_ncol, p.fwd_vsplit);
     return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@ struct Plan {
     int cone_stride = 1;            // cone forward: slices between the lanes of one instruction
     int cone_unit = 0;              // cone forward: some slab saves work (the slab-reading kernel)
     int cone_ty = 4;                // cone forward: tile rows (CTX x cone_ty pixels, 4 or 8)
+    int cone_ncol = 1;              // cone forward: row-profile columns per wave (1, or cone_stride: interleaved slabs)
 };
 
 constexpr int BT = 16;   // back tile edge (pixels), 256 threads
@@ -65,9 +66,12 @@ constexpr int FRS2Y = 32;
 inline int fwd_groups(int rsx, int rsy) { return ((rsx * rsy + 79) / 80) * 5; }
 constexpr int CTX = 8;   // cone forward tile (pixels along x); 4 or 8 rows of them (Plan::cone_ty)
 constexpr int CFW = 4;   // cone forward waves per workgroup (one view each at a time)
-// LDS floats of one cone forward wave: its detector window [nwcap][nrp] and a
-// one-column row profile [nrp] (rows of the window, the first projection step)
-__host__ __device__ inline int cone_fwd_wave_words(int nwcap, int nrp) { return (nwcap + 1) * nrp; }
+// LDS floats of one cone forward wave: its detector window [nwcap][nrp] and
+// ncol row-profile columns [ncol][nrp] (rows of the window, the first
+// projection step; with ncol = stride, lanes of one instruction add into
+// column lane mod stride where a slab takes consecutive slices on rows
+// closer than one apart)
+__host__ __device__ inline int cone_fwd_wave_words(int nwcap, int nrp, int ncol) { return (nwcap + ncol) * nrp; }
 
 hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
 hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st);

@@ -104,11 +104,20 @@ WinMax window_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int 
 // whose rows can reach the detector in that view, conservatively for every
 // pixel of the tile (rows within half a row of [-r, R - 1 + r], a slice of
 // margin each side; the kernel still tests each slice exactly), as (first
-// slice, passes, unit stride, 0).  With the tile's smallest row advance per
-// slice (magnification times the voxel pitch) at least one, consecutive
-// slices fall on distinct rows, and lanes may take consecutive slices from
-// the first one; that is used when it needs no more passes than the planned
-// stride.  Zero passes: no slice of the chunk reaches the detector in that view.
+// slice, passes, mode, 0).  Lanes of one instruction adding into one profile
+// column must hold slices on distinct rows:
+//   mode 1 (unit): the tile's smallest row advance per slice (magnification
+//     times the voxel pitch) is at least one, so lane l takes consecutive
+//     slices from the first one, all into one column;
+//   mode 2 (interleaved): lane l takes consecutive slices from the first one
+//     and adds into profile column l mod stride, whose slices are then
+//     `stride` apart (stride times the smallest advance is at least one);
+//     used where it takes fewer passes than the stride, if the plan gives
+//     each wave `stride` profile columns;
+//   mode 0 (strided): lane l takes slices l * stride + ph over the whole
+//     chunk, one column (as many passes as mode 2 would take there, with
+//     one profile column to read instead of `stride`).
+// Zero passes: no slice of the chunk reaches the detector in that view.
 struct SlabRange {
     double kglo, kghi;   // the tile's slices that can reach the detector (all chunks)
     double mlo;          // the tile's smallest row magnification
@@ -130,7 +139,7 @@ SlabRange slab_range(const Geo &g, const ViewK &vk, int i0, int i1, int j0, int 
     return {std::floor(zlo / g.dv + g.cz) - 1.0, std::ceil(zhi / g.dv + g.cz) + 1.0, mlo};
 }
 
-Window slab_of(const Geo &g, const SlabRange &sr, int k0, int nk, int stride) {
+Window slab_of(const Geo &g, const SlabRange &sr, int k0, int nk, int stride, bool inter_ok) {
     Window s;
     s.n0 = 0;
     s.nw = 0;
@@ -144,16 +153,17 @@ Window slab_of(const Geo &g, const SlabRange &sr, int k0, int nk, int stride) {
         // Unit stride also where it takes as many passes: the rows of one
         // instruction then sit about mr apart instead of stride * mr
         const bool unit = stride > 1 && sr.mlo * g.dv >= 1.0 + 1e-9 && nit_unit <= stride;
-        s.n0 = unit ? klo : 0;
-        s.nw = unit ? nit_unit : stride;
-        s.m0 = unit ? 1 : 0;
+        const bool inter = inter_ok && !unit && stride > 1 && nit_unit < stride;
+        s.n0 = unit || inter ? klo : 0;
+        s.nw = unit || inter ? nit_unit : stride;
+        s.m0 = unit ? 1 : (inter ? 2 : 0);
     }
     return s;
 }
 
 // Slabs of every (view, tile, slice chunk), in the window table's order.
 void slab_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_, int sl, int stride,
-                std::vector<Window> *out) {
+                bool inter_ok, std::vector<Window> *out) {
     const int ty = (g.ny + ty_ - 1) / ty_, tx = (g.nx + tx_ - 1) / tx_;
     const int nch = (g.ns + sl - 1) / sl;
     out->resize((size_t)g.nv * ty * tx * nch);
@@ -166,7 +176,7 @@ void slab_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_,
                 const SlabRange sr = slab_range(g, views[v], i0, i1, j0, j1);
                 for (int c = 0; c < nch; ++c, ++e) {
                     const int k0 = c * sl, nk = std::min(sl, g.ns - k0);
-                    (*out)[e] = slab_of(g, sr, k0, nk, stride);
+                    (*out)[e] = slab_of(g, sr, k0, nk, stride, inter_ok);
                 }
             }
 }
@@ -181,7 +191,9 @@ void slab_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_,
 // 256^3 cone forward of a dense volume 15.0 ms at 8 x 4, flush-bound, and
 // 11.3 ms at 8 x 8; the 512^2 x 96 helical scan 61.5 ms at 8 x 4,
 // work-bound, and 66.9 ms at 8 x 8).
-double cone_forward_cost(const Geo &g, const std::vector<ViewK> &views, int ty_, int sl, int stride) {
+// With `passes`, the sampled pixel-passes instead (slab passes times tile pixels).
+double cone_forward_cost(const Geo &g, const std::vector<ViewK> &views, int ty_, int sl, int stride, bool inter_ok,
+                         bool passes = false) {
     const int ty = (g.ny + ty_ - 1) / ty_, tx = (g.nx + CTX - 1) / CTX;
     const int nch = (g.ns + sl - 1) / sl;
     const int step = std::max(1, g.nv / 64);
@@ -198,12 +210,13 @@ double cone_forward_cost(const Geo &g, const std::vector<ViewK> &views, int ty_,
                     const int k0 = c * sl, nk = std::min(sl, g.ns - k0);
                     const Window w = tile_window(g, views[v], i0, i1, j0, j1, k0, k0 + nk - 1);
                     if (w.nw <= 0 || w.nrw <= 0) continue;
-                    pixpass += npx * slab_of(g, sr, k0, nk, stride).nw;
+                    pixpass += npx * slab_of(g, sr, k0, nk, stride, inter_ok).nw;
                     const int r0 = std::max(w.m0, 0), r1 = std::min(w.m0 + w.nrw - 1, g.nr - 1);
                     const int c0 = std::max(w.n0, 0), c1 = std::min(w.n0 + w.nw - 1, g.nc - 1);
                     if (r1 >= r0 && c1 >= c0) lines += (double)(r1 - r0 + 1) * (c1 / 16 - c0 / 16 + 1);
                 }
             }
+    if (passes) return pixpass;
     const double scale = nsample > 0 ? (double)g.nv / nsample : 0.0;
     const double work = pixpass * scale * 0.12e-9 * (ty_ == 8 ? 1.05 : 1.0);
     const double flush = lines * scale / 21.6e9;
@@ -415,14 +428,21 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         else if (gp->forward_strategy == PROJ_FORWARD_CONE_TILE_8X8)
             plan.cone_ty = 8;
         else
-            plan.cone_ty = cone_forward_cost(g, views, 8, plan.fwd_sl, stride) <
-                                   cone_forward_cost(g, views, 4, plan.fwd_sl, stride)
+            plan.cone_ty = cone_forward_cost(g, views, 8, plan.fwd_sl, stride, false) <
+                                   cone_forward_cost(g, views, 4, plan.fwd_sl, stride, false)
                                ? 8
                                : 4;
+        // `stride` profile columns per wave where the interleaved slabs save a
+        // tenth of the slice passes or more (each column costs LDS, which can
+        // cost a workgroup per CU)
+        plan.cone_ncol = 1;
+        if (stride > 1 && cone_forward_cost(g, views, plan.cone_ty, plan.fwd_sl, stride, true, true) <=
+                              0.9 * cone_forward_cost(g, views, plan.cone_ty, plan.fwd_sl, stride, false, true))
+            plan.cone_ncol = stride;
         const WinMax wf = max_window(g, views, CTX, plan.cone_ty, plan.fwd_sl);
         plan.fwd_nwcap = wf.nw;
         plan.fwd_nrcap = wf.nr | 1;
-        plan.fwd_lds = (size_t)CFW * cone_fwd_wave_words(plan.fwd_nwcap, plan.fwd_nrcap) * sizeof(float);
+        plan.fwd_lds = (size_t)CFW * cone_fwd_wave_words(plan.fwd_nwcap, plan.fwd_nrcap, plan.cone_ncol) * sizeof(float);
     }
     if (plan.back_lds > kMaxLds || plan.fwd_lds > kMaxLdsOptIn) {
         char buf[160];
@@ -471,7 +491,8 @@ int describe(const Plan &p, int64_t table_bytes, char *buf, int len) {
                    ? "gather: per-view sorted walk of all pixels, lanes=16 slices x 4 views, voxels from memory"
                    : (p.fwd_spl == 2 ? "tile: channel-ordered region walk, lanes=16 x 4 views with 2 slices each, ring accumulators"
                                      : "tile: channel-ordered region walk, lanes=16 slices x 4 views, ring accumulators"))
-            : "wave per view: lanes=strided slices into a row profile, then lanes=rows into channel ring accumulators",
+            : (p.cone_ncol > 1 ? "wave per view: lanes=slices into interleaved row-profile columns, then lanes=rows into channel ring accumulators"
+                               : "wave per view: lanes=strided slices into a row profile, then lanes=rows into channel ring accumulators"),
         p.fwd_sl,
         p.fwd_nwcap, par ? p.fwd_sl : p.fwd_nrcap, p.fwd_lds, p.fwd_vsplit, (long long)table_bytes);
 }
@@ -617,9 +638,9 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
             window_table(geo, views, BT, BT, plan.back_sl, &bw);
             if (geo.kind != 0) {
                 window_table(geo, views, CTX, plan.cone_ty, plan.fwd_sl, &fw);
-                slab_table(geo, views, CTX, plan.cone_ty, plan.fwd_sl, plan.cone_stride, &fs);
-                // the slab-reading kernel when some slab saves work (a unit-stride
-                // walk, or a chunk that misses the detector in a view)
+                slab_table(geo, views, CTX, plan.cone_ty, plan.fwd_sl, plan.cone_stride, plan.cone_ncol > 1, &fs);
+                // the slab-reading kernel when some slab saves work (a walk of
+                // consecutive slices, or a chunk that misses the detector in a view)
                 for (const Window &w : fs) h->plan.cone_unit |= (w.m0 != 0 || w.nw == 0) ? 1 : 0;
             }
             e = hipMalloc((void **)&h->d_bwin, bw.size() * sizeof(Window));

@@ -169,6 +169,18 @@ def test_helical_radius2_plans(bp):
     assert "radius=2 taps=5" in desc, desc
 
 
+@pytest.mark.parametrize("name,inter", [("cone-256x256x256-360v", False), ("helical-512x512x96-1338v", True)])
+def test_cone_forward_profile_columns(bp, name, inter):
+    """Interleaved row-profile columns only where they save slice passes: the
+    helical scan's far pixels reach the detector with fewer than 64 slices of
+    the 128-slice chunk, which then take one pass instead of two; every chunk
+    of the 256^3 cone is active over nearly all its slices, so it keeps one
+    column (and its LDS: a second column would cost a workgroup per CU)."""
+    w = W.get(name)
+    desc = bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape)
+    assert ("interleaved row-profile columns" in desc) == inter, desc
+
+
 @pytest.mark.parametrize("name,tile", [("cone-256x256x256-360v", "8x8"), ("helical-512x512x96-1338v", "8x4")])
 def test_cone_forward_tile_choice(bp, name, tile):
     """The cone forward's tile from the planner's estimate: the 256^3 cone,
