@@ -659,10 +659,13 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         // chunk: lanes past the chunk's last slice never use the value, and
         // loads that are all unconditional let the compiler wait for the
         // current pixel's alone, not for the prefetch behind them.
+        // (through a global address-space pointer: a generic one would make
+        // these flat loads, which the LDS waits of the walk also wait for)
         auto load_px = [&](int q, float (&xv)[P]) {
-            const float *src = reinterpret_cast<const float *>(
-                ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(cyl_hi, q) << 32) |
-                (uint64_t)(uint32_t)__builtin_amdgcn_readlane(cyl_lo, q));
+            const __attribute__((address_space(1))) float *src =
+                reinterpret_cast<const __attribute__((address_space(1))) float *>(
+                    ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(cyl_hi, q) << 32) |
+                    (uint64_t)(uint32_t)__builtin_amdgcn_readlane(cyl_lo, q));
 #pragma unroll
             for (int ph = 0; ph < P; ++ph) xv[ph] = src[kkc[ph]];
         };
