@@ -38,73 +38,138 @@
 
 namespace bpamd {
 
-template <int SL, int NTAP, int NCG, int POW>
-__global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restrict__ sino,
-                                                           float *__restrict__ recon,
-                                                           const int32_t *__restrict__ rec,
-                                                           const int4 *__restrict__ wtab, Geo g, int nwcap) {
+// Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle,
+// no index stride (the loads below address bytes directly).
+constexpr int kRawDwordRsrc = 0x00020000;
+// A byte offset past the view's buffer range (one view of the sinogram, below
+// 2^31 bytes): the range check makes its load a zero.
+constexpr unsigned kOffRange = 0x80000000u;
+// s_waitcnt immediate: vmcnt(n) and lgkmcnt(0) (expcnt at its maximum), and
+// vmcnt(n) alone.
+__host__ __device__ constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+__host__ __device__ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Back projection.  Per view, the sinogram cells the tile can reach arrive in
+// two steps, two views ahead of their use, with no registers held:
+//   1. direct global-to-LDS loads copy the window's SL rows (RP = 32 or 64
+//      channels each, the sinogram's own layout; cells off the detector or
+//      past the last slice come in as zeros from the buffer range check) into
+//      one of two raw buffers, wave w taking rows [w SL/4, (w + 1) SL/4);
+//   2. each wave transposes the rows it loaded itself (its own load count is
+//      all it waits for) into the slice-fastest window the gather reads, four
+//      slices of one channel per 16-byte store.
+// One barrier per view publishes the transposed window.  The barrier is the
+// bare instruction behind compiler-only fences, with the waits written out:
+// the workgroup fence of __syncthreads would wait for every load in flight,
+// the next views' included.  The four buffers are separate LDS arrays and the
+// view loop is unrolled by two, so that every access names its buffer and the
+// compiler's own waits for the direct loads cover only the buffer they write;
+// every load of a view is issued unconditionally (clamped indices past the
+// last view), so that the wait counts are the same on every path.
+template <int SL, int NTAP, int RP, int POW>
+__global__ __launch_bounds__(BT *BT, 4) void par_back_kernel(const float *__restrict__ sino,
+                                                              float *__restrict__ recon,
+                                                              const int32_t *__restrict__ rec,
+                                                              const int4 *__restrict__ wtab, Geo g, int nwcap) {
     // LDS pitch of one channel column: a multiple of four floats, so a lane
     // reads four slices of a tap with one 16-byte read; SLP / 4 is odd, so
     // 16 lanes on consecutive channels hit 16 distinct bank groups
     constexpr int SLP = SL + 4;
-    static_assert(SL % 4 == 0 && (SLP / 4) % 2 == 1, "16-byte column reads need SL a multiple of 4");
+    static_assert(SL % 8 == 0 && (SLP / 4) % 2 == 1, "16-byte column reads need SL a multiple of 8");
+    static_assert(RP == 32 || RP == 64, "raw rows of 32 or 64 channels");
+    static_assert(RP == 32 || SL <= 32, "LDS: 64-channel windows take chunks of at most 32 slices");
     constexpr int NREC = 1 + NTAP;
-    constexpr int RPT = (SL + 7) / 8;     // staged rows per thread: 8 row groups of 32 lanes
-    extern __shared__ float lds[];        // two windows of [nwcap][SLP], slices fastest
+    constexpr int R4 = SL / 4;            // raw rows per wave
+    constexpr int RPI = 64 / RP;          // raw rows per load instruction
+    constexpr int KD = R4 / RPI;          // load instructions per wave per view
+    constexpr int G = R4 >= 4 ? 4 : 2;    // slices per transposed store
+    constexpr int NU = RP * R4 / G;       // transposed stores per wave per view
+    constexpr int UPL = (NU + 63) / 64;   // per lane
+    __shared__ float raw0[SL * RP], raw1[SL * RP];      // [SL][RP]: rows as in the sinogram
+    __shared__ float win0[RP * SLP], win1[RP * SLP];    // [nwcap <= RP][SLP]: slices fastest
 
     const int tiles_x = (g.nx + BT - 1) / BT;
     const int ntiles = tiles_x * ((g.ny + BT - 1) / BT);
     int tile, chunk;
     xcd_work_item((int)gridDim.x, (int)gridDim.y, tile, chunk);
+    tile = __builtin_amdgcn_readfirstlane(tile);
     const int tj0 = (tile % tiles_x) * BT;
     const int ti0 = (tile / tiles_x) * BT;
     const int k0 = chunk * SL;
     const int nk = min(SL, g.ns - k0);
 
-    const int i = ti0 + (int)threadIdx.x / BT;
-    const int j = tj0 + (int)threadIdx.x % BT;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i = ti0 + tid / BT;
+    const int j = tj0 + tid % BT;
     const bool valid = (i < g.ny) && (j < g.nx);
     const int np = g.ny * g.nx;
     const int p = valid ? i * g.nx + j : 0;
-    const int clane = (int)threadIdx.x & 31;       // staging: channel within a 32-wide group
-    const int rgrp = (int)threadIdx.x >> 5;        // staging: rows rgrp, rgrp + 8, ...
+    const int64_t vfl = (int64_t)g.nr * g.nc;      // floats per view (bytes below 2^31, checked by the plan)
+    const int vlast = g.nv - 1;
 
-    // the sinogram cells of one view the tile can reach, into registers
-    auto load_view = [&](int v, const int4 &w, float (&st)[NCG][RPT]) {
-        const float *base = sino + ((int64_t)v * g.nr + k0) * g.nc;
+    // the window of view v (clamped), through a wave-uniform index: a scalar load
+    auto window = [&](int v) { return wtab[(int64_t)__builtin_amdgcn_readfirstlane(min(v, vlast)) * ntiles + tile]; };
+    // step 1 for view v (clamped: past the last view the loads are issued all
+    // the same, into a buffer nothing reads again), window w, into raw buffer
+    // rb: row r of the window is slice k0 + r, lane l of an instruction
+    // channel w.x + l % RP of row l / RP
+    auto dma_view = [&](int v, const int4 &w, float *rb) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(sino + (int64_t)min(v, vlast) * vfl), (short)0, (int)(vfl * 4), kRawDwordRsrc);
+        const int c = lane % RP, n = w.x + c;
+        const bool cok = c < w.y && (unsigned)n < (unsigned)g.nc;
+        // (branch-free: a channel off the detector starts past the range; a
+        // row past the last slice is a detector row past the last one, so its
+        // offset is past the view's range anyway; the sums stay below 2^32)
+        const unsigned base = cok ? (unsigned)(k0 * g.nc + n) * 4u : kOffRange;
 #pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) {
-            const int c = clane + 32 * cg;
-            const int n = w.x + c;
-            const bool cok = c < w.y && n >= 0 && n < g.nc;
+        for (int u = 0; u < KD; ++u) {
+            const int r0 = wave * R4 + u * RPI;          // first row of this instruction
+            const int r = r0 + lane / RP;
+            const unsigned off = base + (unsigned)(r * g.nc) * 4u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(rb + r0 * RP),
+                                                     4, off, 0, 0, 0);
+        }
+    };
+    // step 2: this wave's raw rows into the window: store unit u is channel
+    // u % RP and G slices from row wave R4 + G (u / RP) (with RP = 32 the two
+    // halves of a wave read rows 4 apart, in the same banks: a two-way
+    // conflict on these few reads)
+    auto transpose = [&](const float *rb, float *wb) {
 #pragma unroll
-            for (int u = 0; u < RPT; ++u) {
-                const int r = rgrp + 8 * u;
-                st[cg][u] = (cok && r < nk) ? base[(int64_t)r * g.nc + n] : 0.f;
+        for (int e = 0; e < UPL; ++e) {
+            const int u = lane + 64 * e;
+            const int c = u % RP, r = wave * R4 + G * (u / RP);
+            if (u < NU && c < nwcap) {
+                float x[G];
+#pragma unroll
+                for (int t = 0; t < G; ++t) x[t] = rb[(r + t) * RP + c];
+                float *dst = wb + c * SLP + r;
+                if constexpr (G == 4)
+                    *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+                else
+                    *reinterpret_cast<float2 *>(dst) = make_float2(x[0], x[1]);
             }
         }
     };
-    auto store_view = [&](float *buf, const float (&st)[NCG][RPT]) {
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) {
-            const int c = clane + 32 * cg;
-            if (c < nwcap) {
-#pragma unroll
-                for (int u = 0; u < RPT; ++u) {
-                    const int r = rgrp + 8 * u;
-                    if (r < SL) buf[c * SLP + r] = st[cg][u];
-                }
-            }
-        }
-    };
+    // the tap records of view v (clamped) for this lane's pixel (pixel 0 for
+    // lanes outside the volume, whose records are never used)
     auto load_taps = [&](int v, int &nf, float (&w)[NTAP]) {
-        const int32_t *r = rec + ((int64_t)v * np + p) * NREC;
-        nf = valid ? r[0] : INT32_MAX;
+        const int32_t *r = rec + ((int64_t)min(v, vlast) * np + p) * NREC;
+        nf = r[0];
 #pragma unroll
         for (int t = 0; t < NTAP; ++t) {
-            const float wt = valid ? __int_as_float(r[1 + t]) : 0.f;
+            const float wt = __int_as_float(r[1 + t]);
             w[t] = POW == 2 ? wt * wt : wt;       // squared weights: the Hessian-diagonal back projection
         }
+    };
+    auto barrier = [&]() {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));   // this wave's LDS stores done
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
 
     float acc[SL];
@@ -112,29 +177,36 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
     for (int k = 0; k < SL; ++k) acc[k] = 0.f;
     if (g.nv == 0) return;
 
-    // double-buffered pipeline: view v + 1 is fetched while view v is gathered
-    float st[NCG][RPT];
-    int4 wcur = wtab[tile];
-    load_view(0, wcur, st);
-    store_view(lds, st);
-    int nf;
-    float w[NTAP];
-    load_taps(0, nf, w);
-    __syncthreads();
-    for (int v = 0; v < g.nv; ++v) {
-        const float *buf = lds + (v & 1) * nwcap * SLP;
-        const bool more = v + 1 < g.nv;
-        int4 wnext = wcur;
-        float nst[NCG][RPT];
-        int nnf = INT32_MAX;
-        float nw[NTAP];
-        if (more) {
-            wnext = wtab[(int64_t)(v + 1) * ntiles + tile];
-            load_view(v + 1, wnext, nst);
-            load_taps(v + 1, nnf, nw);
-        }
-        if (nf != INT32_MAX && wcur.y > 0) {
-            const float4 *col = reinterpret_cast<const float4 *>(buf + (nf - wcur.x) * SLP);
+    // prologue: views 0 and 1 loaded, view 0 transposed.  The tap records
+    // go to staging registers two views ahead (one set per view parity) and
+    // reach the working set (nf, wt) after the wait that covers them, so the
+    // gather never waits for a load
+    int4 wa = window(0), wb = window(1);
+    dma_view(0, wa, raw0);
+    dma_view(1, wb, raw1);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    int nf, nfa, nfb;
+    float wt[NTAP], wta[NTAP], wtb[NTAP];
+    load_taps(0, nf, wt);
+    load_taps(1, nfb, wtb);
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    transpose(raw0, win0);
+    barrier();
+
+    // one view: gather view v (working taps; window wv) from window buffer wc;
+    // the loads of view v + 2 go out first (into rc, the raw buffer of view v,
+    // transposed in the previous step), its tap records after the gather
+    // (into the staging set sc of view v's parity); view v + 1's rows, loaded
+    // one step earlier into rn, are transposed last, into wn, and its records
+    // (staging set sn) become the working taps
+    auto step = [&](int v, int4 &wv, int &nfc, float (&wtc)[NTAP], const int &nfn, const float (&wtn)[NTAP],
+                    float *rc, const float *wc, const float *rn, float *wn) {
+        const int4 w2 = window(v + 2);
+        dma_view(v + 2, w2, rc);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (valid && nf != INT32_MAX && wv.y > 0) {
+            const float4 *col = reinterpret_cast<const float4 *>(wc + (nf - wv.x) * SLP);
 #pragma unroll
             for (int q = 0; q < SL / 4; ++q) {
                 float4 c[NTAP];
@@ -143,10 +215,10 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
                 float s0 = acc[4 * q], s1 = acc[4 * q + 1], s2 = acc[4 * q + 2], s3 = acc[4 * q + 3];
 #pragma unroll
                 for (int t = 0; t < NTAP; ++t) {
-                    s0 = fmaf(w[t], c[t].x, s0);
-                    s1 = fmaf(w[t], c[t].y, s1);
-                    s2 = fmaf(w[t], c[t].z, s2);
-                    s3 = fmaf(w[t], c[t].w, s3);
+                    s0 = fmaf(wt[t], c[t].x, s0);
+                    s1 = fmaf(wt[t], c[t].y, s1);
+                    s2 = fmaf(wt[t], c[t].z, s2);
+                    s3 = fmaf(wt[t], c[t].w, s3);
                 }
                 acc[4 * q] = s0;
                 acc[4 * q + 1] = s1;
@@ -154,15 +226,37 @@ __global__ __launch_bounds__(BT *BT) void par_back_kernel(const float *__restric
                 acc[4 * q + 3] = s3;
             }
         }
-        if (more) {
-            store_view(lds + ((v + 1) & 1) * nwcap * SLP, nst);
-            wcur = wnext;
-            nf = nnf;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        load_taps(v + 2, nfc, wtc);
+        wv = w2;
+        // issued after this wave's loads of view v + 1: its tap records, view
+        // v + 2's KD rows and its records (the record loads are not counted,
+        // however many instructions they take: all but the last KD loads
+        // landed covers view v + 1, rows and records)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(wait_vm(KD));
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (v + 1 < g.nv) transpose(rn, wn);
+        // the working taps, redefined by an empty statement: any wait for the
+        // staged loads falls here, after the one above that covers them, and
+        // not in front of the next gather
+        nf = nfn;
+        asm volatile("" : "+v"(nf));
 #pragma unroll
-            for (int t = 0; t < NTAP; ++t) w[t] = nw[t];
+        for (int t = 0; t < NTAP; ++t) {
+            wt[t] = wtn[t];
+            asm volatile("" : "+v"(wt[t]));
         }
-        __syncthreads();
+        barrier();
+    };
+    for (int v = 0; v < g.nv; v += 2) {
+        step(v, wa, nfa, wta, nfb, wtb, raw0, win0, raw1, win1);
+        if (v + 1 >= g.nv) break;
+        step(v + 1, wb, nfb, wtb, nfa, wta, raw1, win1, raw0, win0);
     }
+    // (the loads issued for views past the last one land before the wave
+    // ends; nothing reads them)
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
     if (valid) {
         float *out = recon + (int64_t)p * g.ns + k0;
 #pragma unroll
@@ -536,12 +630,17 @@ static hipError_t par_back_t(const Plan &p, const float *sino, float *recon, hip
     const Geo &g = p.g;
     const int tiles = ((g.nx + BT - 1) / BT) * ((g.ny + BT - 1) / BT);
     const int chunks = (g.ns + SL - 1) / SL;
-    if (p.back_ncg == 1)
-        hipLaunchKernelGGL((par_back_kernel<SL, NTAP, 1, POW>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st,
+    // (LDS is static in the kernel: raw and transposed windows of 32 or 64 channels)
+    if (p.back_ncg == 1) {
+        hipLaunchKernelGGL((par_back_kernel<SL, NTAP, 32, POW>), dim3(tiles, chunks), dim3(BT * BT), 0, st,
                            sino, recon, p.rec, p.bwin, g, p.back_nwcap);
-    else
-        hipLaunchKernelGGL((par_back_kernel<SL, NTAP, 2, POW>), dim3(tiles, chunks), dim3(BT * BT), p.back_lds, st,
-                           sino, recon, p.rec, p.bwin, g, p.back_nwcap);
+    } else {
+        if constexpr (SL <= 32)
+            hipLaunchKernelGGL((par_back_kernel<SL, NTAP, 64, POW>), dim3(tiles, chunks), dim3(BT * BT), 0, st,
+                               sino, recon, p.rec, p.bwin, g, p.back_nwcap);
+        else
+            return hipErrorInvalidValue;   // the plan takes chunks of at most 32 slices for 64-channel windows
+    }
     return hipGetLastError();
 }
 

@@ -290,6 +290,10 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
     }
     if (V * Ny * Nx >= kMaxElems || Ny * Nx * S >= kMaxElems || V * R * C >= kMaxElems)
         return fail(PROJ_ERR_UNSUPPORTED, "an array or the index table would reach 2^31 elements");
+    // the back projections copy window rows out of one view of the sinogram
+    // with 32-bit byte offsets below 2^31
+    if (R * C * 4 >= ((int64_t)1 << 31))
+        return fail(PROJ_ERR_UNSUPPORTED, "one view of the sinogram is 2 GiB or more");
 
     g.kind = gp->kind;
     g.radius = gp->psf_radius;
@@ -338,7 +342,10 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
             const WinMax w = max_window(g, views, BT, BT, sl);
             plan.back_sl = sl;
             plan.back_nwcap = w.nw + 2;
-            plan.back_lds = 2 * (size_t)plan.back_nwcap * (sl + 4) * sizeof(float);   // pitch: par_back_kernel
+            // two raw windows [sl][rp] and two transposed ones [rp][sl + 4], rp =
+            // 32 or 64 channels (static arrays of par_back_kernel)
+            const size_t rp = w.nw + 2 <= 32 ? 32 : 64;
+            plan.back_lds = (2 * (size_t)sl * rp + 2 * rp * (sl + 4)) * sizeof(float);
             if (plan.back_lds <= kMaxLds || sl == 8) break;
         }
         if (plan.back_nwcap > 64)
@@ -386,10 +393,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
     } else {
         // two windows (double buffer) of [rows][channels], channels fastest with
         // an odd pitch of 33, 65, 129 or 257 floats (a compile-time constant of the
-        // kernel); the window rows are copied from one view of the sinogram
-        // with 32-bit byte offsets below 2^31
-        if ((int64_t)R * C * 4 >= ((int64_t)1 << 31))
-            return fail(PROJ_ERR_UNSUPPORTED, "cone back: one view of the sinogram is 2 GiB or more");
+        // kernel)
         auto back_bytes = [&](int sl, int &nwcap, int &nrcap, int &pc) {
             const WinMax w = max_window(g, views, BT, BT, sl);
             nwcap = w.nw + 2;
