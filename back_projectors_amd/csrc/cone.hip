@@ -111,8 +111,9 @@ __device__ __forceinline__ ConeVPB cone_vp_back(const Geo &g, const ViewK &vk, d
 // model) moves no weight while the footprint is no wider than 2R rows: every
 // tap is the overlap of one cell with the footprint.  The row taps run in fp32
 // (clamped edges by v_med3).  Two cases take the row in fp64, in the model's
-// operation order, with the taps formed as interval overlaps from fp32 pairs
-// (accurate for thin taps): a tap cell off the detector's top or bottom edge,
+// operation order, with each tap the model's own fp64 overlap of its cell with
+// the footprint (exact for thin taps): a tap cell off the detector's top or
+// bottom edge,
 // and a footprint wider than 2R rows (its outermost taps cut it, so the tap
 // row must be the model's even at an exact half).  The chord scale
 // sqrt(d^2 + a^2 + dz^2) runs in fp32, with the per-pixel factor dv / M folded
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                 const float *col = win + (v & 1) * wsz + (ncur - R - wv.n0) - (wv.m0 + 2 * R) * PC;
                 const double wrow = q.mr * g.dv;        // footprint width in rows = row advance per slice
                 const double hrowd = 0.5 * wrow;
-                const float hrow = (float)hrowd, wcap = fminf(1.f, (float)wrow);
+                const float hrow = (float)hrowd;
                 // a footprint wider than the 2R + 1 tap rows loses a sliver to the
                 // outermost taps, which one it loses depends on the tap row, so
                 // that row must be the model's own rounding even at an exact
@@ -308,27 +309,23 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                             // footprint edge on a cell boundary gives an exactly
                             // empty tap there (a voxel that only grazes the
                             // detector then adds exactly nothing).  A voxel whose
-                            // rows graze that edge in every view sums nothing but
-                            // thin edge taps, so each tap is the overlap min(1,
-                            // b_t - lo, hi - b_(t-1), hi - lo) of its cell
-                            // [b_(t-1), b_t] with the footprint [lo, hi], with lo
-                            // and hi carried as fp32 pairs: a thin tap is then an
-                            // exact difference of nearby numbers plus the low part
+                            // rows graze that edge sums nothing but thin edge
+                            // taps, so each tap is the model's own overlap of
+                            // cell m = mk + t - R with the footprint, in the
+                            // model's operations (d = m - w_k, then the clipped
+                            // interval [d - 1/2, d + 1/2] against [-W/2, W/2]):
+                            // a thin tap is then an exact difference of nearby
+                            // numbers, rounded once
                             const double dz = slice_z(g, k0v + k) - vk.zsrc;
                             const double wk = q.mr * dz + g.crow;    // product, then sum (no contraction)
                             const double mk = rint(wk);
                             ok = mk >= -R && mk <= g.nr - 1 + R;
                             hr = ok ? (int)mk + R : R;
-                            const double fd = wk - mk;
-                            const double lod = fd - hrowd, hid = fd + hrowd;
-                            const float loh = (float)lod, lol = (float)(lod - (double)loh);
-                            const float hih = (float)hid, hil = (float)(hid - (double)hih);
 #pragma unroll
                             for (int t = 0; t < NTAP; ++t) {
-                                const float bt = (float)t - (float)R + 0.5f;
-                                const float xa = (bt - loh) - lol;
-                                const float ya = (hih - (bt - 1.f)) + hil;
-                                gw[t] = __builtin_amdgcn_fmed3f(fminf(xa, ya), 0.f, wcap);
+                                const double d = (mk + (double)(t - R)) - wk;
+                                const double hi = fmin(d + 0.5, hrowd), lo = fmax(d - 0.5, -hrowd);
+                                gw[t] = hi > lo ? (float)(hi - lo) : 0.f;
                             }
                         }
                         if (ok) {
