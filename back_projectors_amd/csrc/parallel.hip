@@ -351,12 +351,17 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
     const int k0 = (slot % nch) * CS;
     const int rp = rsx * rsy;
 
+    // a pixel's CS slices in LDS; with two slices per lane, slices k and
+    // k + 16 side by side (k < 16), so that a lane's pair is one aligned
+    // 8-byte read: two rows of a wave then share banks only when their pixels
+    // have the same parity, where slices 16 apart shared them whenever that
+    // held for any two of the four rows
     for (int e = (int)threadIdx.x; e < rp * CS; e += FRW * 64) {
         const int p = e / CS, k = e % CS;
         const int i = i0 + p / rsx, j = j0 + p % rsx;
         float val = 0.f;
         if (i < g.ny && j < g.nx && k0 + k < g.ns) val = recon[(int64_t)(i * g.nx + j) * g.ns + k0 + k];
-        xr[e] = val;
+        xr[SPL == 2 ? p * CS + (k % 16) * 2 + k / 16 : e] = val;
     }
     __syncthreads();
 
@@ -407,11 +412,10 @@ __global__ __launch_bounds__(FRW * 64) void par_forward_kernel(const float *__re
             XV xq[16];
             auto read_x = [&](auto SC) {
                 constexpr int S = decltype(SC)::value;
-                const float *xs = reinterpret_cast<const float *>(xb + (row_bcast<S>(R[0]) + l4));
                 if constexpr (SPL == 2)
-                    xq[S] = make_float2(xs[0], xs[16]);
+                    xq[S] = *reinterpret_cast<const float2 *>(xb + (row_bcast<S>(R[0]) + 2u * l4));
                 else
-                    xq[S] = xs[0];
+                    xq[S] = *reinterpret_cast<const float *>(xb + (row_bcast<S>(R[0]) + l4));
             };
             static_for(read_x, std::make_integer_sequence<int, D>{});
             static_for(
