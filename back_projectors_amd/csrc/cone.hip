@@ -236,21 +236,28 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                 for (int t = 0; t < NTAP; ++t)
                     h[t] = POW == 2 ? ((float)(hd[t] * hd[t]) * (q.lsc * q.lsc)) : ((float)hd[t] * q.lsc);
                 // window cell of row offset sg, channel tap t at slice k:
-                // col[(m_k + R) PC + sg PC + t]
-                const float *col = win + (v & 1) * wsz + (ncur - R - wv.n0) - (wv.m0 + 2 * R) * PC;
+                // col[(m_k + R + 1) PC + sg PC + t]
+                const float *col = win + (v & 1) * wsz + (ncur - R - wv.n0) - (wv.m0 + 2 * R + 1) * PC;
                 const double wrow = q.mr * g.dv;        // footprint width in rows = row advance per slice
                 const double hrowd = 0.5 * wrow;
                 const float hrow = (float)hrowd;
+                // the fast row taps' offsets: tap t != R is clamp(ct[t] -+ phi,
+                // 0, 1) (below), the centre one what remains of the width wf
+                float ct[NTAP];
+#pragma unroll
+                for (int t = 0; t < NTAP; ++t)
+                    ct[t] = t < R ? hrow - (float)(R - 1 - t) : hrow - (float)(t - R);
+                const float wf = 2.f * hrow;
                 // a footprint wider than the 2R + 1 tap rows loses a sliver to the
                 // outermost taps, which one it loses depends on the tap row, so
                 // that row must be the model's own rounding even at an exact
                 // half: such pixels take the fp64 placement for every slice
                 const bool wide = wrow > 2.0 * R;
-                // slice k0 sits dz0 above the source; w + R + 1/2 in 32.32 fixed point
+                // slice k0 sits dz0 above the source; w + R + 3/2 in 32.32 fixed point
                 const double dz0 = slice_z(g, k0) - vk.zsrc;
                 // (clamped into the integer range first: a row that far off is off
                 // the detector for every slice of the chunk either way)
-                const double t0 = fmin(fmax((q.mr * dz0 + g.crow) + (0.5 + (double)R), -1e9), 1e9);
+                const double t0 = fmin(fmax((q.mr * dz0 + g.crow) + (1.5 + (double)R), -1e9), 1e9);
                 const double fl0 = floor(t0);
                 uint64_t wfx = ((uint64_t)(uint32_t)(int)fl0 << 32) | (uint64_t)(uint32_t)((t0 - fl0) * 4294967296.0);
                 const uint64_t afx = (uint64_t)(fmin(wrow, 1e6) * 4294967296.0 + 0.5);
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                 asm volatile("s_mov_b32 %0, %1" : "=s"(k0v) : "s"(k0));
 #pragma unroll
                 for (int k = 0; k < SL; ++k) {
-                    const int hk = (int)(wfx >> 32);            // m_k + R
+                    const int hk = (int)(wfx >> 32);            // m_k + R + 1
                     const uint32_t fr = (uint32_t)wfx;          // (w_k - m_k + 1/2) 2^32
                     const float dzk = dzf;
                     wfx += afx;
@@ -276,32 +283,33 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                     // the edge branch below decides those rows in fp64, as it
                     // decides every slice of a wide footprint
                     const unsigned rl1 = k < nkv ? rlim + 3u : 0u;
-                    if ((unsigned)(hk + 1) < rl1 || (wide && k < nkv)) {
+                    if ((unsigned)hk < rl1 || (wide && k < nkv)) {
                         // inside the detector, a footprint no wider than 2R
-                        // rows: cell edges sit at (j - R) - phi with phi = fr
-                        // 2^-32 = w_k - m_k + 1/2, the outermost ones (j = 0 and
-                        // 2R + 1) beyond the footprint, so their clamps are the
-                        // footprint's own edges; the 1e-7 absolute error of fp32
-                        // clamps stays far below the tolerance.  Formed for
-                        // every lane (straight-line code); the branch below
-                        // replaces it where it does not apply.
+                        // rows: with phi = fr 2^-32 = w_k - m_k + 1/2 it spans
+                        // [R + phi - W/2, R + phi + W/2] in units of the tap
+                        // cells [t, t + 1], and never leaves them, so a cell
+                        // below the centre one overlaps it by clamp(W/2 - (R -
+                        // 1 - t) - phi, 0, 1), one above by clamp(W/2 - (t - R)
+                        // + phi, 0, 1), and the centre one by what remains of
+                        // W: one fma with the clamp modifier per outer tap,
+                        // about 1e-7 absolute error, far below the tolerance.
+                        // Formed for every lane (straight-line code); the
+                        // branch below replaces it where it does not apply.
                         float gw[NTAP];
                         {
                             const float phr = (float)fr;
-                            float gp = -hrow;
+                            float mid = wf;
 #pragma unroll
                             for (int t = 0; t < NTAP; ++t) {
-                                const float gn =
-                                    t == NTAP - 1
-                                        ? hrow
-                                        : __builtin_amdgcn_fmed3f(fmaf(phr, -0x1p-32f, (float)(t + 1 - R)), -hrow, hrow);
-                                gw[t] = gn - gp;
-                                gp = gn;
+                                if (t == R) continue;
+                                gw[t] = __builtin_amdgcn_fmed3f(fmaf(phr, t < R ? -0x1p-32f : 0x1p-32f, ct[t]), 0.f, 1.f);
+                                mid -= gw[t];
                             }
+                            gw[R] = mid;
                         }
-                        int hr = hk;                            // tap centre row + R
+                        int hr = hk;                            // tap centre row + R + 1
                         bool ok = true;
-                        if (wide || ib < 0 || (unsigned)(hk - 2 * R) > (unsigned)ib) {
+                        if (wide || ib < 0 || (unsigned)(hk - (2 * R + 1)) > (unsigned)ib) {
                             // a footprint wider than the taps, or a tap cell off
                             // the top or bottom detector edge: the row is placed
                             // in fp64 in the model's operation order, so that
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
                             const double wk = q.mr * dz + g.crow;    // product, then sum (no contraction)
                             const double mk = rint(wk);
                             ok = mk >= -R && mk <= g.nr - 1 + R;
-                            hr = ok ? (int)mk + R : R;
+                            hr = ok ? (int)mk + (R + 1) : R + 1;
 #pragma unroll
                             for (int t = 0; t < NTAP; ++t) {
                                 const double d = (mk + (double)(t - R)) - wk;
