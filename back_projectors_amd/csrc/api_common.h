@@ -70,6 +70,8 @@ struct proj_handle_s {
     int32_t *d_rec = nullptr;       // parallel tap records
     uint32_t *d_wrec = nullptr;     // parallel forward walk steps
     float *d_facc = nullptr;        // parallel forward accumulation buffer (slices fastest)
+    int32_t *d_bsort = nullptr;     // parallel batch forward: sorted records, then key offsets
+    int bsort_nb = 0;               // entries per batch sort pass
     hipEvent_t fwd_done = nullptr;  // parallel: last forward on this handle, orders calls that share d_facc
     bpamd::Window *d_bwin = nullptr;       // back projection windows per (view, tile, chunk)
     bpamd::Window *d_fwin = nullptr;       // cone forward windows per (view, tile, chunk)

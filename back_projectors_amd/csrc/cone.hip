@@ -624,9 +624,11 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                         // be 1e-15 and alone in its sinogram cell); the middle
                         // one is never thin (at least min(2h, 1) minus the
                         // outer two), so the box width minus the outer two in
-                        // fp32 is accurate
-                        gf[0] = (float)fmax(hwm - f, 0.0);
-                        gf[2] = (float)fmax(hwm + f, 0.0);
+                        // fp32 is accurate.  (hwm -+ f is at most 1, so the
+                        // upper clamp never binds: the clamp to [0, 1] is the
+                        // add's own output modifier.)
+                        gf[0] = (float)fmin(fmax(hwm - f, 0.0), 1.0);
+                        gf[2] = (float)fmin(fmax(hwm + f, 0.0), 1.0);
                         gf[1] = (wboxf - gf[0]) - gf[2];
                     } else {
                         double gp = NARROW ? nhw : fmin(fmax((-0.5 - (double)R) - f, nhw), hw);

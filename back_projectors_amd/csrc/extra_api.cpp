@@ -69,8 +69,24 @@ proj_status proj_back_pixels(proj_handle h, const float *sino_dev, const int32_t
         if (e != hipSuccess) return device_fail(e, "zero fill");
         return ok();
     }
+    // a large parallel batch reads a copy of the sinogram packed into the
+    // accumulation buffer, so it is ordered like the forwards that share it
+    const bool packs = back_pixels_packs(h->plan, n);
+    bool capturing = false;
+    if (packs) {
+        e = stream_capturing(st, capturing);
+        if (e != hipSuccess) return device_fail(e, "hipStreamIsCapturing");
+        if (!capturing) {
+            e = hipStreamWaitEvent(st, h->fwd_done, 0);
+            if (e != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
+        }
+    }
     e = launch_back_pixels(h->plan, sino_dev, pixels_dev, (int)n, cyl_dev, st);
     if (e != hipSuccess) return device_fail(e, "batch back projection launch");
+    if (packs && !capturing) {
+        e = hipEventRecord(h->fwd_done, st);
+        if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+    }
     return ok();
 }
 

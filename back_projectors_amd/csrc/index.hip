@@ -8,36 +8,12 @@
 // fusing a product into a sum, and fp64 division on gfx950 is correctly
 // rounded.  With the view cosines and sines taken from the host C library,
 // n_c = rint(u) is therefore reproducible bit for bit, ties to even included.
+#include "chan.h"
 #include "launch.h"
 
 #pragma clang fp contract(off)
 
 namespace bpamd {
-
-__device__ __noinline__ double channel_coord_exact(const Geo &g, const ViewK &vk, int i, int j) {
-    const double x = pix_x(g, j);
-    const double y = pix_y(g, i);
-    if (g.kind == 0) {
-        const double xc = x * vk.c;
-        const double ys = y * vk.s;
-        const double t = xc + ys;
-        const double tq = t / g.dch;
-        const double u = tq + g.cch;
-        return u + vk.shift;
-    }
-    const double xc = x * vk.c;
-    const double ys = y * vk.s;
-    const double yc = y * vk.c;
-    const double xs = x * vk.s;
-    const double a = xc + ys;
-    const double b = yc - xs;
-    const double d = g.sid + b;
-    const double dc = d * g.dch;
-    const double mc = g.sdd / dc;
-    const double ma = mc * a;
-    const double u = ma + g.cch;
-    return u + vk.shift;
-}
 
 __global__ __launch_bounds__(256) void channel_index_kernel(Geo g, const ViewK *__restrict__ views,
                                                             int32_t *__restrict__ idx) {
@@ -54,20 +30,7 @@ __global__ __launch_bounds__(256) void channel_index_kernel(Geo g, const ViewK *
     }
 }
 
-// Overlap of the unit cell centred at e with the centred box [-a/2, a/2].
-__device__ __forceinline__ double cell_overlap(double e, double a) {
-    const double hi = fmin(e + 0.5, a / 2.0);
-    const double lo = fmax(e - 0.5, -a / 2.0);
-    const double r = hi - lo;
-    return r > 0.0 ? r : 0.0;
-}
-
-// Parallel-beam tap records, one per (view, pixel): the first channel that can
-// carry weight, n_f, and the fp32 weights of channels n_f .. n_f + NTAP - 1.
-// The weights are L ov(n - u; W) evaluated in fp64 from the exact channel
-// coordinate and rounded once, taps outside [n_c - r, n_c + r] (the PSF radius)
-// or off the detector get weight 0, and a pixel none of whose taps reaches the
-// detector is marked with n_f = INT_MAX so the projectors skip it.
+// Parallel-beam tap records, one per (view, pixel) (par_tap_record).
 __global__ __launch_bounds__(256) void par_taps_kernel(Geo g, const ViewK *__restrict__ views,
                                                        int32_t *__restrict__ rec, int ntap) {
     const int np = g.ny * g.nx;
@@ -78,25 +41,11 @@ __global__ __launch_bounds__(256) void par_taps_kernel(Geo g, const ViewK *__res
         const int p = (int)(e - (int64_t)v * np);
         const int i = p / g.nx;
         const int j = p - i * g.nx;
-        const ViewK vk = views[v];
-        const double u = channel_coord_exact(g, vk, i, j);
-        const int nc = (int)rint(u);
-        // first cell with positive overlap, kept so that all ntap taps stay
-        // inside the PSF radius [n_c - r, n_c + r]
-        int nf = (int)floor(u - 0.5 * vk.W - 0.5) + 1;
-        if (nf < nc - g.radius) nf = nc - g.radius;
-        if (nf > nc + g.radius - ntap + 1) nf = nc + g.radius - ntap + 1;
+        float w[7];
+        const int nf = par_tap_record(g, views[v], i, j, ntap, w);
         int32_t *r = rec + e * (1 + ntap);
-        bool any = false;
-        for (int t = 0; t < ntap; ++t) {
-            const int n = nf + t;
-            double w = 0.0;
-            if (n <= nc + g.radius && n >= 0 && n < g.nc) w = vk.L * cell_overlap((double)n - u, vk.W);
-            const float wf = (float)w;
-            any = any || wf != 0.f;
-            r[1 + t] = __float_as_int(wf);
-        }
-        r[0] = any ? nf : INT32_MAX;
+        for (int t = 0; t < ntap; ++t) r[1 + t] = __float_as_int(w[t]);
+        r[0] = nf;
     }
 }
 

@@ -31,6 +31,9 @@ struct Plan {
     const int4 *fwin = nullptr;     // cone forward windows [V][tiles][chunks]
     const int4 *fslab = nullptr;    // cone forward slabs [V][tiles][chunks] (first slice, passes, unit stride, 0)
     int ntap = 0;                   // parallel: taps per record
+    int32_t *bsort = nullptr;       // parallel batch forward: sorted records [V][2 + ntap][bsort_nb] (null: atomics)
+    int32_t *boff = nullptr;        // parallel batch forward: key offsets [V][fwd_cb + 1]
+    int bsort_nb = 0;               // parallel batch forward: entries per sort pass
 
     // back projection: lanes = pixels of a BT x BT tile, SL slices per lane
     int back_sl = 0;                // slices per chunk (accumulators per lane)
@@ -88,6 +91,18 @@ hipError_t par_forward_allow_lds(int ntap, int spl, size_t bytes);
 // the slice-fastest accumulation buffer -> the sinogram (parallel beam)
 hipError_t launch_par_unpack(const Plan &p, float *sino, hipStream_t st);
 // batches of voxel cylinders (entries outside [0, Ny*Nx) are inert padding)
+// Entries per pass of the parallel batch forward's sort at most (4 per thread
+// of its 1024-thread workgroup).
+constexpr int kBatchPass = 4096;
+// LDS bytes of the batch sort: a count per key (cb + 1) and the pass's sorted
+// records (2 + ntap fields of nb entries).
+inline size_t batch_sort_lds(int cb, int ntap, int nb) {
+    return ((size_t)cb + 1 + (size_t)(2 + ntap) * nb) * sizeof(int);
+}
+hipError_t batch_sort_allow_lds(int ntap, size_t bytes);
+// Whether the parallel batch back of n entries reads a slice-fastest copy of
+// the sinogram (packed into facc first) rather than the sinogram itself.
+bool back_pixels_packs(const Plan &p, int64_t n);
 hipError_t launch_back_pixels(const Plan &p, const float *sino, const int32_t *pix, int n, float *cyl,
                               hipStream_t st);
 hipError_t launch_forward_pixels(const Plan &p, const int32_t *pix, int n, const float *cyl, float *sino,

@@ -630,6 +630,31 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                 e = hipMalloc((void **)&h->d_facc, facc_bytes);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(forward accumulation buffer)");
                 rec_bytes += facc_bytes;
+                // the batch forward's sort: its LDS holds a count per key
+                // (fwd_cb + 1 of them) and a pass's sorted records; those take
+                // at most about 128 MiB in memory
+                int lds_max = 0;
+                e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, hip_device);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipDeviceGetAttribute");
+                const int64_t rs = 2 + plan.ntap;
+                int64_t nb = ((int64_t)128 << 20) / ((int64_t)geo.nv * rs * 4);
+                // (less 256 bytes: the sort's static LDS, its scan's wave sums)
+                nb = std::min<int64_t>(nb, (((int64_t)lds_max - 256) / 4 - plan.fwd_cb - 1) / rs);
+                nb = std::min<int64_t>(kBatchPass, nb / 256 * 256);
+                if (nb >= 256) {
+                    const size_t sort_bytes =
+                        ((size_t)geo.nv * rs * nb + (size_t)geo.nv * (plan.fwd_cb + 1)) * sizeof(int32_t);
+                    const size_t sort_lds = batch_sort_lds(plan.fwd_cb, plan.ntap, (int)nb);
+                    // (a device that refuses the LDS keeps the atomic batch forward)
+                    if (sort_lds <= kMaxLds || batch_sort_allow_lds(plan.ntap, sort_lds) == hipSuccess) {
+                        e = hipMalloc((void **)&h->d_bsort, sort_bytes);
+                        if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(batch sort)");
+                        h->bsort_nb = (int)nb;
+                        rec_bytes += sort_bytes;
+                    } else {
+                        (void)hipGetLastError();
+                    }
+                }
                 e = hipEventCreateWithFlags(&h->fwd_done, hipEventDisableTiming);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipEventCreateWithFlags");
             }
@@ -680,6 +705,11 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
         h->plan.rec = h->d_rec;
         h->plan.wrec = h->d_wrec;
         h->plan.facc = h->d_facc;
+        if (h->d_bsort) {
+            h->plan.bsort = h->d_bsort;
+            h->plan.boff = h->d_bsort + (int64_t)geo.nv * (2 + plan.ntap) * h->bsort_nb;
+            h->plan.bsort_nb = h->bsort_nb;
+        }
         h->plan.bwin = reinterpret_cast<const int4 *>(h->d_bwin);
         h->plan.fwin = reinterpret_cast<const int4 *>(h->d_fwin);
         h->plan.fslab = reinterpret_cast<const int4 *>(h->d_fslab);
@@ -788,6 +818,7 @@ void proj_destroy(proj_handle h) {
         if (h->d_rec) (void)hipFree(h->d_rec);
         if (h->d_wrec) (void)hipFree(h->d_wrec);
         if (h->d_facc) (void)hipFree(h->d_facc);
+        if (h->d_bsort) (void)hipFree(h->d_bsort);
         if (h->fwd_done) (void)hipEventDestroy(h->fwd_done);
         if (h->d_bwin) (void)hipFree(h->d_bwin);
         if (h->d_fwin) (void)hipFree(h->d_fwin);

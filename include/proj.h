@@ -155,11 +155,12 @@ proj_status proj_create(const proj_geometry *g, const int64_t recon_shape[3],
  * proj_forward_pixels and proj_back_pixels allocate, copy and synchronise
  * nothing and use no memset, so they can be captured into a HIP graph.  Outside
  * a capture, parallel-beam forwards on one handle (proj_forward and
- * proj_forward_pixels) are ordered on the GPU (they share the handle's
- * accumulation buffer); inside a capture that ordering is the graph's.  So two
- * captured forwards on one handle must not run concurrently, and a replayed
- * graph holding a parallel forward must be ordered by the caller against
- * every other parallel forward of the same handle on another stream (an
+ * proj_forward_pixels) and batch back projections large enough to pack the
+ * sinogram (proj_back_pixels) are ordered on the GPU (they share the handle's
+ * accumulation and sort buffers); inside a capture that ordering is the
+ * graph's.  So two such captured calls on one handle must not run
+ * concurrently, and a replayed graph holding one must be ordered by the caller
+ * against every other such call of the same handle on another stream (an
  * event after the replay, a stream wait before the next one).  The solvers
  * (proj_cgls, proj_sirt) synchronise and cannot be captured.
  */
@@ -230,7 +231,13 @@ proj_status proj_back_squared(proj_handle h, const float *sino_dev, float *recon
  *
  * Both are exact adjoints of each other on the listed pixels.  No buffer may
  * overlap another.  Asynchronous on hip_stream.  These serve batches: their
- * cost grows with n*S*V, not with the volume.
+ * cost grows with n*S*V, not with the volume, plus one pass over the sinogram
+ * (the forward writes all of it; a parallel back of a large batch first packs
+ * it slices-fastest).  A parallel forward sorts each view's entries by channel
+ * in passes of up to 4096 entries and writes every sinogram cell from one
+ * wave, without atomics; the entries of one channel are summed in the order
+ * the sort placed them, which may differ between calls (results then differ
+ * by rounding only).
  */
 proj_status proj_forward_pixels(proj_handle h, const int32_t *pixels_dev, int64_t n, const float *cyl_dev,
                                 float *sino_dev, void *hip_stream);

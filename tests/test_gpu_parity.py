@@ -697,6 +697,62 @@ def test_pixel_batch_empty_and_all_padding(bp):
         proj.close()
 
 
+PAR_BATCH = [w for w in SMALL_CASES if w.kind == W.PARALLEL]
+
+
+@pytest.mark.parametrize("w", PAR_BATCH, ids=lambda w: w.name)
+def test_pixel_batch_back_direct_and_packed_agree(bp, orc, w):
+    """The parallel batch back reads the sinogram itself for a few entries and
+    a slice-fastest copy of it for many: three listed pixels alone (the first
+    form) and the same three inside a batch of 203 (the second) give the same
+    bits, and match the reference."""
+    note(f"batch back forms {w.name}")
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    _, y = inputs(w)
+    np_ = w.ny * w.nx
+    few = np.array([0, np_ // 2 + 3, np_ - 1], np.int32)
+    big, _, _ = batch(w, 203, seed=w.seed_y)
+    at = [5, 100, 202]
+    big[at] = few
+    r_few = host(proj.back_pixels(dev(y), dev(few)))
+    r_big = host(proj.back_pixels(dev(y), dev(big)))
+    assert np.array_equal(r_few, r_big[at]), "the two batch back forms differ"
+    xo, ax = orc.back_pixels(g, y, few, with_abs=True)
+    assert_close(r_few, xo, ax, f"{w.name} back at three pixels")
+    proj.close()
+
+
+@pytest.mark.parametrize("w", [PAR_RAGGED, PAR_FINE], ids=lambda w: w.name)
+def test_pixel_batch_forward_in_passes(bp, orc, w):
+    """A parallel batch forward longer than one sort pass (4096 entries): 9000
+    entries, ids repeated many times, padding in every pass; the passes after
+    the first add to the sinogram."""
+    note(f"batch forward in passes {w.name}")
+    g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
+    proj = bp.Projector(w.geometry(), w.recon_shape, w.sino_shape)
+    rng = np.random.default_rng(w.seed_x + 5)
+    n = 9000
+    pix = rng.integers(0, w.ny * w.nx, n).astype(np.int32)
+    pad = np.array([2, 4100, 8999, 6000])
+    pix[pad] = [-1, w.ny * w.nx, 2 ** 31 - 1, -7]
+    cyl = rng.standard_normal((n, w.ns)).astype(np.float32)
+    cyl[pad] = np.nan
+    yg = host(proj.forward_pixels(dev(pix), dev(cyl)))
+    assert np.isfinite(yg).all(), "padding leaked into the forward"
+    yo, ay = orc.forward_pixels(g, pix, cyl, with_abs=True)
+    assert_close(yg, yo, ay, f"{w.name} forward of 9000 entries")
+    _, y = inputs(w)
+    xg = host(proj.back_pixels(dev(y), dev(pix)))
+    keep = np.ones(n, bool)
+    keep[pad] = False
+    lhs = float((yg.astype(np.float64) * y).sum())
+    rhs = float((cyl[keep].astype(np.float64) * xg[keep]).sum())
+    gap = abs(lhs - rhs) / (np.linalg.norm(yg) * np.linalg.norm(y))
+    assert gap < ADJOINT, f"batch adjoint gap {gap:.2e}"
+    proj.close()
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_pixel_batch_sampled(bp, orc, name, full_cache):
     """A batch of 1000 distinct pixels (plus padding) at the full sizes: the
