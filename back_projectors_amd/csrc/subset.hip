@@ -303,7 +303,7 @@ __global__ __launch_bounds__(PB_SORT_THREADS) void par_batch_sort_kernel(const i
 #pragma unroll
     for (int u = 0; u < PB_EPT; ++u) {
         if (key[u] < 0) continue;
-        lrec[pos[u]] = tid + u * PB_SORT_THREADS;
+        lrec[pos[u]] = (tid + u * PB_SORT_THREADS) * g.ns;     // the entry's cylinder offset
         lrec[nbmax + pos[u]] = key[u];
 #pragma unroll
         for (int t = 0; t < NTAP; ++t) lrec[(2 + t) * nbmax + pos[u]] = __float_as_int(wr[u][t]);
@@ -336,6 +336,7 @@ __global__ __launch_bounds__(SW * 64) void par_batch_walk_kernel(const float *__
     const int32_t *ov = off + (int64_t)v * (cb + 1);
     const int j0 = ov[ca], j1 = ov[ce + G];
     const int32_t *sv = srt + (int64_t)v * RS * nbmax;
+    const float *cb0 = cyl + (int64_t)b0 * g.ns + kc;
 
     float acc[NTAP];
 #pragma unroll
@@ -356,25 +357,32 @@ __global__ __launch_bounds__(SW * 64) void par_batch_walk_kernel(const float *__
 #pragma unroll
             for (int f = 0; f < RS; ++f) R[f] = sv[(int64_t)f * nbmax + j];
         };
-        auto load_x = [&](int e) { return cyl[(int64_t)(b0 + e) * g.ns + kc]; };
+        auto load_x = [&](int o) { return cb0[(uint32_t)o]; };
         float xq[PB_D];
         // one block of 64 entries from records R, with the next block's in N
         // (fetched meanwhile); the voxels of entry s + PB_D are loaded while
         // entry s is added
+        // (unrolled by PB_D only, so that the buffer index is fixed; the
+        // record lanes are uniform scalar indices)
         auto block = [&](int jb, int (&R)[RS], int (&N)[RS]) {
             load_recs(jb + 64, N);
 #pragma unroll
-            for (int s = 0; s < 64; ++s) {
-                const float x = xq[s % PB_D];
-                const int e2 = s + PB_D < 64 ? __builtin_amdgcn_readlane(R[0], s + PB_D)
-                                             : __builtin_amdgcn_readlane(N[0], s + PB_D - 64);
-                xq[s % PB_D] = load_x(e2);
-                if (jb + s < j1) {
-                    const int nf = __builtin_amdgcn_readlane(R[1], s) - G;
-                    while (lo < nf) finish();        // channels the walk has passed
+            for (int s0 = 0; s0 < 64; s0 += PB_D) {
+                const bool last = s0 + PB_D >= 64;
 #pragma unroll
-                    for (int t = 0; t < NTAP; ++t)
-                        acc[t] = fmaf(__int_as_float(__builtin_amdgcn_readlane(R[2 + t], s)), x, acc[t]);
+                for (int d = 0; d < PB_D; ++d) {
+                    const int s = s0 + d;
+                    const float x = xq[d];
+                    const int o2 = last ? __builtin_amdgcn_readlane(N[0], s + PB_D - 64)
+                                        : __builtin_amdgcn_readlane(R[0], s + PB_D);
+                    xq[d] = load_x(o2);
+                    if (jb + s < j1) {
+                        const int nf = __builtin_amdgcn_readlane(R[1], s) - G;
+                        while (lo < nf) finish();    // channels the walk has passed
+#pragma unroll
+                        for (int t = 0; t < NTAP; ++t)
+                            acc[t] = fmaf(__int_as_float(__builtin_amdgcn_readlane(R[2 + t], s)), x, acc[t]);
+                    }
                 }
             }
         };
@@ -392,16 +400,18 @@ __global__ __launch_bounds__(SW * 64) void par_batch_walk_kernel(const float *__
     while (lo < ce) finish();
     // the tile's rows into the sinogram: half a wave per row (lanes of a row
     // on consecutive channels); LDS operations of a wave complete in order,
-    // so the tile written above is what these reads see
+    // so the tile written above is what these reads see.  (Storing each
+    // finished channel straight into its 64 rows instead, 64 scattered
+    // 4-byte stores, took three times as long.)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const int hc = lane & 31, hr = lane >> 5;
     const bool cok = ca + hc < ce;
-    float *sv_out = sino + ((int64_t)v * g.nr + k0) * g.nc + ca + hc;
+    float *out = sino + ((int64_t)v * g.nr + k0) * g.nc + ca + hc;
     for (int r = hr; r < 64 && k0 + r < g.nr; r += 2) {
         if (cok) {
             float val = tile[r][hc];
-            if (accumulate) val += sv_out[(int64_t)r * g.nc];
-            sv_out[(int64_t)r * g.nc] = val;
+            if (accumulate) val += out[(int64_t)r * g.nc];
+            out[(int64_t)r * g.nc] = val;
         }
     }
 }
