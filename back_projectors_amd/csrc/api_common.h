@@ -13,6 +13,7 @@
 namespace bpamd {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;      // work arrays stay below 2^31 elements
+constexpr int64_t kConeBatchBufMax = (int64_t)4 << 30; // cone handles keep a transposed sinogram up to 4 GiB
 
 // Record `why` as the calling thread's last error and return `s`.
 proj_status fail(proj_status s, const std::string &why);
@@ -72,6 +73,7 @@ struct proj_handle_s {
     float *d_facc = nullptr;        // parallel forward accumulation buffer (slices fastest)
     int32_t *d_bsort = nullptr;     // parallel batch forward: sorted records, then key offsets
     int bsort_nb = 0;               // entries per batch sort pass
+    float *d_ctr = nullptr;         // cone batches: the sinogram transposed [V][C][R]
     hipEvent_t fwd_done = nullptr;  // parallel: last forward on this handle, orders calls that share d_facc
     bpamd::Window *d_bwin = nullptr;       // back projection windows per (view, tile, chunk)
     bpamd::Window *d_fwin = nullptr;       // cone forward windows per (view, tile, chunk)

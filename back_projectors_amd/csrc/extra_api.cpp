@@ -37,8 +37,11 @@ proj_status proj_forward_pixels(proj_handle h, const int32_t *pixels_dev, int64_
         if (e != hipSuccess) return device_fail(e, "zero fill");
         return ok();
     }
+    // (parallel: the accumulation and sort buffers; cone: the transposed
+    // sinogram, where the handle keeps one)
+    const bool shared = h->plan.g.kind == 0 || h->plan.ctr;
     bool capturing = false;
-    if (h->plan.g.kind == 0) {
+    if (shared) {
         e = stream_capturing(st, capturing);
         if (e != hipSuccess) return device_fail(e, "hipStreamIsCapturing");
         if (!capturing) {
@@ -48,7 +51,7 @@ proj_status proj_forward_pixels(proj_handle h, const int32_t *pixels_dev, int64_
     }
     e = launch_forward_pixels(h->plan, pixels_dev, (int)n, cyl_dev, sino_dev, st);
     if (e != hipSuccess) return device_fail(e, "batch forward projection launch");
-    if (h->plan.g.kind == 0 && !capturing) {
+    if (shared && !capturing) {
         e = hipEventRecord(h->fwd_done, st);
         if (e != hipSuccess) return device_fail(e, "hipEventRecord");
     }
@@ -69,8 +72,9 @@ proj_status proj_back_pixels(proj_handle h, const float *sino_dev, const int32_t
         if (e != hipSuccess) return device_fail(e, "zero fill");
         return ok();
     }
-    // a large parallel batch reads a copy of the sinogram packed into the
-    // accumulation buffer, so it is ordered like the forwards that share it
+    // a large batch reads a copy of the sinogram packed into the handle's
+    // accumulation buffer (parallel) or its transposed sinogram (cone), so it
+    // is ordered like the forwards that share it
     const bool packs = back_pixels_packs(h->plan, n);
     bool capturing = false;
     if (packs) {

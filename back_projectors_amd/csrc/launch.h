@@ -34,6 +34,7 @@ struct Plan {
     int32_t *bsort = nullptr;       // parallel batch forward: sorted records [V][2 + ntap][bsort_nb] (null: atomics)
     int32_t *boff = nullptr;        // parallel batch forward: key offsets [V][fwd_cb + 1]
     int bsort_nb = 0;               // parallel batch forward: entries per sort pass
+    float *ctr = nullptr;           // cone batches: the sinogram transposed, [V][C][R] (null: direct forms)
 
     // back projection: lanes = pixels of a BT x BT tile, SL slices per lane
     int back_sl = 0;                // slices per chunk (accumulators per lane)
@@ -90,6 +91,9 @@ hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hi
 hipError_t par_forward_allow_lds(int ntap, int spl, size_t bytes);
 // the slice-fastest accumulation buffer -> the sinogram (parallel beam)
 hipError_t launch_par_unpack(const Plan &p, float *sino, hipStream_t st);
+// buf [V][cb][s] (rows fastest, guard channels on each side) -> sino [V][R][C]
+hipError_t launch_unpack_rows(const float *buf, float *sino, int nv, int nr, int nc, int cb, int s, int guard,
+                              hipStream_t st);
 // batches of voxel cylinders (entries outside [0, Ny*Nx) are inert padding)
 // Entries per pass of the parallel batch forward's sort at most (4 per thread
 // of its 1024-thread workgroup).

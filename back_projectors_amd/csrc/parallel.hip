@@ -604,7 +604,8 @@ __global__ __launch_bounds__(FRW * 64) void par_gather_kernel(const float *__res
 }
 
 // facc [V][cb][s16] (slices fastest, K - 1 guard channels each side) ->
-// sino [V][R][C] (channels fastest), through a 64 x 64 LDS tile.
+// sino [V][R][C] (channels fastest), through a 64 x 64 LDS tile.  (The cone
+// batches use it too, on the sinogram transposed, with no guard channels.)
 __global__ __launch_bounds__(256) void par_unpack_kernel(const float *__restrict__ facc, float *__restrict__ sino,
                                                          int nr, int nc, int cb, int s64, int guard, int tn) {
     __shared__ float t[64][65];
@@ -734,12 +735,17 @@ hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hi
     return launch_par_unpack(p, sino, st);
 }
 
-hipError_t launch_par_unpack(const Plan &p, float *sino, hipStream_t st) {
-    const Geo &g = p.g;
-    const int tn = (g.nc + 63) / 64;
-    hipLaunchKernelGGL(par_unpack_kernel, dim3((unsigned)(g.nv * tn), (g.nr + 63) / 64), dim3(256), 0, st, p.facc,
-                       sino, g.nr, g.nc, p.fwd_cb, p.fwd_s16, p.ntap - 1, tn);
+hipError_t launch_unpack_rows(const float *buf, float *sino, int nv, int nr, int nc, int cb, int s, int guard,
+                              hipStream_t st) {
+    const int tn = (nc + 63) / 64;
+    if (nv == 0 || tn == 0 || nr == 0) return hipSuccess;
+    hipLaunchKernelGGL(par_unpack_kernel, dim3((unsigned)(nv * tn), (nr + 63) / 64), dim3(256), 0, st, buf, sino, nr,
+                       nc, cb, s, guard, tn);
     return hipGetLastError();
+}
+
+hipError_t launch_par_unpack(const Plan &p, float *sino, hipStream_t st) {
+    return launch_unpack_rows(p.facc, sino, p.g.nv, p.g.nr, p.g.nc, p.fwd_cb, p.fwd_s16, p.ntap - 1, st);
 }
 
 // The region walk holds its voxels in more LDS than the default limit.

@@ -658,6 +658,15 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                 e = hipEventCreateWithFlags(&h->fwd_done, hipEventDisableTiming);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipEventCreateWithFlags");
             }
+            if (geo.kind != 0 && h->sino_elems > 0 && h->sino_elems * 4 <= kConeBatchBufMax) {
+                // the cone batches' transposed sinogram, and the event that
+                // orders the calls sharing it
+                e = hipMalloc((void **)&h->d_ctr, (size_t)h->sino_elems * sizeof(float));
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(batch buffer)");
+                rec_bytes += (size_t)h->sino_elems * sizeof(float);
+                e = hipEventCreateWithFlags(&h->fwd_done, hipEventDisableTiming);
+                if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipEventCreateWithFlags");
+            }
             e = hipDeviceSynchronize();
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "table passes");
         }
@@ -705,6 +714,7 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
         h->plan.rec = h->d_rec;
         h->plan.wrec = h->d_wrec;
         h->plan.facc = h->d_facc;
+        h->plan.ctr = h->d_ctr;
         if (h->d_bsort) {
             h->plan.bsort = h->d_bsort;
             h->plan.boff = h->d_bsort + (int64_t)geo.nv * (2 + plan.ntap) * h->bsort_nb;
@@ -819,6 +829,7 @@ void proj_destroy(proj_handle h) {
         if (h->d_wrec) (void)hipFree(h->d_wrec);
         if (h->d_facc) (void)hipFree(h->d_facc);
         if (h->d_bsort) (void)hipFree(h->d_bsort);
+        if (h->d_ctr) (void)hipFree(h->d_ctr);
         if (h->fwd_done) (void)hipEventDestroy(h->fwd_done);
         if (h->d_bwin) (void)hipFree(h->d_bwin);
         if (h->d_fwin) (void)hipFree(h->d_fwin);

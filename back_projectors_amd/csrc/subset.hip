@@ -443,78 +443,129 @@ __global__ __launch_bounds__(256) void par_pack_kernel(const float *__restrict__
     }
 }
 
-// The cone footprint of one voxel-view: channel taps h (from the channel
-// index), the row mk and row taps gd of slice k, and the chord scale lk, with
-// the same fp64 arithmetic as the full cone projectors.
-template <int R>
-__device__ __forceinline__ bool cone_voxel(const Geo &g, const ViewK &vk, double x, double y, int ncv, int k,
-                                           float (&h)[2 * R + 1], double (&gd)[2 * R + 1], int &mk, float &lk) {
-    const double xc = x * vk.c, ys = y * vk.s, yc = y * vk.c, xs = x * vk.s;
-    const double a = xc + ys;
-    const double b = yc - xs;
-    const double d = g.sid + b;
-    const double drw = d * g.drow;
-    const double mr = g.sdd / drw;
-    const double mc = g.sdd / (d * g.dch);
-    const double f = (mc * a + g.cch + vk.shift) - (double)ncv;
-    const double mm = fmax(fabs(y + vk.c * g.sid), fabs(vk.s * g.sid - x));
-    const double wch = mc * g.dv * mm / d;
-    double hd[2 * R + 1];
-    tap_weights_d<R>(f, wch, hd);
-#pragma unroll
-    for (int t = 0; t < 2 * R + 1; ++t) h[t] = (float)hd[t];
-    const double dz = slice_z(g, k) - vk.zsrc;
-    const double t0 = mr * dz;
-    const double wk = t0 + g.crow;
-    const double mkd = rint(wk);
-    if (mkd < -R || mkd > g.nr - 1 + R) return false;
-    tap_weights_d<R>(wk - mkd, mr * g.dv, gd);
-    mk = (int)mkd;
-    lk = (float)(g.dv / mm) * sqrtf((float)(d * d + a * a + dz * dz));
-    return true;
-}
+// Cone back at the listed pixels: the footprint of each voxel-view in fp64
+// with the full projectors' formulas (channel taps from the channel index,
+// row placement product-then-sum, row taps, chord), split into its
+// per-(view, pixel) part and its per-slice part.  A workgroup takes one listed
+// pixel and 64 slices; its four waves take a quarter of the views each and
+// their partial sums are added in a fixed order.  In a wave, lane l evaluates
+// the per-(view, pixel) part for view vb + l (channel index, channel taps, row
+// magnification, d^2 + a^2 and the chord factor),
+// and the wave reads them out per view; lanes (slices) then place their row
+// and gather.  A view without a footprint, a row off the detector or a tap
+// cell off it adds an exact +0 (the sums are never -0), so the views run
+// without branches, four at a time, their loads in flight together.  With PK
+// the cells come from the sinogram transposed to [V][C][R]: the rows of one
+// channel that 64 slices reach are then one run of memory instead of one
+// cache line each.
+constexpr int CB_U = 4;                           // views per group of the cone batch back
 
-template <int R>
-__global__ __launch_bounds__(SW * 64) void cone_back_pixels_kernel(const float *__restrict__ sino,
-                                                                   const int32_t *__restrict__ pix, int n,
-                                                                   float *__restrict__ cyl,
-                                                                   const int32_t *__restrict__ idx,
-                                                                   const ViewK *__restrict__ views, Geo g) {
+template <int R, bool PK>
+__global__ __launch_bounds__(256) void cone_back_pixels_kernel(const float *__restrict__ sino,
+                                                               const int32_t *__restrict__ pix, int n,
+                                                               float *__restrict__ cyl,
+                                                               const int32_t *__restrict__ idx,
+                                                               const ViewK *__restrict__ views, Geo g) {
     constexpr int NTAP = 2 * R + 1;
+    __shared__ float part[4][64];
     const int lane = (int)threadIdx.x & 63;
-    const int i = (int)blockIdx.x * SW + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    if (i >= n) return;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int i = (int)blockIdx.x;
     const int np = g.ny * g.nx;
     const int k = (int)blockIdx.y * 64 + lane;
     const int p = listed_pixel(pix, i, np);
+    const int vper = (g.nv + 3) / 4;
+    const int vbeg = wave * vper, vend = min(g.nv, vbeg + vper);
     float acc = 0.f;
-    if (p >= 0 && k < g.ns) {
+    if (p >= 0 && vbeg < vend) {
         const double x = pix_x(g, p % g.nx), y = pix_y(g, p / g.nx);
-        for (int v = 0; v < g.nv; ++v) {
-            const int ncv = idx[(int64_t)v * np + p];
-            if (ncv < -R || ncv > g.nc - 1 + R) continue;
-            float h[NTAP], lk;
-            double gd[NTAP];
-            int mk;
-            if (!cone_voxel<R>(g, views[v], x, y, ncv, k, h, gd, mk, lk)) continue;
-            const float *sv = sino + (int64_t)v * g.nr * g.nc;
-            float s = 0.f;
+        const double zk = slice_z(g, k);
+        const int64_t vstride = (int64_t)g.nr * g.nc;
+        auto rl_d = [](double d, int q) {         // lane q's double, as a wave-uniform value
+            const long long b = __double_as_longlong(d);
+            const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), q);
+            const int hi = __builtin_amdgcn_readlane((int)(b >> 32), q);
+            return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+        };
+        auto rl_f = [](float f, int q) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), q)); };
+        for (int vb = vbeg; vb < vend; vb += 64) {
+            // lane l: the per-(view, pixel) part for view vb + l
+            const int vl = min(vb + lane, vend - 1);
+            const ViewK vk = views[vl];
+            const int ncv = idx[(int64_t)vl * np + p];
+            const bool on = vb + lane < vend && ncv >= -R && ncv <= g.nc - 1 + R;
+            const double xc = x * vk.c, ys = y * vk.s, yc = y * vk.c, xs = x * vk.s;
+            const double a = xc + ys;
+            const double b = yc - xs;
+            const double d = g.sid + b;
+            const double drw = d * g.drow;
+            const double mr = g.sdd / drw;
+            const double mc = g.sdd / (d * g.dch);
+            const double f = (mc * a + g.cch + vk.shift) - (double)ncv;
+            const double mm = fmax(fabs(y + vk.c * g.sid), fabs(vk.s * g.sid - x));
+            const double wch = mc * g.dv * mm / d;
+            double hd[NTAP];
+            tap_weights_d<R>(f, wch, hd);
+            float hl[NTAP];
 #pragma unroll
-            for (int sg = 0; sg < NTAP; ++sg) {
-                const int m = mk - R + sg;
-                if (m < 0 || m >= g.nr) continue;
-                float rv = 0.f;
+            for (int t = 0; t < NTAP; ++t) hl[t] = (float)hd[t];
+            const double mrdv = mr * g.dv;
+            const double r2 = d * d + a * a;              // the chord's (d^2 + a^2) + dz^2, summed in that order
+            const float lsc = (float)(g.dv / mm);
+            const uint64_t onm = __builtin_amdgcn_ballot_w64(on);
+            const int cnt = min(64, vend - vb);
+            for (int j0 = 0; j0 < cnt; j0 += CB_U) {
+                float sv[CB_U];
 #pragma unroll
-                for (int t = 0; t < NTAP; ++t) {
-                    const int c = ncv - R + t;
-                    if (c >= 0 && c < g.nc) rv = fmaf(h[t], sv[(int64_t)m * g.nc + c], rv);
+                for (int u = 0; u < CB_U; ++u) {
+                    const int j = min(j0 + u, cnt - 1);
+                    const bool von = j0 + u < cnt && ((onm >> j) & 1u);
+                    const int nc_j = __builtin_amdgcn_readlane(ncv, j);
+                    const double mr_j = rl_d(mr, j), mrdv_j = rl_d(mrdv, j), r2_j = rl_d(r2, j);
+                    const double zs_j = rl_d(vk.zsrc, j);
+                    const float lsc_j = rl_f(lsc, j);
+                    float h[NTAP];
+#pragma unroll
+                    for (int t = 0; t < NTAP; ++t) h[t] = rl_f(hl[t], j);
+                    // this lane's slice: its row, row taps and chord
+                    const double dz = zk - zs_j;
+                    const double t0 = mr_j * dz;
+                    const double wk = t0 + g.crow;
+                    const double mkd = rint(wk);
+                    const bool rok = von && !(mkd < -R || mkd > g.nr - 1 + R);
+                    double gd[NTAP];
+                    tap_weights_d<R>(wk - mkd, mrdv_j, gd);
+                    const int mk = rok ? (int)mkd : 0;
+                    const float lk = lsc_j * sqrtf((float)(r2_j + dz * dz));
+                    const float *svv = sino + (int64_t)(vb + j) * vstride;
+                    float s = 0.f;
+#pragma unroll
+                    for (int sg = 0; sg < NTAP; ++sg) {
+                        const int m = mk - R + sg;
+                        const bool mok = rok && m >= 0 && m < g.nr;
+                        float rv = 0.f;
+#pragma unroll
+                        for (int t = 0; t < NTAP; ++t) {
+                            const int c = nc_j - R + t;
+                            const bool in = mok && c >= 0 && c < g.nc;
+                            // (PK: the sinogram transposed, [V][C][R], so the
+                            // 64 slices' rows of one channel are adjacent)
+                            const float val = svv[in ? (PK ? (int64_t)c * g.nr + m : (int64_t)m * g.nc + c) : 0];
+                            rv = fmaf(h[t], in ? val : 0.f, rv);
+                        }
+                        s = fmaf(lk * (float)gd[sg], rv, s);
+                    }
+                    sv[u] = rok ? s : 0.f;
                 }
-                s = fmaf(lk * (float)gd[sg], rv, s);
+#pragma unroll
+                for (int u = 0; u < CB_U; ++u) acc += sv[u];
             }
-            acc += s;
         }
     }
-    if (k < g.ns) cyl[(int64_t)i * g.ns + k] = acc;
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && k < g.ns)
+        cyl[(int64_t)i * g.ns + k] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
 }
 
 // Cone forward of a batch: per view the wave first adds its slices' taps into
@@ -525,94 +576,152 @@ __global__ __launch_bounds__(SW * 64) void cone_back_pixels_kernel(const float *
 // that pass's residue (the plan's stride puts the rows of one pass on distinct
 // rows, as in the full cone forward; LDS float atomics cost tens of times
 // more).  Then it adds the band to the sinogram, one global atomic per touched
-// cell, the channels of a row adjacent (about 66 requests per view at 256^3
-// against 9 per slice when every tap is its own global atomic).  A band taller
-// than the LDS holds (magnification far above one) takes the direct form.
+// cell: with TR into the sinogram transposed to [V][C][R] (unpacked after), the
+// lanes along the rows of one channel, a few 64-byte requests per channel;
+// otherwise into the sinogram itself, the channels of a row adjacent (about 66
+// requests per view at 256^3).  A band taller than the LDS holds
+// (magnification far above one) takes the direct form.
 constexpr int CPB_CELLS = 1536;         // LDS band cells per wave (rows x taps)
 
-template <int R>
-__global__ __launch_bounds__(SW * 64) void cone_forward_pixels_kernel(const int32_t *__restrict__ pix, int n,
-                                                                      const float *__restrict__ cyl,
-                                                                      float *__restrict__ sino,
-                                                                      const int32_t *__restrict__ idx,
-                                                                      const ViewK *__restrict__ views, Geo g,
-                                                                      int stride) {
+template <int R, bool TR>
+__global__ __launch_bounds__(256) void cone_forward_pixels_kernel(const int32_t *__restrict__ pix, int n,
+                                                                  const float *__restrict__ cyl,
+                                                                  float *__restrict__ sino,
+                                                                  const int32_t *__restrict__ idx,
+                                                                  const ViewK *__restrict__ views, Geo g,
+                                                                  int stride) {
     constexpr int NTAP = 2 * R + 1;
     constexpr int PROW = CPB_CELLS / NTAP;      // band rows at most
-    __shared__ float band_all[SW * CPB_CELLS];
+    __shared__ float band_all[4 * CPB_CELLS];
     const int lane = (int)threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int i = (int)blockIdx.x * SW + wave;
-    if (i >= n) return;                             // whole waves only: no workgroup barrier below
+    const int i = (int)blockIdx.x;                  // a listed pixel per workgroup, a quarter of the views per wave
     const int np = g.ny * g.nx;
     const int k = (int)blockIdx.y * 64 + lane;
     const int p = listed_pixel(pix, i, np);
-    if (p < 0) return;                              // padding contributes nothing
+    if (p < 0) return;                              // padding contributes nothing (no workgroup barrier below)
+    const int vper = (g.nv + 3) / 4;
+    const int vbeg = wave * vper, vend = min(g.nv, vbeg + vper);
     const bool kin = k < g.ns;
     const float xv = kin ? cyl[(int64_t)i * g.ns + k] : 0.f;
     const double x = pix_x(g, p % g.nx), y = pix_y(g, p / g.nx);
+    const double zk = slice_z(g, k);
     float *band = band_all + wave * CPB_CELLS;
     for (int e = lane; e < CPB_CELLS; e += 64) band[e] = 0.f;
-    for (int v = 0; v < g.nv; ++v) {
-        const int ncv = idx[(int64_t)v * np + p];
-        if (ncv < -R || ncv > g.nc - 1 + R) continue;   // uniform
-        float h[NTAP], lk = 0.f;
-        double gd[NTAP];
-        int mk = 0;
-        const bool ok = kin && cone_voxel<R>(g, views[v], x, y, ncv, k, h, gd, mk, lk);
-        const uint64_t act = __builtin_amdgcn_ballot_w64(ok);
-        if (!act) continue;
-        const int first = (int)__builtin_ctzll(act), last = 63 - (int)__builtin_clzll(act);
-        const int lo = max(__builtin_amdgcn_readlane(mk, first) - R, 0);
-        const int hi = min(__builtin_amdgcn_readlane(mk, last) + R, g.nr - 1);
-        float *sv = sino + (int64_t)v * g.nr * g.nc;
-        if (hi - lo + 1 > PROW) {                    // uniform: the direct form
-            if (ok) {
+    auto rl_d = [](double d, int q) {             // lane q's double, as a wave-uniform value
+        const long long b = __double_as_longlong(d);
+        const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), q);
+        const int hi = __builtin_amdgcn_readlane((int)(b >> 32), q);
+        return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+    };
+    auto rl_f = [](float f, int q) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), q)); };
+    for (int vb = vbeg; vb < vend; vb += 64) {
+        // lane l: the per-(view, pixel) part of the footprint for view vb + l
+        // (the back's fp64 operations), read out by the wave per view
+        const int vl = min(vb + lane, vend - 1);
+        const ViewK vkl = views[vl];
+        const int ncl = idx[(int64_t)vl * np + p];
+        const bool onl = vb + lane < vend && ncl >= -R && ncl <= g.nc - 1 + R;
+        double mrl, mrdvl, r2l;
+        float hl[NTAP], lscl;
+        {
+            const double xc = x * vkl.c, ys = y * vkl.s, yc = y * vkl.c, xs = x * vkl.s;
+            const double a = xc + ys;
+            const double b = yc - xs;
+            const double d = g.sid + b;
+            const double drw = d * g.drow;
+            mrl = g.sdd / drw;
+            const double mc = g.sdd / (d * g.dch);
+            const double f = (mc * a + g.cch + vkl.shift) - (double)ncl;
+            const double mm = fmax(fabs(y + vkl.c * g.sid), fabs(vkl.s * g.sid - x));
+            const double wch = mc * g.dv * mm / d;
+            double hd[NTAP];
+            tap_weights_d<R>(f, wch, hd);
 #pragma unroll
-                for (int sg = 0; sg < NTAP; ++sg) {
-                    const int m = mk - R + sg;
-                    if (m < 0 || m >= g.nr) continue;
-                    const float c = lk * (float)gd[sg] * xv;
-#pragma unroll
-                    for (int t = 0; t < NTAP; ++t) {
-                        const int ch = ncv - R + t;
-                        if (ch >= 0 && ch < g.nc && h[t] != 0.f)
-                            unsafeAtomicAdd(&sv[(int64_t)m * g.nc + ch], h[t] * c);
-                    }
-                }
-            }
-            continue;
+            for (int t = 0; t < NTAP; ++t) hl[t] = (float)hd[t];
+            mrdvl = mrl * g.dv;
+            r2l = d * d + a * a;                        // the chord's (d^2 + a^2) + dz^2, summed in that order
+            lscl = (float)(g.dv / mm);
         }
-        for (int ph = 0; ph < stride; ++ph) {        // uniform
-            if (ok && lane % stride == ph) {
+        const uint64_t onm = __builtin_amdgcn_ballot_w64(onl);
+        const int cnt = min(64, vend - vb);
+        for (int j = 0; j < cnt; ++j) {
+            if (!((onm >> j) & 1u)) continue;          // uniform: no footprint in this view
+            const int v = vb + j;
+            const int ncv = __builtin_amdgcn_readlane(ncl, j);
+            float h[NTAP];
 #pragma unroll
-                for (int sg = 0; sg < NTAP; ++sg) {
-                    const int m = mk - R + sg;
-                    if (m >= lo && m <= hi) {
+            for (int t = 0; t < NTAP; ++t) h[t] = rl_f(hl[t], j);
+            // this lane's slice: its row, row taps and chord
+            const double dz = zk - rl_d(vkl.zsrc, j);
+            const double t0 = rl_d(mrl, j) * dz;
+            const double wk = t0 + g.crow;
+            const double mkd = rint(wk);
+            const bool ok = kin && !(mkd < -R || mkd > g.nr - 1 + R);
+            double gd[NTAP];
+            tap_weights_d<R>(wk - mkd, rl_d(mrdvl, j), gd);
+            const int mk = ok ? (int)mkd : 0;
+            const float lk = rl_f(lscl, j) * sqrtf((float)(rl_d(r2l, j) + dz * dz));
+            const uint64_t act = __builtin_amdgcn_ballot_w64(ok);
+            if (!act) continue;
+            const int first = (int)__builtin_ctzll(act), last = 63 - (int)__builtin_clzll(act);
+            const int lo = max(__builtin_amdgcn_readlane(mk, first) - R, 0);
+            const int hi = min(__builtin_amdgcn_readlane(mk, last) + R, g.nr - 1);
+            float *sv = sino + (int64_t)v * g.nr * g.nc;
+            if (hi - lo + 1 > PROW) {                    // uniform: the direct form
+                if (ok) {
+#pragma unroll
+                    for (int sg = 0; sg < NTAP; ++sg) {
+                        const int m = mk - R + sg;
+                        if (m < 0 || m >= g.nr) continue;
                         const float c = lk * (float)gd[sg] * xv;
-                        float *cell = band + (m - lo) * NTAP;
 #pragma unroll
-                        for (int t = 0; t < NTAP; ++t) cell[t] = fmaf(h[t], c, cell[t]);
+                        for (int t = 0; t < NTAP; ++t) {
+                            const int ch = ncv - R + t;
+                            if (ch >= 0 && ch < g.nc && h[t] != 0.f)
+                                unsafeAtomicAdd(&sv[TR ? (int64_t)ch * g.nr + m : (int64_t)m * g.nc + ch], h[t] * c);
+                        }
                     }
-                    // a lane's next row is its neighbour's (in the pass) current
-                    // one: LDS operations of a wave run in order, and the fence
-                    // keeps the compiler from moving the next round up
-                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 }
+                continue;
             }
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            for (int ph = 0; ph < stride; ++ph) {        // uniform
+                if (ok && lane % stride == ph) {
+#pragma unroll
+                    for (int sg = 0; sg < NTAP; ++sg) {
+                        const int m = mk - R + sg;
+                        if (m >= lo && m <= hi) {
+                            const float c = lk * (float)gd[sg] * xv;
+                            float *cell = band + (m - lo) * NTAP;
+#pragma unroll
+                            for (int t = 0; t < NTAP; ++t) cell[t] = fmaf(h[t], c, cell[t]);
+                        }
+                        // a lane's next row is its neighbour's (in the pass) current
+                        // one: LDS operations of a wave run in order, and the fence
+                        // keeps the compiler from moving the next round up
+                        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    }
+                }
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            }
+            // the band's adds are done (LDS operations of a wave complete in
+            // order; the fence keeps the compiler from moving the reads up)
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            const int rows = hi - lo + 1, cells = rows * NTAP;
+            for (int e = lane; e < cells; e += 64) {
+                // TR: lanes along the rows of one channel, adjacent in the
+                // transposed sinogram (a few 64-byte requests per channel instead
+                // of one per row)
+                const int mm = TR ? e % rows : e / NTAP, t = TR ? e / rows : e % NTAP;
+                float *cell = band + mm * NTAP + t;
+                const float val = *cell;
+                *cell = 0.f;
+                const int m = lo + mm, ch = ncv - R + t;
+                if (val != 0.f && ch >= 0 && ch < g.nc)
+                    unsafeAtomicAdd(&sv[TR ? (int64_t)ch * g.nr + m : (int64_t)m * g.nc + ch], val);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
-        // the band's adds are done (LDS operations of a wave complete in
-        // order; the fence keeps the compiler from moving the reads up)
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        const int cells = (hi - lo + 1) * NTAP;
-        for (int e = lane; e < cells; e += 64) {
-            const float val = band[e];
-            band[e] = 0.f;
-            const int m = lo + e / NTAP, ch = ncv - R + e % NTAP;
-            if (val != 0.f && ch >= 0 && ch < g.nc) unsafeAtomicAdd(&sv[(int64_t)m * g.nc + ch], val);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
 }
 
@@ -627,26 +736,31 @@ __global__ __launch_bounds__(SW * 64) void cone_forward_pixels_kernel(const int3
     default: return hipErrorInvalidValue;                                                                     \
     }
 
-#define BPAMD_SUBSET_R(KERN, ...)                                                                             \
+#define BPAMD_SUBSET_R2(KERN, B, ...)                                                                         \
     switch (g.radius) {                                                                                       \
-    case 1: hipLaunchKernelGGL((KERN<1>), __VA_ARGS__); break;                                                \
-    case 2: hipLaunchKernelGGL((KERN<2>), __VA_ARGS__); break;                                                \
-    case 3: hipLaunchKernelGGL((KERN<3>), __VA_ARGS__); break;                                                \
-    case 4: hipLaunchKernelGGL((KERN<4>), __VA_ARGS__); break;                                                \
+    case 1: hipLaunchKernelGGL((KERN<1, B>), __VA_ARGS__); break;                                             \
+    case 2: hipLaunchKernelGGL((KERN<2, B>), __VA_ARGS__); break;                                             \
+    case 3: hipLaunchKernelGGL((KERN<3, B>), __VA_ARGS__); break;                                             \
+    case 4: hipLaunchKernelGGL((KERN<4, B>), __VA_ARGS__); break;                                             \
     default: return hipErrorInvalidValue;                                                                     \
     }
 
 bool back_pixels_packs(const Plan &p, int64_t n) {
     const Geo &g = p.g;
-    if (g.kind != 0 || !p.facc || n <= 0 || g.ns <= 0) return false;
+    if (n <= 0 || g.ns <= 0) return false;
+    if (g.kind == 0 ? !p.facc : !p.ctr) return false;
     const double lanes = (double)std::min(64, g.ns);
-    const double taps = (double)n * ((g.ns + 63) / 64) * g.nv * p.ntap;
-    // cache lines: a tap read of 64 lanes touches one line per lane in the
-    // sinogram, and lanes * 4 / 64 (+1 unaligned) in the packed copy, which
-    // costs one read of the sinogram and one write of the copy
-    const double direct = taps * lanes;
-    const double packed = taps * (std::ceil(lanes * 4.0 / 64.0) + 1.0) +
-                          ((double)g.nv * g.nr * g.nc + (double)g.nv * p.fwd_cb * p.fwd_s16) * 4.0 / 64.0;
+    // tap columns per (listed pixel, chunk, view): the parallel record's
+    // channels; the cone's 2r + 1 channels (its 2r + 1 rows share their lines)
+    const double cols = (double)n * ((g.ns + 63) / 64) * g.nv * (g.kind == 0 ? p.ntap : 2 * g.radius + 1);
+    // cache lines: a column of 64 lanes touches one line per lane in the
+    // sinogram, and lanes * 4 / 64 (+1 unaligned, +1 more for the cone's rows
+    // beyond the slices) in the packed copy, which costs one read of the
+    // sinogram and one write of the copy
+    const double direct = cols * lanes;
+    const double copy = g.kind == 0 ? (double)g.nv * p.fwd_cb * p.fwd_s16 : (double)g.nv * g.nr * g.nc;
+    const double packed = cols * (std::ceil(lanes * 4.0 / 64.0) + (g.kind == 0 ? 1.0 : 2.0)) +
+                          ((double)g.nv * g.nr * g.nc + copy) * 4.0 / 64.0;
     return packed < direct;
 }
 
@@ -685,8 +799,17 @@ hipError_t launch_back_pixels(const Plan &p, const float *sino, const int32_t *p
         default: return hipErrorInvalidValue;
         }
     }
-    const dim3 grid((unsigned)((n + SW - 1) / SW), (unsigned)((g.ns + 63) / 64));
-    BPAMD_SUBSET_R(cone_back_pixels_kernel, grid, dim3(SW * 64), 0, st, sino, pix, n, cyl, p.idx, p.views, g)
+    const dim3 grid((unsigned)n, (unsigned)((g.ns + 63) / 64));       // a listed pixel per workgroup
+    if (back_pixels_packs(p, n)) {
+        const int tn = (g.nc + 63) / 64;
+        hipLaunchKernelGGL(par_pack_kernel, dim3((unsigned)(g.nv * tn), (unsigned)((g.nr + 63) / 64)), dim3(256), 0,
+                           st, sino, p.ctr, g.nr, g.nc, g.nc, g.nr, 0, tn);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        BPAMD_SUBSET_R2(cone_back_pixels_kernel, true, grid, dim3(256), 0, st, p.ctr, pix, n, cyl, p.idx, p.views, g)
+    } else {
+        BPAMD_SUBSET_R2(cone_back_pixels_kernel, false, grid, dim3(256), 0, st, sino, pix, n, cyl, p.idx, p.views, g)
+    }
     return hipGetLastError();
 }
 
@@ -755,11 +878,20 @@ hipError_t launch_forward_pixels(const Plan &p, const int32_t *pix, int n, const
         }
         return launch_par_unpack(p, sino, st);
     }
+    const dim3 grid((unsigned)n, (unsigned)((g.ns + 63) / 64));       // a listed pixel per workgroup
+    if (p.ctr && n > 0) {          // into the transposed sinogram, then unpacked
+        hipError_t e = launch_fill_zero(p.ctr, (int64_t)g.nv * g.nr * g.nc, st);
+        if (e != hipSuccess) return e;
+        BPAMD_SUBSET_R2(cone_forward_pixels_kernel, true, grid, dim3(256), 0, st, pix, n, cyl, p.ctr, p.idx,
+                        p.views, g, p.cone_stride)
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_unpack_rows(p.ctr, sino, g.nv, g.nr, g.nc, g.nc, g.nr, 0, st);
+    }
     hipError_t e = launch_fill_zero(sino, (int64_t)g.nv * g.nr * g.nc, st);
     if (e != hipSuccess || n == 0) return e;
-    const dim3 grid((unsigned)((n + SW - 1) / SW), (unsigned)((g.ns + 63) / 64));
-    BPAMD_SUBSET_R(cone_forward_pixels_kernel, grid, dim3(SW * 64), 0, st, pix, n, cyl, sino, p.idx, p.views, g,
-                   p.cone_stride)
+    BPAMD_SUBSET_R2(cone_forward_pixels_kernel, false, grid, dim3(256), 0, st, pix, n, cyl, sino, p.idx, p.views,
+                    g, p.cone_stride)
     return hipGetLastError();
 }
 
