@@ -155,9 +155,10 @@ proj_status proj_create(const proj_geometry *g, const int64_t recon_shape[3],
  * proj_forward_pixels and proj_back_pixels allocate, copy and synchronise
  * nothing and use no memset, so they can be captured into a HIP graph.  Outside
  * a capture, parallel-beam forwards on one handle (proj_forward and
- * proj_forward_pixels) and batch back projections large enough to pack the
- * sinogram (proj_back_pixels) are ordered on the GPU (they share the handle's
- * accumulation and sort buffers); inside a capture that ordering is the
+ * proj_forward_pixels), cone-beam batch forwards (proj_forward_pixels) and
+ * batch back projections large enough to pack the sinogram (proj_back_pixels)
+ * are ordered on the GPU (they share the handle's accumulation, sort or
+ * transposed-sinogram buffer); inside a capture that ordering is the
  * graph's.  So two such captured calls on one handle must not run
  * concurrently, and a replayed graph holding one must be ordered by the caller
  * against every other such call of the same handle on another stream (an
@@ -232,8 +233,10 @@ proj_status proj_back_squared(proj_handle h, const float *sino_dev, float *recon
  * Both are exact adjoints of each other on the listed pixels.  No buffer may
  * overlap another.  Asynchronous on hip_stream.  These serve batches: their
  * cost grows with n*S*V, not with the volume, plus one pass over the sinogram
- * (the forward writes all of it; a parallel back of a large batch first packs
- * it slices-fastest).  A parallel forward sorts each view's entries by channel
+ * (the forward writes all of it; a back of a large batch first packs it into
+ * a layout with its columns contiguous).  A cone-beam handle keeps a
+ * transposed copy of the sinogram's size for this (at most 4 GiB; beyond that
+ * the batches read and add the sinogram in place).  A parallel forward sorts each view's entries by channel
  * in passes of up to 4096 entries and writes every sinogram cell from one
  * wave, without atomics; the entries of one channel are summed in the order
  * the sort placed them, which may differ between calls (results then differ
