@@ -74,6 +74,7 @@ struct proj_handle_s {
     int32_t *d_bsort = nullptr;     // parallel batch forward: sorted records, then key offsets
     int bsort_nb = 0;               // entries per batch sort pass
     float *d_ctr = nullptr;         // cone batches: the sinogram transposed [V][C][R]
+    float *d_col = nullptr;         // column forward (translation scans): column sums [Nx][S]
     hipEvent_t fwd_done = nullptr;  // parallel: last forward on this handle, orders calls that share d_facc
     bpamd::Window *d_bwin = nullptr;       // back projection windows per (view, tile, chunk)
     bpamd::Window *d_fwin = nullptr;       // cone forward windows per (view, tile, chunk)

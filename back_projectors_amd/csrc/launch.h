@@ -35,6 +35,8 @@ struct Plan {
     int32_t *boff = nullptr;        // parallel batch forward: key offsets [V][fwd_cb + 1]
     int bsort_nb = 0;               // parallel batch forward: entries per sort pass
     float *ctr = nullptr;           // cone batches: the sinogram transposed, [V][C][R] (null: direct forms)
+    int colmode = 0;                // parallel, every view at angle 0 (sin exactly 0): the column forms
+    float *col = nullptr;           // column forward: the column sums [Nx][S]
 
     // back projection: lanes = pixels of a BT x BT tile, SL slices per lane
     int back_sl = 0;                // slices per chunk (accumulators per lane)
@@ -56,6 +58,9 @@ struct Plan {
     int cone_ncol = 1;              // cone forward: row-profile columns per wave (1, or cone_stride: interleaved slabs)
 };
 
+// Plan::fwd_strategy of the column forward (the public forward_strategy value
+// that asks for it).
+constexpr int kForwardColumn = 5;
 constexpr int BT = 16;   // back tile edge (pixels), 256 threads
 constexpr int FRW = 16;  // parallel forward waves per workgroup (four views each at a time)
 constexpr int FRS = 48;  // parallel forward region edge (pixels): 48 * 48 voxels of 16 slices = 144 KiB of LDS

@@ -54,7 +54,11 @@ extern "C" proj_status proj_forward_noalloc(proj_handle h, const float *recon_de
     const Plan &plan = h->plan;
     const bool par = plan.g.kind == 0;
     const bool work = plan.back_sl != 0;      // 0: empty volume or no views, the sinogram is zero
-    const int64_t need = par && work ? (int64_t)plan.g.nv * plan.fwd_cb * plan.fwd_s16 * (int64_t)sizeof(float) : 0;
+    // (the column forward of a translation scan needs only its column sums)
+    const bool colf = par && plan.fwd_strategy == kForwardColumn;
+    const int64_t need = !(par && work) ? 0
+                         : colf         ? (int64_t)plan.g.nx * plan.g.ns * (int64_t)sizeof(float)
+                                        : (int64_t)plan.g.nv * plan.fwd_cb * plan.fwd_s16 * (int64_t)sizeof(float);
     if (need > kNoallocScratchBytes)
         return fail(PROJ_ERR_UNSUPPORTED, "the forward needs " + std::to_string(need) +
                                               " bytes of accumulation buffer, more than the fixed 144 MiB "
@@ -79,10 +83,12 @@ extern "C" proj_status proj_forward_noalloc(proj_handle h, const float *recon_de
         if (e != hipSuccess) return device_fail(e, "forward projection launch");
         return ok();
     }
-    // the walk, its zero fill and the unpack use the fixed array in place of
-    // the handle's buffer (the fill clears what the last call left there)
+    // the walk, its zero fill and the unpack (or the column sums) use the
+    // fixed array in place of the handle's buffer (the fill clears what the
+    // last call left there; the column sums overwrite it)
     Plan p = plan;
     p.facc = ptr;
+    p.col = ptr;
     e = launch_par_forward(p, recon_dev, sino_dev, st);
     if (e != hipSuccess) return device_fail(e, "forward projection launch");
     return ok();

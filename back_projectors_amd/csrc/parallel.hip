@@ -603,6 +603,151 @@ __global__ __launch_bounds__(FRW * 64) void par_gather_kernel(const float *__res
     // every segment's last step flushes all accumulators (the records say so)
 }
 
+// Translation scans (every view at angle 0, the detector shifted per view):
+// the channel coordinate of a pixel centre, (x cos + y sin) / dch + ... with
+// sin = 0 exactly, does not depend on the pixel's row, so every pixel of a
+// column j has the same tap record in every view (the creation pass's records
+// of row 0 serve for all rows, bit for bit).  The operator then factors
+// through the column sums: sino[v][k][n] = sum over j of w_{n - nf(v,j)}(v, j)
+// times the sum over rows i of x[i][j][k], and the back projection is one
+// value per (column, slice), the same in every row.
+
+// cs[j][k] = sum over rows i of x[i][j][k]: a workgroup takes 64 consecutive
+// (column, slice) cells, each wave a quarter of the rows (16 rows' loads in
+// flight), and adds the four partial sums in a fixed order.
+__global__ __launch_bounds__(256) void par_colsum_kernel(const float *__restrict__ x, float *__restrict__ cs, int ny,
+                                                         int tot) {
+    __shared__ float part[4][64];
+    const int lane = (int)threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int e = (int)blockIdx.x * 64 + lane;            // j * S + k
+    const float *px = x + min(e, tot - 1);
+    const int rper = (ny + 3) / 4, r0 = wave * rper, r1 = min(ny, r0 + rper);
+    float s = 0.f;
+    int i = r0;
+    for (; i + 16 <= r1; i += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = px[(int64_t)(i + u) * tot];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += v[u];
+    }
+    for (; i < r1; ++i) s += px[(int64_t)i * tot];
+    part[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && e < tot) cs[e] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+}
+
+// The forward from the column sums: a wave owns view v, a block of 64
+// channels and a chunk of 64 slices, and adds into an LDS tile [channel][slice]
+// every column whose taps reach the block (columns in order; the records of 64
+// columns per vector load, read out by readlane; the column sums of eight
+// columns loaded together), then stores the tile as sinogram rows.  Each lane
+// adds only into its own slice of the tile.
+template <int NTAP, int POW>
+__global__ __launch_bounds__(64) void par_colfwd_kernel(const float *__restrict__ cs, const int32_t *__restrict__ rec,
+                                                        float *__restrict__ sino, Geo g, int nblk, int nchk) {
+    __shared__ float tile[64][65];
+    const int lane = (int)threadIdx.x;
+    const int item = (int)blockIdx.x;
+    const int chunk = item % nchk, blk = (item / nchk) % nblk, v = item / (nchk * nblk);
+    const int n0 = blk * 64, k0 = chunk * 64;
+    const int kc = min(k0 + lane, g.ns - 1);               // lanes past the last slice add, but store nothing
+    const int np = g.ny * g.nx;
+    const int32_t *rv = rec + (int64_t)v * np * (1 + NTAP);   // row 0 of view v
+#pragma unroll 8
+    for (int c = 0; c < 64; ++c) tile[c][lane] = 0.f;
+    for (int j0 = 0; j0 < g.nx; j0 += 64) {
+        const int32_t *r = rv + (int64_t)min(j0 + lane, g.nx - 1) * (1 + NTAP);
+        const int rnf = r[0];
+        int rw[NTAP];
+#pragma unroll
+        for (int t = 0; t < NTAP; ++t) rw[t] = r[1 + t];
+        // the columns of this group whose taps reach the block, in order,
+        // eight at a time: their column sums are loaded together, then added
+        uint64_t m = __builtin_amdgcn_ballot_w64(j0 + lane < g.nx && rnf != INT32_MAX && rnf <= n0 + 63 &&
+                                                 rnf + NTAP - 1 >= n0);
+        while (m) {
+            int js[8];
+            float xs[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                js[u] = m ? (int)__builtin_ctzll(m) : -1;
+                m &= m - 1;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) xs[u] = cs[(int64_t)(j0 + max(js[u], 0)) * g.ns + kc];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (js[u] < 0) break;                 // uniform
+                const int nf = __builtin_amdgcn_readlane(rnf, js[u]);
+#pragma unroll
+                for (int t = 0; t < NTAP; ++t) {
+                    const int c = nf + t - n0;
+                    float w = __int_as_float(__builtin_amdgcn_readlane(rw[t], js[u]));
+                    if (POW == 2) w = w * w;
+                    if (c >= 0 && c < 64) tile[c][lane] = fmaf(w, xs[u], tile[c][lane]);
+                }
+            }
+        }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);    // (LDS operations of a wave complete in order)
+    const int n = n0 + lane;
+    if (n < g.nc)
+        for (int r = 0; r < 64 && k0 + r < g.nr; ++r) sino[((int64_t)v * g.nr + k0 + r) * g.nc + n] = tile[lane][r];
+}
+
+// The back of a translation scan: lane e of the grid is the (column, slice)
+// cell j * S + k; it sums over views, taps in order, exactly as the back
+// kernel does for any pixel of column j (the same bits), eight views' loads
+// in flight, then stores the value into every row, the cells of a wave
+// contiguous in each.
+template <int NTAP, int POW>
+__global__ __launch_bounds__(64) void par_colback_kernel(const float *__restrict__ sino,
+                                                         const int32_t *__restrict__ rec, float *__restrict__ recon,
+                                                         Geo g) {
+    constexpr int U = 8;
+    const int tot = g.nx * g.ns;
+    const int e = (int)blockIdx.x * 64 + (int)threadIdx.x;
+    const int ec = min(e, tot - 1);
+    const int j = ec / g.ns, k = ec - j * g.ns;
+    const int np = g.ny * g.nx;
+    float acc = 0.f;
+    for (int v0 = 0; v0 < g.nv; v0 += U) {
+        int nf[U];
+        float w[U][NTAP], y[U][NTAP];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = min(v0 + u, g.nv - 1);
+            const int32_t *r = rec + ((int64_t)v * np + j) * (1 + NTAP);
+            nf[u] = v0 + u < g.nv ? r[0] : INT32_MAX;
+#pragma unroll
+            for (int t = 0; t < NTAP; ++t) {
+                const float wt = __int_as_float(r[1 + t]);
+                w[u][t] = POW == 2 ? wt * wt : wt;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float *row = sino + ((int64_t)min(v0 + u, g.nv - 1) * g.nr + k) * g.nc;
+#pragma unroll
+            for (int t = 0; t < NTAP; ++t) {
+                const int c = nf[u] + t;
+                const bool in = nf[u] != INT32_MAX && c >= 0 && c < g.nc;
+                const float val = row[in ? c : 0];
+                y[u][t] = in ? val : 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (nf[u] != INT32_MAX)                  // a view without a footprint here is left out, as in the back
+#pragma unroll
+                for (int t = 0; t < NTAP; ++t) acc = fmaf(w[u][t], y[u][t], acc);
+    }
+    if (e < tot)
+        for (int i = 0; i < g.ny; ++i) recon[(int64_t)i * tot + e] = acc;
+}
+
 // facc [V][cb][s16] (slices fastest, K - 1 guard channels each side) ->
 // sino [V][R][C] (channels fastest), through a 64 x 64 LDS tile.  (The cone
 // batches use it too, on the sinogram transposed, with no guard channels.)
@@ -690,8 +835,47 @@ static hipError_t par_back_pow(const Plan &p, const float *sino, float *recon, h
     }
 }
 
+template <int POW>
+static hipError_t par_colback_pow(const Plan &p, const float *sino, float *recon, hipStream_t st) {
+    const Geo &g = p.g;
+    const int64_t tot = (int64_t)g.nx * g.ns;
+    const dim3 grid((unsigned)((tot + 63) / 64));
+    switch (p.ntap) {
+    case 2: hipLaunchKernelGGL((par_colback_kernel<2, POW>), grid, dim3(64), 0, st, sino, p.rec, recon, g); break;
+    case 3: hipLaunchKernelGGL((par_colback_kernel<3, POW>), grid, dim3(64), 0, st, sino, p.rec, recon, g); break;
+    case 4: hipLaunchKernelGGL((par_colback_kernel<4, POW>), grid, dim3(64), 0, st, sino, p.rec, recon, g); break;
+    case 5: hipLaunchKernelGGL((par_colback_kernel<5, POW>), grid, dim3(64), 0, st, sino, p.rec, recon, g); break;
+    case 6: hipLaunchKernelGGL((par_colback_kernel<6, POW>), grid, dim3(64), 0, st, sino, p.rec, recon, g); break;
+    case 7: hipLaunchKernelGGL((par_colback_kernel<7, POW>), grid, dim3(64), 0, st, sino, p.rec, recon, g); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_par_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st) {
+    if (p.colmode) return power == 2 ? par_colback_pow<2>(p, sino, recon, st) : par_colback_pow<1>(p, sino, recon, st);
     return power == 2 ? par_back_pow<2>(p, sino, recon, st) : par_back_pow<1>(p, sino, recon, st);
+}
+
+// The forward of a translation scan: column sums, then the channel gather.
+static hipError_t par_colfwd(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+    const Geo &g = p.g;
+    const int tot = g.nx * g.ns;
+    hipLaunchKernelGGL(par_colsum_kernel, dim3((unsigned)((tot + 63) / 64)), dim3(256), 0, st, recon, p.col, g.ny, tot);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nblk = (g.nc + 63) / 64, nchk = (g.ns + 63) / 64;
+    const dim3 grid((unsigned)((int64_t)g.nv * nblk * nchk));
+    switch (p.ntap) {
+    case 2: hipLaunchKernelGGL((par_colfwd_kernel<2, 1>), grid, dim3(64), 0, st, p.col, p.rec, sino, g, nblk, nchk); break;
+    case 3: hipLaunchKernelGGL((par_colfwd_kernel<3, 1>), grid, dim3(64), 0, st, p.col, p.rec, sino, g, nblk, nchk); break;
+    case 4: hipLaunchKernelGGL((par_colfwd_kernel<4, 1>), grid, dim3(64), 0, st, p.col, p.rec, sino, g, nblk, nchk); break;
+    case 5: hipLaunchKernelGGL((par_colfwd_kernel<5, 1>), grid, dim3(64), 0, st, p.col, p.rec, sino, g, nblk, nchk); break;
+    case 6: hipLaunchKernelGGL((par_colfwd_kernel<6, 1>), grid, dim3(64), 0, st, p.col, p.rec, sino, g, nblk, nchk); break;
+    case 7: hipLaunchKernelGGL((par_colfwd_kernel<7, 1>), grid, dim3(64), 0, st, p.col, p.rec, sino, g, nblk, nchk); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <int K>
@@ -708,6 +892,7 @@ static hipError_t par_gather_t(const Plan &p, const float *recon, hipStream_t st
 // unpack writes in full, so the sinogram needs no fill of its own).
 hipError_t launch_par_forward(const Plan &p, const float *recon, float *sino, hipStream_t st) {
     const Geo &g = p.g;
+    if (p.fwd_strategy == kForwardColumn) return par_colfwd(p, recon, sino, st);
     hipError_t e = launch_fill_zero(p.facc, (int64_t)g.nv * p.fwd_cb * p.fwd_s16, st);
     if (e != hipSuccess) return e;
     if (p.fwd_strategy == 2) {

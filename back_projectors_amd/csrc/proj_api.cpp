@@ -271,8 +271,11 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         return fail(PROJ_ERR_INVALID_ARGUMENT, "non-finite detector offset");
     if (gp->psf_radius < 1 || gp->psf_radius > 4)
         return fail(PROJ_ERR_INVALID_ARGUMENT, "psf_radius must be in [1, 4]");
-    if (gp->kind == PROJ_PARALLEL && (gp->forward_strategy < PROJ_FORWARD_AUTO || gp->forward_strategy > PROJ_FORWARD_GATHER))
-        return fail(PROJ_ERR_INVALID_ARGUMENT, "parallel forward_strategy must be PROJ_FORWARD_AUTO, _TILE or _GATHER");
+    if (gp->kind == PROJ_PARALLEL && gp->forward_strategy != PROJ_FORWARD_AUTO &&
+        gp->forward_strategy != PROJ_FORWARD_TILE && gp->forward_strategy != PROJ_FORWARD_GATHER &&
+        gp->forward_strategy != PROJ_FORWARD_COLUMN)
+        return fail(PROJ_ERR_INVALID_ARGUMENT,
+                    "parallel forward_strategy must be PROJ_FORWARD_AUTO, _TILE, _GATHER or _COLUMN");
     if (gp->kind != PROJ_PARALLEL && gp->forward_strategy != PROJ_FORWARD_AUTO &&
         gp->forward_strategy != PROJ_FORWARD_CONE_TILE_8X4 && gp->forward_strategy != PROJ_FORWARD_CONE_TILE_8X8)
         return fail(PROJ_ERR_INVALID_ARGUMENT, "cone forward_strategy must be PROJ_FORWARD_AUTO, _CONE_TILE_8X4 or _8X8");
@@ -379,7 +382,15 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         plan.gat_nseg = (plan.gat_ng + plan.gat_segg - 1) / plan.gat_segg;
         const bool gather_ok = Ny * Nx * S * 4 < ((int64_t)1 << 32) &&
                                64 * (int64_t)(plan.fwd_cb + 2 * plan.ntap) * plan.fwd_s16 * 4 < ((int64_t)1 << 31);
-        plan.fwd_strategy = gp->forward_strategy == PROJ_FORWARD_AUTO ? choose_forward(g, plan) : gp->forward_strategy;
+        // every view at angle 0 exactly (sine 0): a pixel's channel does not
+        // depend on its row, and the column forms apply (translation scans)
+        plan.colmode = V > 0 && Ny * Nx > 0 && S > 0;
+        for (const ViewK &vk : views) plan.colmode = plan.colmode && vk.s == 0.0;
+        if (gp->forward_strategy == PROJ_FORWARD_COLUMN && !plan.colmode)
+            return fail(PROJ_ERR_UNSUPPORTED, "column forward: needs every view angle at 0 (sine exactly 0)");
+        plan.fwd_strategy = gp->forward_strategy == PROJ_FORWARD_AUTO
+                                ? (plan.colmode ? PROJ_FORWARD_COLUMN : choose_forward(g, plan))
+                                : gp->forward_strategy;
         if (plan.fwd_strategy == PROJ_FORWARD_GATHER && !gather_ok) {
             if (gp->forward_strategy == PROJ_FORWARD_GATHER)
                 return fail(PROJ_ERR_UNSUPPORTED, "gather forward: volume or detector too large for its 32-bit offsets");
@@ -389,7 +400,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         plan.fwd_nbin = max_window(g, views, plan.rsx, plan.rsy, 64).nw + 2;
         if (plan.fwd_strategy == PROJ_FORWARD_TILE && plan.fwd_nbin > 8192)
             return fail(PROJ_ERR_UNSUPPORTED, "a forward region spans more than 8190 channels");
-        if (plan.fwd_strategy == PROJ_FORWARD_GATHER) plan.fwd_lds = 0;
+        if (plan.fwd_strategy == PROJ_FORWARD_GATHER || plan.fwd_strategy == PROJ_FORWARD_COLUMN) plan.fwd_lds = 0;
     } else {
         // two windows (double buffer) of [rows][channels], channels fastest with
         // an odd pitch of 33, 65, 129 or 257 floats (a compile-time constant of the
@@ -486,12 +497,16 @@ int describe(const Plan &p, int64_t table_bytes, char *buf, int len) {
     const bool par = g.kind == 0;
     return std::snprintf(
         buf, (size_t)std::max(len, 0),
-        "kind=%s V=%d R=%d C=%d Ny=%d Nx=%d S=%d radius=%d taps=%d | back: %dx%d px tile, lanes=pixels, %d "
-        "slices/lane, window %d ch x %d rows, %zu B LDS | forward: %dx%d px tile, %s, %d slices, window %d ch x %d "
+        "kind=%s V=%d R=%d C=%d Ny=%d Nx=%d S=%d radius=%d taps=%d | back: %s%dx%d px tile, lanes=pixels, %d "
+        "slices/lane, window %d ch x %d rows, %zu B LDS%s | forward: %dx%d px tile, %s, %d slices, window %d ch x %d "
         "rows, %zu B LDS, %d view ranges | tables and buffers %lld B",
         par ? "parallel" : "cone_flat", g.nv, g.nr, g.nc, g.ny, g.nx, g.ns, g.radius, par ? p.ntap : 2 * g.radius + 1,
-        BT, BT, p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, par ? p.rsx : CTX, par ? p.rsy : p.cone_ty,
-        par ? (p.fwd_strategy == PROJ_FORWARD_GATHER
+        p.colmode ? "column: one value per (column, slice) over the views, written to every row (else " : "", BT, BT,
+        p.back_sl, p.back_nwcap, par ? p.back_sl : p.back_nrcap, p.back_lds, p.colmode ? ")" : "",
+        par ? p.rsx : CTX, par ? p.rsy : p.cone_ty,
+        par ? (p.fwd_strategy == PROJ_FORWARD_COLUMN
+                   ? "column: every view at angle 0, column sums over rows, then per view a channel gather of the columns"
+               : p.fwd_strategy == PROJ_FORWARD_GATHER
                    ? "gather: per-view sorted walk of all pixels, lanes=16 slices x 4 views, voxels from memory"
                    : (p.fwd_spl == 2 ? "tile: channel-ordered region walk, lanes=16 x 4 views with 2 slices each, ring accumulators"
                                      : "tile: channel-ordered region walk, lanes=16 slices x 4 views, ring accumulators"))
@@ -582,7 +597,13 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(tap records)");
                 e = launch_par_taps(geo, h->d_views, h->d_rec, plan.ntap, nullptr);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "tap record pass");
-                if (plan.fwd_strategy == PROJ_FORWARD_GATHER) {
+                if (plan.fwd_strategy == PROJ_FORWARD_COLUMN) {
+                    // the column sums (the records of row 0 serve for every row)
+                    const size_t col_bytes = (size_t)geo.nx * geo.ns * sizeof(float);
+                    e = hipMalloc((void **)&h->d_col, col_bytes);
+                    if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipMalloc(column sums)");
+                    rec_bytes += col_bytes;
+                } else if (plan.fwd_strategy == PROJ_FORWARD_GATHER) {
                     const int64_t per_view = (int64_t)plan.gat_ng * (2 + plan.ntap) * 16;
                     const size_t wrec_bytes = (size_t)(geo.nv + 1) * per_view * sizeof(uint32_t);
                     e = hipMalloc((void **)&h->d_wrec, wrec_bytes);
@@ -715,6 +736,7 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
         h->plan.wrec = h->d_wrec;
         h->plan.facc = h->d_facc;
         h->plan.ctr = h->d_ctr;
+        h->plan.col = h->d_col;
         if (h->d_bsort) {
             h->plan.bsort = h->d_bsort;
             h->plan.boff = h->d_bsort + (int64_t)geo.nv * (2 + plan.ntap) * h->bsort_nb;
@@ -830,6 +852,7 @@ void proj_destroy(proj_handle h) {
         if (h->d_facc) (void)hipFree(h->d_facc);
         if (h->d_bsort) (void)hipFree(h->d_bsort);
         if (h->d_ctr) (void)hipFree(h->d_ctr);
+        if (h->d_col) (void)hipFree(h->d_col);
         if (h->fwd_done) (void)hipEventDestroy(h->fwd_done);
         if (h->d_bwin) (void)hipFree(h->d_bwin);
         if (h->d_fwin) (void)hipFree(h->d_fwin);

@@ -96,7 +96,8 @@ typedef struct {
     double det_row_offset;       /* detector centre offset, rows (usually 0) */
     int32_t psf_radius;          /* taps on each side of the centre channel (and row), 1..4 */
     int32_t forward_strategy;    /* PROJ_FORWARD_AUTO (0): chosen from the shapes; parallel beam:
-                                    PROJ_FORWARD_TILE (1) or PROJ_FORWARD_GATHER (2); cone beam:
+                                    PROJ_FORWARD_TILE (1), PROJ_FORWARD_GATHER (2) or
+                                    PROJ_FORWARD_COLUMN (5); cone beam:
                                     PROJ_FORWARD_CONE_TILE_8X4 (3) or _8X8 (4) */
 } proj_geometry;
 
@@ -109,8 +110,16 @@ typedef struct {
  *             each finished channel is added once per (view, region).
  *   GATHER -- per view every pixel, sorted by channel at creation; walks read
  *             the voxels from memory, each channel is added about once per view.
- * AUTO takes the choice from the shapes alone; both give the same sinogram up
- * to the order of fp32 additions.
+ *   COLUMN -- only where every view angle has a sine of exactly 0 (a
+ *             translation scan at angle 0): a pixel's channel coordinate then
+ *             does not depend on its row, so each column of the volume is
+ *             summed over its rows once and each view adds the column sums
+ *             through the columns' taps.  (The back projection of such a scan
+ *             likewise computes one value per column and slice and writes it
+ *             to every row, whatever the forward strategy; it gives the same
+ *             bits as the general back projection.)
+ * AUTO takes the choice from the shapes alone (COLUMN wherever it applies);
+ * all give the same sinogram up to the order of fp32 additions.
  * Cone-beam forward tiles: a workgroup holds 8 x 4 or 8 x 8 pixels and adds
  * a detector window per view to the sinogram with one global atomic per
  * cell; larger tiles flush fewer cells per voxel, smaller ones skip more
@@ -123,7 +132,8 @@ enum {
     PROJ_FORWARD_TILE = 1,
     PROJ_FORWARD_GATHER = 2,
     PROJ_FORWARD_CONE_TILE_8X4 = 3,
-    PROJ_FORWARD_CONE_TILE_8X8 = 4
+    PROJ_FORWARD_CONE_TILE_8X8 = 4,
+    PROJ_FORWARD_COLUMN = 5
 };
 
 /*

@@ -77,6 +77,10 @@ CONE = dict(kind=1, source_iso=100.0, source_detector=150.0, delta_channel=1.5, 
 
 BAD = [
     ("kind", base_geo(kind=3), (8, 8, 4), (4, 4, 16), -1),
+    ("column forward on a rotating scan", base_geo(forward_strategy=5), (8, 8, 4), (4, 4, 16), -2),
+    ("column forward with one view off 0", base_geo(angles=np.array([0.0, 0.0, 1e-300, 0.0]), forward_strategy=5),
+     (8, 8, 4), (4, 4, 16), -2),
+    ("column forward on a cone", dict(base_geo(forward_strategy=5), **CONE), (8, 8, 4), (4, 4, 16), -1),
     ("views mismatch", base_geo(num_views=5, angles=np.zeros(5)), (8, 8, 4), (4, 4, 16), -1),
     ("nan angle", base_geo(angles=np.array([0.0, math.nan, 1.0, 2.0])), (8, 8, 4), (4, 4, 16), -1),
     ("inf shift", base_geo(channel_shift=np.array([0.0, math.inf, 0.0, 0.0])), (8, 8, 4), (4, 4, 16), -1),
@@ -197,15 +201,30 @@ def test_cone_forward_tile_choice(bp, name, tile):
 
 @pytest.mark.parametrize("ny,ns,nv,kind,word", [
     (64, 8, 90, "parallel", "gather:"), (512, 64, 8, "parallel", "gather:"), (512, 64, 12, "parallel", "gather:"),
-    (512, 64, 16, "parallel", "tile:"), (512, 32, 16, "translation", "gather:"), (512, 32, 24, "translation", "gather:"),
-    (512, 32, 64, "translation", "tile:"), (256, 32, 96, "parallel", "tile:"), (512, 64, 720, "parallel", "tile:"),
+    (512, 64, 16, "parallel", "tile:"), (512, 32, 16, "translation", "column:"),
+    (512, 32, 24, "translation", "column:"), (512, 32, 64, "translation", "column:"), (256, 32, 96, "parallel", "tile:"),
+    (512, 64, 720, "parallel", "tile:"),
 ])
 def test_forward_strategy_rule(bp, ny, ns, nv, kind, word):
     """The planner's parallel forward strategy on shapes of the gfx950 sweep:
-    gather up to 1e8 voxel-views, and up to 2.5e8 with at most 32 views."""
+    gather up to 1e8 voxel-views, and up to 2.5e8 with at most 32 views;
+    translation scans (every view at angle 0) take the column forms."""
     base = W.get("translation-512x512x32-64v" if kind == "translation" else W.BENCH)
     w = W.scaled(base, "sweep", ny=ny, nx=ny, ns=ns, nr=ns, nv=nv, nc=int(ny * 1.5) + 16)
-    assert word in bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape).split("forward:")[1]
+    desc = bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape)
+    assert word in desc.split("forward:")[1]
+    assert ("back: column:" in desc) == (kind == "translation")
+
+
+def test_translation_column_forward_is_chosen_and_can_be_overridden(bp):
+    """A translation scan plans the column forward by itself; tile and gather
+    can still be forced, and the back stays in its column form either way."""
+    w = W.get("translation-512x512x32-64v")
+    assert "column:" in bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape).split("forward:")[1]
+    assert "column:" in bp.plan_query(dict(w.geometry(), forward_strategy=5), w.recon_shape, w.sino_shape)
+    for code, word in ((1, "tile:"), (2, "gather:")):
+        desc = bp.plan_query(dict(w.geometry(), forward_strategy=code), w.recon_shape, w.sino_shape)
+        assert word in desc.split("forward:")[1] and "back: column:" in desc
 
 
 @pytest.mark.parametrize("strategy,word", [(1, "tile:"), (2, "gather:")])

@@ -74,10 +74,12 @@ def test_noalloc_forward_two_calls_second_smaller(bp, orc):
 
 
 @pytest.mark.parametrize("name,strategy", [
-    ("translation", 1), ("ragged-gather", 2), ("ragged-tile", 1), ("cone", 0), ("helical", 0)])
+    ("translation", 1), ("translation", 0), ("ragged-gather", 2), ("ragged-tile", 1), ("cone", 0), ("helical", 0)])
 def test_noalloc_forward_strategies_and_geometries(bp, orc, name, strategy):
-    """Both parallel strategies, a translation scan and the cone geometries
-    (which use no scratch) through the allocation-free entry point."""
+    """Both parallel strategies, a translation scan (forced region walk, and
+    its own column forward, whose column sums then live in the scratch) and
+    the cone geometries (which use no scratch) through the allocation-free
+    entry point."""
     w = {
         "translation": W.scaled(W.get("translation-512x512x32-64v"), "translation-40x48x12-9v", ny=40, nx=48, ns=12,
                                 nv=9, nr=12, nc=96, shift_step=3.0, seed_x=27),
