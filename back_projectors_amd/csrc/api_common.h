@@ -13,7 +13,6 @@
 namespace bpamd {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;      // work arrays stay below 2^31 elements
-constexpr int64_t kConeBatchBufMax = (int64_t)4 << 30; // cone handles keep a transposed sinogram up to 4 GiB
 
 // Record `why` as the calling thread's last error and return `s`.
 proj_status fail(proj_status s, const std::string &why);

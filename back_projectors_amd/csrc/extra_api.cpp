@@ -38,7 +38,7 @@ proj_status proj_forward_pixels(proj_handle h, const int32_t *pixels_dev, int64_
         return ok();
     }
     // (parallel: the accumulation and sort buffers; cone: the transposed
-    // sinogram, where the handle keeps one)
+    // sinogram)
     const bool shared = h->plan.g.kind == 0 || h->plan.ctr;
     bool capturing = false;
     if (shared) {

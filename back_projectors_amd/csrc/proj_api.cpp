@@ -679,7 +679,7 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                 e = hipEventCreateWithFlags(&h->fwd_done, hipEventDisableTiming);
                 if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipEventCreateWithFlags");
             }
-            if (geo.kind != 0 && h->sino_elems > 0 && h->sino_elems * 4 <= kConeBatchBufMax) {
+            if (geo.kind != 0 && h->sino_elems > 0) {
                 // the cone batches' transposed sinogram, and the event that
                 // orders the calls sharing it
                 e = hipMalloc((void **)&h->d_ctr, (size_t)h->sino_elems * sizeof(float));

@@ -575,15 +575,15 @@ __global__ __launch_bounds__(256) void cone_back_pixels_kernel(const float *__re
 // read-modify-writes in `stride` passes, each taking the lanes whose slice is
 // that pass's residue (the plan's stride puts the rows of one pass on distinct
 // rows, as in the full cone forward; LDS float atomics cost tens of times
-// more).  Then it adds the band to the sinogram, one global atomic per touched
-// cell: with TR into the sinogram transposed to [V][C][R] (unpacked after), the
-// lanes along the rows of one channel, a few 64-byte requests per channel;
-// otherwise into the sinogram itself, the channels of a row adjacent (about 66
-// requests per view at 256^3).  A band taller than the LDS holds
-// (magnification far above one) takes the direct form.
+// more).  Then it adds the band, one global atomic per touched cell, to the
+// sinogram transposed to [V][C][R] (the handle's; unpacked after), the lanes
+// along the rows of one channel: a few 64-byte requests per channel, where the
+// sinogram itself took one per row (about 66 per view at 256^3).  A band
+// taller than the LDS holds (magnification far above one) takes the direct
+// form, into the same transposed sinogram.
 constexpr int CPB_CELLS = 1536;         // LDS band cells per wave (rows x taps)
 
-template <int R, bool TR>
+template <int R>
 __global__ __launch_bounds__(256) void cone_forward_pixels_kernel(const int32_t *__restrict__ pix, int n,
                                                                   const float *__restrict__ cyl,
                                                                   float *__restrict__ sino,
@@ -679,7 +679,7 @@ __global__ __launch_bounds__(256) void cone_forward_pixels_kernel(const int32_t 
                         for (int t = 0; t < NTAP; ++t) {
                             const int ch = ncv - R + t;
                             if (ch >= 0 && ch < g.nc && h[t] != 0.f)
-                                unsafeAtomicAdd(&sv[TR ? (int64_t)ch * g.nr + m : (int64_t)m * g.nc + ch], h[t] * c);
+                                unsafeAtomicAdd(&sv[(int64_t)ch * g.nr + m], h[t] * c);
                         }
                     }
                 }
@@ -709,16 +709,16 @@ __global__ __launch_bounds__(256) void cone_forward_pixels_kernel(const int32_t 
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             const int rows = hi - lo + 1, cells = rows * NTAP;
             for (int e = lane; e < cells; e += 64) {
-                // TR: lanes along the rows of one channel, adjacent in the
-                // transposed sinogram (a few 64-byte requests per channel instead
-                // of one per row)
-                const int mm = TR ? e % rows : e / NTAP, t = TR ? e / rows : e % NTAP;
+                // lanes along the rows of one channel, adjacent in the
+                // transposed sinogram (a few 64-byte requests per channel
+                // instead of one per row in the sinogram itself)
+                const int mm = e % rows, t = e / rows;
                 float *cell = band + mm * NTAP + t;
                 const float val = *cell;
                 *cell = 0.f;
                 const int m = lo + mm, ch = ncv - R + t;
                 if (val != 0.f && ch >= 0 && ch < g.nc)
-                    unsafeAtomicAdd(&sv[TR ? (int64_t)ch * g.nr + m : (int64_t)m * g.nc + ch], val);
+                    unsafeAtomicAdd(&sv[(int64_t)ch * g.nr + m], val);
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
@@ -733,6 +733,15 @@ __global__ __launch_bounds__(256) void cone_forward_pixels_kernel(const int32_t 
     case 5: hipLaunchKernelGGL((KERN<5>), __VA_ARGS__); break;                                                \
     case 6: hipLaunchKernelGGL((KERN<6>), __VA_ARGS__); break;                                                \
     case 7: hipLaunchKernelGGL((KERN<7>), __VA_ARGS__); break;                                                \
+    default: return hipErrorInvalidValue;                                                                     \
+    }
+
+#define BPAMD_SUBSET_R(KERN, ...)                                                                             \
+    switch (g.radius) {                                                                                       \
+    case 1: hipLaunchKernelGGL((KERN<1>), __VA_ARGS__); break;                                                \
+    case 2: hipLaunchKernelGGL((KERN<2>), __VA_ARGS__); break;                                                \
+    case 3: hipLaunchKernelGGL((KERN<3>), __VA_ARGS__); break;                                                \
+    case 4: hipLaunchKernelGGL((KERN<4>), __VA_ARGS__); break;                                                \
     default: return hipErrorInvalidValue;                                                                     \
     }
 
@@ -878,21 +887,17 @@ hipError_t launch_forward_pixels(const Plan &p, const int32_t *pix, int n, const
         }
         return launch_par_unpack(p, sino, st);
     }
+    if (n == 0) return launch_fill_zero(sino, (int64_t)g.nv * g.nr * g.nc, st);
+    if (!p.ctr) return hipErrorInvalidValue;      // (every cone handle with a sinogram keeps one)
+    // into the handle's transposed sinogram, then unpacked
     const dim3 grid((unsigned)n, (unsigned)((g.ns + 63) / 64));       // a listed pixel per workgroup
-    if (p.ctr && n > 0) {          // into the transposed sinogram, then unpacked
-        hipError_t e = launch_fill_zero(p.ctr, (int64_t)g.nv * g.nr * g.nc, st);
-        if (e != hipSuccess) return e;
-        BPAMD_SUBSET_R2(cone_forward_pixels_kernel, true, grid, dim3(256), 0, st, pix, n, cyl, p.ctr, p.idx,
-                        p.views, g, p.cone_stride)
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return launch_unpack_rows(p.ctr, sino, g.nv, g.nr, g.nc, g.nc, g.nr, 0, st);
-    }
-    hipError_t e = launch_fill_zero(sino, (int64_t)g.nv * g.nr * g.nc, st);
-    if (e != hipSuccess || n == 0) return e;
-    BPAMD_SUBSET_R2(cone_forward_pixels_kernel, false, grid, dim3(256), 0, st, pix, n, cyl, sino, p.idx, p.views,
-                    g, p.cone_stride)
-    return hipGetLastError();
+    hipError_t e = launch_fill_zero(p.ctr, (int64_t)g.nv * g.nr * g.nc, st);
+    if (e != hipSuccess) return e;
+    BPAMD_SUBSET_R(cone_forward_pixels_kernel, grid, dim3(256), 0, st, pix, n, cyl, p.ctr, p.idx, p.views, g,
+                   p.cone_stride)
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_unpack_rows(p.ctr, sino, g.nv, g.nr, g.nc, g.nc, g.nr, 0, st);
 }
 
 }  // namespace bpamd

@@ -245,8 +245,7 @@ proj_status proj_back_squared(proj_handle h, const float *sino_dev, float *recon
  * cost grows with n*S*V, not with the volume, plus one pass over the sinogram
  * (the forward writes all of it; a back of a large batch first packs it into
  * a layout with its columns contiguous).  A cone-beam handle keeps a
- * transposed copy of the sinogram's size for this (at most 4 GiB; beyond that
- * the batches read and add the sinogram in place).  A parallel forward sorts each view's entries by channel
+ * transposed copy of the sinogram's size for this.  A parallel forward sorts each view's entries by channel
  * in passes of up to 4096 entries and writes every sinogram cell from one
  * wave, without atomics; the entries of one channel are summed in the order
  * the sort placed them, which may differ between calls (results then differ
