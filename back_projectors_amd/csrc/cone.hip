@@ -134,7 +134,7 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
     const int ntiles = tiles_x * ((g.ny + BT - 1) / BT);
     const int nch = (g.ns + SL - 1) / SL;
     int tile, chunk;
-    xcd_work_item((int)gridDim.x, (int)gridDim.y, tile, chunk);
+    xcd_work_item_blocked((int)gridDim.x, (int)gridDim.y, tiles_x, (g.ny + BT - 1) / BT, tile, chunk);
     const int tj0 = (tile % tiles_x) * BT;
     const int ti0 = (tile / tiles_x) * BT;
     const int k0 = chunk * SL;

@@ -144,4 +144,47 @@ __device__ inline void xcd_work_item(int gx, int gy, int &tile, int &chunk) {
     chunk = w / gx;
 }
 
+// Tile t of a tx x ty tile grid in blocked order: blocks of 8 x 8 tiles, the
+// blocks row-major and the tiles of a block row-major (the blocks of the last
+// block row and column are cut to the grid).  A run of consecutive t is then
+// a compact patch of tiles instead of a strip across the volume.  A
+// bijection of [0, tx ty).
+__device__ inline int blocked_tile(int t, int tx, int ty) {
+    const int br = t / (8 * tx);              // block row
+    const int h = min(8, ty - 8 * br);        // its height in tiles
+    const int o = t - br * 8 * tx;
+    const int bc = o / (8 * h);               // block column (all before it are 8 wide)
+    const int bw = min(8, tx - 8 * bc);       // its width in tiles
+    const int oo = o - bc * 8 * h;
+    const int r = oo / bw, c = oo - r * bw;
+    return (8 * br + r) * tx + 8 * bc + c;
+}
+
+// The (tile, chunk) work item of this workgroup in a grid of gx = tx ty tiles
+// by gy chunks, for kernels whose chunks read disjoint detector rows and whose
+// neighbouring tiles share detector channels.  Where gx is a multiple of 8,
+// XCD x takes the same eighth of the tiles in every chunk, chunk by chunk
+// (each XCD gets an equal share of every chunk's work, and the chunks' work
+// can differ), and its tiles are consecutive in blocked order, so that the
+// workgroups resident on one XCD at a time form a compact patch whose
+// windows overlap in its L2.  Otherwise the grid is split as by
+// xcd_work_item, with the tiles in blocked order.  A bijection of the grid.
+__device__ inline void xcd_work_item_blocked(int gx, int gy, int tx, int ty, int &tile, int &chunk) {
+    const int lin = (int)blockIdx.y * gx + (int)blockIdx.x;
+    const int xcd = lin & 7, slot = lin >> 3;
+    int t;
+    if ((gx & 7) == 0) {
+        const int per = gx >> 3;
+        chunk = slot / per;
+        t = xcd * per + slot % per;
+    } else {
+        const int n = gx * gy;
+        const int q = n >> 3, r = n & 7;
+        const int w = xcd * q + (xcd < r ? xcd : r) + slot;
+        t = w % gx;
+        chunk = w / gx;
+    }
+    tile = blocked_tile(t, tx, ty);
+}
+
 }  // namespace bpamd
