@@ -579,7 +579,13 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         }
 
         const int nrw = wd.nrw;
-        const int npass = (nrw + 63) >> 6;                   // row passes of 64 lanes
+        // Only the window rows on the detector are ever flushed, so step 2
+        // walks those alone: rows rb .. re - 1 of the window, in passes of 64
+        // lanes.  (Step 1 also adds into the profile rows off the detector;
+        // they are never read, and are cleared when the view is done.)
+        const int rb = max(0, -wd.m0);
+        const int re = min(nrw, g.nr - wd.m0);
+        const int npass = re > rb ? (re - rb + 63) >> 6 : 0;
         const int cbase = kmin - R;                          // first channel of the walk
         const int clast = kmax + R;                          // last channel of the walk
         float *const colb = win + (cbase - wd.n0) * nrp + lane;   // this lane's row of the first column
@@ -678,13 +684,14 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         };
 
         // Row groups of NPG passes: the ring accumulators of one group live
-        // in registers; a window taller than 64 * NPG rows walks the pixels
-        // once per group (the profile is cleared in full every time).  Row
-        // passes that lie inside the profile column and the window column
+        // in registers; a window taller than 64 * NPG detector rows walks the
+        // pixels once per group (the profile is cleared in full every time).
+        // Row passes that lie inside the profile column and the window column
         // whatever this view's window (a single group, and passes below the
         // plan's row pitch nrp) read, clear and write without a row guard:
-        // rows past this view's window hold zeros in the profile and are never
-        // flushed from the window.  The last pass of a group is guarded.
+        // rows past the detector rows of this view's window are never flushed
+        // from the window, and reading them only clears them.  The last pass
+        // of a group is guarded.
         auto walk_groups = [&](auto full_c) {
             constexpr bool FULL = decltype(full_c)::value;
             for (int grp = 0; grp * NPG < npass; ++grp) {
@@ -695,12 +702,12 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                     for (int s = 0; s < NTAP; ++s) acc[ps][s] = 0.f;
                 bool rowok[NPG];
 #pragma unroll
-                for (int ps = 0; ps < NPG; ++ps) rowok[ps] = (FULL && ps + 1 < NPG) || (grp * NPG + ps) * 64 + lane < nrw;
+                for (int ps = 0; ps < NPG; ++ps) rowok[ps] = (FULL && ps + 1 < NPG) || rb + (grp * NPG + ps) * 64 + lane < re;
                 int lo = cbase;                                   // channel of ring slot 0
                 // write channel lo's accumulators into its window column and
                 // shift the ring down by one channel (slot t holds channel lo + t)
                 auto finish = [&]() {
-                    float *col = colb + (lo - cbase) * nrp + grp * NPG * 64;
+                    float *col = colb + (lo - cbase) * nrp + rb + grp * NPG * 64;
                     // (a pass past the window's rows has no lane with rowok and
                     // only ever adds zeros, so no pass needs a guard of its own)
 #pragma unroll
@@ -722,7 +729,7 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                         h[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hq[t]), q));
 #pragma unroll
                     for (int ps = 0; ps < NPG; ++ps) {
-                        float *cell = prof + (grp * NPG + ps) * 64 + lane;
+                        float *cell = prof + rb + (grp * NPG + ps) * 64 + lane;
                         float r = 0.f;
                         if (rowok[ps]) {
                             r = *cell;
@@ -740,8 +747,8 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                     }
                     if (!FULL && npass > NPG) {                   // the other groups' rows: cleared only
                         for (int pp = 0; pp < npass; ++pp)
-                            if (pp / NPG != grp && pp * 64 + lane < nrw)
-                                for (int c = 0; c < (inter ? P : 1); ++c) prof[c * nrp + pp * 64 + lane] = 0.f;
+                            if (pp / NPG != grp && rb + pp * 64 + lane < re)
+                                for (int c = 0; c < (inter ? P : 1); ++c) prof[c * nrp + rb + pp * 64 + lane] = 0.f;
                     }
                 };
                 auto visit = [&](int i, const float (&xv)[P]) {
@@ -771,10 +778,15 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                 while (lo <= clast) finish();
             }
         };
-        if (npass <= NPG && nrp >= (NPG - 1) * 64)
+        if (npass <= NPG && nrp >= rb + (NPG - 1) * 64)
             walk_groups(std::true_type{});
         else
             walk_groups(std::false_type{});
+        // the profile rows off the detector, which step 1 added into and
+        // step 2 never read
+        for (int m = lane; m < nrw; m += 64)
+            if (m < rb || m >= re)
+                for (int c = 0; c < (inter ? P : 1); ++c) prof[c * nrp + m] = 0.f;
 
         // add the walked columns of the window to the sinogram: lanes along
         // channels, coalesced.  A span of at most 64 channels goes dm = 64 /
@@ -859,11 +871,12 @@ static hipError_t cone_back_t(const Plan &p, const float *sino, float *recon, in
     }
 }
 
-// Row passes of 64 lanes held in registers per row group: 2 where the
-// windows have at most 128 rows (radius 1), else 3.
+// Row passes of 64 lanes held in registers per row group, from the most
+// detector rows a window can hold (the window's rows, at most the detector's):
+// 1 where that is at most 64, 2 where at most 128 (radius 1), else 3.
 template <int R>
-constexpr int cone_fwd_npg(int nrcap) {
-    return (R == 1 && nrcap <= 128) ? 2 : 3;
+constexpr int cone_fwd_npg(int rows) {
+    return rows <= 64 ? 1 : ((R == 1 && rows <= 128) ? 2 : 3);
 }
 
 template <int R, int P, bool U, int TY, int NPG>
@@ -889,8 +902,10 @@ static hipError_t cone_fwd_n(const Plan &p, const float *recon, float *sino, hip
 
 template <int R, int P>
 static hipError_t cone_fwd_t(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+    const int npg = cone_fwd_npg<R>(std::min(p.fwd_nrcap, p.g.nr));
+    if (npg == 1) return cone_fwd_n<R, P, 1>(p, recon, sino, st);
     if constexpr (R == 1) {
-        if (cone_fwd_npg<R>(p.fwd_nrcap) == 2) return cone_fwd_n<R, P, 2>(p, recon, sino, st);
+        if (npg == 2) return cone_fwd_n<R, P, 2>(p, recon, sino, st);
     }
     return cone_fwd_n<R, P, 3>(p, recon, sino, st);
 }
@@ -934,7 +949,7 @@ hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, h
 }
 
 // Dynamic LDS above the default limit needs the opt-in attribute.
-hipError_t cone_forward_allow_lds(int radius, int stride, int ty, int nrcap, size_t bytes) {
+hipError_t cone_forward_allow_lds(int radius, int stride, int ty, int rows, size_t bytes) {
     const void *f = nullptr;
     const void *fu = nullptr;
 #define BPAMD_CFN(RR, PP, NN)                                                                                 \
@@ -946,8 +961,10 @@ hipError_t cone_forward_allow_lds(int radius, int stride, int ty, int nrcap, siz
     }
 #define BPAMD_CF(RR, PP)                                                                                      \
     if (radius == RR && stride == PP) {                                                                       \
-        if constexpr (RR == 1) {                                                                              \
-            if (cone_fwd_npg<RR>(nrcap) == 2) BPAMD_CFN(RR, PP, 2) else BPAMD_CFN(RR, PP, 3)                  \
+        if (cone_fwd_npg<RR>(rows) == 1)                                                                      \
+            BPAMD_CFN(RR, PP, 1)                                                                              \
+        else if constexpr (RR == 1) {                                                                         \
+            if (cone_fwd_npg<RR>(rows) == 2) BPAMD_CFN(RR, PP, 2) else BPAMD_CFN(RR, PP, 3)                   \
         } else                                                                                                \
             BPAMD_CFN(RR, PP, 3)                                                                              \
     }

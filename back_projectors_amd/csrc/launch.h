@@ -140,6 +140,6 @@ hipError_t launch_vec(int op, float *d, const float *a, const float *b, const do
 
 hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st);
 hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
-hipError_t cone_forward_allow_lds(int radius, int stride, int ty, int nrcap, size_t bytes);
+hipError_t cone_forward_allow_lds(int radius, int stride, int ty, int rows, size_t bytes);
 
 }  // namespace bpamd

@@ -726,7 +726,8 @@ proj_status proj_create(const proj_geometry *gp, const int64_t recon_shape[3], c
                 proj_destroy(h);
                 return fail(PROJ_ERR_UNSUPPORTED, "device LDS per workgroup below the forward plan's need");
             }
-            e = cone_forward_allow_lds(geo.radius, plan.cone_stride, plan.cone_ty, plan.fwd_nrcap, plan.fwd_lds);
+            e = cone_forward_allow_lds(geo.radius, plan.cone_stride, plan.cone_ty, std::min(plan.fwd_nrcap, geo.nr),
+                                       plan.fwd_lds);
             if (e != hipSuccess) return cleanup(PROJ_OK, e, "hipFuncSetAttribute(LDS)");
         }
         h->table_bytes = (size_t)h->index_elems * sizeof(int32_t) + views.size() * sizeof(ViewK) + rec_bytes;

@@ -165,6 +165,18 @@ def test_cone_forward_window_wider_than_a_flush_step(bp):
     assert nw > 64, desc
 
 
+def test_cone_forward_window_taller_than_a_row_group(bp):
+    """Detector rows far finer than the voxels: the cone forward's windows
+    hold more detector rows than the three 64-lane passes of one row group,
+    so its walk takes several groups (the GPU parity case of this geometry,
+    cone-20x24x64-9v-vtallrows, runs that walk)."""
+    geo = dict(kind=1, num_views=9, angles=2 * np.pi / 9 * np.arange(9), delta_voxel=1.0, delta_channel=2.0,
+               delta_row=0.45, source_iso=60.0, source_detector=120.0, psf_radius=1)
+    desc = bp.plan_query(geo, (20, 24, 64), (9, 260, 40))
+    nr = int(re.search(r"forward: .*? window \d+ ch x (\d+) rows", desc).group(1))
+    assert min(nr, 260) > 3 * 64, desc
+
+
 def test_helical_radius2_plans(bp):
     """The helical scan at psf radius 2 (no truncated footprint) plans with
     5x5 taps."""

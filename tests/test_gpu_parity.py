@@ -105,9 +105,15 @@ CONE_WIDEWIN = W.Workload("cone-20x24x16-5v-widewindow", W.CONE_FLAT, 20, 24, 16
 # the small helical scan at psf radius 2: its footprints near the source are
 # up to 2.6 channels wide, which radius 1 truncates and radius 2 keeps whole
 HELIX_R2 = W.scaled(HELIX_SMALL, "helical-36x36x40-47v-r2", radius=2, seed_x=71, seed_y=72)
+# rows far finer than the voxels (about 4.4 rows per slice, footprints wider
+# than the three row taps): the forward windows hold all 260 detector rows,
+# more than the three passes of 64 lanes one row group keeps in registers, so
+# the forward walks its pixels once per row group
+CONE_VTALL = W.Workload("cone-20x24x64-9v-vtallrows", W.CONE_FLAT, 20, 24, 64, 9, 260, 40, dch=2.0, drow=0.45,
+                        sid=60.0, sdd=120.0, seed_x=83, seed_y=84)
 SMALL_CASES = [W.get(W.SMALL), PAR_RAGGED, PAR_FINE, PAR_WIDE, TRANS_SMALL, PAR_R4, CONE_RAGGED, CONE_R2, CONE_R3,
                CONE_R4, HELIX_SMALL, CONE_TALL, PAR_TRUNC, CONE_FINECH, CONE_TALL_R3, CONE_UNIT, CONE_COARSE,
-               CONE_WIDEWIN, HELIX_R2, TRANS_R2]
+               CONE_WIDEWIN, HELIX_R2, TRANS_R2, CONE_VTALL]
 
 
 def inputs(w):
