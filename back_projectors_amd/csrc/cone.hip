@@ -179,8 +179,13 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
     // View v's window into buf: wave w copies window rows w, w + 4, ..., each
     // as direct global-to-LDS loads of 64 channels (lane c: channel n0 + c to
     // LDS cell [row][c]).  A cell off the detector gets an offset past the
-    // view's buffer range, which the range check turns into a zero; lanes past
-    // the window's width write nothing (no tap reads there).
+    // view's buffer range, which the range check turns into a zero: a channel
+    // off the detector is given such an offset outright; a row off it needs no
+    // test, since 4 (row nc + n) taken modulo 2^32 is then at least the
+    // view's nr nc floats (rows below the detector wrap to at least 2^31, and
+    // the view is under 2^31 bytes), so the offset just advances by one row
+    // step per load.  Lanes past the window's width write nothing (no tap
+    // reads there).
     const int64_t vfl = (int64_t)g.nr * g.nc;    // floats per view (bytes below 2^31, checked by the plan)
     auto stage = [&](int v, const Window &w, float *buf) {
         if (w.nw <= 0 || w.nrw <= 0) return;
@@ -190,13 +195,11 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
             const int c = c0 + wl, n = w.n0 + c;
             const bool nok = (unsigned)n < (unsigned)g.nc;
             if (c < w.nw) {
-                for (int m = wave; m < w.nrw; m += NT / 64) {
-                    const int row = w.m0 + m;
-                    const unsigned off =
-                        nok && (unsigned)row < (unsigned)g.nr ? (unsigned)(row * g.nc + n) * 4u : kOffRange;
+                unsigned off = nok ? (unsigned)((w.m0 + wave) * g.nc + n) * 4u : kOffRange;
+                const unsigned step = nok ? (unsigned)(NT / 64 * g.nc) * 4u : 0u;
+                for (int m = wave; m < w.nrw; m += NT / 64, off += step)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(buf + m * PC + c0),
                                                              4, off, 0, 0, 0);
-                }
             }
         }
     };

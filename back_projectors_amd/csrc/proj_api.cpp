@@ -297,6 +297,11 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
     // with 32-bit byte offsets below 2^31
     if (R * C * 4 >= ((int64_t)1 << 31))
         return fail(PROJ_ERR_UNSUPPORTED, "one view of the sinogram is 2 GiB or more");
+    // the cone back stages a window row at the byte offset 4 (row C + n)
+    // modulo 2^32, which lies past the view for every row off the detector a
+    // window can reach (from -2r to R - 1 + 2r) while 8 r C < 2^31
+    if (gp->kind != PROJ_PARALLEL && 8 * (int64_t)gp->psf_radius * C >= ((int64_t)1 << 31))
+        return fail(PROJ_ERR_UNSUPPORTED, "cone detector of 2^28 / psf_radius channels or more");
 
     g.kind = gp->kind;
     g.radius = gp->psf_radius;

@@ -105,6 +105,8 @@ BAD = [
     ("cone detector 20x finer", base_geo(**dict(CONE, delta_channel=0.05, delta_row=0.05)), (8, 8, 4), (4, 200, 400),
      -2),
     ("cone rows 8x coarser", base_geo(**dict(CONE, delta_row=8.0)), (8, 8, 4), (4, 6, 16), -2),
+    ("cone detector of 2^28 / radius channels", base_geo(**dict(CONE, psf_radius=4)), (8, 8, 4), (4, 1, 1 << 26),
+     -2),
     ("forward strategy 3", base_geo(forward_strategy=3), (8, 8, 4), (4, 4, 16), -1),
     ("forward strategy -1", base_geo(forward_strategy=-1), (8, 8, 4), (4, 4, 16), -1),
     ("cone forward strategy", base_geo(**dict(CONE, forward_strategy=2)), (8, 8, 4), (4, 6, 16), -1),
