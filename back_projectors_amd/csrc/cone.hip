@@ -937,6 +937,7 @@ hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, int 
     case 8: BPAMD_DISPATCH_R(cone_back_t, 8, p, sino, recon, power, st)
     case 16: BPAMD_DISPATCH_R(cone_back_t, 16, p, sino, recon, power, st)
     case 32: BPAMD_DISPATCH_R(cone_back_t, 32, p, sino, recon, power, st)
+    case 48: BPAMD_DISPATCH_R(cone_back_t, 48, p, sino, recon, power, st)
     default: return hipErrorInvalidValue;
     }
 }

@@ -417,7 +417,11 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
             pc = nwcap <= 33 ? 33 : (nwcap <= 65 ? 65 : (nwcap <= 129 ? 129 : 257));
             return 2 * (size_t)nrcap * pc * sizeof(float);
         };
-        for (int sl = pick_chunk(S, {8, 16, 32});; sl /= 2) {
+        // (48-slice chunks: a 96-slice volume in two chunks instead of three,
+        // each view's window staged twice instead of three times; the larger
+        // accumulator file costs no occupancy where the window's LDS already
+        // limits the kernel to four workgroups per CU)
+        for (int sl = pick_chunk(S, {8, 16, 32, 48});; sl = sl == 48 ? 32 : sl / 2) {
             plan.back_sl = sl;
             plan.back_lds = back_bytes(sl, plan.back_nwcap, plan.back_nrcap, plan.back_pc);
             if ((plan.back_lds <= kMaxLds && plan.back_nwcap <= 257) || sl == 8) break;
