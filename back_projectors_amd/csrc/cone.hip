@@ -104,18 +104,18 @@ __device__ __forceinline__ ConeVPB cone_vp_back(const Geo &g, const ViewK &vk, d
 //
 // Per (view, pixel) the row coordinate w_k = Mr dz_k + c_row is affine in the
 // slice index, so it is carried in 32.32 fixed point (from the fp64 value at
-// the chunk's first slice, advanced by one 64-bit add per slice, about 4e-9 of
-// a row off after 32 slices): the high word is the tap row m_k = floor(w_k +
-// 1/2) (offset by R) and the low word the position inside it.  A row chosen
-// differently at an exact half (round half up here, half to even in the
-// model) moves no weight while the footprint is no wider than 2R rows: every
-// tap is the overlap of one cell with the footprint.  The row taps run in fp32
-// (clamped edges by v_med3).  Two cases take the row in fp64, in the model's
-// operation order, with each tap the model's own fp64 overlap of its cell with
-// the footprint (exact for thin taps): a tap cell off the detector's top or
-// bottom edge,
-// and a footprint wider than 2R rows (its outermost taps cut it, so the tap
-// row must be the model's even at an exact half).  The chord scale
+// the chunk's first slice, advanced by one 64-bit add per slice: about 4e-9
+// of a row off after 32 slices, 6e-9 after 48): the high word is the tap row
+// m_k = floor(w_k + 1/2) (plus R + 1) and the low word the position inside
+// it.  A row chosen differently at an exact half (round half up here, half to
+// even in the model) moves no weight while the footprint is no wider than 2R
+// rows: every tap is the overlap of one cell with the footprint.  The row taps
+// run in fp32 (clamped edges by v_med3).  Two cases take the row in fp64, in
+// the model's operation order, with each tap the model's own fp64 overlap of
+// its cell with the footprint (exact for thin taps): a tap cell off the
+// detector's top or bottom edge, and a footprint wider than 2R rows (its
+// outermost taps cut it, so the tap row must be the model's even at an exact
+// half).  The chord scale
 // sqrt(d^2 + a^2 + dz^2) runs in fp32, with the per-pixel factor dv / M folded
 // into the channel taps.
 template <int SL, int R, int POW, int PC>
@@ -390,9 +390,10 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
 //      slices of one instruction fall on distinct rows: every add is a plain
 //      read-modify-write with no two lanes on one cell (float atomics in LDS
 //      cost tens of times a plain update on gfx950).
-//   2. rows -> channels.  Lanes are rows of the window (64 per pass); each
-//      reads and clears its profile cell and adds h_t times it into 2R+1
-//      register accumulators, one per channel of the pixel's taps.  The tile's
+//   2. rows -> channels.  Lanes are the window's rows on the detector (64
+//      per pass; the flush drops the others); each reads and clears its
+//      profile cell and adds h_t times it into 2R+1 register accumulators,
+//      one per channel of the pixel's taps.  The tile's
 //      pixels are walked in the order of their channel index, so a channel is
 //      finished once the walk has passed it: it is written into its window
 //      column once (rows of the pass) and the accumulators shift down by one
