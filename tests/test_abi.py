@@ -179,6 +179,17 @@ def test_cone_forward_window_taller_than_a_row_group(bp):
     assert min(nr, 260) > 3 * 64, desc
 
 
+@pytest.mark.parametrize("drow,slices", [(0.8, 48), (0.7, 32), (0.5, 16)])
+def test_cone_back_chunk_falls_back_when_the_window_overflows(bp, drow, slices):
+    """96 slices take 48-slice back chunks (two, no padding) while their
+    double-buffered window fits the workgroup's LDS; finer rows make the window
+    taller and the planner steps down 48 -> 32 -> 16 slices."""
+    geo = dict(kind=1, num_views=8, angles=2 * np.pi / 8 * np.arange(8), delta_voxel=1.0, delta_channel=1.0,
+               delta_row=drow, source_iso=100.0, source_detector=150.0, psf_radius=1)
+    desc = bp.plan_query(geo, (32, 32, 96), (8, 300, 80))
+    assert f"back: 16x16 px tile, lanes=pixels, {slices} slices/lane" in desc, desc
+
+
 def test_helical_radius2_plans(bp):
     """The helical scan at psf radius 2 (no truncated footprint) plans with
     5x5 taps."""
