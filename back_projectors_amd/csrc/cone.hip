@@ -399,8 +399,13 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
 //      column once (rows of the pass) and the accumulators shift down by one
 //      channel (slot t holds channel lo + t, so every register index is
 //      fixed at compile time).
-// The window is then added to the sinogram with coalesced global atomics, one
-// per cell per (view, tile, chunk).  Per voxel-view this does 2R+1 LDS
+// A finished channel goes straight from the ring to memory: one global atomic
+// add per nonzero cell per (view, tile, chunk), lanes along the channel's
+// rows.  Into the handle's transposed sinogram [view][channel][row] (then
+// unpacked) those are whole 64-byte lines, four per pass; the row-major
+// sinogram takes the same adds one line per row (cst, rst: the destination's
+// channel and row strides).  So a wave keeps only its row profile in LDS, and
+// LDS no longer bounds the workgroups per CU.  Per voxel-view this does 2R+1 LDS
 // read-modify-writes on one column instead of (2R+1)^2 on the block, and the
 // (2R+1)^2 products become 2R+1 per slice and 2R+1 per row.
 template <int R, int P, bool U, int TY, int NPG>
@@ -409,8 +414,8 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                                                                  const int32_t *__restrict__ idx,
                                                                  const ViewK *__restrict__ views,
                                                                  const int4 *__restrict__ wtab,
-                                                                 const int4 *__restrict__ stab, Geo g, int nwcap,
-                                                                 int nrp, int ncol, int vsplit) {
+                                                                 const int4 *__restrict__ stab, Geo g, int nrp,
+                                                                 int ncol, int vsplit, int cst, int rst) {
     constexpr int NTAP = 2 * R + 1;
     constexpr int CH = 64 * P;            // slices per chunk
     constexpr int NPX = CTX * TY;         // pixels per tile (at most one per lane)
@@ -418,8 +423,7 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
     extern __shared__ float lds[];
     const int lane = (int)threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    float *win = lds + wave * cone_fwd_wave_words(nwcap, nrp, ncol);   // this wave's window [nwcap][nrp]
-    float *prof = win + nwcap * nrp;                                   // and row profile columns [ncol][nrp]
+    float *prof = lds + wave * cone_fwd_wave_words(nrp, ncol);   // this wave's row profile columns [ncol][nrp]
 
     const int tiles_x = (g.nx + CTX - 1) / CTX;
     const int ntiles = tiles_x * ((g.ny + TY - 1) / TY);
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         const int npass = re > rb ? (re - rb + 63) >> 6 : 0;
         const int cbase = kmin - R;                          // first channel of the walk
         const int clast = kmax + R;                          // last channel of the walk
-        float *const colb = win + (cbase - wd.n0) * nrp + lane;   // this lane's row of the first column
+        float *const dview = sino + (int64_t)v * g.nr * g.nc;   // this view of the destination
 
         // Step 1 for one pixel: its cylinder's slices into the row profile.
         // Per slice: the row (fp64, bit-exact with the model), the row taps
@@ -704,19 +708,28 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
                 for (int ps = 0; ps < NPG; ++ps)
 #pragma unroll
                     for (int s = 0; s < NTAP; ++s) acc[ps][s] = 0.f;
-                bool rowok[NPG];
+                bool rowin[NPG], rowok[NPG];     // a detector row of the window; and read in step 2
 #pragma unroll
-                for (int ps = 0; ps < NPG; ++ps) rowok[ps] = (FULL && ps + 1 < NPG) || rb + (grp * NPG + ps) * 64 + lane < re;
+                for (int ps = 0; ps < NPG; ++ps) {
+                    rowin[ps] = rb + (grp * NPG + ps) * 64 + lane < re;
+                    rowok[ps] = (FULL && ps + 1 < NPG) || rowin[ps];
+                }
+                // this lane's first detector row, as a destination offset
+                const int dro = (wd.m0 + rb + grp * NPG * 64 + lane) * rst;
                 int lo = cbase;                                   // channel of ring slot 0
                 // write channel lo's accumulators into its window column and
                 // shift the ring down by one channel (slot t holds channel lo + t)
                 auto finish = [&]() {
-                    float *col = colb + (lo - cbase) * nrp + rb + grp * NPG * 64;
-                    // (a pass past the window's rows has no lane with rowok and
-                    // only ever adds zeros, so no pass needs a guard of its own)
+                    if ((unsigned)lo < (unsigned)g.nc) {            // uniform: a channel on the detector
+                        float *dcol = dview + lo * cst + dro;
+#pragma unroll
+                        for (int ps = 0; ps < NPG; ++ps) {
+                            const float val = acc[ps][0];
+                            if (rowin[ps] && val != 0.f) unsafeAtomicAdd(dcol + ps * 64 * rst, val);
+                        }
+                    }
 #pragma unroll
                     for (int ps = 0; ps < NPG; ++ps) {
-                        if (rowok[ps]) col[ps * 64] = acc[ps][0];
 #pragma unroll
                         for (int t = 0; t + 1 < NTAP; ++t) acc[ps][t] = acc[ps][t + 1];
                         acc[ps][NTAP - 1] = 0.f;
@@ -791,44 +804,6 @@ __global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__r
         for (int m = lane; m < nrw; m += 64)
             if (m < rb || m >= re)
                 for (int c = 0; c < (inter ? P : 1); ++c) prof[c * nrp + m] = 0.f;
-
-        // add the walked columns of the window to the sinogram: lanes along
-        // channels, coalesced.  A span of at most 64 channels goes dm = 64 /
-        // nw rows per step, each lane keeping one channel (lanes past dm * nw
-        // idle), so the LDS offset, the sinogram offset and the row advance by
-        // uniform steps; a wider one walks its cells in order, 64 per step.
-        // (The view's sinogram is under 2^31 cells.)  Every cell of these
-        // columns was written by the walk, so nothing needs clearing.
-        const int nw = clast - cbase + 1;
-        const int n0 = cbase;
-        const float *wsrc = win + (cbase - wd.n0) * nrp;
-        float *sv = sino + (int64_t)v * g.nr * g.nc;
-        if (nw <= 64) {
-            const int dm = 64 / nw;
-            const int m1 = (int)(((float)lane + 0.5f) * (1.0f / (float)nw));
-            if (m1 < dm) {
-                const int c = lane - m1 * nw;
-                const int n = n0 + c;
-                const bool nok = (unsigned)n < (unsigned)g.nc;
-                int row = wd.m0 + m1, lo2 = c * nrp + m1, go = row * g.nc + n;
-                const int rend = wd.m0 + nrw, gs = dm * g.nc;
-                for (; row < rend; row += dm, lo2 += dm, go += gs) {
-                    const float val = wsrc[lo2];
-                    if (val != 0.f && nok && (unsigned)row < (unsigned)g.nr) unsafeAtomicAdd(sv + go, val);
-                }
-            }
-        } else {
-            const int total = nw * nrw;
-            const float rnw = 1.0f / (float)nw;
-            for (int e = lane; e < total; e += 64) {
-                const int m = (int)(((float)e + 0.5f) * rnw);
-                const int c = e - m * nw;
-                const float val = wsrc[c * nrp + m];
-                const int row = wd.m0 + m, n = n0 + c;
-                if (val != 0.f && (unsigned)row < (unsigned)g.nr && (unsigned)n < (unsigned)g.nc)
-                    unsafeAtomicAdd(sv + (row * g.nc + n), val);
-            }
-        }
     };
 
     // three prefetch buffers in rotation: the view two turns ahead is loaded
@@ -884,42 +859,42 @@ constexpr int cone_fwd_npg(int rows) {
 }
 
 template <int R, int P, bool U, int TY, int NPG>
-static hipError_t cone_fwd_u(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+static hipError_t cone_fwd_u(const Plan &p, const float *recon, float *sino, bool tr, hipStream_t st) {
     const Geo &g = p.g;
     const int tiles = ((g.nx + CTX - 1) / CTX) * ((g.ny + TY - 1) / TY);
     const int chunks = (g.ns + 64 * P - 1) / (64 * P);
     hipLaunchKernelGGL((cone_forward_kernel<R, P, U, TY, NPG>), dim3(tiles, chunks, p.fwd_vsplit), dim3(CFW * 64),
-                       p.fwd_lds, st, recon, sino, p.idx, p.views, p.fwin, p.fslab, g, p.fwd_nwcap, p.fwd_nrcap,
-                       p.cone_ncol, p.fwd_vsplit);
+                       p.fwd_lds, st, recon, sino, p.idx, p.views, p.fwin, p.fslab, g, p.fwd_nrcap, p.cone_ncol,
+                       p.fwd_vsplit, tr ? g.nr : 1, tr ? 1 : g.nc);
     return hipGetLastError();
 }
 
 template <int R, int P, int NPG>
-static hipError_t cone_fwd_n(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+static hipError_t cone_fwd_n(const Plan &p, const float *recon, float *sino, bool tr, hipStream_t st) {
     if (p.cone_ty == 8) {
-        if (p.cone_unit) return cone_fwd_u<R, P, true, 8, NPG>(p, recon, sino, st);
-        return cone_fwd_u<R, P, false, 8, NPG>(p, recon, sino, st);
+        if (p.cone_unit) return cone_fwd_u<R, P, true, 8, NPG>(p, recon, sino, tr, st);
+        return cone_fwd_u<R, P, false, 8, NPG>(p, recon, sino, tr, st);
     }
-    if (p.cone_unit) return cone_fwd_u<R, P, true, 4, NPG>(p, recon, sino, st);
-    return cone_fwd_u<R, P, false, 4, NPG>(p, recon, sino, st);
+    if (p.cone_unit) return cone_fwd_u<R, P, true, 4, NPG>(p, recon, sino, tr, st);
+    return cone_fwd_u<R, P, false, 4, NPG>(p, recon, sino, tr, st);
 }
 
 template <int R, int P>
-static hipError_t cone_fwd_t(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+static hipError_t cone_fwd_t(const Plan &p, const float *recon, float *sino, bool tr, hipStream_t st) {
     const int npg = cone_fwd_npg<R>(std::min(p.fwd_nrcap, p.g.nr));
-    if (npg == 1) return cone_fwd_n<R, P, 1>(p, recon, sino, st);
+    if (npg == 1) return cone_fwd_n<R, P, 1>(p, recon, sino, tr, st);
     if constexpr (R == 1) {
-        if (npg == 2) return cone_fwd_n<R, P, 2>(p, recon, sino, st);
+        if (npg == 2) return cone_fwd_n<R, P, 2>(p, recon, sino, tr, st);
     }
-    return cone_fwd_n<R, P, 3>(p, recon, sino, st);
+    return cone_fwd_n<R, P, 3>(p, recon, sino, tr, st);
 }
 
 template <int R>
-static hipError_t cone_fwd_r(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+static hipError_t cone_fwd_r(const Plan &p, const float *recon, float *sino, bool tr, hipStream_t st) {
     switch (p.cone_stride) {
-    case 1: return cone_fwd_t<R, 1>(p, recon, sino, st);
-    case 2: return cone_fwd_t<R, 2>(p, recon, sino, st);
-    case 3: return cone_fwd_t<R, 3>(p, recon, sino, st);
+    case 1: return cone_fwd_t<R, 1>(p, recon, sino, tr, st);
+    case 2: return cone_fwd_t<R, 2>(p, recon, sino, tr, st);
+    case 3: return cone_fwd_t<R, 3>(p, recon, sino, tr, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -943,12 +918,12 @@ hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, int 
     }
 }
 
-hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st) {
+hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, bool transposed, hipStream_t st) {
     switch (p.g.radius) {
-    case 1: return cone_fwd_r<1>(p, recon, sino, st);
-    case 2: return cone_fwd_r<2>(p, recon, sino, st);
-    case 3: return cone_fwd_r<3>(p, recon, sino, st);
-    case 4: return cone_fwd_r<4>(p, recon, sino, st);
+    case 1: return cone_fwd_r<1>(p, recon, sino, transposed, st);
+    case 2: return cone_fwd_r<2>(p, recon, sino, transposed, st);
+    case 3: return cone_fwd_r<3>(p, recon, sino, transposed, st);
+    case 4: return cone_fwd_r<4>(p, recon, sino, transposed, st);
     default: return hipErrorInvalidValue;
     }
 }

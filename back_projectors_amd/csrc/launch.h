@@ -80,7 +80,7 @@ constexpr int CFW = 4;   // cone forward waves per workgroup (one view each at a
 // projection step; with ncol = stride, lanes of one instruction add into
 // column lane mod stride where a slab takes consecutive slices on rows
 // closer than one apart)
-__host__ __device__ inline int cone_fwd_wave_words(int nwcap, int nrp, int ncol) { return (nwcap + ncol) * nrp; }
+__host__ __device__ inline int cone_fwd_wave_words(int nrp, int ncol) { return ncol * nrp; }
 
 hipError_t launch_channel_index(const Geo &g, const ViewK *views, int32_t *idx, hipStream_t st);
 hipError_t launch_par_taps(const Geo &g, const ViewK *views, int32_t *rec, int ntap, hipStream_t st);
@@ -139,7 +139,9 @@ hipError_t launch_vec(int op, float *d, const float *a, const float *b, const do
                       hipStream_t st);
 
 hipError_t launch_cone_back(const Plan &p, const float *sino, float *recon, int power, hipStream_t st);
-hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, hipStream_t st);
+// transposed: sino is the handle's [V][C][R] buffer (then unpacked), else the
+// caller's [V][R][C] sinogram; either must hold zeros
+hipError_t launch_cone_forward(const Plan &p, const float *recon, float *sino, bool transposed, hipStream_t st);
 hipError_t cone_forward_allow_lds(int radius, int stride, int ty, int rows, size_t bytes);
 
 }  // namespace bpamd

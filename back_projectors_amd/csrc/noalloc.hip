@@ -79,7 +79,7 @@ extern "C" proj_status proj_forward_noalloc(proj_handle h, const float *recon_de
     }
     if (!work) return ok();
     if (!par) {
-        e = launch_cone_forward(plan, recon_dev, sino_dev, st);
+        e = launch_cone_forward(plan, recon_dev, sino_dev, false, st);
         if (e != hipSuccess) return device_fail(e, "forward projection launch");
         return ok();
     }

@@ -184,13 +184,14 @@ void slab_table(const Geo &g, const std::vector<ViewK> &views, int tx_, int ty_,
 // Estimated time of a cone forward call with CTX x ty tiles, from the same
 // windows and slabs the call uses, on a sample of at most about 64 views:
 // the slice-to-row work (tile pixels times slab passes, about 0.12 ns each
-// on gfx950) and the window flush of a dense volume (64-byte atomic requests:
-// window rows on the detector times the cache lines their channels span,
-// about 21.6 G per second).  The two overlap, so the call takes about the
-// larger; the 8 x 8 tiles cost about 5% more work per pass (measured: the
-// 256^3 cone forward of a dense volume 15.0 ms at 8 x 4, flush-bound, and
-// 11.3 ms at 8 x 8; the 512^2 x 96 helical scan 61.5 ms at 8 x 4,
-// work-bound, and 66.9 ms at 8 x 8).
+// on gfx950) and the atomic adds of a dense volume (64-byte requests: each
+// window channel's rows on the detector, contiguous in the transposed
+// sinogram, about 21.6 G per second).  The two overlap, so the call takes
+// about the larger; the 8 x 8 tiles cost about 5% more work per pass.
+// (Measured when the windows were flushed row by row into the sinogram
+// itself: the 256^3 cone forward of a dense volume 15.0 ms at 8 x 4,
+// flush-bound, and 11.3 ms at 8 x 8; with the direct adds into the transposed
+// sinogram 8.90 ms at 8 x 4 and 9.05 ms at 8 x 8, both bound by the work.)
 // With `passes`, the sampled pixel-passes instead (slab passes times tile pixels).
 double cone_forward_cost(const Geo &g, const std::vector<ViewK> &views, int ty_, int sl, int stride, bool inter_ok,
                          bool passes = false) {
@@ -213,7 +214,10 @@ double cone_forward_cost(const Geo &g, const std::vector<ViewK> &views, int ty_,
                     pixpass += npx * slab_of(g, sr, k0, nk, stride, inter_ok).nw;
                     const int r0 = std::max(w.m0, 0), r1 = std::min(w.m0 + w.nrw - 1, g.nr - 1);
                     const int c0 = std::max(w.n0, 0), c1 = std::min(w.n0 + w.nw - 1, g.nc - 1);
-                    if (r1 >= r0 && c1 >= c0) lines += (double)(r1 - r0 + 1) * (c1 / 16 - c0 / 16 + 1);
+                    // the forward adds a finished channel's rows into the
+                    // transposed sinogram, where they are contiguous: about
+                    // (rows + 15) / 16 lines of 64 bytes per channel
+                    if (r1 >= r0 && c1 >= c0) lines += (double)(c1 - c0 + 1) * (r1 - r0 + 16) / 16.0;
                 }
             }
     if (passes) return pixpass;
@@ -445,8 +449,8 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
             return fail(PROJ_ERR_UNSUPPORTED, "row magnification below 1/3 (detector rows far coarser than the voxels)");
         plan.cone_stride = stride;
         plan.fwd_sl = 64 * stride;
-        // tile rows: 8 x 4 pixels, or 8 x 8 where the flush of the narrower
-        // tiles' windows would bound the call (forced by forward_strategy)
+        // tile rows: 8 x 4 pixels, or 8 x 8 where the atomic adds of the
+        // narrower tiles would bound the call (forced by forward_strategy)
         if (gp->forward_strategy == PROJ_FORWARD_CONE_TILE_8X4)
             plan.cone_ty = 4;
         else if (gp->forward_strategy == PROJ_FORWARD_CONE_TILE_8X8)
@@ -457,8 +461,8 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
                                ? 8
                                : 4;
         // `stride` profile columns per wave where the interleaved slabs save a
-        // tenth of the slice passes or more (each column costs LDS, which can
-        // cost a workgroup per CU)
+        // tenth of the slice passes or more (each column costs a little LDS
+        // and one more read and clear per row in step 2)
         plan.cone_ncol = 1;
         if (stride > 1 && cone_forward_cost(g, views, plan.cone_ty, plan.fwd_sl, stride, true, true) <=
                               0.9 * cone_forward_cost(g, views, plan.cone_ty, plan.fwd_sl, stride, false, true))
@@ -466,7 +470,7 @@ proj_status plan_geometry(const proj_geometry *gp, const int64_t rs[3], const in
         const WinMax wf = max_window(g, views, CTX, plan.cone_ty, plan.fwd_sl);
         plan.fwd_nwcap = wf.nw;
         plan.fwd_nrcap = wf.nr | 1;
-        plan.fwd_lds = (size_t)CFW * cone_fwd_wave_words(plan.fwd_nwcap, plan.fwd_nrcap, plan.cone_ncol) * sizeof(float);
+        plan.fwd_lds = (size_t)CFW * cone_fwd_wave_words(plan.fwd_nrcap, plan.cone_ncol) * sizeof(float);
     }
     if (plan.back_lds > kMaxLds || plan.fwd_lds > kMaxLdsOptIn) {
         char buf[160];
@@ -780,11 +784,36 @@ proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev,
     if (dg.err != hipSuccess) return device_fail(dg.err, "hipSetDevice");
     hipStream_t st = (hipStream_t)hip_stream;
     hipError_t e;
-    if (h->plan.back_sl == 0 || h->plan.g.kind != 0) {
+    const bool cone_tr = h->plan.g.kind != 0 && h->plan.back_sl != 0 && h->plan.ctr;
+    if (h->plan.back_sl == 0 || (h->plan.g.kind != 0 && !cone_tr)) {
         e = launch_fill_zero(sino_dev, h->sino_elems, st);
         if (e != hipSuccess) return device_fail(e, "zero fill");
     }
     if (h->plan.back_sl == 0) return ok();     // empty volume or no views: the sinogram is zero
+    if (cone_tr) {
+        // into the handle's transposed sinogram (zeroed first), then unpacked
+        // into sino_dev; the buffer belongs to the handle, so a call on another
+        // stream waits on the GPU for the previous user
+        bool capturing = false;
+        e = stream_capturing(st, capturing);
+        if (e != hipSuccess) return device_fail(e, "hipStreamIsCapturing");
+        if (!capturing) {
+            e = hipStreamWaitEvent(st, h->fwd_done, 0);
+            if (e != hipSuccess) return device_fail(e, "hipStreamWaitEvent");
+        }
+        const Geo &g = h->plan.g;
+        e = launch_fill_zero(h->plan.ctr, h->sino_elems, st);
+        if (e != hipSuccess) return device_fail(e, "zero fill");
+        e = launch_cone_forward(h->plan, recon_dev, h->plan.ctr, true, st);
+        if (e != hipSuccess) return device_fail(e, "forward projection launch");
+        e = launch_unpack_rows(h->plan.ctr, sino_dev, g.nv, g.nr, g.nc, g.nc, g.nr, 0, st);
+        if (e != hipSuccess) return device_fail(e, "forward unpack launch");
+        if (!capturing) {
+            e = hipEventRecord(h->fwd_done, st);
+            if (e != hipSuccess) return device_fail(e, "hipEventRecord");
+        }
+        return ok();
+    }
     if (h->plan.g.kind == 0) {
         // the accumulation buffer belongs to the handle: a call on another
         // stream waits on the GPU for the previous one
@@ -803,7 +832,7 @@ proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev,
         }
         return ok();
     }
-    e = launch_cone_forward(h->plan, recon_dev, sino_dev, st);
+    e = launch_cone_forward(h->plan, recon_dev, sino_dev, false, st);
     if (e != hipSuccess) return device_fail(e, "forward projection launch");
     return ok();
 }

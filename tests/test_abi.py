@@ -210,17 +210,22 @@ def test_cone_forward_profile_columns(bp, name, inter):
     assert ("interleaved row-profile columns" in desc) == inter, desc
 
 
-@pytest.mark.parametrize("name,tile", [("cone-256x256x256-360v", "8x8"), ("helical-512x512x96-1338v", "8x4")])
-def test_cone_forward_tile_choice(bp, name, tile):
-    """The cone forward's tile from the planner's estimate: the 256^3 cone,
-    whose dense flush of 8 x 4 windows would bound the call, takes 8 x 8
-    tiles; the helical scan, bound by its slice work, keeps 8 x 4.  Either can
-    be forced."""
+@pytest.mark.parametrize("name,rows_scale,tile", [("cone-256x256x256-360v", 1, "8x4"),
+                                                  ("helical-512x512x96-1338v", 1, "8x4"),
+                                                  ("cone-256x256x256-360v", 2, "8x8")])
+def test_cone_forward_tile_choice(bp, name, rows_scale, tile):
+    """The cone forward's tile from the planner's estimate: the 256^3 cone and
+    the helical scan, both bound by their slice work, take 8 x 4 tiles; the
+    256^3 cone on a detector with twice the rows at half the pitch, whose
+    atomic adds from 8 x 4 tiles would bound the call, takes 8 x 8 (half the
+    adds per voxel-view).  Either can be forced."""
     w = W.get(name)
+    geo = dict(w.geometry(), delta_row=w.geometry()["delta_row"] / rows_scale)
+    sino = (w.sino_shape[0], w.sino_shape[1] * rows_scale, w.sino_shape[2])
     fwd = lambda d: d.split("forward:")[1]
-    assert f"{tile} px tile" in fwd(bp.plan_query(w.geometry(), w.recon_shape, w.sino_shape))
+    assert f"{tile} px tile" in fwd(bp.plan_query(geo, w.recon_shape, sino))
     for code, forced in ((3, "8x4"), (4, "8x8")):
-        desc = bp.plan_query(dict(w.geometry(), forward_strategy=code), w.recon_shape, w.sino_shape)
+        desc = bp.plan_query(dict(geo, forward_strategy=code), w.recon_shape, sino)
         assert f"{forced} px tile" in fwd(desc), desc
 
 
