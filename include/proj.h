@@ -164,12 +164,11 @@ proj_status proj_create(const proj_geometry *g, const int64_t recon_shape[3],
  * Graph capture: proj_forward, proj_back, proj_back_squared,
  * proj_forward_pixels and proj_back_pixels allocate, copy and synchronise
  * nothing and use no memset, so they can be captured into a HIP graph.  Outside
- * a capture, parallel-beam forwards on one handle (proj_forward and
- * proj_forward_pixels), cone-beam batch forwards (proj_forward_pixels) and
- * batch back projections large enough to pack the sinogram (proj_back_pixels)
- * are ordered on the GPU (they share the handle's accumulation, sort or
- * transposed-sinogram buffer); inside a capture that ordering is the
- * graph's.  So two such captured calls on one handle must not run
+ * a capture, forwards on one handle (proj_forward and proj_forward_pixels,
+ * both geometries) and batch back projections large enough to pack the
+ * sinogram (proj_back_pixels) are ordered on the GPU (they share the handle's
+ * accumulation, sort or transposed-sinogram buffer); inside a capture that
+ * ordering is the graph's.  So two such captured calls on one handle must not run
  * concurrently, and a replayed graph holding one must be ordered by the caller
  * against every other such call of the same handle on another stream (an
  * event after the replay, a stream wait before the next one).  The solvers
@@ -187,7 +186,10 @@ proj_status proj_forward(proj_handle h, const float *recon_dev, float *sino_dev,
  * handle's accumulation buffer; the buffer needs V * (C + 2 (taps - 1)) *
  * (S rounded up to 16 or 32) * 4 bytes (142 MB for 512x512x64 at 720 views),
  * and a handle that needs more returns PROJ_ERR_UNSUPPORTED before any
- * write.  Cone beam needs no scratch.
+ * write.  Cone beam needs no scratch: its kernels add straight into sino_dev
+ * (one 64-byte request per detector row of a window column, where
+ * proj_forward adds into the handle's transposed sinogram, whole lines at a
+ * time, and unpacks it), so the cone forward runs slower here.
  * Every call on one GPU shares that array: two calls that can overlap in time
  * on one GPU (other streams, a replayed graph beside an eager call, any
  * handles) race and must be ordered by the caller.  Calls of proj_forward on
