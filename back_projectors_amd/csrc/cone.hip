@@ -408,8 +408,20 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
 // LDS no longer bounds the workgroups per CU.  Per voxel-view this does 2R+1 LDS
 // read-modify-writes on one column instead of (2R+1)^2 on the block, and the
 // (2R+1)^2 products become 2R+1 per slice and 2R+1 per row.
+// Waves per SIMD the compiler must fit (registers capped at 512 / waves).
+// Without a window in LDS the registers bound the occupancy, and more waves
+// hide more of the walk's LDS and memory latency, even at the price of a few
+// spilled registers: at radius 1 and 2, eight where one row group is one pass
+// (the helical scan: forward 47.0 -> 43.5 ms; radius 2 61.6 -> 60.1 ms), else
+// seven (the 256^3 cone: 8.87 -> 8.39 ms; eight there, 9.39 ms, spill too
+// much).  Radius 3 and 4 hold too many taps for that and are left free.
+template <int R, int NPG>
+constexpr int cone_fwd_waves() {
+    return R <= 2 ? (NPG == 1 ? 8 : 7) : 1;
+}
+
 template <int R, int P, bool U, int TY, int NPG>
-__global__ __launch_bounds__(CFW * 64) void cone_forward_kernel(const float *__restrict__ recon,
+__global__ __launch_bounds__(CFW * 64, (cone_fwd_waves<R, NPG>())) void cone_forward_kernel(const float *__restrict__ recon,
                                                                  float *__restrict__ sino,
                                                                  const int32_t *__restrict__ idx,
                                                                  const ViewK *__restrict__ views,
