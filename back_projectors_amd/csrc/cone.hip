@@ -410,14 +410,15 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
 // (2R+1)^2 products become 2R+1 per slice and 2R+1 per row.
 // Waves per SIMD the compiler must fit (registers capped at 512 / waves).
 // Without a window in LDS the registers bound the occupancy, and more waves
-// hide more of the walk's LDS and memory latency, even at the price of a few
-// spilled registers: at radius 1 and 2, eight where one row group is one pass
-// (the helical scan: forward 47.0 -> 43.5 ms; radius 2 61.6 -> 60.1 ms), else
-// seven (the 256^3 cone: 8.87 -> 8.39 ms; eight there, 9.39 ms, spill too
-// much).  Radius 3 and 4 hold too many taps for that and are left free.
+// hide more of the walk's LDS and memory latency, at the price of spilled
+// registers, whose traffic goes through the caches: six at radius 1 and 2
+// (20-40 bytes spilled per lane).  Measured, 5 / 6 / 7 or 8 waves: 256^3 cone
+// forward 8.92 / 8.68 / 8.42 ms with 1.2 / 3.7 / 9.1 GB fetched per call;
+// helical 47.2 / 45.0 / 43.8 ms with 8.8 / 10.8 / 66 GB.  Radius 3 and 4 hold
+// too many taps for that and are left free.
 template <int R, int NPG>
 constexpr int cone_fwd_waves() {
-    return R <= 2 ? (NPG == 1 ? 8 : 7) : 1;
+    return R <= 2 ? 6 : 1;
 }
 
 template <int R, int P, bool U, int TY, int NPG>
