@@ -71,14 +71,15 @@ def test_forward_back_graph_replays(bp, w, strategy):
     proj.close()
 
 
-@pytest.mark.parametrize("strategy", [1, 2], ids=["tile", "gather"])
-def test_replay_and_eager_forward_on_other_streams(bp, strategy):
-    """A replayed parallel forward and an eager one on another stream share
-    the handle's accumulation buffer, and inside a graph the library cannot
-    order them: the caller does, with an event after the replay and a stream
-    wait before the next replay.  Done that way, replay / eager / replay on
-    alternating streams all give the eager result."""
-    w = PAR_RAGGED
+@pytest.mark.parametrize("w,strategy", [(PAR_RAGGED, 1), (PAR_RAGGED, 2), (CONE_RAGGED, None)],
+                         ids=["tile", "gather", "cone"])
+def test_replay_and_eager_forward_on_other_streams(bp, w, strategy):
+    """A replayed forward and an eager one on another stream share a handle
+    buffer (the parallel accumulation buffer, the cone's transposed sinogram),
+    and inside a graph the library cannot order them: the caller does, with an
+    event after the replay and a stream wait before the next replay.  Done
+    that way, replay / eager / replay on alternating streams all give the
+    eager result."""
     note(f"replay then eager on another stream {w.name} strategy={strategy}")
     proj = bp.Projector(_geometry(w, strategy), w.recon_shape, w.sino_shape)
     x, _ = inputs(w)

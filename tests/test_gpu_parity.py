@@ -240,15 +240,17 @@ def test_repeat_calls_and_streams(bp):
     proj.close()
 
 
-@pytest.mark.parametrize("strategy", [1, 2], ids=["tile", "gather"])
-def test_parallel_forwards_on_two_streams(bp, orc, strategy):
-    """Parallel forwards share the handle's accumulation buffer: forwards of
-    different volumes issued on two streams back to back (no host sync between
-    them) are ordered on the GPU and each gets its own correct sinogram; so do
-    forwards interleaved with batch forwards on a third stream."""
-    w = PAR_RAGGED
+@pytest.mark.parametrize("w,strategy", [(PAR_RAGGED, 1), (PAR_RAGGED, 2), (CONE_RAGGED, None), (HELIX_SMALL, None)],
+                         ids=["tile", "gather", "cone", "helical"])
+def test_forwards_on_two_streams(bp, orc, w, strategy):
+    """Forwards share a handle buffer (the parallel accumulation buffer, the
+    cone's transposed sinogram): forwards of different volumes issued on two
+    streams back to back (no host sync between them) are ordered on the GPU
+    and each gets its own correct sinogram; so do forwards interleaved with
+    batch forwards on a third stream."""
     note(f"two-stream forwards {w.name} strategy={strategy}")
-    proj = bp.Projector(dict(w.geometry(), forward_strategy=strategy), w.recon_shape, w.sino_shape)
+    geo = w.geometry() if strategy is None else dict(w.geometry(), forward_strategy=strategy)
+    proj = bp.Projector(geo, w.recon_shape, w.sino_shape)
     g = orc.Geometry(w.geometry(), w.recon_shape, w.sino_shape)
     rng = np.random.default_rng(17)
     xs = [rng.standard_normal(w.recon_shape).astype(np.float32) for _ in range(4)]
