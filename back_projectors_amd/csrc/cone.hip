@@ -412,7 +412,7 @@ __global__ __launch_bounds__(BT *BT, 3) void cone_back_kernel(const float *__res
 // Without a window in LDS the registers bound the occupancy, and more waves
 // hide more of the walk's LDS and memory latency, at the price of spilled
 // registers, whose traffic goes through the caches: six at radius 1 and 2
-// (20-40 bytes spilled per lane).  Measured, 5 / 6 / 7 or 8 waves: 256^3 cone
+// (12-36 bytes spilled per lane).  Measured, 5 / 6 / 7 or 8 waves: 256^3 cone
 // forward 8.92 / 8.68 / 8.42 ms with 1.2 / 3.7 / 9.1 GB fetched per call;
 // helical 47.2 / 45.0 / 43.8 ms with 8.8 / 10.8 / 66 GB.  Radius 3 and 4 hold
 // too many taps for that and are left free.
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(CFW * 64, (cone_fwd_waves<R, NPG>())) void cone_for
         recon + ((int64_t)min(il, g.ny - 1) * g.nx + min(jl, g.nx - 1)) * g.ns + k0);
     const int cyl_lo = (int)(uint32_t)cyl, cyl_hi = (int)(uint32_t)(cyl >> 32);
 
-    // Per-view data, fetched two views ahead with vector loads: lanes 0-17
+    // Per-view data, fetched one view ahead with vector loads: lanes 0-17
     // hold the view's constants (ViewK, 18 dwords), lanes 18-21 its window,
     // lanes 22-25 its slab, and every lane the channel index of its pixel.
     static_assert(sizeof(ViewK) == 72, "ViewK is read as 18 dwords");
@@ -819,22 +819,19 @@ __global__ __launch_bounds__(CFW * 64, (cone_fwd_waves<R, NPG>())) void cone_for
                 for (int c = 0; c < (inter ? P : 1); ++c) prof[c * nrp + m] = 0.f;
     };
 
-    // three prefetch buffers in rotation: the view two turns ahead is loaded
-    // while this one is walked (no copies, so the waits stay narrow)
+    // two prefetch buffers in turn: the next view's data is loaded while this
+    // one is walked (no copies, so the waits stay narrow; a third buffer, two
+    // views ahead, gained nothing and held two more registers)
     if (wave >= cnt) return;
-    uint32_t pvA, pvB, pvC;
-    int pnA, pnB, pnC;
+    uint32_t pvA, pvB;
+    int pnA, pnB;
     prefetch(wave, pvA, pnA);
-    prefetch(wave + CFW, pvB, pnB);
-    for (int it = wave; it < cnt; it += 3 * CFW) {
-        prefetch(it + 2 * CFW, pvC, pnC);
+    for (int it = wave; it < cnt; it += 2 * CFW) {
+        prefetch(it + CFW, pvB, pnB);
         walk_view(it, pvA, pnA);
         if (it + CFW >= cnt) break;
-        prefetch(it + 3 * CFW, pvA, pnA);
+        prefetch(it + 2 * CFW, pvA, pnA);
         walk_view(it + CFW, pvB, pnB);
-        if (it + 2 * CFW >= cnt) break;
-        prefetch(it + 4 * CFW, pvB, pnB);
-        walk_view(it + 2 * CFW, pvC, pnC);
     }
 }
 
